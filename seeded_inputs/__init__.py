@@ -1,0 +1,129 @@
+"""Seeded synthetic inputs for triangle attention.
+
+This module only draws random tensors and builds key masks. It holds none of
+the method's arithmetic, so both the HIP path (through its tests and the bench)
+and the FP64 oracle can take their inputs from it without sharing any code.
+
+Shapes follow the Pairformer pair representation that the TurboPairFormer pages
+describe (crop sizes 384/640/768, "Результаты тестирования" / "crop size不是一个普通参数"):
+  q, k, v, dO : [B, N, N, H, D] bfloat16, element [b, i, j, h, c], c contiguous
+  bias        : [B, H, N, N]    bfloat16, element [b, h, j, k] (shared by all rows i)
+  mask        : [B, N, N]       uint8,    element [b, i, k], nonzero = key k attends
+
+The pages train on real OpenFold3 pair activations at those crop sizes; no dataset
+or trained weights are used here. i.i.d. normal tensors of the same shapes stand in
+for them, rounded to bfloat16 with round-to-nearest-even.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+# tensor tags: each tensor of a workload draws from its own generator,
+# seeded with seed * 16 + tag
+_TAG = {"q": 0, "k": 1, "v": 2, "do": 3, "bias": 4, "length": 5}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int          # 1-based position in the workload list; seed = 1000 + index
+    B: int
+    N: int
+    H: int
+    D: int
+    bias_std: float
+    mask: str           # "none" | "pad32" | "ragged512"
+    description: str
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.index
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("tiny64", 1, 1, 64, 4, 32, 1.0, "none",
+                 "B=1 N=64 H=4 d=32, all keys valid"),
+        Workload("pad256", 2, 1, 256, 4, 32, 1.0, "pad32",
+                 "B=1 N=256 H=4 d=32, last 32 keys of every row masked"),
+        Workload("crop384", 3, 1, 384, 4, 32, 1.0, "none",
+                 "B=1 N=384 H=4 d=32, all keys valid"),
+        Workload("crop640", 4, 1, 640, 4, 32, 4.0, "ragged512",
+                 "B=1 N=640 H=4 d=32, bias ~ N(0, 4^2), seeded valid length in [512, 640]"),
+        Workload("crop768", 5, 1, 768, 4, 32, 1.0, "none",
+                 "B=1 N=768 H=4 d=32, all keys valid (starting and ending node)"),
+    ]
+}
+
+
+def _gen(seed: int, tag: str) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed * 16 + _TAG[tag])
+    return g
+
+
+def _randn_bf16(shape, seed: int, tag: str, std: float = 1.0) -> torch.Tensor:
+    x = torch.randn(shape, generator=_gen(seed, tag), dtype=torch.float32)
+    if std != 1.0:
+        x = x * std
+    return x.to(torch.bfloat16)
+
+
+def make_mask(B: int, N: int, kind: str, seed: int) -> torch.Tensor:
+    """Key mask [B, N, N] uint8 (mask[b, i, k] != 0: key k is attended in row i)."""
+    m = torch.ones((B, N, N), dtype=torch.uint8)
+    if kind == "none":
+        return m
+    if kind == "pad32":
+        m[:, :, N - 32:] = 0
+        return m
+    if kind == "ragged512":
+        lengths = valid_lengths(B, N, kind, seed)
+        for b in range(B):
+            m[b, :, lengths[b]:] = 0
+        return m
+    if kind == "random":
+        g = _gen(seed, "length")
+        m = (torch.rand((B, N, N), generator=g) < 0.8).to(torch.uint8)
+        return m
+    raise ValueError(f"unknown mask kind {kind!r}")
+
+
+def valid_lengths(B: int, N: int, kind: str, seed: int) -> list[int]:
+    """Per-batch valid key length; for "ragged512" drawn uniformly from [512, N]."""
+    if kind == "ragged512":
+        g = _gen(seed, "length")
+        return [int(x) for x in torch.randint(512, N + 1, (B,), generator=g)]
+    if kind == "pad32":
+        return [N - 32] * B
+    return [N] * B
+
+
+def make_problem(B: int, N: int, H: int, D: int, seed: int, *,
+                 bias_std: float = 1.0, mask: str = "none") -> dict:
+    """Seeded bf16 inputs of one triangle-attention problem (CPU tensors)."""
+    shp = (B, N, N, H, D)
+    return {
+        "q": _randn_bf16(shp, seed, "q"),
+        "k": _randn_bf16(shp, seed, "k"),
+        "v": _randn_bf16(shp, seed, "v"),
+        "do": _randn_bf16(shp, seed, "do"),
+        "bias": _randn_bf16((B, H, N, N), seed, "bias", bias_std),
+        "mask": make_mask(B, N, mask, seed),
+    }
+
+
+def make_workload(name: str) -> dict:
+    w = WORKLOADS[name]
+    return make_problem(w.B, w.N, w.H, w.D, w.seed, bias_std=w.bias_std, mask=w.mask)
+
+
+def flop_count(B: int, N: int, H: int, D: int, mask: torch.Tensor | None) -> int:
+    """Algorithmic fwd+bwd FLOP count: 2 forward and 5 backward products of
+    2*D flop per valid (b, i, h, j, k) score element (exp and the bias-gradient
+    adds are not counted)."""
+    valid = N * N * B if mask is None else int(mask.to(torch.int64).sum())
+    return 14 * D * H * N * valid
