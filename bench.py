@@ -1,0 +1,188 @@
+#!/usr/bin/env python3
+"""Triangle-attention forward+backward throughput on one MI355X.
+
+Workload: the crop-768 Pairformer configuration (B=1, N=768, H=4, D=32, bf16
+q, k, v, dO and bias drawn N(0,1) from a fixed seed, all keys attended,
+starting node).  One step = tri_attn_fwd followed by tri_attn_bwd (every
+kernel of the path) on inputs already resident in HBM.  The metric is
+algorithmic TFLOP/s: 14 * D flop per valid score element (two forward and five
+backward products; exp and the bias-gradient additions are not counted).
+
+The JSON line also carries
+  roofline     : the backward main kernel (the dominant one), timed with HIP
+                 events recorded by the library on the launch stream, against
+                 the MI355X dense bf16 MFMA peak;
+  cpu_baseline : the FP64 oracle timed on this host on a bounded sample of the
+                 same workload (sampled attention rows and bias-gradient rows),
+                 scaled to the whole workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+MFMA_PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (published)
+HBM_PEAK_GBS = 8000.0
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch has already loaded (the
+    library records them on the launch stream; torch's own Event objects are
+    created lazily and cannot be handed to it before their first record)."""
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        e = self.ct.c_void_p()
+        if self.hip.hipEventCreate(self.ct.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, e: int) -> None:
+        self.hip.hipEventDestroy(e)
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(inp, rows: int, dbias_rows: int):
+    """Oracle time on `rows` attention rows (o, lse, dq, dk, dv) plus `dbias_rows`
+    bias-gradient rows, scaled to the full problem."""
+    import numpy as np
+    import oracle
+    import seeded_inputs as si
+
+    B, N, _, H, D = inp["q"].shape
+    threads = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    p = oracle.Problem(inp["q"], inp["k"], inp["v"], inp["bias"], inp["mask"], inp["do"])
+    rng = np.random.default_rng(0)
+    sel_rows = [(0, int(r)) for r in rng.choice(N, size=min(rows, N), replace=False)]
+    sel_db = [(0, int(h), int(j)) for h, j in zip(rng.integers(0, H, dbias_rows),
+                                                  rng.integers(0, N, dbias_rows))]
+    t0 = time.perf_counter()
+    p.rows(sel_rows)
+    t1 = time.perf_counter()
+    p.dbias(sel_db)
+    t2 = time.perf_counter()
+    t_full = (t1 - t0) * (B * N / len(sel_rows)) + (t2 - t1) * (B * H * N / len(sel_db))
+    flops = si.flop_count(B, N, H, D, inp["mask"])
+    return {
+        "value": flops / t_full / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(os.environ.get("OMP_NUM_THREADS", threads)),
+        "kind": "oracle",
+        "sample": (f"{len(sel_rows)} of {B * N} attention rows (forward and q/k/v gradients, "
+                   f"{t1 - t0:.1f} s) and {len(sel_db)} of {B * H * N} bias-gradient rows "
+                   f"({t2 - t1:.1f} s), scaled to the whole workload; est. {t_full:.0f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="crop768")
+    ap.add_argument("--ending", action="store_true", help="ending-node orientation")
+    ap.add_argument("--cpu-rows", type=int, default=48)
+    ap.add_argument("--cpu-dbias-rows", type=int, default=96)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
+                                   "supported (use --gpus 1)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import seeded_inputs as si
+    import triangle_attention_amd as ta
+
+    w = si.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log(f"workload {w.name}: {w.description}")
+    inp = si.make_workload(w.name)
+    g = {k: v.to(dev) for k, v in inp.items()}
+    mask = g["mask"] if w.mask != "none" else None
+    ta.load_library()
+    ws = torch.empty(ta.bwd_workspace_bytes(w.B, w.N, w.H, w.D, ending=args.ending),
+                     dtype=torch.uint8, device=dev)
+
+    def step(events=None):
+        o, res, lse = ta.tri_attn_fwd(g["q"], g["k"], g["v"], g["bias"], mask, ending=args.ending)
+        return ta.tri_attn_bwd(g["q"], g["k"], g["v"], g["bias"], mask, o, res, lse, g["do"],
+                               ending=args.ending, workspace=ws, main_events=events)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    hip = HipEvents()
+    ev = [(hip.create(), hip.create()) for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    main_ms = sum(hip.elapsed_ms(a, b) for a, b in ev) / args.steps
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
+    log(f"{ms:.3f} ms/step, backward main kernel {main_ms:.3f} ms")
+
+    flops = si.flop_count(w.B, w.N, w.H, w.D, inp["mask"])
+    value = flops / (ms * 1e-3) / 1e12
+    bwd_main_flops = flops * 10 / 14   # S, dP, dV, dK, dQ products of the backward
+    achieved = bwd_main_flops / (main_ms * 1e-3) / 1e12
+    line = {
+        "metric": "triangle-attn fwd+bwd TFLOP/s at N=768 bf16; % of MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name} ({w.description})", "B": w.B, "N": w.N, "H": w.H,
+                   "D": w.D, "orientation": "ending" if args.ending else "starting",
+                   "mfma_peak_frac": round(value / MFMA_PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"kernel": "bwd_main_kernel", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_ms": round(main_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle sample)")
+        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows, args.cpu_dbias_rows)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,35 @@
+"""Compile the gfx950 HIP library in-tree: triangle_attention_amd/libtri_attn.so."""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from pathlib import Path
+
+HERE = Path(__file__).resolve().parent
+ROOT = HERE.parent
+SRC = HERE / "csrc" / "tri_attn.hip"
+LIB = HERE / "libtri_attn.so"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+# Packed fp32 VALU forms are disabled for all device code (-packed-fp32-ops).
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wno-unused-command-line-argument"]
+
+
+def build(verbose: bool = False) -> Path:
+    tmp = LIB.with_suffix(".so.tmp")
+    cmd = [HIPCC, *FLAGS, "-I", str(ROOT / "include"), "-o", str(tmp), str(SRC)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc failed building {SRC}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

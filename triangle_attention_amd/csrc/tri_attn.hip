@@ -1,0 +1,892 @@
+// Triangle attention forward and backward for MI355X (gfx950, CDNA4).
+//
+// Operation: TurboPairFormer pages (Lambda post, "Как работает TurboPairFormer";
+// biocloudservice page, "它优化了什么").  Each attention row r of the pair tensor
+// is an independent softmax-attention problem over N queries and N keys (head
+// dim 32) whose logits also get a pair bias shared by all rows and a key mask.
+//
+// Kernels
+//   fwd       flash-style forward: S^T = K Q^T on MFMA with the scaled pair bias
+//             as the accumulator's initial value, online softmax in fp32, O^T =
+//             V^T P^T on MFMA; writes bf16 o, its exact fp32 rounding residual
+//             and the fp32 log-sum-exp.
+//   bwd_prep  D = rowsum(dO * (o + residual)) in fp32, fixed channel order.
+//   bwd_main  key-block-parallel backward: one workgroup owns a block of keys
+//             for a chunk of rows and every query; each probability tile is
+//             recomputed once from the saved log-sum-exp and feeds dV, dK, dQ
+//             and dbias.  dK/dV are reduced across waves in a fixed order, dbias
+//             accumulates over the chunk's rows in registers, dQ leaves one fp32
+//             partial per key block.
+//   bwd_reduce fixed-order sums of the dQ partials (over key blocks) and the
+//             dbias partials (over row chunks).
+// No floating-point atomics are used anywhere, so results are bitwise
+// reproducible (Lambda post, third point of "Как работает TurboPairFormer").
+//
+// MFMA layouts used (v_mfma_f32_32x32x16_bf16, 64 lanes, hh = lane / 32):
+//   A (32 x 16): lane supplies A[lane % 32][8*hh + e], e = 0..7
+//   B (16 x 32): lane supplies B[8*hh + e][lane % 32]
+//   C (32 x 32): lane holds C[8*(r/4) + 4*hh + r%4][lane % 32], r = 0..15
+// ds_read_b64_tr_b16: in each 16-lane group, lane 4*m + s addresses 4 consecutive
+// 16-bit values forming columns 4s..4s+3 of row m of a 4x16 block; lane c of the
+// group receives column c of rows 0..3.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+#include <math.h>
+
+#include "tri_attn.h"
+
+namespace {
+
+constexpr int HD = 32;  // head dimension handled by this build
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *(const u32x4 *)p; }
+__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+// round-to-nearest-even pack of two floats (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+  bf16x2 r = __builtin_convertvector((f32x2){a, b}, bf16x2);
+  return __builtin_bit_cast(unsigned, r);
+}
+__device__ __forceinline__ bf16x8 pack8(const float *x) {
+  u32x4 w = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
+  return as_bf16x8(w);
+}
+// Two transposing LDS reads forming one 8-element MFMA operand.
+__device__ __forceinline__ bf16x8 tr_read(const uint16_t *p0, const uint16_t *p1) {
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p0);
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p1);
+  typedef __attribute__((ext_vector_type(8))) short i16x8;
+  i16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+// Transposed operand of a row-major [rows][32] bf16 tile in LDS: lane gets
+// column (lane % 32) of rows base + {4*hh + 0..3} and base + 8 + {4*hh + 0..3}.
+// This is the contraction order shared with the accumulator-derived operands.
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t *tile, int base_row, int lane) {
+  const int g = lane >> 4, w = lane & 15, m = w >> 2, s = w & 3;
+  const int col = 16 * (g & 1) + 4 * s;
+  const int row = base_row + 4 * (g >> 1) + m;
+  return tr_read(tile + row * HD + col, tile + (row + 8) * HD + col);
+}
+
+// Workgroup index -> tile index such that consecutive tiles share an XCD
+// (workgroups are dealt to the 8 XCDs round-robin).
+__device__ __forceinline__ int xcd_remap(int L, int G) {
+  const int per = G >> 3;
+  if (L < (per << 3)) return (L & 7) * per + (L >> 3);
+  return L;
+}
+
+struct Frame {
+  long long sB, sR, sQ;  // element strides of [B,N,N,H,D] tensors: batch, attention row, position
+  long long mB, mR, mK;  // mask strides: batch, attention row, key
+};
+
+// ------------------------------------------------------------------------------------
+// Forward
+// ------------------------------------------------------------------------------------
+constexpr int FWD_WAVES = 8;
+constexpr int FWD_BJ = 32;
+
+struct FwdArgs {
+  const uint16_t *q, *k, *v, *bias;
+  const uint8_t *mask;
+  uint16_t *o;
+  float *res, *lse;
+  Frame f;
+  int B, N, H;
+  int n_jblocks, n_chunks, rows_per_chunk;
+  float alpha, inv_alpha, c1;  // c1 = alpha * log2(e)
+};
+
+__global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
+  extern __shared__ float4 smem_f4[];
+  float *bias_s = (float *)smem_f4;
+  const int N = a.N;
+  const int bstride = N + 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int jl = lane & 31, hh = lane >> 5;
+  int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int jb = t % a.n_jblocks; t /= a.n_jblocks;
+  const int chunk = t % a.n_chunks; t /= a.n_chunks;
+  const int h = t % a.H;
+  const int b = t / a.H;
+  const int j0 = jb * FWD_BJ;
+  uint16_t *vbuf = (uint16_t *)(bias_s + FWD_BJ * bstride) + wave * (32 * HD);
+
+  // pair bias of this query block, scaled by 1/alpha: the MFMA then yields
+  // q.k + bias/alpha, i.e. the logit divided by alpha.
+  {
+    const uint16_t *src = a.bias + (((long long)b * a.H + h) * N + j0) * N;
+    const int per_row = N / 8;
+    for (int idx = tid; idx < FWD_BJ * per_row; idx += FWD_WAVES * 64) {
+      const int row = idx / per_row, c8 = idx - row * per_row;
+      const u32x4 w = ld16(src + (long long)row * N + c8 * 8);
+      float *dst = bias_s + row * bstride + c8 * 8;
+      f32x4 lo = {bf_lo(w[0]) * a.inv_alpha, bf_hi(w[0]) * a.inv_alpha, bf_lo(w[1]) * a.inv_alpha,
+                  bf_hi(w[1]) * a.inv_alpha};
+      f32x4 hi = {bf_lo(w[2]) * a.inv_alpha, bf_hi(w[2]) * a.inv_alpha, bf_lo(w[3]) * a.inv_alpha,
+                  bf_hi(w[3]) * a.inv_alpha};
+      *(f32x4 *)dst = lo;
+      *(f32x4 *)(dst + 4) = hi;
+    }
+  }
+  __syncthreads();
+
+  const int r0 = chunk * a.rows_per_chunk;
+  const int r1 = min(N, r0 + a.rows_per_chunk);
+  const float c1 = a.c1;
+  for (int r = r0 + wave; r < r1; r += FWD_WAVES) {
+    const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
+    const uint16_t *qp = a.q + base + (long long)(j0 + jl) * a.f.sQ;
+    const bf16x8 qB0 = as_bf16x8(ld16(qp + 8 * hh));
+    const bf16x8 qB1 = as_bf16x8(ld16(qp + 16 + 8 * hh));
+    const uint8_t *mrow = a.mask ? a.mask + (long long)b * a.f.mB + (long long)r * a.f.mR : nullptr;
+
+    float m = -INFINITY;  // running max of the lane's query, in logit/alpha units
+    float lsum = 0.f;
+    f32x16 oacc = {};
+    for (int kt = 0; kt < N / 32; ++kt) {
+      unsigned valid = 0xffffffffu;
+      if (mrow) {
+        const uint8_t mv = mrow[(long long)(kt * 32 + jl) * a.f.mK];
+        valid = (unsigned)__ballot(mv != 0);
+      }
+      if (valid == 0u) continue;
+      const uint16_t *kp = a.k + base + (long long)(kt * 32 + jl) * a.f.sQ;
+      const bf16x8 kA0 = as_bf16x8(ld16(kp + 8 * hh));
+      const bf16x8 kA1 = as_bf16x8(ld16(kp + 16 + 8 * hh));
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int ch = lane + 64 * u, key = ch >> 2, part = ch & 3;
+        const u32x4 w = ld16(a.v + base + (long long)(kt * 32 + key) * a.f.sQ + part * 8);
+        *(u32x4 *)(vbuf + key * HD + part * 8) = w;
+      }
+      f32x16 acc;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 bv = *(const f32x4 *)(bias_s + jl * bstride + kt * 32 + 8 * g + 4 * hh);
+        acc[4 * g + 0] = bv[0];
+        acc[4 * g + 1] = bv[1];
+        acc[4 * g + 2] = bv[2];
+        acc[4 * g + 3] = bv[3];
+      }
+      acc = mfma(kA0, qB0, acc);
+      acc = mfma(kA1, qB1, acc);
+      if (valid != 0xffffffffu) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kl = 8 * (i >> 2) + 4 * hh + (i & 3);
+          if (!((valid >> kl) & 1u)) acc[i] = -INFINITY;
+        }
+      }
+      float mt = acc[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, acc[i]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mnew = fmaxf(m, mt);
+      const float sc = __builtin_amdgcn_exp2f((m - mnew) * c1);
+      lsum *= sc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[i] *= sc;
+      m = mnew;
+      const float negm = -m * c1;
+      float p[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(fmaf(acc[i], c1, negm));
+        lsum += p[i];
+      }
+      const bf16x8 pB0 = pack8(p);
+      const bf16x8 pB1 = pack8(p + 8);
+      const bf16x8 vA0 = tr_operand(vbuf, 0, lane);
+      const bf16x8 vA1 = tr_operand(vbuf, 16, lane);
+      oacc = mfma(vA0, pB0, oacc);
+      oacc = mfma(vA1, pB1, oacc);
+    }
+    lsum += __shfl_xor(lsum, 32);
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    const long long obase = base + (long long)(j0 + jl) * a.f.sQ;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      float ov[4], rv[4];
+      unsigned pk[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[i] = oacc[4 * g + i] * inv;
+      pk[0] = pack_bf16(ov[0], ov[1]);
+      pk[1] = pack_bf16(ov[2], ov[3]);
+      rv[0] = ov[0] - bf_lo(pk[0]);
+      rv[1] = ov[1] - bf_hi(pk[0]);
+      rv[2] = ov[2] - bf_lo(pk[1]);
+      rv[3] = ov[3] - bf_hi(pk[1]);
+      const int c = 8 * g + 4 * hh;
+      *(u32x2 *)(a.o + obase + c) = (u32x2){pk[0], pk[1]};
+      if (a.res) *(f32x4 *)(a.res + obase + c) = (f32x4){rv[0], rv[1], rv[2], rv[3]};
+    }
+    if (hh == 0) {
+      const float L = lsum > 0.f ? a.alpha * m + logf(lsum) : INFINITY;
+      a.lse[(((long long)b * N + r) * a.H + h) * N + j0 + jl] = L;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Backward: D = rowsum(dO * O) in fp32 (O = float(o) + residual when saved)
+// ------------------------------------------------------------------------------------
+struct PrepArgs {
+  const uint16_t *o, *d_o;
+  const float *res;
+  float *delta;
+  Frame f;
+  int B, N, H;
+};
+
+__global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
+  const long long total = (long long)a.B * a.N * a.H * a.N;
+  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int q = (int)(idx % a.N);
+  long long t = idx / a.N;
+  const int h = (int)(t % a.H);
+  t /= a.H;
+  const int r = (int)(t % a.N);
+  const int b = (int)(t / a.N);
+  const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)q * a.f.sQ + h * HD;
+  float acc = 0.f;
+#pragma unroll
+  for (int c8 = 0; c8 < HD; c8 += 8) {
+    const u32x4 gw = ld16(a.d_o + base + c8);
+    const u32x4 ow = ld16(a.o + base + c8);
+    float ov[8], gv[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ov[2 * i] = bf_lo(ow[i]);
+      ov[2 * i + 1] = bf_hi(ow[i]);
+      gv[2 * i] = bf_lo(gw[i]);
+      gv[2 * i + 1] = bf_hi(gw[i]);
+    }
+    if (a.res) {
+      const f32x4 r0 = *(const f32x4 *)(a.res + base + c8);
+      const f32x4 r1 = *(const f32x4 *)(a.res + base + c8 + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ov[i] += r0[i];
+        ov[4 + i] += r1[i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf(gv[i], ov[i], acc);
+  }
+  a.delta[idx] = acc;
+}
+
+// ------------------------------------------------------------------------------------
+// Backward main kernel
+// ------------------------------------------------------------------------------------
+constexpr int BWD_WAVES = 4;
+
+struct BwdArgs {
+  const uint16_t *q, *k, *v, *bias, *d_o;
+  const uint8_t *mask;
+  const float *lse, *delta;
+  uint16_t *dk, *dv;
+  float *dq_part;  // [T][B][N][N][H][D], attended frame
+  float *db_part;  // [C][B][H][N][N]
+  Frame f;
+  int B, N, H;
+  int n_kblocks, n_chunks, rows_per_chunk;
+  float alpha, c1;
+};
+
+template <int KT, int JT>
+__global__ __launch_bounds__(BWD_WAVES * 64) void bwd_main_kernel(BwdArgs a) {
+  constexpr int BK = 32 * KT;  // keys per workgroup
+  extern __shared__ float4 smem_f4[];
+  const int N = a.N;
+  const int bstr = N + 8;  // bf16 row stride of the transposed bias tile
+  uint16_t *biasT = (uint16_t *)smem_f4;             // [BK][N (+8)]: bias[j][k] stored at [k][j]
+  uint16_t *kbuf = biasT + BK * bstr;                // [BK][32]
+  uint16_t *vbuf = kbuf + BK * HD;                   // [BK][32]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hh = lane >> 5, ll = lane & 31;
+  constexpr int WAVE_ELEMS = (64 + BK) * HD;          // q, dO tiles and dS^T tile, bf16
+  uint16_t *wq = vbuf + BK * HD + wave * WAVE_ELEMS;  // [32][32]
+  uint16_t *wdo = wq + 32 * HD;                       // [32][32]
+  uint16_t *wds = wdo + 32 * HD;                      // [BK][32]: dS^T of the current query tile
+  float *wred = (float *)wq;                          // [BK][32] fp32 reduction slot (reuses the above)
+
+  int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int kb = t % a.n_kblocks; t /= a.n_kblocks;
+  const int chunk = t % a.n_chunks; t /= a.n_chunks;
+  const int h = t % a.H;
+  const int b = t / a.H;
+  const int k0 = kb * BK;
+  const int njt = N / 32;
+
+  // transposed pair-bias tile: biasT[kk][j] = bias[b, h, j, k0 + kk]
+  {
+    const uint16_t *src = a.bias + ((long long)b * a.H + h) * N * N + k0;
+    constexpr int per_row = BK / 8;
+    for (int idx = tid; idx < N * per_row; idx += BWD_WAVES * 64) {
+      const int j = idx / per_row, c8 = idx - j * per_row;
+      const u32x4 w = ld16(src + (long long)j * N + c8 * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        biasT[(c8 * 8 + 2 * i) * bstr + j] = (uint16_t)(w[i] & 0xffffu);
+        biasT[(c8 * 8 + 2 * i + 1) * bstr + j] = (uint16_t)(w[i] >> 16);
+      }
+    }
+  }
+
+  float dbias[JT][KT][16];
+#pragma unroll
+  for (int jj = 0; jj < JT; ++jj)
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dbias[jj][kt][i] = 0.f;
+
+  const int r0 = chunk * a.rows_per_chunk;
+  const int r1 = min(N, r0 + a.rows_per_chunk);
+  const float c1 = a.c1;
+  const long long E = (long long)a.B * N * N * a.H * HD;
+  float *dq_part = a.dq_part + (long long)kb * E;
+
+  for (int r = r0; r < r1; ++r) {
+    const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
+    // stage this row's keys and values of the block
+    for (int ch = tid; ch < 2 * BK * 4; ch += BWD_WAVES * 64) {
+      const int which = ch / (BK * 4), rem = ch - which * BK * 4, key = rem >> 2, part = rem & 3;
+      const uint16_t *src = (which ? a.v : a.k) + base + (long long)(k0 + key) * a.f.sQ + part * 8;
+      *(u32x4 *)((which ? vbuf : kbuf) + key * HD + part * 8) = ld16(src);
+    }
+    // keys of the block this lane owns in the score layout, and their mask
+    bool kvalid[KT];
+    unsigned tile_full = 1u;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      bool ok = true;
+      if (a.mask)
+        ok = a.mask[(long long)b * a.f.mB + (long long)r * a.f.mR + (long long)(k0 + 32 * kt + ll) * a.f.mK] != 0;
+      kvalid[kt] = ok;
+      if (__ballot(ok) != ~0ull) tile_full = 0u;
+    }
+    __syncthreads();
+
+    bf16x8 kB[KT][2], vB[KT][2], kT[2 * KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      const uint16_t *kr = kbuf + (32 * kt + ll) * HD;
+      const uint16_t *vr = vbuf + (32 * kt + ll) * HD;
+      kB[kt][0] = as_bf16x8(*(const u32x4 *)(kr + 8 * hh));
+      kB[kt][1] = as_bf16x8(*(const u32x4 *)(kr + 16 + 8 * hh));
+      vB[kt][0] = as_bf16x8(*(const u32x4 *)(vr + 8 * hh));
+      vB[kt][1] = as_bf16x8(*(const u32x4 *)(vr + 16 + 8 * hh));
+    }
+#pragma unroll
+    for (int s = 0; s < 2 * KT; ++s) kT[s] = tr_operand(kbuf, 16 * s, lane);
+
+    f32x16 dK[KT], dV[KT];
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt) {
+      dK[kt] = (f32x16){};
+      dV[kt] = (f32x16){};
+    }
+
+#pragma unroll
+    for (int jj = 0; jj < JT; ++jj) {
+      const int jt = wave + BWD_WAVES * jj;
+      if (jt >= njt) break;
+      const int j0 = jt * 32;
+      // stage the query and upstream-gradient tiles of this query block
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int ch = lane + 64 * u, which = ch >> 7, rem = ch & 127, jr = rem >> 2, part = rem & 3;
+        const uint16_t *src = (which ? a.d_o : a.q) + base + (long long)(j0 + jr) * a.f.sQ + part * 8;
+        *(u32x4 *)((which ? wdo : wq) + jr * HD + part * 8) = ld16(src);
+      }
+      const bf16x8 qA0 = as_bf16x8(*(const u32x4 *)(wq + ll * HD + 8 * hh));
+      const bf16x8 qA1 = as_bf16x8(*(const u32x4 *)(wq + ll * HD + 16 + 8 * hh));
+      const bf16x8 dA0 = as_bf16x8(*(const u32x4 *)(wdo + ll * HD + 8 * hh));
+      const bf16x8 dA1 = as_bf16x8(*(const u32x4 *)(wdo + ll * HD + 16 + 8 * hh));
+      const bf16x8 qB0 = tr_operand(wq, 0, lane);
+      const bf16x8 qB1 = tr_operand(wq, 16, lane);
+      const bf16x8 dB0 = tr_operand(wdo, 0, lane);
+      const bf16x8 dB1 = tr_operand(wdo, 16, lane);
+      // per-query statistics for the lane's 16 queries j0 + 8g + 4hh + i
+      float L2[16];
+      f32x16 negD;
+      const long long sbase = (((long long)b * N + r) * a.H + h) * N + j0 + 4 * hh;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 lv = *(const f32x4 *)(a.lse + sbase + 8 * g);
+        const f32x4 dv4 = *(const f32x4 *)(a.delta + sbase + 8 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          L2[4 * g + i] = lv[i] * kLog2e;
+          negD[4 * g + i] = -dv4[i];
+        }
+      }
+
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        f32x16 s = {};
+        s = mfma(qA0, kB[kt][0], s);
+        s = mfma(qA1, kB[kt][1], s);
+        f32x16 dp = mfma(dA0, vB[kt][0], negD);  // dP - D
+        dp = mfma(dA1, vB[kt][1], dp);
+        const uint16_t *brow = biasT + (32 * kt + ll) * bstr + j0 + 4 * hh;
+        float p[16], ds[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x2 bw = *(const u32x2 *)(brow + 8 * g);
+          const float beta[4] = {bf_lo(bw[0]), bf_hi(bw[0]), bf_lo(bw[1]), bf_hi(bw[1])};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int idx = 4 * g + i;
+            const float u = fmaf(s[idx], c1, fmaf(beta[i], kLog2e, -L2[idx]));
+            p[idx] = __builtin_amdgcn_exp2f(u);
+          }
+        }
+        if (!tile_full && !kvalid[kt]) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) p[i] = 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          ds[i] = p[i] * dp[i];
+          dbias[jj][kt][i] += ds[i];
+        }
+        const bf16x8 pA0 = pack8(p), pA1 = pack8(p + 8);
+        const bf16x8 sA0 = pack8(ds), sA1 = pack8(ds + 8);
+        dV[kt] = mfma(pA0, dB0, dV[kt]);
+        dV[kt] = mfma(pA1, dB1, dV[kt]);
+        dK[kt] = mfma(sA0, qB0, dK[kt]);
+        dK[kt] = mfma(sA1, qB1, dK[kt]);
+        // dS^T rows of this key tile for the dQ product
+        const u32x4 s0 = __builtin_bit_cast(u32x4, sA0), s1 = __builtin_bit_cast(u32x4, sA1);
+        uint16_t *drow = wds + (32 * kt + ll) * HD + 4 * hh;
+        *(u32x2 *)(drow + 0) = (u32x2){s0[0], s0[1]};
+        *(u32x2 *)(drow + 8) = (u32x2){s0[2], s0[3]};
+        *(u32x2 *)(drow + 16) = (u32x2){s1[0], s1[1]};
+        *(u32x2 *)(drow + 24) = (u32x2){s1[2], s1[3]};
+      }
+      // dQ partial of this key block: dS (32 queries x BK keys) times K (BK x 32)
+      f32x16 dq = {};
+#pragma unroll
+      for (int s = 0; s < 2 * KT; ++s) dq = mfma(tr_operand(wds, 16 * s, lane), kT[s], dq);
+      float *qout = dq_part + ((((long long)b * N + r) * N + j0) * a.H + h) * HD + ll;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int jrow = 8 * (i >> 2) + 4 * hh + (i & 3);
+        qout[(long long)jrow * a.H * HD] = dq[i];
+      }
+    }
+
+    // fixed-order cross-wave reduction of dV then dK for this row
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      __syncthreads();
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const f32x16 &acc = which ? dK[kt] : dV[kt];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int krow = 32 * kt + 8 * (i >> 2) + 4 * hh + (i & 3);
+          wred[krow * HD + ll] = acc[i];
+        }
+      }
+      __syncthreads();
+      const float scale = which ? a.alpha : 1.f;
+      uint16_t *dst = which ? a.dk : a.dv;
+      for (int e = tid * 4; e < BK * HD; e += BWD_WAVES * 64 * 4) {
+        const int kr = e / HD, c = e - kr * HD;
+        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < BWD_WAVES; ++w) {
+          const f32x4 part = *(const f32x4 *)((const float *)(vbuf + BK * HD + w * WAVE_ELEMS) + e);
+          sum += part;
+        }
+        sum *= scale;
+        const long long off = base + (long long)(k0 + kr) * a.f.sQ + c;
+        *(u32x2 *)(dst + off) = (u32x2){pack_bf16(sum[0], sum[1]), pack_bf16(sum[2], sum[3])};
+      }
+    }
+    __syncthreads();
+  }
+
+  // dbias partial of this row chunk for the block's keys and every query
+  float *dbo = a.db_part + (((long long)chunk * a.B + b) * a.H + h) * N * N + k0;
+#pragma unroll
+  for (int jj = 0; jj < JT; ++jj) {
+    const int jt = wave + BWD_WAVES * jj;
+    if (jt >= njt) break;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = jt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+        dbo[(long long)j * N + 32 * kt + ll] = dbias[jj][kt][i];
+      }
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Backward: fixed-order reductions of the partials
+// ------------------------------------------------------------------------------------
+struct ReduceArgs {
+  const float *dq_part, *db_part;
+  uint16_t *dq;
+  void *dbias;
+  Frame f;
+  int B, N, H, T, C, dbias_fp32;
+  float alpha;
+};
+
+__global__ __launch_bounds__(256) void reduce_dq_kernel(ReduceArgs a) {
+  const long long E = (long long)a.B * a.N * a.N * a.H * HD;
+  const long long e = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (e >= E) return;
+  f32x4 s = *(const f32x4 *)(a.dq_part + e);
+  for (int t = 1; t < a.T; ++t) s += *(const f32x4 *)(a.dq_part + (long long)t * E + e);
+  s *= a.alpha;
+  // attended-frame element (b, r, q, h, c) -> caller's frame
+  const int c = (int)(e % HD);
+  long long u = e / HD;
+  const int h = (int)(u % a.H);
+  u /= a.H;
+  const int q = (int)(u % a.N);
+  u /= a.N;
+  const int r = (int)(u % a.N);
+  const int b = (int)(u / a.N);
+  const long long off = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)q * a.f.sQ + h * HD + c;
+  *(u32x2 *)(a.dq + off) = (u32x2){pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3])};
+}
+
+__global__ __launch_bounds__(256) void reduce_dbias_kernel(ReduceArgs a) {
+  const long long E = (long long)a.B * a.H * a.N * a.N;
+  const long long e = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (e >= E) return;
+  f32x4 s = *(const f32x4 *)(a.db_part + e);
+  for (int c = 1; c < a.C; ++c) s += *(const f32x4 *)(a.db_part + (long long)c * E + e);
+  if (a.dbias_fp32) {
+    *(f32x4 *)((float *)a.dbias + e) = s;
+  } else {
+    *(u32x2 *)((uint16_t *)a.dbias + e) = (u32x2){pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3])};
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Host side
+// ------------------------------------------------------------------------------------
+constexpr int64_t kMaxN = 768;
+constexpr int64_t kMaxH = 64;
+
+bool aligned16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range span(const void *p, size_t bytes) { return {(uintptr_t)p, (uintptr_t)p + bytes}; }
+bool overlap(Range x, Range y) { return x.lo < y.hi && y.lo < x.hi; }
+
+tri_attn_status check_problem(const tri_attn_problem *p) {
+  if (!p) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (p->abi_version != TRI_ATTN_ABI_VERSION) return TRI_ATTN_ERROR_ABI_MISMATCH;
+  if (p->B < 1 || p->N < 1 || p->H < 1 || p->D < 1) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (p->flags & ~(TRI_ATTN_FLAG_ENDING_NODE | TRI_ATTN_FLAG_DBIAS_FP32)) return TRI_ATTN_ERROR_NOT_SUPPORTED;
+  if (p->D != HD || p->N % 32 != 0 || p->N > kMaxN || p->H > kMaxH) return TRI_ATTN_ERROR_NOT_SUPPORTED;
+  if (p->B * p->N * p->N * p->H * p->D > (int64_t)1 << 40) return TRI_ATTN_ERROR_NOT_SUPPORTED;
+  return TRI_ATTN_SUCCESS;
+}
+
+Frame make_frame(const tri_attn_problem *p) {
+  Frame f;
+  const long long N = p->N, H = p->H;
+  f.sB = N * N * H * HD;
+  f.mB = N * N;
+  if (p->flags & TRI_ATTN_FLAG_ENDING_NODE) {
+    f.sR = H * HD;
+    f.sQ = N * H * HD;
+    f.mR = 1;
+    f.mK = N;
+  } else {
+    f.sR = N * H * HD;
+    f.sQ = H * HD;
+    f.mR = N;
+    f.mK = 1;
+  }
+  return f;
+}
+
+float alpha_of(const tri_attn_problem *p) {
+  return p->softmax_scale > 0.f ? p->softmax_scale : 1.f / sqrtf((float)p->D);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct BwdPlan {
+  int KT, JT, T, C, rows_per_chunk;
+  size_t lds_bytes;
+  size_t off_delta, off_dq, off_db, total;
+};
+
+BwdPlan plan_bwd(const tri_attn_problem *p) {
+  BwdPlan pl;
+  const int N = (int)p->N;
+  const int njt = N / 32;
+  pl.JT = (njt + BWD_WAVES - 1) / BWD_WAVES;
+  pl.KT = pl.JT <= 5 ? 2 : 1;
+  const int BK = 32 * pl.KT;
+  pl.T = N / BK;
+  if (N % BK) {  // N = 32 * odd: fall back to one key tile per workgroup
+    pl.KT = 1;
+    pl.T = N / 32;
+  }
+  const int groups = (int)(p->B * p->H * pl.T);
+  const int per_cu = pl.KT == 2 ? 1 : 2;
+  int C = (256 * per_cu) / groups;
+  if (C < 1) C = 1;
+  if (C > N) C = N;
+  pl.rows_per_chunk = (N + C - 1) / C;
+  pl.C = (N + pl.rows_per_chunk - 1) / pl.rows_per_chunk;
+  const int BKk = 32 * pl.KT;
+  pl.lds_bytes = (size_t)BKk * (N + 8) * 2 + (size_t)2 * BKk * HD * 2 +
+                 (size_t)BWD_WAVES * (64 + BKk) * HD * 2;
+  const size_t B = p->B, NN = (size_t)N * N, H = p->H;
+  pl.off_delta = 0;
+  pl.off_dq = align256(B * N * H * N * 4);
+  pl.off_db = pl.off_dq + align256((size_t)pl.T * B * NN * H * HD * 4);
+  pl.total = pl.off_db + align256((size_t)pl.C * B * H * NN * 4);
+  return pl;
+}
+
+template <int KT, int JT>
+hipError_t launch_main(const BwdArgs &args, int grid, size_t lds, hipStream_t stream) {
+  auto kern = bwd_main_kernel<KT, JT>;
+  hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(BWD_WAVES * 64), lds, stream, args);
+  return hipGetLastError();
+}
+
+template <int KT>
+hipError_t dispatch_main(int JT, const BwdArgs &args, int grid, size_t lds, hipStream_t stream) {
+  switch (JT) {
+    case 1: return launch_main<KT, 1>(args, grid, lds, stream);
+    case 2: return launch_main<KT, 2>(args, grid, lds, stream);
+    case 3: return launch_main<KT, 3>(args, grid, lds, stream);
+    case 4: return launch_main<KT, 4>(args, grid, lds, stream);
+    case 5: return launch_main<KT, 5>(args, grid, lds, stream);
+    case 6: return launch_main<1, 6>(args, grid, lds, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int tri_attn_abi_version(void) { return TRI_ATTN_ABI_VERSION; }
+
+const char *tri_attn_status_string(int status) {
+  switch (status) {
+    case TRI_ATTN_SUCCESS: return "success";
+    case TRI_ATTN_ERROR_INVALID_VALUE: return "invalid value";
+    case TRI_ATTN_ERROR_NOT_SUPPORTED: return "not supported by this build";
+    case TRI_ATTN_ERROR_INSUFFICIENT_WORKSPACE: return "insufficient workspace";
+    case TRI_ATTN_ERROR_LAUNCH_FAILED: return "kernel launch failed";
+    case TRI_ATTN_ERROR_ABI_MISMATCH: return "ABI version mismatch";
+    default: return "unknown status";
+  }
+}
+
+tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, const void *k, const void *v,
+                             const void *bias, const uint8_t *mask, void *o, float *o_residual, float *lse,
+                             hipStream_t stream) {
+  tri_attn_status st = check_problem(problem);
+  if (st != TRI_ATTN_SUCCESS) return st;
+  const tri_attn_problem &p = *problem;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(bias) || !aligned16(o) || !aligned16(lse))
+    return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (o_residual && !aligned16(o_residual)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  const size_t E = (size_t)p.B * p.N * p.N * p.H * p.D;
+  const Range ins[] = {span(q, E * 2), span(k, E * 2), span(v, E * 2), span(bias, (size_t)p.B * p.H * p.N * p.N * 2),
+                       span(mask, mask ? (size_t)p.B * p.N * p.N : 0)};
+  const Range outs[] = {span(o, E * 2), span(o_residual, o_residual ? E * 4 : 0),
+                        span(lse, (size_t)p.B * p.N * p.H * p.N * 4)};
+  for (const Range &x : outs) {
+    for (const Range &y : ins)
+      if (overlap(x, y)) return TRI_ATTN_ERROR_INVALID_VALUE;
+    for (const Range &y : outs)
+      if (&x != &y && overlap(x, y)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  }
+
+  FwdArgs a;
+  a.q = (const uint16_t *)q;
+  a.k = (const uint16_t *)k;
+  a.v = (const uint16_t *)v;
+  a.bias = (const uint16_t *)bias;
+  a.mask = mask;
+  a.o = (uint16_t *)o;
+  a.res = o_residual;
+  a.lse = lse;
+  a.f = make_frame(problem);
+  a.B = (int)p.B;
+  a.N = (int)p.N;
+  a.H = (int)p.H;
+  a.alpha = alpha_of(problem);
+  a.inv_alpha = 1.f / a.alpha;
+  a.c1 = a.alpha * kLog2e;
+  a.n_jblocks = a.N / FWD_BJ;
+  const int groups = a.B * a.H * a.n_jblocks;
+  int chunks = (768 + groups - 1) / groups;
+  if (chunks > a.N) chunks = a.N;
+  a.rows_per_chunk = (a.N + chunks - 1) / chunks;
+  a.n_chunks = (a.N + a.rows_per_chunk - 1) / a.rows_per_chunk;
+  const size_t lds = (size_t)FWD_BJ * (a.N + 4) * 4 + (size_t)FWD_WAVES * 32 * HD * 2;
+  if (hipFuncSetAttribute((const void *)fwd_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+      hipSuccess)
+    return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  hipLaunchKernelGGL(fwd_kernel, dim3(groups * a.n_chunks), dim3(FWD_WAVES * 64), lds, stream, a);
+  return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH_FAILED;
+}
+
+size_t tri_attn_bwd_workspace_bytes(const tri_attn_problem *problem) {
+  if (check_problem(problem) != TRI_ATTN_SUCCESS) return 0;
+  return plan_bwd(problem).total;
+}
+
+tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const void *q, const void *k,
+                                      const void *v, const void *bias, const uint8_t *mask, const void *o,
+                                      const float *o_residual, const float *lse, const void *d_o, void *dq,
+                                      void *dk, void *dv, void *dbias, void *workspace, size_t workspace_bytes,
+                                      hipEvent_t main_start, hipEvent_t main_stop, hipStream_t stream) {
+  tri_attn_status st = check_problem(problem);
+  if (st != TRI_ATTN_SUCCESS) return st;
+  const tri_attn_problem &p = *problem;
+  const void *need16[] = {q, k, v, bias, o, lse, d_o, dq, dk, dv, dbias};
+  for (const void *x : need16)
+    if (!aligned16(x)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (o_residual && !aligned16(o_residual)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!workspace || ((uintptr_t)workspace & 255u)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  const BwdPlan pl = plan_bwd(problem);
+  if (workspace_bytes < pl.total) return TRI_ATTN_ERROR_INSUFFICIENT_WORKSPACE;
+  const size_t E = (size_t)p.B * p.N * p.N * p.H * p.D;
+  const size_t nb = (size_t)p.B * p.H * p.N * p.N;
+  const Range ins[] = {span(q, E * 2),
+                       span(k, E * 2),
+                       span(v, E * 2),
+                       span(bias, nb * 2),
+                       span(mask, mask ? (size_t)p.B * p.N * p.N : 0),
+                       span(o, E * 2),
+                       span(o_residual, o_residual ? E * 4 : 0),
+                       span(lse, (size_t)p.B * p.N * p.H * p.N * 4),
+                       span(d_o, E * 2)};
+  const Range outs[] = {span(dq, E * 2), span(dk, E * 2), span(dv, E * 2),
+                        span(dbias, nb * ((p.flags & TRI_ATTN_FLAG_DBIAS_FP32) ? 4 : 2)),
+                        span(workspace, pl.total)};
+  for (const Range &x : outs) {
+    for (const Range &y : ins)
+      if (overlap(x, y)) return TRI_ATTN_ERROR_INVALID_VALUE;
+    for (const Range &y : outs)
+      if (&x != &y && overlap(x, y)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  }
+
+  const Frame f = make_frame(problem);
+  const float alpha = alpha_of(problem);
+  char *ws = (char *)workspace;
+  float *delta = (float *)(ws + pl.off_delta);
+  float *dq_part = (float *)(ws + pl.off_dq);
+  float *db_part = (float *)(ws + pl.off_db);
+
+  PrepArgs pa;
+  pa.o = (const uint16_t *)o;
+  pa.d_o = (const uint16_t *)d_o;
+  pa.res = o_residual;
+  pa.delta = delta;
+  pa.f = f;
+  pa.B = (int)p.B;
+  pa.N = (int)p.N;
+  pa.H = (int)p.H;
+  const long long nrows = (long long)p.B * p.N * p.H * p.N;
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((nrows + 255) / 256)), dim3(256), 0, stream, pa);
+  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+
+  BwdArgs ba;
+  ba.q = (const uint16_t *)q;
+  ba.k = (const uint16_t *)k;
+  ba.v = (const uint16_t *)v;
+  ba.bias = (const uint16_t *)bias;
+  ba.d_o = (const uint16_t *)d_o;
+  ba.mask = mask;
+  ba.lse = lse;
+  ba.delta = delta;
+  ba.dk = (uint16_t *)dk;
+  ba.dv = (uint16_t *)dv;
+  ba.dq_part = dq_part;
+  ba.db_part = db_part;
+  ba.f = f;
+  ba.B = (int)p.B;
+  ba.N = (int)p.N;
+  ba.H = (int)p.H;
+  ba.n_kblocks = pl.T;
+  ba.n_chunks = pl.C;
+  ba.rows_per_chunk = pl.rows_per_chunk;
+  ba.alpha = alpha;
+  ba.c1 = alpha * kLog2e;
+  const int grid = ba.B * ba.H * pl.T * pl.C;
+  if (main_start && hipEventRecord(main_start, stream) != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  const hipError_t e = pl.KT == 2 ? dispatch_main<2>(pl.JT, ba, grid, pl.lds_bytes, stream)
+                                  : dispatch_main<1>(pl.JT, ba, grid, pl.lds_bytes, stream);
+  if (e != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  if (main_stop && hipEventRecord(main_stop, stream) != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+
+  ReduceArgs ra;
+  ra.dq_part = dq_part;
+  ra.db_part = db_part;
+  ra.dq = (uint16_t *)dq;
+  ra.dbias = dbias;
+  ra.f = f;
+  ra.B = (int)p.B;
+  ra.N = (int)p.N;
+  ra.H = (int)p.H;
+  ra.T = pl.T;
+  ra.C = pl.C;
+  ra.dbias_fp32 = (p.flags & TRI_ATTN_FLAG_DBIAS_FP32) ? 1 : 0;
+  ra.alpha = alpha;
+  hipLaunchKernelGGL(reduce_dq_kernel, dim3((unsigned)((E / 4 + 255) / 256)), dim3(256), 0, stream, ra);
+  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  hipLaunchKernelGGL(reduce_dbias_kernel, dim3((unsigned)((nb / 4 + 255) / 256)), dim3(256), 0, stream, ra);
+  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  return TRI_ATTN_SUCCESS;
+}
+
+tri_attn_status tri_attn_bwd(const tri_attn_problem *problem, const void *q, const void *k, const void *v,
+                             const void *bias, const uint8_t *mask, const void *o, const float *o_residual,
+                             const float *lse, const void *d_o, void *dq, void *dk, void *dv, void *dbias,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  return tri_attn_bwd_profiled(problem, q, k, v, bias, mask, o, o_residual, lse, d_o, dq, dk, dv, dbias,
+                               workspace, workspace_bytes, nullptr, nullptr, stream);
+}
+
+}  // extern "C"
