@@ -259,49 +259,69 @@ struct PrepArgs {
   int B, N, H;
 };
 
+// One thread per (b, r, q, h), heads fastest so that a wave reads whole
+// 256-byte (position, all heads) segments; the channel sum runs in a fixed order.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
-  const long long total = (long long)a.B * a.N * a.H * a.N;
+  const long long total = (long long)a.B * a.N * a.N * a.H;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= total) return;
-  const int q = (int)(idx % a.N);
-  long long t = idx / a.N;
-  const int h = (int)(t % a.H);
-  t /= a.H;
+  const int h = (int)(idx % a.H);
+  long long t = idx / a.H;
+  const int q = (int)(t % a.N);
+  t /= a.N;
   const int r = (int)(t % a.N);
   const int b = (int)(t / a.N);
   const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)q * a.f.sQ + h * HD;
+  u32x4 gw[4], ow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    gw[i] = ld16(a.d_o + base + 8 * i);
+    ow[i] = ld16(a.o + base + 8 * i);
+  }
+  f32x4 rw[8];
+  if (a.res) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rw[i] = *(const f32x4 *)(a.res + base + 4 * i);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rw[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
   float acc = 0.f;
 #pragma unroll
-  for (int c8 = 0; c8 < HD; c8 += 8) {
-    const u32x4 gw = ld16(a.d_o + base + c8);
-    const u32x4 ow = ld16(a.o + base + c8);
-    float ov[8], gv[8];
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ov[2 * i] = bf_lo(ow[i]);
-      ov[2 * i + 1] = bf_hi(ow[i]);
-      gv[2 * i] = bf_lo(gw[i]);
-      gv[2 * i + 1] = bf_hi(gw[i]);
+    for (int w = 0; w < 4; ++w) {
+      const int c = 8 * i + 2 * w;  // channels c, c+1
+      const float o0 = bf_lo(ow[i][w]) + rw[c >> 2][c & 3];
+      const float o1 = bf_hi(ow[i][w]) + rw[(c + 1) >> 2][(c + 1) & 3];
+      acc = fmaf(bf_lo(gw[i][w]), o0, acc);
+      acc = fmaf(bf_hi(gw[i][w]), o1, acc);
     }
-    if (a.res) {
-      const f32x4 r0 = *(const f32x4 *)(a.res + base + c8);
-      const f32x4 r1 = *(const f32x4 *)(a.res + base + c8 + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ov[i] += r0[i];
-        ov[4 + i] += r1[i];
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc = fmaf(gv[i], ov[i], acc);
   }
-  a.delta[idx] = acc;
+  a.delta[(((long long)b * a.N + r) * a.H + h) * a.N + q] = acc;
 }
 
 // ------------------------------------------------------------------------------------
 // Backward main kernel
 // ------------------------------------------------------------------------------------
+// One workgroup (4 waves, one per SIMD) owns a block of 64 keys of one head for a
+// chunk of attention rows, and every query.  Per row, the block's keys and values
+// and the row's per-query statistics (lse, D) are staged in LDS by direct
+// global-to-LDS loads, double-buffered so that the next row's arrive while this
+// row is computed.  Each wave walks its query tiles (32 queries; the next tile's
+// q and dO are fetched into LDS while the current one is computed) and for every
+// 32x32 (query, key) tile recomputes the scores and probabilities once, then
+//   dP - D   = dO V^T + (-D)            (MFMA, -D as the accumulator's initial value)
+//   dS       = P * (dP - D)             (fp32)
+//   dV, dK  += P^T dO, dS^T q           (MFMA, per-wave partials)
+//   dbias   += I * dS                   (MFMA against an identity, fp32 accumulators
+//                                        held over the chunk's rows)
+//   dQ^T     = K^T dS^T over 64 keys    (MFMA, one partial per key block)
+// At the end of a row the four waves' dK/dV partials are summed in LDS in wave
+// order; dbias leaves the kernel as one partial per row chunk.
 constexpr int BWD_WAVES = 4;
+constexpr int BWD_BK = 64;
+constexpr int BWD_WAVE_ELEMS = (64 + BWD_BK) * HD;  // bf16 staging per wave: q, dO, dS^T
 
 struct BwdArgs {
   const uint16_t *q, *k, *v, *bias, *d_o;
@@ -316,35 +336,52 @@ struct BwdArgs {
   float alpha, c1;
 };
 
-template <int KT, int JT>
-__global__ __launch_bounds__(BWD_WAVES * 64) void bwd_main_kernel(BwdArgs a) {
-  constexpr int BK = 32 * KT;  // keys per workgroup
+typedef __attribute__((address_space(3))) void lds_void;
+// 16 bytes per lane from global memory straight into LDS at dst + 16 * lane.
+__device__ __forceinline__ void load_lds16(const void *src, void *dst_wave) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void *)dst_wave, 16, 0, 0);
+}
+// wait until at most n vector-memory operations of this wave are outstanding
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+template <int JT>
+__global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) {
   extern __shared__ float4 smem_f4[];
   const int N = a.N;
-  const int bstr = N + 8;  // bf16 row stride of the transposed bias tile
-  uint16_t *biasT = (uint16_t *)smem_f4;             // [BK][N (+8)]: bias[j][k] stored at [k][j]
-  uint16_t *kbuf = biasT + BK * bstr;                // [BK][32]
-  uint16_t *vbuf = kbuf + BK * HD;                   // [BK][32]
+  const int bstr = N + 8;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, ll = lane & 31;
-  constexpr int WAVE_ELEMS = (64 + BK) * HD;          // q, dO tiles and dS^T tile, bf16
-  uint16_t *wq = vbuf + BK * HD + wave * WAVE_ELEMS;  // [32][32]
-  uint16_t *wdo = wq + 32 * HD;                       // [32][32]
-  uint16_t *wds = wdo + 32 * HD;                      // [BK][32]: dS^T of the current query tile
-  float *wred = (float *)wq;                          // [BK][32] fp32 reduction slot (reuses the above)
+  uint16_t *biasT = (uint16_t *)smem_f4;                 // [64][N + 8]: bias[j][k0 + kk] at [kk][j]
+  uint16_t *kvs = biasT + BWD_BK * bstr;                 // [2 bufs][K, V][64][32]
+  float *stats = (float *)(kvs + 2 * 2 * BWD_BK * HD);  // [2 bufs][lse, D][N]
+  uint16_t *wstage = (uint16_t *)(stats + 4 * N);       // per wave: q [32][32], dO [32][32], dS^T [64][32]
+  uint16_t *wq = wstage + wave * BWD_WAVE_ELEMS;
+  uint16_t *wdo = wq + 32 * HD;
+  uint16_t *wds = wdo + 32 * HD;
+  float *wred = (float *)wq;  // [64][32] fp32 reduction slot (reuses the staging)
 
   int t = xcd_remap(blockIdx.x, gridDim.x);
   const int kb = t % a.n_kblocks; t /= a.n_kblocks;
   const int chunk = t % a.n_chunks; t /= a.n_chunks;
   const int h = t % a.H;
   const int b = t / a.H;
-  const int k0 = kb * BK;
+  const int k0 = kb * BWD_BK;
+  const int nkt = min(2, (N - k0) / 32);  // key tiles present in this block (1 at a ragged end)
   const int njt = N / 32;
+  const int r0 = chunk * a.rows_per_chunk;
+  const int r1 = min(N, r0 + a.rows_per_chunk);
+  const float c1 = a.c1;
+  const float inv_alpha = 1.f / a.alpha;
 
   // transposed pair-bias tile: biasT[kk][j] = bias[b, h, j, k0 + kk]
   {
     const uint16_t *src = a.bias + ((long long)b * a.H + h) * N * N + k0;
-    constexpr int per_row = BK / 8;
+    const int per_row = nkt * 4;  // 8-key chunks per query row
     for (int idx = tid; idx < N * per_row; idx += BWD_WAVES * 64) {
       const int j = idx / per_row, c8 = idx - j * per_row;
       const u32x4 w = ld16(src + (long long)j * N + c8 * 8);
@@ -356,44 +393,85 @@ __global__ __launch_bounds__(BWD_WAVES * 64) void bwd_main_kernel(BwdArgs a) {
     }
   }
 
-  float dbias[JT][KT][16];
+  // identity operands for the dbias accumulation: lane supplies I[j = lane%32][jj(kk)]
+  // in the contraction order of the score-layout operands (see tr_operand)
+  bf16x8 ident[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    unsigned w[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      unsigned lo = 0, hi = 0;
+      const int e0 = 2 * e2, e1 = 2 * e2 + 1;
+      if (ll == 16 * s + 8 * (e0 >> 2) + 4 * hh + (e0 & 3)) lo = 0x3f80u;
+      if (ll == 16 * s + 8 * (e1 >> 2) + 4 * hh + (e1 & 3)) hi = 0x3f80u;
+      w[e2] = lo | (hi << 16);
+    }
+    ident[s] = as_bf16x8((u32x4){w[0], w[1], w[2], w[3]});
+  }
+
+  // row staging (direct to LDS): keys and values of the block, lse and D of the row.
+  // Each wave moves 2 KB of K/V and up to 2 KB of statistics: 4 instructions.
+  const long long stat_row = (long long)a.H * N;
+  auto stage_row = [&](int r, int buf) {
+    const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
+    uint16_t *kd = kvs + buf * 2 * BWD_BK * HD;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int ch = 64 * (2 * wave + u) + lane;  // 16-byte chunk of [K | V]
+      const int which = ch >> 8, rem = ch & 255, key = min(k0 + (rem >> 2), N - 1), part = rem & 3;
+      load_lds16((which ? a.v : a.k) + base + (long long)key * a.f.sQ + part * 8,
+                 kd + 64 * (2 * wave + u) * 8);
+    }
+    const long long so = ((long long)b * N + r) * stat_row + (long long)h * N;
+    float *sd = stats + buf * 2 * N;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c0 = 64 * (2 * wave + u), c = c0 + lane;  // 16-byte chunk of [lse | D]
+      if (c < N / 2) {
+        const float *src = c < N / 4 ? a.lse + so + 4 * c : a.delta + so + 4 * (c - N / 4);
+        load_lds16(src, sd + 4 * c0);
+      }
+    }
+  };
+
+  f32x16 dbias[JT][2];
 #pragma unroll
   for (int jj = 0; jj < JT; ++jj)
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) dbias[jj][kt][i] = 0.f;
+    for (int kt = 0; kt < 2; ++kt) dbias[jj][kt] = (f32x16){};
 
-  const int r0 = chunk * a.rows_per_chunk;
-  const int r1 = min(N, r0 + a.rows_per_chunk);
-  const float c1 = a.c1;
   const long long E = (long long)a.B * N * N * a.H * HD;
   float *dq_part = a.dq_part + (long long)kb * E;
 
-  for (int r = r0; r < r1; ++r) {
-    const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
-    // stage this row's keys and values of the block
-    for (int ch = tid; ch < 2 * BK * 4; ch += BWD_WAVES * 64) {
-      const int which = ch / (BK * 4), rem = ch - which * BK * 4, key = rem >> 2, part = rem & 3;
-      const uint16_t *src = (which ? a.v : a.k) + base + (long long)(k0 + key) * a.f.sQ + part * 8;
-      *(u32x4 *)((which ? vbuf : kbuf) + key * HD + part * 8) = ld16(src);
-    }
-    // keys of the block this lane owns in the score layout, and their mask
-    bool kvalid[KT];
-    unsigned tile_full = 1u;
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      bool ok = true;
-      if (a.mask)
-        ok = a.mask[(long long)b * a.f.mB + (long long)r * a.f.mR + (long long)(k0 + 32 * kt + ll) * a.f.mK] != 0;
-      kvalid[kt] = ok;
-      if (__ballot(ok) != ~0ull) tile_full = 0u;
-    }
-    __syncthreads();
+  if (r0 < r1) stage_row(r0, 0);
+  wait_vm<0>();
+  __syncthreads();
 
-    bf16x8 kB[KT][2], vB[KT][2], kT[2 * KT];
+  for (int r = r0; r < r1; ++r) {
+    const int cur = (r - r0) & 1;
+    const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
+    const uint16_t *kbuf = kvs + cur * 2 * BWD_BK * HD;
+    const uint16_t *vbuf = kbuf + BWD_BK * HD;
+    const float *Ls = stats + cur * 2 * N;
+    const float *Ds = Ls + N;
+
+    // mask of the keys this lane owns in the score layout
+    bool kvalid[2];
+    bool tile_full = true;
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = k0 + 32 * kt + ll;
+      bool ok = key < N;
+      if (ok && a.mask)
+        ok = a.mask[(long long)b * a.f.mB + (long long)r * a.f.mR + (long long)key * a.f.mK] != 0;
+      kvalid[kt] = ok;
+      if (__ballot(ok) != ~0ull) tile_full = false;
+    }
+
+    bf16x8 kB[2][2], vB[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
       const uint16_t *kr = kbuf + (32 * kt + ll) * HD;
       const uint16_t *vr = vbuf + (32 * kt + ll) * HD;
       kB[kt][0] = as_bf16x8(*(const u32x4 *)(kr + 8 * hh));
@@ -401,28 +479,35 @@ __global__ __launch_bounds__(BWD_WAVES * 64) void bwd_main_kernel(BwdArgs a) {
       vB[kt][0] = as_bf16x8(*(const u32x4 *)(vr + 8 * hh));
       vB[kt][1] = as_bf16x8(*(const u32x4 *)(vr + 16 + 8 * hh));
     }
+    f32x16 dK[2], dV[2];
 #pragma unroll
-    for (int s = 0; s < 2 * KT; ++s) kT[s] = tr_operand(kbuf, 16 * s, lane);
-
-    f32x16 dK[KT], dV[KT];
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = 0; kt < 2; ++kt) {
       dK[kt] = (f32x16){};
       dV[kt] = (f32x16){};
     }
+
+    // q and dO of a query tile into this wave's staging (4 instructions)
+    auto stage_tile = [&](int j0) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int ch = lane + 64 * u, jr = ch >> 2, part = ch & 3;
+        const long long off = base + (long long)(j0 + jr) * a.f.sQ + part * 8;
+        load_lds16(a.q + off, wq + 512 * u);
+        load_lds16(a.d_o + off, wdo + 512 * u);
+      }
+    };
+    // the next row's staging goes to the other buffer, last read during the previous row
+    const bool has_next = r + 1 < r1;
+    if (has_next) stage_row(r + 1, cur ^ 1);
+    wait_lgkm0();  // this wave's reads of its staging (previous row) are done
+    if (wave < njt) stage_tile(wave * 32);
 
 #pragma unroll
     for (int jj = 0; jj < JT; ++jj) {
       const int jt = wave + BWD_WAVES * jj;
       if (jt >= njt) break;
       const int j0 = jt * 32;
-      // stage the query and upstream-gradient tiles of this query block
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int ch = lane + 64 * u, which = ch >> 7, rem = ch & 127, jr = rem >> 2, part = rem & 3;
-        const uint16_t *src = (which ? a.d_o : a.q) + base + (long long)(j0 + jr) * a.f.sQ + part * 8;
-        *(u32x4 *)((which ? wdo : wq) + jr * HD + part * 8) = ld16(src);
-      }
+      wait_vm<0>();  // this tile's q and dO have landed in LDS
       const bf16x8 qA0 = as_bf16x8(*(const u32x4 *)(wq + ll * HD + 8 * hh));
       const bf16x8 qA1 = as_bf16x8(*(const u32x4 *)(wq + ll * HD + 16 + 8 * hh));
       const bf16x8 dA0 = as_bf16x8(*(const u32x4 *)(wdo + ll * HD + 8 * hh));
@@ -431,25 +516,26 @@ __global__ __launch_bounds__(BWD_WAVES * 64) void bwd_main_kernel(BwdArgs a) {
       const bf16x8 qB1 = tr_operand(wq, 16, lane);
       const bf16x8 dB0 = tr_operand(wdo, 0, lane);
       const bf16x8 dB1 = tr_operand(wdo, 16, lane);
-      // per-query statistics for the lane's 16 queries j0 + 8g + 4hh + i
-      float L2[16];
-      f32x16 negD;
-      const long long sbase = (((long long)b * N + r) * a.H + h) * N + j0 + 4 * hh;
+      f32x16 negL, negD;  // accumulator inits: -lse/alpha and -D for the lane's queries
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 lv = *(const f32x4 *)(a.lse + sbase + 8 * g);
-        const f32x4 dv4 = *(const f32x4 *)(a.delta + sbase + 8 * g);
+        const f32x4 lv = *(const f32x4 *)(Ls + j0 + 8 * g + 4 * hh);
+        const f32x4 dv4 = *(const f32x4 *)(Ds + j0 + 8 * g + 4 * hh);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          L2[4 * g + i] = lv[i] * kLog2e;
+          negL[4 * g + i] = -lv[i] * inv_alpha;
           negD[4 * g + i] = -dv4[i];
         }
       }
+      // prefetch the next query tile once the operand reads have returned
+      wait_lgkm0();
+      if (jj + 1 < JT && jt + BWD_WAVES < njt) stage_tile(j0 + 32 * BWD_WAVES);
 
+      f32x16 dqT = {};  // dQ^T partial of this key block: K^T (32 x 64 keys) dS^T (64 keys x 32 queries)
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        f32x16 s = {};
-        s = mfma(qA0, kB[kt][0], s);
+      for (int kt = 0; kt < 2; ++kt) {
+        if (kt >= nkt) continue;  // absent key tile at a ragged end
+        f32x16 s = mfma(qA0, kB[kt][0], negL);  // q.k - lse/alpha
         s = mfma(qA1, kB[kt][1], s);
         f32x16 dp = mfma(dA0, vB[kt][0], negD);  // dP - D
         dp = mfma(dA1, vB[kt][1], dp);
@@ -460,53 +546,46 @@ __global__ __launch_bounds__(BWD_WAVES * 64) void bwd_main_kernel(BwdArgs a) {
           const u32x2 bw = *(const u32x2 *)(brow + 8 * g);
           const float beta[4] = {bf_lo(bw[0]), bf_hi(bw[0]), bf_lo(bw[1]), bf_hi(bw[1])};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int idx = 4 * g + i;
-            const float u = fmaf(s[idx], c1, fmaf(beta[i], kLog2e, -L2[idx]));
-            p[idx] = __builtin_amdgcn_exp2f(u);
-          }
+          for (int i = 0; i < 4; ++i)
+            p[4 * g + i] = __builtin_amdgcn_exp2f(fmaf(s[4 * g + i], c1, beta[i] * kLog2e));
         }
         if (!tile_full && !kvalid[kt]) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) p[i] = 0.f;
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          ds[i] = p[i] * dp[i];
-          dbias[jj][kt][i] += ds[i];
-        }
+        for (int i = 0; i < 16; ++i) ds[i] = p[i] * dp[i];
         const bf16x8 pA0 = pack8(p), pA1 = pack8(p + 8);
         const bf16x8 sA0 = pack8(ds), sA1 = pack8(ds + 8);
         dV[kt] = mfma(pA0, dB0, dV[kt]);
         dV[kt] = mfma(pA1, dB1, dV[kt]);
         dK[kt] = mfma(sA0, qB0, dK[kt]);
         dK[kt] = mfma(sA1, qB1, dK[kt]);
-        // dS^T rows of this key tile for the dQ product
+        dbias[jj][kt] = mfma(ident[0], sA0, dbias[jj][kt]);
+        dbias[jj][kt] = mfma(ident[1], sA1, dbias[jj][kt]);
         const u32x4 s0 = __builtin_bit_cast(u32x4, sA0), s1 = __builtin_bit_cast(u32x4, sA1);
         uint16_t *drow = wds + (32 * kt + ll) * HD + 4 * hh;
         *(u32x2 *)(drow + 0) = (u32x2){s0[0], s0[1]};
         *(u32x2 *)(drow + 8) = (u32x2){s0[2], s0[3]};
         *(u32x2 *)(drow + 16) = (u32x2){s1[0], s1[1]};
         *(u32x2 *)(drow + 24) = (u32x2){s1[2], s1[3]};
-      }
-      // dQ partial of this key block: dS (32 queries x BK keys) times K (BK x 32)
-      f32x16 dq = {};
 #pragma unroll
-      for (int s = 0; s < 2 * KT; ++s) dq = mfma(tr_operand(wds, 16 * s, lane), kT[s], dq);
-      float *qout = dq_part + ((((long long)b * N + r) * N + j0) * a.H + h) * HD + ll;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int jrow = 8 * (i >> 2) + 4 * hh + (i & 3);
-        qout[(long long)jrow * a.H * HD] = dq[i];
+        for (int s = 2 * kt; s < 2 * kt + 2; ++s)
+          dqT = mfma(tr_operand(kbuf, 16 * s, lane), tr_operand(wds, 16 * s, lane), dqT);
       }
+      float *qout = dq_part + ((((long long)b * N + r) * N + j0 + ll) * a.H + h) * HD + 4 * hh;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(f32x4 *)(qout + 8 * g) = (f32x4){dqT[4 * g], dqT[4 * g + 1], dqT[4 * g + 2], dqT[4 * g + 3]};
     }
 
     // fixed-order cross-wave reduction of dV then dK for this row
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
+      wait_lgkm0();
       __syncthreads();
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
+      for (int kt = 0; kt < 2; ++kt) {
         const f32x16 &acc = which ? dK[kt] : dV[kt];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -517,19 +596,21 @@ __global__ __launch_bounds__(BWD_WAVES * 64) void bwd_main_kernel(BwdArgs a) {
       __syncthreads();
       const float scale = which ? a.alpha : 1.f;
       uint16_t *dst = which ? a.dk : a.dv;
-      for (int e = tid * 4; e < BK * HD; e += BWD_WAVES * 64 * 4) {
-        const int kr = e / HD, c = e - kr * HD;
-        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < BWD_WAVES; ++w) {
-          const f32x4 part = *(const f32x4 *)((const float *)(vbuf + BK * HD + w * WAVE_ELEMS) + e);
-          sum += part;
-        }
+      for (int u = 0; u < 2; ++u) {
+        const int e = 4 * (tid + 256 * u);
+        const int kr = e / HD, c = e - kr * HD;
+        if (k0 + kr >= N) continue;
+        f32x4 sum = *(const f32x4 *)((const float *)wstage + e);
+#pragma unroll
+        for (int w = 1; w < BWD_WAVES; ++w) sum += *(const f32x4 *)((const float *)(wstage + w * BWD_WAVE_ELEMS) + e);
         sum *= scale;
         const long long off = base + (long long)(k0 + kr) * a.f.sQ + c;
         *(u32x2 *)(dst + off) = (u32x2){pack_bf16(sum[0], sum[1]), pack_bf16(sum[2], sum[3])};
       }
     }
+    // the next row's staging must have landed in LDS for every wave before the barrier
+    wait_vm<0>();
     __syncthreads();
   }
 
@@ -540,12 +621,14 @@ __global__ __launch_bounds__(BWD_WAVES * 64) void bwd_main_kernel(BwdArgs a) {
     const int jt = wave + BWD_WAVES * jj;
     if (jt >= njt) break;
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
+    for (int kt = 0; kt < 2; ++kt) {
+      if (kt >= nkt) continue;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int j = jt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
         dbo[(long long)j * N + 32 * kt + ll] = dbias[jj][kt][i];
       }
+    }
   }
 }
 
@@ -645,7 +728,7 @@ float alpha_of(const tri_attn_problem *p) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct BwdPlan {
-  int KT, JT, T, C, rows_per_chunk;
+  int JT, T, C, rows_per_chunk;
   size_t lds_bytes;
   size_t off_delta, off_dq, off_db, total;
 };
@@ -655,23 +738,16 @@ BwdPlan plan_bwd(const tri_attn_problem *p) {
   const int N = (int)p->N;
   const int njt = N / 32;
   pl.JT = (njt + BWD_WAVES - 1) / BWD_WAVES;
-  pl.KT = pl.JT <= 5 ? 2 : 1;
-  const int BK = 32 * pl.KT;
-  pl.T = N / BK;
-  if (N % BK) {  // N = 32 * odd: fall back to one key tile per workgroup
-    pl.KT = 1;
-    pl.T = N / 32;
-  }
+  pl.T = (N + BWD_BK - 1) / BWD_BK;
+  // one workgroup per CU (its LDS and registers fill one); one wave of workgroups
   const int groups = (int)(p->B * p->H * pl.T);
-  const int per_cu = pl.KT == 2 ? 1 : 2;
-  int C = (256 * per_cu) / groups;
+  int C = 256 / groups;
   if (C < 1) C = 1;
   if (C > N) C = N;
   pl.rows_per_chunk = (N + C - 1) / C;
   pl.C = (N + pl.rows_per_chunk - 1) / pl.rows_per_chunk;
-  const int BKk = 32 * pl.KT;
-  pl.lds_bytes = (size_t)BKk * (N + 8) * 2 + (size_t)2 * BKk * HD * 2 +
-                 (size_t)BWD_WAVES * (64 + BKk) * HD * 2;
+  pl.lds_bytes = (size_t)BWD_BK * (N + 8) * 2 + (size_t)2 * 2 * BWD_BK * HD * 2 + (size_t)2 * 2 * N * 4 +
+                 (size_t)BWD_WAVES * BWD_WAVE_ELEMS * 2;
   const size_t B = p->B, NN = (size_t)N * N, H = p->H;
   pl.off_delta = 0;
   pl.off_dq = align256(B * N * H * N * 4);
@@ -680,24 +756,23 @@ BwdPlan plan_bwd(const tri_attn_problem *p) {
   return pl;
 }
 
-template <int KT, int JT>
+template <int JT>
 hipError_t launch_main(const BwdArgs &args, int grid, size_t lds, hipStream_t stream) {
-  auto kern = bwd_main_kernel<KT, JT>;
+  auto kern = bwd_main_kernel<JT>;
   hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(BWD_WAVES * 64), lds, stream, args);
   return hipGetLastError();
 }
 
-template <int KT>
 hipError_t dispatch_main(int JT, const BwdArgs &args, int grid, size_t lds, hipStream_t stream) {
   switch (JT) {
-    case 1: return launch_main<KT, 1>(args, grid, lds, stream);
-    case 2: return launch_main<KT, 2>(args, grid, lds, stream);
-    case 3: return launch_main<KT, 3>(args, grid, lds, stream);
-    case 4: return launch_main<KT, 4>(args, grid, lds, stream);
-    case 5: return launch_main<KT, 5>(args, grid, lds, stream);
-    case 6: return launch_main<1, 6>(args, grid, lds, stream);
+    case 1: return launch_main<1>(args, grid, lds, stream);
+    case 2: return launch_main<2>(args, grid, lds, stream);
+    case 3: return launch_main<3>(args, grid, lds, stream);
+    case 4: return launch_main<4>(args, grid, lds, stream);
+    case 5: return launch_main<5>(args, grid, lds, stream);
+    case 6: return launch_main<6>(args, grid, lds, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -828,7 +903,7 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
   pa.B = (int)p.B;
   pa.N = (int)p.N;
   pa.H = (int)p.H;
-  const long long nrows = (long long)p.B * p.N * p.H * p.N;
+  const long long nrows = (long long)p.B * p.N * p.N * p.H;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((nrows + 255) / 256)), dim3(256), 0, stream, pa);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
 
@@ -856,8 +931,7 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
   ba.c1 = alpha * kLog2e;
   const int grid = ba.B * ba.H * pl.T * pl.C;
   if (main_start && hipEventRecord(main_start, stream) != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
-  const hipError_t e = pl.KT == 2 ? dispatch_main<2>(pl.JT, ba, grid, pl.lds_bytes, stream)
-                                  : dispatch_main<1>(pl.JT, ba, grid, pl.lds_bytes, stream);
+  const hipError_t e = dispatch_main(pl.JT, ba, grid, pl.lds_bytes, stream);
   if (e != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
   if (main_stop && hipEventRecord(main_stop, stream) != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
 
