@@ -33,6 +33,7 @@
 #include <stdint.h>
 #include <string.h>
 #include <math.h>
+#include <type_traits>
 
 #include "tri_attn.h"
 
@@ -103,8 +104,20 @@ struct Frame {
 // ------------------------------------------------------------------------------------
 // Forward
 // ------------------------------------------------------------------------------------
-constexpr int FWD_WAVES = 8;
+// One workgroup = (batch, head, 32 queries, chunk of rows); 12 waves, each working
+// on one attention row at a time.  The block's pair bias, scaled by 1/alpha, sits
+// in LDS in fp32 and is the initial value of the score MFMA, so S^T = K Q^T +
+// bias^T/alpha costs no VALU work.  Per 32-key tile each lane owns one query and
+// 16 keys: p = exp2(c1 * (s - m)) with m a per-query reference maximum.  m is the
+// first attended tile's maximum and is only raised (rescaling the running sum and
+// output) when a later tile would push a probability beyond 2^16, which the
+// tile's probability sum reveals; most tiles need no maximum at all.  K^T rows
+// are MFMA operands read straight from global memory; V goes through a per-wave
+// LDS buffer and is read transposed.  The next tile's K and V are fetched into
+// registers while the current tile is computed.
+constexpr int FWD_WAVES = 12;
 constexpr int FWD_BJ = 32;
+constexpr float kFwdOverflow = 65536.f;  // largest tile probability sum before a rescale
 
 struct FwdArgs {
   const uint16_t *q, *k, *v, *bias;
@@ -154,6 +167,7 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
   const int r0 = chunk * a.rows_per_chunk;
   const int r1 = min(N, r0 + a.rows_per_chunk);
   const float c1 = a.c1;
+  const int nkt = N / 32;
   for (int r = r0 + wave; r < r1; r += FWD_WAVES) {
     const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
     const uint16_t *qp = a.q + base + (long long)(j0 + jl) * a.f.sQ;
@@ -161,25 +175,31 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
     const bf16x8 qB1 = as_bf16x8(ld16(qp + 16 + 8 * hh));
     const uint8_t *mrow = a.mask ? a.mask + (long long)b * a.f.mB + (long long)r * a.f.mR : nullptr;
 
-    float m = -INFINITY;  // running max of the lane's query, in logit/alpha units
+    // operands of one key tile: K^T rows (MFMA A), V chunks (to LDS), the lane's mask byte
+    u32x4 nk0, nk1, nv0, nv1;
+    uint8_t nmv = 1;
+    auto fetch = [&](int kt) {
+      const uint16_t *kp = a.k + base + (long long)(kt * 32 + jl) * a.f.sQ;
+      nk0 = ld16(kp + 8 * hh);
+      nk1 = ld16(kp + 16 + 8 * hh);
+      const int key0 = lane >> 2, part = lane & 3;
+      nv0 = ld16(a.v + base + (long long)(kt * 32 + key0) * a.f.sQ + part * 8);
+      nv1 = ld16(a.v + base + (long long)(kt * 32 + 16 + key0) * a.f.sQ + part * 8);
+      if (mrow) nmv = mrow[(long long)(kt * 32 + jl) * a.f.mK];
+    };
+    fetch(0);
+
+    float m = -INFINITY;  // reference maximum of the lane's query, in logit/alpha units
     float lsum = 0.f;
     f32x16 oacc = {};
-    for (int kt = 0; kt < N / 32; ++kt) {
-      unsigned valid = 0xffffffffu;
-      if (mrow) {
-        const uint8_t mv = mrow[(long long)(kt * 32 + jl) * a.f.mK];
-        valid = (unsigned)__ballot(mv != 0);
-      }
+    for (int kt = 0; kt < nkt; ++kt) {
+      const u32x4 k0w = nk0, k1w = nk1, v0w = nv0, v1w = nv1;
+      const uint8_t mv = nmv;
+      if (kt + 1 < nkt) fetch(kt + 1);
+      const unsigned valid = mrow ? (unsigned)__ballot(mv != 0) : 0xffffffffu;
       if (valid == 0u) continue;
-      const uint16_t *kp = a.k + base + (long long)(kt * 32 + jl) * a.f.sQ;
-      const bf16x8 kA0 = as_bf16x8(ld16(kp + 8 * hh));
-      const bf16x8 kA1 = as_bf16x8(ld16(kp + 16 + 8 * hh));
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int ch = lane + 64 * u, key = ch >> 2, part = ch & 3;
-        const u32x4 w = ld16(a.v + base + (long long)(kt * 32 + key) * a.f.sQ + part * 8);
-        *(u32x4 *)(vbuf + key * HD + part * 8) = w;
-      }
+      *(u32x4 *)(vbuf + (lane >> 2) * HD + (lane & 3) * 8) = v0w;
+      *(u32x4 *)(vbuf + (16 + (lane >> 2)) * HD + (lane & 3) * 8) = v1w;
       f32x16 acc;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -189,8 +209,8 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
         acc[4 * g + 2] = bv[2];
         acc[4 * g + 3] = bv[3];
       }
-      acc = mfma(kA0, qB0, acc);
-      acc = mfma(kA1, qB1, acc);
+      acc = mfma(as_bf16x8(k0w), qB0, acc);
+      acc = mfma(as_bf16x8(k1w), qB1, acc);
       if (valid != 0xffffffffu) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -198,23 +218,39 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
           if (!((valid >> kl) & 1u)) acc[i] = -INFINITY;
         }
       }
-      float mt = acc[0];
+      auto tile_max = [&]() {
+        float mt = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mt = fmaxf(mt, acc[i]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mnew = fmaxf(m, mt);
-      const float sc = __builtin_amdgcn_exp2f((m - mnew) * c1);
-      lsum *= sc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[i] *= sc;
-      m = mnew;
-      const float negm = -m * c1;
-      float p[16];
+        for (int i = 3; i < 15; i += 2) mt = fmaxf(fmaxf(mt, acc[i]), acc[i + 1]);
+        mt = fmaxf(mt, acc[15]);
+        return fmaxf(mt, __shfl_xor(mt, 32));
+      };
+      if (m == -INFINITY) m = tile_max();  // first attended tile (the same for every lane)
+      float p[16], tsum = 0.f;
+      float negm = -m * c1;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         p[i] = __builtin_amdgcn_exp2f(fmaf(acc[i], c1, negm));
-        lsum += p[i];
+        tsum += p[i];
       }
+      if (__ballot(!(tsum <= kFwdOverflow)) != 0ull) {
+        // a probability grew past the bound: raise the reference maximum to this
+        // tile's, rescale what has been accumulated and recompute the tile
+        const float mnew = fmaxf(m, tile_max());
+        const float sc = __builtin_amdgcn_exp2f((m - mnew) * c1);
+        lsum *= sc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[i] *= sc;
+        m = mnew;
+        negm = -m * c1;
+        tsum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(fmaf(acc[i], c1, negm));
+          tsum += p[i];
+        }
+      }
+      lsum += tsum;
       const bf16x8 pB0 = pack8(p);
       const bf16x8 pB1 = pack8(p + 8);
       const bf16x8 vA0 = tr_operand(vbuf, 0, lane);
@@ -319,9 +355,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
 //   dQ^T     = K^T dS^T over 64 keys    (MFMA, one partial per key block)
 // At the end of a row the four waves' dK/dV partials are summed in LDS in wave
 // order; dbias leaves the kernel as one partial per row chunk.
+//
+// Every staging buffer is its own __shared__ array and the two row buffers are
+// addressed through compile-time parity, so that the compiler's alias analysis
+// can tell the in-flight direct-to-LDS writes apart from the reads of the
+// current data and does not serialise the prefetches.
 constexpr int BWD_WAVES = 4;
 constexpr int BWD_BK = 64;
-constexpr int BWD_WAVE_ELEMS = (64 + BWD_BK) * HD;  // bf16 staging per wave: q, dO, dS^T
 
 struct BwdArgs {
   const uint16_t *q, *k, *v, *bias, *d_o;
@@ -342,6 +382,7 @@ __device__ __forceinline__ void load_lds16(const void *src, void *dst_wave) {
   __builtin_amdgcn_global_load_lds(src, (lds_void *)dst_wave, 16, 0, 0);
 }
 // wait until at most n vector-memory operations of this wave are outstanding
+// (gfx9 vector memory operations complete in issue order)
 template <int n>
 __device__ __forceinline__ void wait_vm() {
   static_assert(n >= 0 && n < 64, "vmcnt range");
@@ -351,19 +392,20 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f
 
 template <int JT>
 __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) {
-  extern __shared__ float4 smem_f4[];
+  constexpr int NMAX = 32 * BWD_WAVES * JT;
+  __shared__ __attribute__((aligned(16))) uint16_t s_biasT[BWD_BK * (NMAX + 8)];
+  __shared__ __attribute__((aligned(16))) uint16_t s_kv0[2 * BWD_BK * HD], s_kv1[2 * BWD_BK * HD];
+  __shared__ __attribute__((aligned(16))) float s_st0[2 * NMAX], s_st1[2 * NMAX];
+  __shared__ __attribute__((aligned(16))) uint16_t s_q[BWD_WAVES * 32 * HD], s_do[BWD_WAVES * 32 * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t s_ds[BWD_WAVES * BWD_BK * HD];
+
   const int N = a.N;
   const int bstr = N + 8;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, ll = lane & 31;
-  uint16_t *biasT = (uint16_t *)smem_f4;                 // [64][N + 8]: bias[j][k0 + kk] at [kk][j]
-  uint16_t *kvs = biasT + BWD_BK * bstr;                 // [2 bufs][K, V][64][32]
-  float *stats = (float *)(kvs + 2 * 2 * BWD_BK * HD);  // [2 bufs][lse, D][N]
-  uint16_t *wstage = (uint16_t *)(stats + 4 * N);       // per wave: q [32][32], dO [32][32], dS^T [64][32]
-  uint16_t *wq = wstage + wave * BWD_WAVE_ELEMS;
-  uint16_t *wdo = wq + 32 * HD;
-  uint16_t *wds = wdo + 32 * HD;
-  float *wred = (float *)wq;  // [64][32] fp32 reduction slot (reuses the staging)
+  uint16_t *wq = s_q + wave * 32 * HD;
+  uint16_t *wdo = s_do + wave * 32 * HD;
+  uint16_t *wds = s_ds + wave * BWD_BK * HD;
 
   int t = xcd_remap(blockIdx.x, gridDim.x);
   const int kb = t % a.n_kblocks; t /= a.n_kblocks;
@@ -387,8 +429,8 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
       const u32x4 w = ld16(src + (long long)j * N + c8 * 8);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        biasT[(c8 * 8 + 2 * i) * bstr + j] = (uint16_t)(w[i] & 0xffffu);
-        biasT[(c8 * 8 + 2 * i + 1) * bstr + j] = (uint16_t)(w[i] >> 16);
+        s_biasT[(c8 * 8 + 2 * i) * bstr + j] = (uint16_t)(w[i] & 0xffffu);
+        s_biasT[(c8 * 8 + 2 * i + 1) * bstr + j] = (uint16_t)(w[i] >> 16);
       }
     }
   }
@@ -410,21 +452,18 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
     ident[s] = as_bf16x8((u32x4){w[0], w[1], w[2], w[3]});
   }
 
-  // row staging (direct to LDS): keys and values of the block, lse and D of the row.
-  // Each wave moves 2 KB of K/V and up to 2 KB of statistics: 4 instructions.
+  // row staging (direct to LDS): keys and values of the block (2 instructions per
+  // wave), lse and D of the row (up to 2 per wave)
   const long long stat_row = (long long)a.H * N;
-  auto stage_row = [&](int r, int buf) {
+  auto stage_row = [&](int r, uint16_t *kd, float *sd) {
     const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
-    uint16_t *kd = kvs + buf * 2 * BWD_BK * HD;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int ch = 64 * (2 * wave + u) + lane;  // 16-byte chunk of [K | V]
       const int which = ch >> 8, rem = ch & 255, key = min(k0 + (rem >> 2), N - 1), part = rem & 3;
-      load_lds16((which ? a.v : a.k) + base + (long long)key * a.f.sQ + part * 8,
-                 kd + 64 * (2 * wave + u) * 8);
+      load_lds16((which ? a.v : a.k) + base + (long long)key * a.f.sQ + part * 8, kd + 64 * (2 * wave + u) * 8);
     }
     const long long so = ((long long)b * N + r) * stat_row + (long long)h * N;
-    float *sd = stats + buf * 2 * N;
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int c0 = 64 * (2 * wave + u), c = c0 + lane;  // 16-byte chunk of [lse | D]
@@ -444,17 +483,14 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
   const long long E = (long long)a.B * N * N * a.H * HD;
   float *dq_part = a.dq_part + (long long)kb * E;
 
-  if (r0 < r1) stage_row(r0, 0);
-  wait_vm<0>();
-  __syncthreads();
-
-  for (int r = r0; r < r1; ++r) {
-    const int cur = (r - r0) & 1;
-    const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
-    const uint16_t *kbuf = kvs + cur * 2 * BWD_BK * HD;
-    const uint16_t *vbuf = kbuf + BWD_BK * HD;
-    const float *Ls = stats + cur * 2 * N;
+  // one attention row; CUR selects the row's staging buffers at compile time
+  auto row_body = [&](auto cur_tag, int r) {
+    constexpr int CUR = decltype(cur_tag)::value;
+    uint16_t *kbuf = CUR ? s_kv1 : s_kv0;
+    const float *Ls = CUR ? s_st1 : s_st0;
     const float *Ds = Ls + N;
+    const uint16_t *vbuf = kbuf + BWD_BK * HD;
+    const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
 
     // mask of the keys this lane owns in the score layout
     bool kvalid[2];
@@ -469,16 +505,6 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
       if (__ballot(ok) != ~0ull) tile_full = false;
     }
 
-    bf16x8 kB[2][2], vB[2][2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const uint16_t *kr = kbuf + (32 * kt + ll) * HD;
-      const uint16_t *vr = vbuf + (32 * kt + ll) * HD;
-      kB[kt][0] = as_bf16x8(*(const u32x4 *)(kr + 8 * hh));
-      kB[kt][1] = as_bf16x8(*(const u32x4 *)(kr + 16 + 8 * hh));
-      vB[kt][0] = as_bf16x8(*(const u32x4 *)(vr + 8 * hh));
-      vB[kt][1] = as_bf16x8(*(const u32x4 *)(vr + 16 + 8 * hh));
-    }
     f32x16 dK[2], dV[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -496,18 +522,24 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
         load_lds16(a.d_o + off, wdo + 512 * u);
       }
     };
-    // the next row's staging goes to the other buffer, last read during the previous row
-    const bool has_next = r + 1 < r1;
-    if (has_next) stage_row(r + 1, cur ^ 1);
     wait_lgkm0();  // this wave's reads of its staging (previous row) are done
     if (wave < njt) stage_tile(wave * 32);
+    // the next row's staging goes to the other buffers, last read during the previous row
+    const bool has_next = r + 1 < r1;
+    if (has_next) stage_row(r + 1, CUR ? s_kv0 : s_kv1, CUR ? s_st0 : s_st1);
 
 #pragma unroll
     for (int jj = 0; jj < JT; ++jj) {
       const int jt = wave + BWD_WAVES * jj;
       if (jt >= njt) break;
       const int j0 = jt * 32;
-      wait_vm<0>();  // this tile's q and dO have landed in LDS
+      // outstanding, oldest first: [next-row staging: >= 2 if has_next] [this tile: 4] for
+      // the first tile; [this tile: 4] [previous tile's dQ stores: 4] afterwards
+      if (jj == 0) {
+        if (has_next) wait_vm<2>(); else wait_vm<0>();
+      } else {
+        wait_vm<4>();
+      }
       const bf16x8 qA0 = as_bf16x8(*(const u32x4 *)(wq + ll * HD + 8 * hh));
       const bf16x8 qA1 = as_bf16x8(*(const u32x4 *)(wq + ll * HD + 16 + 8 * hh));
       const bf16x8 dA0 = as_bf16x8(*(const u32x4 *)(wdo + ll * HD + 8 * hh));
@@ -516,6 +548,9 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
       const bf16x8 qB1 = tr_operand(wq, 16, lane);
       const bf16x8 dB0 = tr_operand(wdo, 0, lane);
       const bf16x8 dB1 = tr_operand(wdo, 16, lane);
+      // prefetch the next query tile once the operand reads have returned
+      wait_lgkm0();
+      if (jj + 1 < JT && jt + BWD_WAVES < njt) stage_tile(j0 + 32 * BWD_WAVES);
       f32x16 negL, negD;  // accumulator inits: -lse/alpha and -D for the lane's queries
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -527,19 +562,18 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
           negD[4 * g + i] = -dv4[i];
         }
       }
-      // prefetch the next query tile once the operand reads have returned
-      wait_lgkm0();
-      if (jj + 1 < JT && jt + BWD_WAVES < njt) stage_tile(j0 + 32 * BWD_WAVES);
 
       f32x16 dqT = {};  // dQ^T partial of this key block: K^T (32 x 64 keys) dS^T (64 keys x 32 queries)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         if (kt >= nkt) continue;  // absent key tile at a ragged end
-        f32x16 s = mfma(qA0, kB[kt][0], negL);  // q.k - lse/alpha
-        s = mfma(qA1, kB[kt][1], s);
-        f32x16 dp = mfma(dA0, vB[kt][0], negD);  // dP - D
-        dp = mfma(dA1, vB[kt][1], dp);
-        const uint16_t *brow = biasT + (32 * kt + ll) * bstr + j0 + 4 * hh;
+        const uint16_t *kr = kbuf + (32 * kt + ll) * HD;
+        const uint16_t *vr = vbuf + (32 * kt + ll) * HD;
+        f32x16 s = mfma(qA0, as_bf16x8(*(const u32x4 *)(kr + 8 * hh)), negL);  // q.k - lse/alpha
+        s = mfma(qA1, as_bf16x8(*(const u32x4 *)(kr + 16 + 8 * hh)), s);
+        f32x16 dp = mfma(dA0, as_bf16x8(*(const u32x4 *)(vr + 8 * hh)), negD);  // dP - D
+        dp = mfma(dA1, as_bf16x8(*(const u32x4 *)(vr + 16 + 8 * hh)), dp);
+        const uint16_t *brow = s_biasT + (32 * kt + ll) * bstr + j0 + 4 * hh;
         float p[16], ds[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -570,8 +604,8 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
         *(u32x2 *)(drow + 16) = (u32x2){s1[0], s1[1]};
         *(u32x2 *)(drow + 24) = (u32x2){s1[2], s1[3]};
 #pragma unroll
-        for (int s = 2 * kt; s < 2 * kt + 2; ++s)
-          dqT = mfma(tr_operand(kbuf, 16 * s, lane), tr_operand(wds, 16 * s, lane), dqT);
+        for (int s2 = 2 * kt; s2 < 2 * kt + 2; ++s2)
+          dqT = mfma(tr_operand(kbuf, 16 * s2, lane), tr_operand(wds, 16 * s2, lane), dqT);
       }
       float *qout = dq_part + ((((long long)b * N + r) * N + j0 + ll) * a.H + h) * HD + 4 * hh;
 #pragma unroll
@@ -579,7 +613,14 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
         *(f32x4 *)(qout + 8 * g) = (f32x4){dqT[4 * g], dqT[4 * g + 1], dqT[4 * g + 2], dqT[4 * g + 3]};
     }
 
-    // fixed-order cross-wave reduction of dV then dK for this row
+    // fixed-order cross-wave reduction of dV then dK for this row.  Each wave's
+    // 64 x 32 fp32 partial goes to its staging: key rows 0-31 to the dS^T
+    // buffer, 32-47 to the q buffer, 48-63 to the dO buffer.
+    auto red_ptr = [&](int w, int krow) -> float * {
+      if (krow < 32) return (float *)(s_ds + w * BWD_BK * HD) + krow * HD;
+      if (krow < 48) return (float *)(s_q + w * 32 * HD) + (krow - 32) * HD;
+      return (float *)(s_do + w * 32 * HD) + (krow - 48) * HD;
+    };
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
       wait_lgkm0();
@@ -590,7 +631,7 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int krow = 32 * kt + 8 * (i >> 2) + 4 * hh + (i & 3);
-          wred[krow * HD + ll] = acc[i];
+          red_ptr(wave, krow)[ll] = acc[i];
         }
       }
       __syncthreads();
@@ -601,9 +642,9 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
         const int e = 4 * (tid + 256 * u);
         const int kr = e / HD, c = e - kr * HD;
         if (k0 + kr >= N) continue;
-        f32x4 sum = *(const f32x4 *)((const float *)wstage + e);
+        f32x4 sum = *(const f32x4 *)(red_ptr(0, kr) + c);
 #pragma unroll
-        for (int w = 1; w < BWD_WAVES; ++w) sum += *(const f32x4 *)((const float *)(wstage + w * BWD_WAVE_ELEMS) + e);
+        for (int w = 1; w < BWD_WAVES; ++w) sum += *(const f32x4 *)(red_ptr(w, kr) + c);
         sum *= scale;
         const long long off = base + (long long)(k0 + kr) * a.f.sQ + c;
         *(u32x2 *)(dst + off) = (u32x2){pack_bf16(sum[0], sum[1]), pack_bf16(sum[2], sum[3])};
@@ -612,6 +653,14 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
     // the next row's staging must have landed in LDS for every wave before the barrier
     wait_vm<0>();
     __syncthreads();
+  };
+
+  if (r0 < r1) stage_row(r0, s_kv0, s_st0);
+  wait_vm<0>();
+  __syncthreads();
+  for (int r = r0; r < r1; r += 2) {
+    row_body(std::integral_constant<int, 0>{}, r);
+    if (r + 1 < r1) row_body(std::integral_constant<int, 1>{}, r + 1);
   }
 
   // dbias partial of this row chunk for the block's keys and every query
@@ -746,8 +795,7 @@ BwdPlan plan_bwd(const tri_attn_problem *p) {
   if (C > N) C = N;
   pl.rows_per_chunk = (N + C - 1) / C;
   pl.C = (N + pl.rows_per_chunk - 1) / pl.rows_per_chunk;
-  pl.lds_bytes = (size_t)BWD_BK * (N + 8) * 2 + (size_t)2 * 2 * BWD_BK * HD * 2 + (size_t)2 * 2 * N * 4 +
-                 (size_t)BWD_WAVES * BWD_WAVE_ELEMS * 2;
+  pl.lds_bytes = 0;  // static LDS, sized by the JT instantiation
   const size_t B = p->B, NN = (size_t)N * N, H = p->H;
   pl.off_delta = 0;
   pl.off_dq = align256(B * N * H * N * 4);
@@ -759,8 +807,6 @@ BwdPlan plan_bwd(const tri_attn_problem *p) {
 template <int JT>
 hipError_t launch_main(const BwdArgs &args, int grid, size_t lds, hipStream_t stream) {
   auto kern = bwd_main_kernel<JT>;
-  hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(BWD_WAVES * 64), lds, stream, args);
   return hipGetLastError();
 }
@@ -834,7 +880,7 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
   a.c1 = a.alpha * kLog2e;
   a.n_jblocks = a.N / FWD_BJ;
   const int groups = a.B * a.H * a.n_jblocks;
-  int chunks = (768 + groups - 1) / groups;
+  int chunks = (768 + groups - 1) / groups;  // about three rounds of one workgroup per CU
   if (chunks > a.N) chunks = a.N;
   a.rows_per_chunk = (a.N + chunks - 1) / chunks;
   a.n_chunks = (a.N + a.rows_per_chunk - 1) / a.rows_per_chunk;
