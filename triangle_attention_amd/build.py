@@ -13,8 +13,12 @@ LIB = HERE / "libtri_attn.so"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU forms are disabled for all device code (-packed-fp32-ops).
+# MFMA results start in architectural VGPRs (-amdgpu-mfma-vgpr-form): the
+# per-tile score, dP and dQ products are read by VALU code, and only the
+# long-lived backward accumulators (dbias, dK, dV) end up in AGPRs.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wno-unused-command-line-argument"]
 
 

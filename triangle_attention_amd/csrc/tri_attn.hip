@@ -285,18 +285,22 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
-// Backward: D = rowsum(dO * O) in fp32 (O = float(o) + residual when saved)
+// Backward: per-query statistics for the main kernel
 // ------------------------------------------------------------------------------------
+// For every (b, r, h, q) the main kernel needs -lse/alpha and -D, the initial values
+// of its score and dP accumulators.  D = rowsum(dO * O) in fp32 with O = float(o) +
+// residual when the residual is saved; the channel sum runs in a fixed order.
 struct PrepArgs {
   const uint16_t *o, *d_o;
-  const float *res;
-  float *delta;
+  const float *res, *lse;
+  float *stats;  // [B][N][H][2][N]: -lse/alpha, then -D
   Frame f;
   int B, N, H;
+  float inv_alpha;
 };
 
 // One thread per (b, r, q, h), heads fastest so that a wave reads whole
-// 256-byte (position, all heads) segments; the channel sum runs in a fixed order.
+// 256-byte (position, all heads) segments.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
   const long long total = (long long)a.B * a.N * a.N * a.H;
   const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -334,39 +338,80 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
       acc = fmaf(bf_hi(gw[i][w]), o1, acc);
     }
   }
-  a.delta[(((long long)b * a.N + r) * a.H + h) * a.N + q] = acc;
+  const long long row = ((long long)b * a.N + r) * a.H + h;
+  const float L = a.lse[row * a.N + q];
+  a.stats[row * 2 * a.N + q] = -L * a.inv_alpha;
+  a.stats[row * 2 * a.N + a.N + q] = -acc;
 }
 
 // ------------------------------------------------------------------------------------
 // Backward main kernel
 // ------------------------------------------------------------------------------------
 // One workgroup (4 waves, one per SIMD) owns a block of 64 keys of one head for a
-// chunk of attention rows, and every query.  Per row, the block's keys and values
-// and the row's per-query statistics (lse, D) are staged in LDS by direct
-// global-to-LDS loads, double-buffered so that the next row's arrive while this
-// row is computed.  Each wave walks its query tiles (32 queries; the next tile's
-// q and dO are fetched into LDS while the current one is computed) and for every
-// 32x32 (query, key) tile recomputes the scores and probabilities once, then
-//   dP - D   = dO V^T + (-D)            (MFMA, -D as the accumulator's initial value)
-//   dS       = P * (dP - D)             (fp32)
-//   dV, dK  += P^T dO, dS^T q           (MFMA, per-wave partials)
-//   dbias   += I * dS                   (MFMA against an identity, fp32 accumulators
-//                                        held over the chunk's rows)
-//   dQ^T     = K^T dS^T over 64 keys    (MFMA, one partial per key block)
+// chunk of attention rows, and every query.  The block's pair bias is held in LDS
+// for the whole chunk (transposed, fp16: bf16 values convert exactly).  Per row the
+// block's keys and values sit in LDS; each wave walks its query tiles (32 queries)
+// and for every 32x32 (query, key) tile recomputes the scores and probabilities once:
+//   S - lse/alpha = Q K^T - lse/alpha     (MFMA)
+//   dP - D        = dO V^T - D            (MFMA)
+//   P             = exp2(c1 (S - lse/alpha) + log2(e) bias)
+//   dS            = P * (dP - D)
+//   dV, dK       += P^T dO, dS^T Q        (MFMA, per-wave partials for the row)
+//   dbias        += I * dS                (MFMA against an identity; fp32 accumulators
+//                                          held over the chunk's rows)
+//   dQ^T          = K^T dS^T over 64 keys (MFMA, one fp32 partial per key block)
 // At the end of a row the four waves' dK/dV partials are summed in LDS in wave
 // order; dbias leaves the kernel as one partial per row chunk.
 //
-// Every staging buffer is its own __shared__ array and the two row buffers are
-// addressed through compile-time parity, so that the compiler's alias analysis
-// can tell the in-flight direct-to-LDS writes apart from the reads of the
-// current data and does not serialise the prefetches.
+// The per-query terms -lse/alpha and -D enter the score and dP products through
+// one more contraction slice: the lane of query j supplies the three-part bf16
+// split (hi + mid + lo, exact for a finite fp32 value) of its term against a
+// column of ones.  The lane therefore carries two floats per query tile instead of
+// the 32 accumulator-layout values an initial-value form would need, which leaves
+// registers for fetching the next query tile (q, dO and the two terms) while the
+// current one is computed.  The next row's keys, values and key mask are fetched
+// into registers while the current row runs.  Query and dO tiles go through a
+// per-wave LDS tile only for the transposed operands of the dK and dV products.
+// The 64-byte rows of LDS tiles have their 16-byte chunks permuted per row
+// (tile_off) so that row reads of MFMA operands and transposing reads are free of
+// bank conflicts.
 constexpr int BWD_WAVES = 4;
 constexpr int BWD_BK = 64;
+
+// Offset of element (row, col) of a [rows][32] bf16 LDS tile whose 16-byte chunks
+// are permuted by bits 1 and 2 of the row.
+__device__ __forceinline__ int tile_off(int row, int col) {
+  const int sw = (row & 2) | ((row >> 2) & 1);
+  return row * HD + (((col >> 3) ^ sw) << 3) + (col & 7);
+}
+// tr_operand for a tile laid out by tile_off (rows base_row + 8 + x share the chunk
+// permutation of rows base_row + x).
+__device__ __forceinline__ bf16x8 tr_operand_sw(const uint16_t *tile, int base_row, int lane) {
+  const int g = lane >> 4, w = lane & 15, m = w >> 2, s = w & 3;
+  const int row = base_row + 4 * (g >> 1) + m;
+  const uint16_t *p = tile + tile_off(row, 16 * (g & 1) + 4 * s);
+  return tr_read(p, p + 8 * HD);
+}
+
+// A-operand slice carrying x for the lane's query row: elements 0..2 of the lanes
+// with hh = 0 hold bf16 hi, mid, lo with hi + mid + lo = x exactly for finite x
+// (x = -inf gives hi = -inf and zeros); every other element is zero.
+__device__ __forceinline__ bf16x8 split3_operand(float x, int hh) {
+  const unsigned w0 = pack_bf16(x, 0.f);
+  const float hi = bf_lo(w0);
+  const float r1 = isfinite(x) ? x - hi : 0.f;
+  const unsigned w1 = pack_bf16(r1, 0.f);
+  const float r2 = r1 - bf_lo(w1);
+  const unsigned lo16 = pack_bf16(r2, 0.f);
+  u32x4 w = {(w0 & 0xffffu) | (w1 << 16), lo16 & 0xffffu, 0u, 0u};
+  if (hh) w = (u32x4){0u, 0u, 0u, 0u};
+  return as_bf16x8(w);
+}
 
 struct BwdArgs {
   const uint16_t *q, *k, *v, *bias, *d_o;
   const uint8_t *mask;
-  const float *lse, *delta;
+  const float *stats;  // [B][N][H][2][N]: -lse/alpha, -D
   uint16_t *dk, *dv;
   float *dq_part;  // [T][B][N][N][H][D], attended frame
   float *db_part;  // [C][B][H][N][N]
@@ -376,36 +421,24 @@ struct BwdArgs {
   float alpha, c1;
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-// 16 bytes per lane from global memory straight into LDS at dst + 16 * lane.
-__device__ __forceinline__ void load_lds16(const void *src, void *dst_wave) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void *)dst_wave, 16, 0, 0);
-}
-// wait until at most n vector-memory operations of this wave are outstanding
-// (gfx9 vector memory operations complete in issue order)
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
-}
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 
 template <int JT>
 __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) {
   constexpr int NMAX = 32 * BWD_WAVES * JT;
-  __shared__ __attribute__((aligned(16))) uint16_t s_biasT[BWD_BK * (NMAX + 8)];
-  __shared__ __attribute__((aligned(16))) uint16_t s_kv0[2 * BWD_BK * HD], s_kv1[2 * BWD_BK * HD];
-  __shared__ __attribute__((aligned(16))) float s_st0[2 * NMAX], s_st1[2 * NMAX];
-  __shared__ __attribute__((aligned(16))) uint16_t s_q[BWD_WAVES * 32 * HD], s_do[BWD_WAVES * 32 * HD];
+  constexpr int BSTR = NMAX + 4;  // fp16 row stride of the bias tile: conflict-free 8-byte reads
+  __shared__ __attribute__((aligned(16))) _Float16 s_bias[BWD_BK * BSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t s_kv[2 * BWD_BK * HD];
+  __shared__ __attribute__((aligned(16))) uint16_t s_qd[BWD_WAVES * 2 * 32 * HD];
   __shared__ __attribute__((aligned(16))) uint16_t s_ds[BWD_WAVES * BWD_BK * HD];
 
   const int N = a.N;
-  const int bstr = N + 8;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, ll = lane & 31;
-  uint16_t *wq = s_q + wave * 32 * HD;
-  uint16_t *wdo = s_do + wave * 32 * HD;
+  uint16_t *wq = s_qd + wave * 2 * 32 * HD;
+  uint16_t *wdo = wq + 32 * HD;
   uint16_t *wds = s_ds + wave * BWD_BK * HD;
+  const uint16_t *s_v = s_kv + BWD_BK * HD;
 
   int t = xcd_remap(blockIdx.x, gridDim.x);
   const int kb = t % a.n_kblocks; t /= a.n_kblocks;
@@ -418,9 +451,52 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
   const int r0 = chunk * a.rows_per_chunk;
   const int r1 = min(N, r0 + a.rows_per_chunk);
   const float c1 = a.c1;
-  const float inv_alpha = 1.f / a.alpha;
 
-  // transposed pair-bias tile: biasT[kk][j] = bias[b, h, j, k0 + kk]
+  // row r of head h of batch b: q, k, v, dO (element offset) and the statistics row
+  auto rowbase = [&](int r) -> long long {
+    return (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
+  };
+  auto stats_of = [&](int r) -> const float * {
+    return a.stats + (((long long)b * N + r) * a.H + h) * 2 * N;
+  };
+  // keys and values of the block: thread tid carries 16 bytes of each (key tid/4, part tid%4)
+  auto load_kv = [&](int r, u32x4 &kw, u32x4 &vw) {
+    const int key = min(k0 + (tid >> 2), N - 1);
+    const long long off = rowbase(r) + (long long)key * a.f.sQ + (tid & 3) * 8;
+    kw = ld16(a.k + off);
+    vw = ld16(a.v + off);
+  };
+  auto store_kv = [&](u32x4 kw, u32x4 vw) {
+    const int row = tid >> 2, part = tid & 3;
+    *(u32x4 *)(s_kv + tile_off(row, part * 8)) = kw;
+    *(u32x4 *)(s_kv + BWD_BK * HD + tile_off(row, part * 8)) = vw;
+  };
+  // mask bytes of the lane's keys (bit 0: key k0 + ll, bit 8: key k0 + 32 + ll)
+  auto load_mask = [&](int r) -> unsigned {
+    unsigned m = 0x101u;
+    if (a.mask) {
+      const uint8_t *mr = a.mask + (long long)b * a.f.mB + (long long)r * a.f.mR;
+      m = mr[(long long)(k0 + ll) * a.f.mK] != 0 ? 1u : 0u;
+      if (nkt > 1 && mr[(long long)(k0 + 32 + ll) * a.f.mK] != 0) m |= 0x100u;
+    }
+    return m;
+  };
+  // one query tile: the lane's q and dO row halves (A operands as loaded) and the
+  // two per-query terms of the lane's query
+  u32x4 tq0, tq1, td0, td1;
+  float tl = 0.f, tdl = 0.f;
+  auto load_qtile = [&](int r, int jt) {
+    const long long off = rowbase(r) + (long long)(jt * 32 + ll) * a.f.sQ + 8 * hh;
+    tq0 = ld16(a.q + off);
+    tq1 = ld16(a.q + off + 16);
+    td0 = ld16(a.d_o + off);
+    td1 = ld16(a.d_o + off + 16);
+    const float *sp = stats_of(r) + jt * 32 + ll;
+    tl = sp[0];
+    tdl = sp[N];
+  };
+
+  // transposed pair-bias tile: s_bias[kk][j] = bias[b, h, j, k0 + kk]
   {
     const uint16_t *src = a.bias + ((long long)b * a.H + h) * N * N + k0;
     const int per_row = nkt * 4;  // 8-key chunks per query row
@@ -429,8 +505,8 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
       const u32x4 w = ld16(src + (long long)j * N + c8 * 8);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s_biasT[(c8 * 8 + 2 * i) * bstr + j] = (uint16_t)(w[i] & 0xffffu);
-        s_biasT[(c8 * 8 + 2 * i + 1) * bstr + j] = (uint16_t)(w[i] >> 16);
+        s_bias[(c8 * 8 + 2 * i) * BSTR + j] = (_Float16)bf_lo(w[i]);
+        s_bias[(c8 * 8 + 2 * i + 1) * BSTR + j] = (_Float16)bf_hi(w[i]);
       }
     }
   }
@@ -451,28 +527,8 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
     }
     ident[s] = as_bf16x8((u32x4){w[0], w[1], w[2], w[3]});
   }
-
-  // row staging (direct to LDS): keys and values of the block (2 instructions per
-  // wave), lse and D of the row (up to 2 per wave)
-  const long long stat_row = (long long)a.H * N;
-  auto stage_row = [&](int r, uint16_t *kd, float *sd) {
-    const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int ch = 64 * (2 * wave + u) + lane;  // 16-byte chunk of [K | V]
-      const int which = ch >> 8, rem = ch & 255, key = min(k0 + (rem >> 2), N - 1), part = rem & 3;
-      load_lds16((which ? a.v : a.k) + base + (long long)key * a.f.sQ + part * 8, kd + 64 * (2 * wave + u) * 8);
-    }
-    const long long so = ((long long)b * N + r) * stat_row + (long long)h * N;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c0 = 64 * (2 * wave + u), c = c0 + lane;  // 16-byte chunk of [lse | D]
-      if (c < N / 2) {
-        const float *src = c < N / 4 ? a.lse + so + 4 * c : a.delta + so + 4 * (c - N / 4);
-        load_lds16(src, sd + 4 * c0);
-      }
-    }
-  };
+  // B operand of the per-query-term slice: ones in contraction rows 0..2
+  const bf16x8 ones3 = as_bf16x8(hh ? (u32x4){0u, 0u, 0u, 0u} : (u32x4){0x3f803f80u, 0x3f80u, 0u, 0u});
 
   f32x16 dbias[JT][2];
 #pragma unroll
@@ -483,27 +539,27 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
   const long long E = (long long)a.B * N * N * a.H * HD;
   float *dq_part = a.dq_part + (long long)kb * E;
 
-  // one attention row; CUR selects the row's staging buffers at compile time
-  auto row_body = [&](auto cur_tag, int r) {
-    constexpr int CUR = decltype(cur_tag)::value;
-    uint16_t *kbuf = CUR ? s_kv1 : s_kv0;
-    const float *Ls = CUR ? s_st1 : s_st0;
-    const float *Ds = Ls + N;
-    const uint16_t *vbuf = kbuf + BWD_BK * HD;
-    const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
+  // prologue: the first row's keys, values, key mask and first query tile
+  u32x4 nk = {}, nv = {};
+  unsigned nmask = 0x101u;
+  if (r0 < r1) {
+    load_kv(r0, nk, nv);
+    nmask = load_mask(r0);
+    if (wave < njt) load_qtile(r0, wave);
+  }
+  store_kv(nk, nv);
+  __syncthreads();
 
-    // mask of the keys this lane owns in the score layout
-    bool kvalid[2];
-    bool tile_full = true;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int key = k0 + 32 * kt + ll;
-      bool ok = key < N;
-      if (ok && a.mask)
-        ok = a.mask[(long long)b * a.f.mB + (long long)r * a.f.mR + (long long)key * a.f.mK] != 0;
-      kvalid[kt] = ok;
-      if (__ballot(ok) != ~0ull) tile_full = false;
+  for (int r = r0; r < r1; ++r) {
+    const bool has_next = r + 1 < r1;
+    const unsigned cmask = nmask;
+    if (has_next) {
+      load_kv(r + 1, nk, nv);
+      nmask = load_mask(r + 1);
     }
+    // exp2 argument offset of the lane's key per key tile: 0, or -inf for a masked key
+    const float moff[2] = {(cmask & 0xffu) ? 0.f : -INFINITY, (cmask >> 8) ? 0.f : -INFINITY};
+    const long long base = rowbase(r);
 
     f32x16 dK[2], dV[2];
 #pragma unroll
@@ -512,80 +568,54 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
       dV[kt] = (f32x16){};
     }
 
-    // q and dO of a query tile into this wave's staging (4 instructions)
-    auto stage_tile = [&](int j0) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int ch = lane + 64 * u, jr = ch >> 2, part = ch & 3;
-        const long long off = base + (long long)(j0 + jr) * a.f.sQ + part * 8;
-        load_lds16(a.q + off, wq + 512 * u);
-        load_lds16(a.d_o + off, wdo + 512 * u);
-      }
-    };
-    wait_lgkm0();  // this wave's reads of its staging (previous row) are done
-    if (wave < njt) stage_tile(wave * 32);
-    // the next row's staging goes to the other buffers, last read during the previous row
-    const bool has_next = r + 1 < r1;
-    if (has_next) stage_row(r + 1, CUR ? s_kv0 : s_kv1, CUR ? s_st0 : s_st1);
-
 #pragma unroll
     for (int jj = 0; jj < JT; ++jj) {
       const int jt = wave + BWD_WAVES * jj;
       if (jt >= njt) break;
       const int j0 = jt * 32;
-      // outstanding, oldest first: [next-row staging: >= 2 if has_next] [this tile: 4] for
-      // the first tile; [this tile: 4] [previous tile's dQ stores: 4] afterwards
-      if (jj == 0) {
-        if (has_next) wait_vm<2>(); else wait_vm<0>();
-      } else {
-        wait_vm<4>();
-      }
-      const bf16x8 qA0 = as_bf16x8(*(const u32x4 *)(wq + ll * HD + 8 * hh));
-      const bf16x8 qA1 = as_bf16x8(*(const u32x4 *)(wq + ll * HD + 16 + 8 * hh));
-      const bf16x8 dA0 = as_bf16x8(*(const u32x4 *)(wdo + ll * HD + 8 * hh));
-      const bf16x8 dA1 = as_bf16x8(*(const u32x4 *)(wdo + ll * HD + 16 + 8 * hh));
-      const bf16x8 qB0 = tr_operand(wq, 0, lane);
-      const bf16x8 qB1 = tr_operand(wq, 16, lane);
-      const bf16x8 dB0 = tr_operand(wdo, 0, lane);
-      const bf16x8 dB1 = tr_operand(wdo, 16, lane);
-      // prefetch the next query tile once the operand reads have returned
-      wait_lgkm0();
-      if (jj + 1 < JT && jt + BWD_WAVES < njt) stage_tile(j0 + 32 * BWD_WAVES);
-      f32x16 negL, negD;  // accumulator inits: -lse/alpha and -D for the lane's queries
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 lv = *(const f32x4 *)(Ls + j0 + 8 * g + 4 * hh);
-        const f32x4 dv4 = *(const f32x4 *)(Ds + j0 + 8 * g + 4 * hh);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          negL[4 * g + i] = -lv[i] * inv_alpha;
-          negD[4 * g + i] = -dv4[i];
-        }
-      }
+      // this tile's q and dO rows: A operands as loaded, and into LDS for the
+      // transposed B operands of the dK and dV products
+      const bf16x8 qA0 = as_bf16x8(tq0), qA1 = as_bf16x8(tq1);
+      const bf16x8 dA0 = as_bf16x8(td0), dA1 = as_bf16x8(td1);
+      const bf16x8 lA = split3_operand(tl, hh), dlA = split3_operand(tdl, hh);
+      *(u32x4 *)(wq + tile_off(ll, 8 * hh)) = tq0;
+      *(u32x4 *)(wq + tile_off(ll, 16 + 8 * hh)) = tq1;
+      *(u32x4 *)(wdo + tile_off(ll, 8 * hh)) = td0;
+      *(u32x4 *)(wdo + tile_off(ll, 16 + 8 * hh)) = td1;
+      const bf16x8 qB0 = tr_operand_sw(wq, 0, lane), qB1 = tr_operand_sw(wq, 16, lane);
+      const bf16x8 dB0 = tr_operand_sw(wdo, 0, lane), dB1 = tr_operand_sw(wdo, 16, lane);
 
-      f32x16 dqT = {};  // dQ^T partial of this key block: K^T (32 x 64 keys) dS^T (64 keys x 32 queries)
+      f32x16 dqT = {};
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        if (kt >= nkt) continue;  // absent key tile at a ragged end
-        const uint16_t *kr = kbuf + (32 * kt + ll) * HD;
-        const uint16_t *vr = vbuf + (32 * kt + ll) * HD;
-        f32x16 s = mfma(qA0, as_bf16x8(*(const u32x4 *)(kr + 8 * hh)), negL);  // q.k - lse/alpha
-        s = mfma(qA1, as_bf16x8(*(const u32x4 *)(kr + 16 + 8 * hh)), s);
-        f32x16 dp = mfma(dA0, as_bf16x8(*(const u32x4 *)(vr + 8 * hh)), negD);  // dP - D
-        dp = mfma(dA1, as_bf16x8(*(const u32x4 *)(vr + 16 + 8 * hh)), dp);
-        const uint16_t *brow = s_biasT + (32 * kt + ll) * bstr + j0 + 4 * hh;
+        if (kt >= nkt) break;  // absent key tile at a ragged end
+        const int krow = 32 * kt + ll;
+        const bf16x8 kB0 = *(const bf16x8 *)(s_kv + tile_off(krow, 8 * hh));
+        const bf16x8 kB1 = *(const bf16x8 *)(s_kv + tile_off(krow, 16 + 8 * hh));
+        const bf16x8 vB0 = *(const bf16x8 *)(s_v + tile_off(krow, 8 * hh));
+        const bf16x8 vB1 = *(const bf16x8 *)(s_v + tile_off(krow, 16 + 8 * hh));
+        f32x16 s = mfma(lA, ones3, (f32x16){});  // -lse/alpha
+        s = mfma(qA0, kB0, s);
+        s = mfma(qA1, kB1, s);                    // q.k - lse/alpha
+        f32x16 dp = mfma(dlA, ones3, (f32x16){}); // -D
+        dp = mfma(dA0, vB0, dp);
+        dp = mfma(dA1, vB1, dp);                  // dP - D
+        if (kt == nkt - 1) {
+          // the tile's q, dO and per-query terms are consumed: fetch the next tile's
+          if (jt + BWD_WAVES < njt)
+            load_qtile(r, jt + BWD_WAVES);
+          else if (has_next)
+            load_qtile(r + 1, wave);
+        }
+        const _Float16 *brow = s_bias + krow * BSTR + j0 + 4 * hh;
         float p[16], ds[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const u32x2 bw = *(const u32x2 *)(brow + 8 * g);
-          const float beta[4] = {bf_lo(bw[0]), bf_hi(bw[0]), bf_lo(bw[1]), bf_hi(bw[1])};
+          const f16x4 bw = *(const f16x4 *)(brow + 8 * g);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            p[4 * g + i] = __builtin_amdgcn_exp2f(fmaf(s[4 * g + i], c1, beta[i] * kLog2e));
-        }
-        if (!tile_full && !kvalid[kt]) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) p[i] = 0.f;
+            p[4 * g + i] =
+                __builtin_amdgcn_exp2f(fmaf((float)bw[i], kLog2e, fmaf(s[4 * g + i], c1, moff[kt])));
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) ds[i] = p[i] * dp[i];
@@ -597,15 +627,14 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
         dK[kt] = mfma(sA1, qB1, dK[kt]);
         dbias[jj][kt] = mfma(ident[0], sA0, dbias[jj][kt]);
         dbias[jj][kt] = mfma(ident[1], sA1, dbias[jj][kt]);
+        // dS^T rows of this key tile for the dQ product (rows = keys, columns = queries)
         const u32x4 s0 = __builtin_bit_cast(u32x4, sA0), s1 = __builtin_bit_cast(u32x4, sA1);
-        uint16_t *drow = wds + (32 * kt + ll) * HD + 4 * hh;
-        *(u32x2 *)(drow + 0) = (u32x2){s0[0], s0[1]};
-        *(u32x2 *)(drow + 8) = (u32x2){s0[2], s0[3]};
-        *(u32x2 *)(drow + 16) = (u32x2){s1[0], s1[1]};
-        *(u32x2 *)(drow + 24) = (u32x2){s1[2], s1[3]};
-#pragma unroll
-        for (int s2 = 2 * kt; s2 < 2 * kt + 2; ++s2)
-          dqT = mfma(tr_operand(kbuf, 16 * s2, lane), tr_operand(wds, 16 * s2, lane), dqT);
+        *(u32x2 *)(wds + tile_off(krow, 4 * hh)) = (u32x2){s0[0], s0[1]};
+        *(u32x2 *)(wds + tile_off(krow, 8 + 4 * hh)) = (u32x2){s0[2], s0[3]};
+        *(u32x2 *)(wds + tile_off(krow, 16 + 4 * hh)) = (u32x2){s1[0], s1[1]};
+        *(u32x2 *)(wds + tile_off(krow, 24 + 4 * hh)) = (u32x2){s1[2], s1[3]};
+        dqT = mfma(tr_operand_sw(s_kv, 32 * kt, lane), tr_operand_sw(wds, 32 * kt, lane), dqT);
+        dqT = mfma(tr_operand_sw(s_kv, 32 * kt + 16, lane), tr_operand_sw(wds, 32 * kt + 16, lane), dqT);
       }
       float *qout = dq_part + ((((long long)b * N + r) * N + j0 + ll) * a.H + h) * HD + 4 * hh;
 #pragma unroll
@@ -614,27 +643,24 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
     }
 
     // fixed-order cross-wave reduction of dV then dK for this row.  Each wave's
-    // 64 x 32 fp32 partial goes to its staging: key rows 0-31 to the dS^T
-    // buffer, 32-47 to the q buffer, 48-63 to the dO buffer.
-    auto red_ptr = [&](int w, int krow) -> float * {
-      if (krow < 32) return (float *)(s_ds + w * BWD_BK * HD) + krow * HD;
-      if (krow < 48) return (float *)(s_q + w * 32 * HD) + (krow - 32) * HD;
-      return (float *)(s_do + w * 32 * HD) + (krow - 48) * HD;
+    // 64 x 32 fp32 partial goes to its own staging: key rows 0-31 to the dS^T
+    // tile, rows 32-63 to the q/dO tiles.
+    auto red_ptr = [&](int w, int kr) -> float * {
+      if (kr < 32) return (float *)(s_ds + w * BWD_BK * HD) + kr * HD;
+      return (float *)(s_qd + w * 2 * 32 * HD) + (kr - 32) * HD;
     };
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
-      wait_lgkm0();
-      __syncthreads();
+      if (which) __syncthreads();  // every wave has read the dV partials
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const f32x16 &acc = which ? dK[kt] : dV[kt];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int krow = 32 * kt + 8 * (i >> 2) + 4 * hh + (i & 3);
-          red_ptr(wave, krow)[ll] = acc[i];
-        }
+        for (int i = 0; i < 16; ++i) red_ptr(wave, 32 * kt + 8 * (i >> 2) + 4 * hh + (i & 3))[ll] = acc[i];
       }
       __syncthreads();
+      // every wave is past its last read of this row's keys and values: stage the next row's
+      if (!which) store_kv(nk, nv);
       const float scale = which ? a.alpha : 1.f;
       uint16_t *dst = which ? a.dk : a.dv;
 #pragma unroll
@@ -650,17 +676,7 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
         *(u32x2 *)(dst + off) = (u32x2){pack_bf16(sum[0], sum[1]), pack_bf16(sum[2], sum[3])};
       }
     }
-    // the next row's staging must have landed in LDS for every wave before the barrier
-    wait_vm<0>();
-    __syncthreads();
-  };
-
-  if (r0 < r1) stage_row(r0, s_kv0, s_st0);
-  wait_vm<0>();
-  __syncthreads();
-  for (int r = r0; r < r1; r += 2) {
-    row_body(std::integral_constant<int, 0>{}, r);
-    if (r + 1 < r1) row_body(std::integral_constant<int, 1>{}, r + 1);
+    __syncthreads();  // partials read, next row's keys and values in LDS
   }
 
   // dbias partial of this row chunk for the block's keys and every query
@@ -779,7 +795,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct BwdPlan {
   int JT, T, C, rows_per_chunk;
   size_t lds_bytes;
-  size_t off_delta, off_dq, off_db, total;
+  size_t off_stats, off_dq, off_db, total;
 };
 
 BwdPlan plan_bwd(const tri_attn_problem *p) {
@@ -797,8 +813,8 @@ BwdPlan plan_bwd(const tri_attn_problem *p) {
   pl.C = (N + pl.rows_per_chunk - 1) / pl.rows_per_chunk;
   pl.lds_bytes = 0;  // static LDS, sized by the JT instantiation
   const size_t B = p->B, NN = (size_t)N * N, H = p->H;
-  pl.off_delta = 0;
-  pl.off_dq = align256(B * N * H * N * 4);
+  pl.off_stats = 0;
+  pl.off_dq = align256(B * N * H * 2 * N * 4);
   pl.off_db = pl.off_dq + align256((size_t)pl.T * B * NN * H * HD * 4);
   pl.total = pl.off_db + align256((size_t)pl.C * B * H * NN * 4);
   return pl;
@@ -936,7 +952,7 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
   const Frame f = make_frame(problem);
   const float alpha = alpha_of(problem);
   char *ws = (char *)workspace;
-  float *delta = (float *)(ws + pl.off_delta);
+  float *stats = (float *)(ws + pl.off_stats);
   float *dq_part = (float *)(ws + pl.off_dq);
   float *db_part = (float *)(ws + pl.off_db);
 
@@ -944,7 +960,9 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
   pa.o = (const uint16_t *)o;
   pa.d_o = (const uint16_t *)d_o;
   pa.res = o_residual;
-  pa.delta = delta;
+  pa.lse = lse;
+  pa.stats = stats;
+  pa.inv_alpha = 1.f / alpha;
   pa.f = f;
   pa.B = (int)p.B;
   pa.N = (int)p.N;
@@ -960,8 +978,7 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
   ba.bias = (const uint16_t *)bias;
   ba.d_o = (const uint16_t *)d_o;
   ba.mask = mask;
-  ba.lse = lse;
-  ba.delta = delta;
+  ba.stats = stats;
   ba.dk = (uint16_t *)dk;
   ba.dv = (uint16_t *)dv;
   ba.dq_part = dq_part;
