@@ -413,8 +413,8 @@ struct BwdArgs {
   const uint8_t *mask;
   const float *stats;  // [B][N][H][2][N]: -lse/alpha, -D
   uint16_t *dk, *dv;
-  float *dq_part;  // [T][B][N][N][H][D], attended frame
-  float *db_part;  // [C][B][H][N][N]
+  uint16_t *dq_part;  // [T][B][N rows][H][N queries][D] bf16, attended frame
+  float *db_part;     // [C][B][H][N][N]
   Frame f;
   int B, N, H;
   int n_kblocks, n_chunks, rows_per_chunk;
@@ -422,6 +422,14 @@ struct BwdArgs {
 };
 
 typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+
+// Workgroup barrier that orders LDS accesses only: outstanding global loads (the
+// prefetches) and stores stay in flight across it, unlike __syncthreads().
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 template <int JT>
 __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) {
@@ -537,7 +545,7 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
     for (int kt = 0; kt < 2; ++kt) dbias[jj][kt] = (f32x16){};
 
   const long long E = (long long)a.B * N * N * a.H * HD;
-  float *dq_part = a.dq_part + (long long)kb * E;
+  uint16_t *dq_part = a.dq_part + (long long)kb * E;
 
   // prologue: the first row's keys, values, key mask and first query tile
   u32x4 nk = {}, nv = {};
@@ -548,7 +556,7 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
     if (wave < njt) load_qtile(r0, wave);
   }
   store_kv(nk, nv);
-  __syncthreads();
+  lds_barrier();
 
   for (int r = r0; r < r1; ++r) {
     const bool has_next = r + 1 < r1;
@@ -636,10 +644,13 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
         dqT = mfma(tr_operand_sw(s_kv, 32 * kt, lane), tr_operand_sw(wds, 32 * kt, lane), dqT);
         dqT = mfma(tr_operand_sw(s_kv, 32 * kt + 16, lane), tr_operand_sw(wds, 32 * kt + 16, lane), dqT);
       }
-      float *qout = dq_part + ((((long long)b * N + r) * N + j0 + ll) * a.H + h) * HD + 4 * hh;
+      // this key block's dQ partial, rounded to bf16 (summed in fp32 over the blocks);
+      // a wave's four stores fill the tile's contiguous 2 KB of the partial
+      uint16_t *qout = dq_part + ((((long long)b * N + r) * a.H + h) * N + j0 + ll) * HD + 4 * hh;
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        *(f32x4 *)(qout + 8 * g) = (f32x4){dqT[4 * g], dqT[4 * g + 1], dqT[4 * g + 2], dqT[4 * g + 3]};
+        *(u32x2 *)(qout + 8 * g) =
+            (u32x2){pack_bf16(dqT[4 * g], dqT[4 * g + 1]), pack_bf16(dqT[4 * g + 2], dqT[4 * g + 3])};
     }
 
     // fixed-order cross-wave reduction of dV then dK for this row.  Each wave's
@@ -651,14 +662,14 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
     };
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
-      if (which) __syncthreads();  // every wave has read the dV partials
+      if (which) lds_barrier();  // every wave has read the dV partials
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const f32x16 &acc = which ? dK[kt] : dV[kt];
 #pragma unroll
         for (int i = 0; i < 16; ++i) red_ptr(wave, 32 * kt + 8 * (i >> 2) + 4 * hh + (i & 3))[ll] = acc[i];
       }
-      __syncthreads();
+      lds_barrier();
       // every wave is past its last read of this row's keys and values: stage the next row's
       if (!which) store_kv(nk, nv);
       const float scale = which ? a.alpha : 1.f;
@@ -676,7 +687,7 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
         *(u32x2 *)(dst + off) = (u32x2){pack_bf16(sum[0], sum[1]), pack_bf16(sum[2], sum[3])};
       }
     }
-    __syncthreads();  // partials read, next row's keys and values in LDS
+    lds_barrier();  // partials read, next row's keys and values in LDS
   }
 
   // dbias partial of this row chunk for the block's keys and every query
@@ -701,7 +712,8 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
 // Backward: fixed-order reductions of the partials
 // ------------------------------------------------------------------------------------
 struct ReduceArgs {
-  const float *dq_part, *db_part;
+  const uint16_t *dq_part;
+  const float *db_part;
   uint16_t *dq;
   void *dbias;
   Frame f;
@@ -709,24 +721,33 @@ struct ReduceArgs {
   float alpha;
 };
 
+// one thread per 8 channels: the bf16 partials of the key blocks summed in fp32 in
+// block order, times alpha, rounded to bf16 in the caller's frame
 __global__ __launch_bounds__(256) void reduce_dq_kernel(ReduceArgs a) {
   const long long E = (long long)a.B * a.N * a.N * a.H * HD;
-  const long long e = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  const long long e = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (e >= E) return;
-  f32x4 s = *(const f32x4 *)(a.dq_part + e);
-  for (int t = 1; t < a.T; ++t) s += *(const f32x4 *)(a.dq_part + (long long)t * E + e);
-  s *= a.alpha;
-  // attended-frame element (b, r, q, h, c) -> caller's frame
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < a.T; ++t) {
+    const u32x4 w = ld16(a.dq_part + (long long)t * E + e);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[2 * i] += bf_lo(w[i]);
+      s[2 * i + 1] += bf_hi(w[i]);
+    }
+  }
+  // partial element (b, r, h, q, c) -> caller's frame
   const int c = (int)(e % HD);
   long long u = e / HD;
-  const int h = (int)(u % a.H);
-  u /= a.H;
   const int q = (int)(u % a.N);
   u /= a.N;
+  const int h = (int)(u % a.H);
+  u /= a.H;
   const int r = (int)(u % a.N);
   const int b = (int)(u / a.N);
   const long long off = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)q * a.f.sQ + h * HD + c;
-  *(u32x2 *)(a.dq + off) = (u32x2){pack_bf16(s[0], s[1]), pack_bf16(s[2], s[3])};
+  *(u32x4 *)(a.dq + off) = (u32x4){pack_bf16(s[0] * a.alpha, s[1] * a.alpha), pack_bf16(s[2] * a.alpha, s[3] * a.alpha),
+                                   pack_bf16(s[4] * a.alpha, s[5] * a.alpha), pack_bf16(s[6] * a.alpha, s[7] * a.alpha)};
 }
 
 __global__ __launch_bounds__(256) void reduce_dbias_kernel(ReduceArgs a) {
@@ -815,7 +836,7 @@ BwdPlan plan_bwd(const tri_attn_problem *p) {
   const size_t B = p->B, NN = (size_t)N * N, H = p->H;
   pl.off_stats = 0;
   pl.off_dq = align256(B * N * H * 2 * N * 4);
-  pl.off_db = pl.off_dq + align256((size_t)pl.T * B * NN * H * HD * 4);
+  pl.off_db = pl.off_dq + align256((size_t)pl.T * B * NN * H * HD * 2);
   pl.total = pl.off_db + align256((size_t)pl.C * B * H * NN * 4);
   return pl;
 }
@@ -953,7 +974,7 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
   const float alpha = alpha_of(problem);
   char *ws = (char *)workspace;
   float *stats = (float *)(ws + pl.off_stats);
-  float *dq_part = (float *)(ws + pl.off_dq);
+  uint16_t *dq_part = (uint16_t *)(ws + pl.off_dq);
   float *db_part = (float *)(ws + pl.off_db);
 
   PrepArgs pa;
@@ -1011,7 +1032,7 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
   ra.C = pl.C;
   ra.dbias_fp32 = (p.flags & TRI_ATTN_FLAG_DBIAS_FP32) ? 1 : 0;
   ra.alpha = alpha;
-  hipLaunchKernelGGL(reduce_dq_kernel, dim3((unsigned)((E / 4 + 255) / 256)), dim3(256), 0, stream, ra);
+  hipLaunchKernelGGL(reduce_dq_kernel, dim3((unsigned)((E / 8 + 255) / 256)), dim3(256), 0, stream, ra);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
   hipLaunchKernelGGL(reduce_dbias_kernel, dim3((unsigned)((nb / 4 + 255) / 256)), dim3(256), 0, stream, ra);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
