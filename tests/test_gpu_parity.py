@@ -242,6 +242,16 @@ def test_fully_masked_rows_and_keys(ta):
     assert torch.all(out["dk"][0, :, 40:63] == 0) and torch.all(out["dv"][0, :, 40:63] == 0)
 
 
+def test_forward_probability_overflow(ta):
+    """A key tile whose logits exceed the first attended tile's maximum by far more
+    than the fp32 exponent range: the forward's per-row overflow check must catch
+    it and recompute the row against the true maximum."""
+    inp = custom(1, 96, 2, 17, "none")
+    inp["bias"][:, :, :, 64:] += 150.0   # keys 64..95: logits about 150 above the rest
+    out, ref = check_full(ta, inp, tag="overflow")
+    assert torch.isfinite(out["o"].float()).all() and torch.isfinite(out["lse"]).all()
+
+
 def test_custom_scale_and_fp32_dbias(ta):
     inp = custom(1, 64, 4, 13, "pad32", bias_std=2.0)
     check_full(ta, inp, scale=0.3, tag="scale0.3")

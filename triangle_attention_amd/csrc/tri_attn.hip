@@ -104,20 +104,26 @@ struct Frame {
 // ------------------------------------------------------------------------------------
 // Forward
 // ------------------------------------------------------------------------------------
-// One workgroup = (batch, head, 32 queries, chunk of rows); 12 waves, each working
-// on one attention row at a time.  The block's pair bias, scaled by 1/alpha, sits
-// in LDS in fp32 and is the initial value of the score MFMA, so S^T = K Q^T +
-// bias^T/alpha costs no VALU work.  Per 32-key tile each lane owns one query and
-// 16 keys: p = exp2(c1 * (s - m)) with m a per-query reference maximum.  m is the
-// first attended tile's maximum and is only raised (rescaling the running sum and
-// output) when a later tile would push a probability beyond 2^16, which the
-// tile's probability sum reveals; most tiles need no maximum at all.  K^T rows
-// are MFMA operands read straight from global memory; V goes through a per-wave
-// LDS buffer and is read transposed.  The next tile's K and V are fetched into
-// registers while the current tile is computed.
+// One workgroup = (batch, head, 32 queries, chunk of rows); 12 waves (three per
+// SIMD), each working on one attention row at a time.  The block's pair bias,
+// scaled by 1/alpha, sits in LDS in fp32 and is the initial value of the score
+// MFMA, so S^T = K Q^T + bias^T/alpha costs no VALU work.  Per 32-key tile each lane
+// owns one query and 16 keys: p = exp2(c1 (s - m)) against a per-query reference m,
+// the maximum of the row's first attended tile, summed in fp32.  m is never raised
+// during the pass: a probability beyond the fp32 range shows up at the end of the
+// row as a non-finite sum or output, and only then is the row recomputed against
+// its true maximum (a maximum pass, then the pass again), so a tile costs the
+// fused multiply-add, exponential, sum and bf16 packing of its probabilities and no
+// per-tile maximum or rescaling.
+// K rows are MFMA operands read straight from global memory; V goes through a
+// per-wave LDS buffer and is read transposed.  Key tiles are processed in pairs
+// with two register sets, so each tile's K, V and mask byte arrive during the
+// previous tile.
 constexpr int FWD_WAVES = 12;
 constexpr int FWD_BJ = 32;
-constexpr float kFwdOverflow = 65536.f;  // largest tile probability sum before a rescale
+
+// a readable byte holding 1: the key mask of a problem without one
+__device__ const uint8_t kMaskAllValid = 1;
 
 struct FwdArgs {
   const uint16_t *q, *k, *v, *bias;
@@ -128,6 +134,13 @@ struct FwdArgs {
   int B, N, H;
   int n_jblocks, n_chunks, rows_per_chunk;
   float alpha, inv_alpha, c1;  // c1 = alpha * log2(e)
+};
+
+// operands of one key tile: K^T rows (MFMA A), the lane's V chunks (to LDS) and the
+// mask byte of key (tile * 32 + lane % 32)
+struct FwdTile {
+  u32x4 k0, k1, v0, v1;
+  unsigned m;
 };
 
 __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
@@ -168,38 +181,35 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
   const int r1 = min(N, r0 + a.rows_per_chunk);
   const float c1 = a.c1;
   const int nkt = N / 32;
+  const int vkey = lane >> 2, vpart = lane & 3;  // the lane's V chunk within a tile
+  const long long mk = a.mask ? a.f.mK : 0;
   for (int r = r0 + wave; r < r1; r += FWD_WAVES) {
     const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
     const uint16_t *qp = a.q + base + (long long)(j0 + jl) * a.f.sQ;
     const bf16x8 qB0 = as_bf16x8(ld16(qp + 8 * hh));
     const bf16x8 qB1 = as_bf16x8(ld16(qp + 16 + 8 * hh));
-    const uint8_t *mrow = a.mask ? a.mask + (long long)b * a.f.mB + (long long)r * a.f.mR : nullptr;
+    const uint8_t *mrow = a.mask ? a.mask + (long long)b * a.f.mB + (long long)r * a.f.mR : &kMaskAllValid;
 
-    // operands of one key tile: K^T rows (MFMA A), V chunks (to LDS), the lane's mask byte
-    u32x4 nk0, nk1, nv0, nv1;
-    uint8_t nmv = 1;
-    auto fetch = [&](int kt) {
-      const uint16_t *kp = a.k + base + (long long)(kt * 32 + jl) * a.f.sQ;
-      nk0 = ld16(kp + 8 * hh);
-      nk1 = ld16(kp + 16 + 8 * hh);
-      const int key0 = lane >> 2, part = lane & 3;
-      nv0 = ld16(a.v + base + (long long)(kt * 32 + key0) * a.f.sQ + part * 8);
-      nv1 = ld16(a.v + base + (long long)(kt * 32 + 16 + key0) * a.f.sQ + part * 8);
-      if (mrow) nmv = mrow[(long long)(kt * 32 + jl) * a.f.mK];
+    // per-lane addresses of tile 0; tile kt is a uniform offset away
+    const uint16_t *kl = a.k + base + (long long)jl * a.f.sQ + 8 * hh;
+    const uint16_t *vl = a.v + base + (long long)vkey * a.f.sQ + vpart * 8;
+    const uint8_t *ml = mrow + (long long)jl * mk;
+    const long long tstep = 32 * a.f.sQ, vhalf = 16 * a.f.sQ, mstep = 32 * mk;
+    // every fetch is unconditional (a tile past the end refetches the last one, which
+    // is then not processed): a load under a branch makes the compiler wait for all
+    // outstanding memory operations where the paths merge
+    auto fetch = [&](int kt, FwdTile &T) {
+      kt = min(kt, nkt - 1);
+      const uint16_t *kp = kl + kt * tstep;
+      const uint16_t *vp = vl + kt * tstep;
+      T.k0 = ld16(kp);
+      T.k1 = ld16(kp + 16);
+      T.v0 = ld16(vp);
+      T.v1 = ld16(vp + vhalf);
+      T.m = ml[kt * mstep];
     };
-    fetch(0);
-
-    float m = -INFINITY;  // reference maximum of the lane's query, in logit/alpha units
-    float lsum = 0.f;
-    f32x16 oacc = {};
-    for (int kt = 0; kt < nkt; ++kt) {
-      const u32x4 k0w = nk0, k1w = nk1, v0w = nv0, v1w = nv1;
-      const uint8_t mv = nmv;
-      if (kt + 1 < nkt) fetch(kt + 1);
-      const unsigned valid = mrow ? (unsigned)__ballot(mv != 0) : 0xffffffffu;
-      if (valid == 0u) continue;
-      *(u32x4 *)(vbuf + (lane >> 2) * HD + (lane & 3) * 8) = v0w;
-      *(u32x4 *)(vbuf + (16 + (lane >> 2)) * HD + (lane & 3) * 8) = v1w;
+    // scores of one tile (logit / alpha), masked keys at -inf
+    auto scores = [&](int kt, const FwdTile &T, unsigned valid) -> f32x16 {
       f32x16 acc;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -209,56 +219,80 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
         acc[4 * g + 2] = bv[2];
         acc[4 * g + 3] = bv[3];
       }
-      acc = mfma(as_bf16x8(k0w), qB0, acc);
-      acc = mfma(as_bf16x8(k1w), qB1, acc);
-      if (valid != 0xffffffffu) {
+      acc = mfma(as_bf16x8(T.k0), qB0, acc);
+      acc = mfma(as_bf16x8(T.k1), qB1, acc);
+      if (__builtin_expect(valid != 0xffffffffu, 0)) {  // a partly masked tile
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kl = 8 * (i >> 2) + 4 * hh + (i & 3);
           if (!((valid >> kl) & 1u)) acc[i] = -INFINITY;
         }
       }
-      auto tile_max = [&]() {
-        float mt = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
+      return acc;
+    };
+    auto tile_max = [&](const f32x16 &acc) {
+      float mt = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
 #pragma unroll
-        for (int i = 3; i < 15; i += 2) mt = fmaxf(fmaxf(mt, acc[i]), acc[i + 1]);
-        mt = fmaxf(mt, acc[15]);
-        return fmaxf(mt, __shfl_xor(mt, 32));
-      };
-      if (m == -INFINITY) m = tile_max();  // first attended tile (the same for every lane)
-      float p[16], tsum = 0.f;
-      float negm = -m * c1;
+      for (int i = 3; i < 15; i += 2) mt = fmaxf(fmaxf(mt, acc[i]), acc[i + 1]);
+      mt = fmaxf(mt, acc[15]);
+      return fmaxf(mt, __shfl_xor(mt, 32));
+    };
+    // one tile of the output pass against the reference maximum m (m = -inf: take
+    // this tile's maximum)
+    auto tile = [&](int kt, const FwdTile &T, float &m, f32x16 &oacc, float &lsum) {
+      const unsigned valid = (unsigned)__ballot(T.m != 0u);
+      if (valid == 0u) return;
+      *(u32x4 *)(vbuf + vkey * HD + vpart * 8) = T.v0;
+      *(u32x4 *)(vbuf + (16 + vkey) * HD + vpart * 8) = T.v1;
+      const f32x16 acc = scores(kt, T, valid);
+      if (__builtin_expect(__ballot(m == -INFINITY) != 0ull, 0)) {  // the first attended tile
+        const float mt = tile_max(acc);
+        if (m == -INFINITY) m = mt;
+      }
+      const float negm = m == -INFINITY ? 0.f : -m * c1;  // no finite score yet: every p is 0
+      float p[16], ts = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         p[i] = __builtin_amdgcn_exp2f(fmaf(acc[i], c1, negm));
-        tsum += p[i];
+        ts += p[i];
       }
-      if (__ballot(!(tsum <= kFwdOverflow)) != 0ull) {
-        // a probability grew past the bound: raise the reference maximum to this
-        // tile's, rescale what has been accumulated and recompute the tile
-        const float mnew = fmaxf(m, tile_max());
-        const float sc = __builtin_amdgcn_exp2f((m - mnew) * c1);
-        lsum *= sc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[i] *= sc;
-        m = mnew;
-        negm = -m * c1;
-        tsum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(fmaf(acc[i], c1, negm));
-          tsum += p[i];
-        }
+      lsum += ts;
+      oacc = mfma(tr_operand(vbuf, 0, lane), pack8(p), oacc);
+      oacc = mfma(tr_operand(vbuf, 16, lane), pack8(p + 8), oacc);
+    };
+    // the row's pass; returns the sum of p over all keys (both lane halves)
+    auto pass = [&](float &m, f32x16 &oacc) -> float {
+      oacc = (f32x16){};
+      float lsum = 0.f;
+      FwdTile A, B;
+      fetch(0, A);
+      for (int kt = 0; kt < nkt; kt += 2) {
+        fetch(kt + 1, B);
+        tile(kt, A, m, oacc, lsum);
+        fetch(kt + 2, A);
+        if (kt + 1 < nkt) tile(kt + 1, B, m, oacc, lsum);
       }
-      lsum += tsum;
-      const bf16x8 pB0 = pack8(p);
-      const bf16x8 pB1 = pack8(p + 8);
-      const bf16x8 vA0 = tr_operand(vbuf, 0, lane);
-      const bf16x8 vA1 = tr_operand(vbuf, 16, lane);
-      oacc = mfma(vA0, pB0, oacc);
-      oacc = mfma(vA1, pB1, oacc);
+      return lsum + __shfl_xor(lsum, 32);
+    };
+
+    float m = -INFINITY;  // reference maximum of the lane's query, in logit/alpha units
+    f32x16 oacc;
+    float lsum = pass(m, oacc);
+    bool bad = !isfinite(lsum);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) bad = bad || !isfinite(oacc[i]);
+    if (__ballot(bad) != 0ull) {
+      // a probability left the fp32 range: take each query's true maximum over the
+      // row, then run the pass again against it
+      m = -INFINITY;
+      FwdTile T;
+      for (int kt = 0; kt < nkt; ++kt) {
+        fetch(kt, T);
+        const unsigned valid = (unsigned)__ballot(T.m != 0u);
+        if (valid != 0u) m = fmaxf(m, tile_max(scores(kt, T, valid)));
+      }
+      lsum = pass(m, oacc);
     }
-    lsum += __shfl_xor(lsum, 32);
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     const long long obase = base + (long long)(j0 + jl) * a.f.sQ;
 #pragma unroll
