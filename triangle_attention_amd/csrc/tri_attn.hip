@@ -88,6 +88,22 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t *tile, int base_row,
   return tr_read(tile + row * HD + col, tile + (row + 8) * HD + col);
 }
 
+// Offset of element (row, col) of a [rows][32] bf16 LDS tile whose 16-byte chunks
+// are permuted by bits 1 and 2 of the row, so that 16-byte row reads by 32 lanes
+// (one row each) and transposing reads are free of bank conflicts.
+__device__ __forceinline__ int tile_off(int row, int col) {
+  const int sw = (row & 2) | ((row >> 2) & 1);
+  return row * HD + (((col >> 3) ^ sw) << 3) + (col & 7);
+}
+// tr_operand for a tile laid out by tile_off (rows base_row + 8 + x share the chunk
+// permutation of rows base_row + x).
+__device__ __forceinline__ bf16x8 tr_operand_sw(const uint16_t *tile, int base_row, int lane) {
+  const int g = lane >> 4, w = lane & 15, m = w >> 2, s = w & 3;
+  const int row = base_row + 4 * (g >> 1) + m;
+  const uint16_t *p = tile + tile_off(row, 16 * (g & 1) + 4 * s);
+  return tr_read(p, p + 8 * HD);
+}
+
 // Workgroup index -> tile index such that consecutive tiles share an XCD
 // (workgroups are dealt to the 8 XCDs round-robin).
 __device__ __forceinline__ int xcd_remap(int L, int G) {
@@ -115,10 +131,11 @@ struct Frame {
 // its true maximum (a maximum pass, then the pass again), so a tile costs the
 // fused multiply-add, exponential, sum and bf16 packing of its probabilities and no
 // per-tile maximum or rescaling.
-// K rows are MFMA operands read straight from global memory; V goes through a
-// per-wave LDS buffer and is read transposed.  Key tiles are processed in pairs
-// with two register sets, so each tile's K, V and mask byte arrive during the
-// previous tile.
+// K and V tiles are fetched with fully coalesced loads (four lanes per 64-byte row)
+// into per-wave LDS tiles: K is read back as row operands, V transposed.  Key tiles
+// are processed in pairs with two register sets, so each tile's K, V and mask byte
+// arrive during the previous tile.  The key mask is a compile-time variant, so an
+// unmasked problem loads no mask at all.
 constexpr int FWD_WAVES = 12;
 constexpr int FWD_BJ = 32;
 
@@ -136,13 +153,14 @@ struct FwdArgs {
   float alpha, inv_alpha, c1;  // c1 = alpha * log2(e)
 };
 
-// operands of one key tile: K^T rows (MFMA A), the lane's V chunks (to LDS) and the
-// mask byte of key (tile * 32 + lane % 32)
+// one key tile in flight: the lane's 16-byte chunks of K and V (rows lane/4 and
+// 16 + lane/4, part lane%4) and the mask byte of key (tile * 32 + lane % 32)
 struct FwdTile {
   u32x4 k0, k1, v0, v1;
   unsigned m;
 };
 
+template <bool MASKED>
 __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
   extern __shared__ float4 smem_f4[];
   float *bias_s = (float *)smem_f4;
@@ -156,7 +174,8 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
   const int h = t % a.H;
   const int b = t / a.H;
   const int j0 = jb * FWD_BJ;
-  uint16_t *vbuf = (uint16_t *)(bias_s + FWD_BJ * bstride) + wave * (32 * HD);
+  uint16_t *kbuf = (uint16_t *)(bias_s + FWD_BJ * bstride) + wave * (2 * 32 * HD);
+  uint16_t *vbuf = kbuf + 32 * HD;
 
   // pair bias of this query block, scaled by 1/alpha: the MFMA then yields
   // q.k + bias/alpha, i.e. the logit divided by alpha.
@@ -181,7 +200,7 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
   const int r1 = min(N, r0 + a.rows_per_chunk);
   const float c1 = a.c1;
   const int nkt = N / 32;
-  const int vkey = lane >> 2, vpart = lane & 3;  // the lane's V chunk within a tile
+  const int vkey = lane >> 2, vpart = lane & 3;  // the lane's K and V chunks within a tile
   const long long mk = a.mask ? a.f.mK : 0;
   for (int r = r0 + wave; r < r1; r += FWD_WAVES) {
     const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
@@ -191,7 +210,7 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
     const uint8_t *mrow = a.mask ? a.mask + (long long)b * a.f.mB + (long long)r * a.f.mR : &kMaskAllValid;
 
     // per-lane addresses of tile 0; tile kt is a uniform offset away
-    const uint16_t *kl = a.k + base + (long long)jl * a.f.sQ + 8 * hh;
+    const uint16_t *kl = a.k + base + (long long)vkey * a.f.sQ + vpart * 8;
     const uint16_t *vl = a.v + base + (long long)vkey * a.f.sQ + vpart * 8;
     const uint8_t *ml = mrow + (long long)jl * mk;
     const long long tstep = 32 * a.f.sQ, vhalf = 16 * a.f.sQ, mstep = 32 * mk;
@@ -203,10 +222,10 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
       const uint16_t *kp = kl + kt * tstep;
       const uint16_t *vp = vl + kt * tstep;
       T.k0 = ld16(kp);
-      T.k1 = ld16(kp + 16);
+      T.k1 = ld16(kp + vhalf);
       T.v0 = ld16(vp);
       T.v1 = ld16(vp + vhalf);
-      T.m = ml[kt * mstep];
+      T.m = MASKED ? (unsigned)ml[kt * mstep] : 1u;
     };
     // scores of one tile (logit / alpha), masked keys at -inf
     auto scores = [&](int kt, const FwdTile &T, unsigned valid) -> f32x16 {
@@ -219,8 +238,8 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
         acc[4 * g + 2] = bv[2];
         acc[4 * g + 3] = bv[3];
       }
-      acc = mfma(as_bf16x8(T.k0), qB0, acc);
-      acc = mfma(as_bf16x8(T.k1), qB1, acc);
+      acc = mfma(*(const bf16x8 *)(kbuf + tile_off(jl, 8 * hh)), qB0, acc);
+      acc = mfma(*(const bf16x8 *)(kbuf + tile_off(jl, 16 + 8 * hh)), qB1, acc);
       if (__builtin_expect(valid != 0xffffffffu, 0)) {  // a partly masked tile
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -240,10 +259,12 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
     // one tile of the output pass against the reference maximum m (m = -inf: take
     // this tile's maximum)
     auto tile = [&](int kt, const FwdTile &T, float &m, f32x16 &oacc, float &lsum) {
-      const unsigned valid = (unsigned)__ballot(T.m != 0u);
+      const unsigned valid = MASKED ? (unsigned)__ballot(T.m != 0u) : 0xffffffffu;
       if (valid == 0u) return;
-      *(u32x4 *)(vbuf + vkey * HD + vpart * 8) = T.v0;
-      *(u32x4 *)(vbuf + (16 + vkey) * HD + vpart * 8) = T.v1;
+      *(u32x4 *)(kbuf + tile_off(vkey, vpart * 8)) = T.k0;
+      *(u32x4 *)(kbuf + tile_off(16 + vkey, vpart * 8)) = T.k1;
+      *(u32x4 *)(vbuf + tile_off(vkey, vpart * 8)) = T.v0;
+      *(u32x4 *)(vbuf + tile_off(16 + vkey, vpart * 8)) = T.v1;
       const f32x16 acc = scores(kt, T, valid);
       if (__builtin_expect(__ballot(m == -INFINITY) != 0ull, 0)) {  // the first attended tile
         const float mt = tile_max(acc);
@@ -257,8 +278,8 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
         ts += p[i];
       }
       lsum += ts;
-      oacc = mfma(tr_operand(vbuf, 0, lane), pack8(p), oacc);
-      oacc = mfma(tr_operand(vbuf, 16, lane), pack8(p + 8), oacc);
+      oacc = mfma(tr_operand_sw(vbuf, 0, lane), pack8(p), oacc);
+      oacc = mfma(tr_operand_sw(vbuf, 16, lane), pack8(p + 8), oacc);
     };
     // the row's pass; returns the sum of p over all keys (both lane halves)
     auto pass = [&](float &m, f32x16 &oacc) -> float {
@@ -288,8 +309,12 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
       FwdTile T;
       for (int kt = 0; kt < nkt; ++kt) {
         fetch(kt, T);
-        const unsigned valid = (unsigned)__ballot(T.m != 0u);
-        if (valid != 0u) m = fmaxf(m, tile_max(scores(kt, T, valid)));
+        const unsigned valid = MASKED ? (unsigned)__ballot(T.m != 0u) : 0xffffffffu;
+        if (valid != 0u) {
+          *(u32x4 *)(kbuf + tile_off(vkey, vpart * 8)) = T.k0;
+          *(u32x4 *)(kbuf + tile_off(16 + vkey, vpart * 8)) = T.k1;
+          m = fmaxf(m, tile_max(scores(kt, T, valid)));
+        }
       }
       lsum = pass(m, oacc);
     }
@@ -412,20 +437,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
 constexpr int BWD_WAVES = 4;
 constexpr int BWD_BK = 64;
 
-// Offset of element (row, col) of a [rows][32] bf16 LDS tile whose 16-byte chunks
-// are permuted by bits 1 and 2 of the row.
-__device__ __forceinline__ int tile_off(int row, int col) {
-  const int sw = (row & 2) | ((row >> 2) & 1);
-  return row * HD + (((col >> 3) ^ sw) << 3) + (col & 7);
-}
-// tr_operand for a tile laid out by tile_off (rows base_row + 8 + x share the chunk
-// permutation of rows base_row + x).
-__device__ __forceinline__ bf16x8 tr_operand_sw(const uint16_t *tile, int base_row, int lane) {
-  const int g = lane >> 4, w = lane & 15, m = w >> 2, s = w & 3;
-  const int row = base_row + 4 * (g >> 1) + m;
-  const uint16_t *p = tile + tile_off(row, 16 * (g & 1) + 4 * s);
-  return tr_read(p, p + 8 * HD);
-}
 
 // A-operand slice carrying x for the lane's query row: elements 0..2 of the lanes
 // with hh = 0 hold bf16 hi, mid, lo with hi + mid + lo = x exactly for finite x
@@ -955,11 +966,15 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
   if (chunks > a.N) chunks = a.N;
   a.rows_per_chunk = (a.N + chunks - 1) / chunks;
   a.n_chunks = (a.N + a.rows_per_chunk - 1) / a.rows_per_chunk;
-  const size_t lds = (size_t)FWD_BJ * (a.N + 4) * 4 + (size_t)FWD_WAVES * 32 * HD * 2;
-  if (hipFuncSetAttribute((const void *)fwd_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+  const size_t lds = (size_t)FWD_BJ * (a.N + 4) * 4 + (size_t)FWD_WAVES * 2 * 32 * HD * 2;
+  const void *kern = mask ? (const void *)fwd_kernel<true> : (const void *)fwd_kernel<false>;
+  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
       hipSuccess)
     return TRI_ATTN_ERROR_LAUNCH_FAILED;
-  hipLaunchKernelGGL(fwd_kernel, dim3(groups * a.n_chunks), dim3(FWD_WAVES * 64), lds, stream, a);
+  if (mask)
+    hipLaunchKernelGGL(fwd_kernel<true>, dim3(groups * a.n_chunks), dim3(FWD_WAVES * 64), lds, stream, a);
+  else
+    hipLaunchKernelGGL(fwd_kernel<false>, dim3(groups * a.n_chunks), dim3(FWD_WAVES * 64), lds, stream, a);
   return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH_FAILED;
 }
 
