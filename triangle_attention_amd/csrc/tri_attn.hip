@@ -120,24 +120,26 @@ struct Frame {
 // ------------------------------------------------------------------------------------
 // Forward
 // ------------------------------------------------------------------------------------
-// One workgroup = (batch, head, 32 queries, chunk of rows); 12 waves (three per
-// SIMD), each working on one attention row at a time.  The block's pair bias,
-// scaled by 1/alpha, sits in LDS in fp32 and is the initial value of the score
-// MFMA, so S^T = K Q^T + bias^T/alpha costs no VALU work.  Per 32-key tile each lane
-// owns one query and 16 keys: p = exp2(c1 (s - m)) against a per-query reference m,
-// the maximum of the row's first attended tile, summed in fp32.  m is never raised
-// during the pass: a probability beyond the fp32 range shows up at the end of the
-// row as a non-finite sum or output, and only then is the row recomputed against
-// its true maximum (a maximum pass, then the pass again), so a tile costs the
-// fused multiply-add, exponential, sum and bf16 packing of its probabilities and no
-// per-tile maximum or rescaling.
-// K and V tiles are fetched with fully coalesced loads (four lanes per 64-byte row)
-// into per-wave LDS tiles: K is read back as row operands, V transposed.  Key tiles
-// are processed in pairs with two register sets, so each tile's K, V and mask byte
-// arrive during the previous tile.  The key mask is a compile-time variant, so an
-// unmasked problem loads no mask at all.
+// One workgroup = (batch, head, 64 queries, chunk of rows); 12 waves (three per
+// SIMD), each working on one attention row at a time and on both 32-query halves of
+// the block, so every K and V tile is loaded once for 64 queries.  K and V tiles are
+// fetched with fully coalesced loads (four lanes per 64-byte row) into per-wave LDS
+// tiles: K is read back as row operands, V transposed, and each is used by both
+// query halves.  The block's pair bias sits in LDS as fp16 (bf16 values convert
+// exactly).  Per 32-key tile and query half each lane owns one query and 16 keys:
+//   t = log2(e) * logit = c1 * (q.k) + log2(e) * bias        (c1 = alpha log2(e))
+//   p = exp2(t - m)
+// with m the query's maximum of t over the row's first attended tile, so a score
+// costs one multiply-add, one mixed-precision multiply-add (fp16 bias operand) and
+// the exponential; p is summed in fp32 and packed to bf16 for O^T += V^T P^T.
+// m is never raised during the pass: a probability beyond the fp32 range shows up
+// at the end of the row as a non-finite sum or output, and only then is the row
+// recomputed against its true maximum (a maximum pass, then the pass again).  A key
+// tile's registers are staged to LDS as soon as they arrive and the next tile's
+// K, V and mask byte are fetched into them while the tile is computed; the key mask
+// is a compile-time variant, so an unmasked problem loads no mask at all.
 constexpr int FWD_WAVES = 12;
-constexpr int FWD_BJ = 32;
+constexpr int FWD_BJ = 64;
 
 // a readable byte holding 1: the key mask of a problem without one
 __device__ const uint8_t kMaskAllValid = 1;
@@ -150,7 +152,8 @@ struct FwdArgs {
   Frame f;
   int B, N, H;
   int n_jblocks, n_chunks, rows_per_chunk;
-  float alpha, inv_alpha, c1;  // c1 = alpha * log2(e)
+  int bstride;  // fp16 row stride of the bias tile
+  float c1;     // alpha * log2(e)
 };
 
 // one key tile in flight: the lane's 16-byte chunks of K and V (rows lane/4 and
@@ -163,9 +166,9 @@ struct FwdTile {
 template <bool MASKED>
 __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
   extern __shared__ float4 smem_f4[];
-  float *bias_s = (float *)smem_f4;
+  _Float16 *bias_s = (_Float16 *)smem_f4;
   const int N = a.N;
-  const int bstride = N + 4;
+  const int bstride = a.bstride;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int jl = lane & 31, hh = lane >> 5;
   int t = xcd_remap(blockIdx.x, gridDim.x);
@@ -174,24 +177,26 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
   const int h = t % a.H;
   const int b = t / a.H;
   const int j0 = jb * FWD_BJ;
+  const bool two = j0 + 32 < N;  // second 32-query half present (N % 64 == 32: not in the last block)
   uint16_t *kbuf = (uint16_t *)(bias_s + FWD_BJ * bstride) + wave * (2 * 32 * HD);
   uint16_t *vbuf = kbuf + 32 * HD;
 
-  // pair bias of this query block, scaled by 1/alpha: the MFMA then yields
-  // q.k + bias/alpha, i.e. the logit divided by alpha.
+  // pair bias of this query block: bias_s[j][k] = bias[b, h, j0 + j, k] in fp16
   {
     const uint16_t *src = a.bias + (((long long)b * a.H + h) * N + j0) * N;
     const int per_row = N / 8;
-    for (int idx = tid; idx < FWD_BJ * per_row; idx += FWD_WAVES * 64) {
+    const int rows = two ? FWD_BJ : 32;
+    for (int idx = tid; idx < rows * per_row; idx += FWD_WAVES * 64) {
       const int row = idx / per_row, c8 = idx - row * per_row;
       const u32x4 w = ld16(src + (long long)row * N + c8 * 8);
-      float *dst = bias_s + row * bstride + c8 * 8;
-      f32x4 lo = {bf_lo(w[0]) * a.inv_alpha, bf_hi(w[0]) * a.inv_alpha, bf_lo(w[1]) * a.inv_alpha,
-                  bf_hi(w[1]) * a.inv_alpha};
-      f32x4 hi = {bf_lo(w[2]) * a.inv_alpha, bf_hi(w[2]) * a.inv_alpha, bf_lo(w[3]) * a.inv_alpha,
-                  bf_hi(w[3]) * a.inv_alpha};
-      *(f32x4 *)dst = lo;
-      *(f32x4 *)(dst + 4) = hi;
+      typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+      f16x8 hv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        hv[2 * i] = (_Float16)bf_lo(w[i]);
+        hv[2 * i + 1] = (_Float16)bf_hi(w[i]);
+      }
+      *(f16x8 *)(bias_s + row * bstride + c8 * 8) = hv;
     }
   }
   __syncthreads();
@@ -202,11 +207,16 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
   const int nkt = N / 32;
   const int vkey = lane >> 2, vpart = lane & 3;  // the lane's K and V chunks within a tile
   const long long mk = a.mask ? a.f.mK : 0;
+  typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
   for (int r = r0 + wave; r < r1; r += FWD_WAVES) {
     const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
-    const uint16_t *qp = a.q + base + (long long)(j0 + jl) * a.f.sQ;
-    const bf16x8 qB0 = as_bf16x8(ld16(qp + 8 * hh));
-    const bf16x8 qB1 = as_bf16x8(ld16(qp + 16 + 8 * hh));
+    bf16x8 qB[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint16_t *qp = a.q + base + (long long)(j0 + (two ? 32 * s : 0) + jl) * a.f.sQ;
+      qB[s][0] = as_bf16x8(ld16(qp + 8 * hh));
+      qB[s][1] = as_bf16x8(ld16(qp + 16 + 8 * hh));
+    }
     const uint8_t *mrow = a.mask ? a.mask + (long long)b * a.f.mB + (long long)r * a.f.mR : &kMaskAllValid;
 
     // per-lane addresses of tile 0; tile kt is a uniform offset away
@@ -227,118 +237,132 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
       T.v1 = ld16(vp + vhalf);
       T.m = MASKED ? (unsigned)ml[kt * mstep] : 1u;
     };
-    // scores of one tile (logit / alpha), masked keys at -inf
-    auto scores = [&](int kt, const FwdTile &T, unsigned valid) -> f32x16 {
-      f32x16 acc;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 bv = *(const f32x4 *)(bias_s + jl * bstride + kt * 32 + 8 * g + 4 * hh);
-        acc[4 * g + 0] = bv[0];
-        acc[4 * g + 1] = bv[1];
-        acc[4 * g + 2] = bv[2];
-        acc[4 * g + 3] = bv[3];
-      }
-      acc = mfma(*(const bf16x8 *)(kbuf + tile_off(jl, 8 * hh)), qB0, acc);
-      acc = mfma(*(const bf16x8 *)(kbuf + tile_off(jl, 16 + 8 * hh)), qB1, acc);
+    auto stage_k = [&](const FwdTile &T) {
+      *(u32x4 *)(kbuf + tile_off(vkey, vpart * 8)) = T.k0;
+      *(u32x4 *)(kbuf + tile_off(16 + vkey, vpart * 8)) = T.k1;
+    };
+    // q.k of query half s against the staged key tile (masked keys at -inf)
+    auto qk = [&](int s, unsigned valid) -> f32x16 {
+      f32x16 acc = mfma(*(const bf16x8 *)(kbuf + tile_off(jl, 8 * hh)), qB[s][0], (f32x16){});
+      acc = mfma(*(const bf16x8 *)(kbuf + tile_off(jl, 16 + 8 * hh)), qB[s][1], acc);
       if (__builtin_expect(valid != 0xffffffffu, 0)) {  // a partly masked tile
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int kl = 8 * (i >> 2) + 4 * hh + (i & 3);
-          if (!((valid >> kl) & 1u)) acc[i] = -INFINITY;
+          const int kk = 8 * (i >> 2) + 4 * hh + (i & 3);
+          if (!((valid >> kk) & 1u)) acc[i] = -INFINITY;
         }
       }
       return acc;
     };
-    auto tile_max = [&](const f32x16 &acc) {
-      float mt = fmaxf(fmaxf(acc[0], acc[1]), acc[2]);
+    // the lane's 16 fp16 bias values of query half s in key tile kt
+    auto bias_of = [&](int s, int kt, f16x4 *bw) {
+      const _Float16 *brow = bias_s + (32 * s + jl) * bstride + kt * 32 + 4 * hh;
 #pragma unroll
-      for (int i = 3; i < 15; i += 2) mt = fmaxf(fmaxf(mt, acc[i]), acc[i + 1]);
-      mt = fmaxf(mt, acc[15]);
+      for (int g = 0; g < 4; ++g) bw[g] = *(const f16x4 *)(brow + 8 * g);
+    };
+    // maximum over the tile of t = c1 q.k + log2(e) bias (both lane halves)
+    auto tile_max = [&](const f32x16 &acc, const f16x4 *bw) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, fmaf((float)bw[i >> 2][i & 3], kLog2e, acc[i] * c1));
       return fmaxf(mt, __shfl_xor(mt, 32));
     };
-    // one tile of the output pass against the reference maximum m (m = -inf: take
-    // this tile's maximum)
-    auto tile = [&](int kt, const FwdTile &T, float &m, f32x16 &oacc, float &lsum) {
+    // one tile of the output pass against the reference maxima m[s] (m[s] = -inf:
+    // take this tile's maximum); T holds tile kt on entry and tile kt + 1 on return
+    auto tile = [&](int kt, FwdTile &T, float *m, f32x16 *oacc, float *lsum) {
       const unsigned valid = MASKED ? (unsigned)__ballot(T.m != 0u) : 0xffffffffu;
+      if (valid != 0u) {
+        stage_k(T);
+        *(u32x4 *)(vbuf + tile_off(vkey, vpart * 8)) = T.v0;
+        *(u32x4 *)(vbuf + tile_off(16 + vkey, vpart * 8)) = T.v1;
+      }
+      fetch(kt + 1, T);
       if (valid == 0u) return;
-      *(u32x4 *)(kbuf + tile_off(vkey, vpart * 8)) = T.k0;
-      *(u32x4 *)(kbuf + tile_off(16 + vkey, vpart * 8)) = T.k1;
-      *(u32x4 *)(vbuf + tile_off(vkey, vpart * 8)) = T.v0;
-      *(u32x4 *)(vbuf + tile_off(16 + vkey, vpart * 8)) = T.v1;
-      const f32x16 acc = scores(kt, T, valid);
-      if (__builtin_expect(__ballot(m == -INFINITY) != 0ull, 0)) {  // the first attended tile
-        const float mt = tile_max(acc);
-        if (m == -INFINITY) m = mt;
-      }
-      const float negm = m == -INFINITY ? 0.f : -m * c1;  // no finite score yet: every p is 0
-      float p[16], ts = 0.f;
+      const bf16x8 vA0 = tr_operand_sw(vbuf, 0, lane), vA1 = tr_operand_sw(vbuf, 16, lane);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(fmaf(acc[i], c1, negm));
-        ts += p[i];
+      for (int s = 0; s < 2; ++s) {
+        if (s == 1 && !two) break;
+        const f32x16 acc = qk(s, valid);
+        f16x4 bw[4];
+        bias_of(s, kt, bw);
+        if (__builtin_expect(__ballot(m[s] == -INFINITY) != 0ull, 0)) {  // the first attended tile
+          const float mt = tile_max(acc, bw);
+          if (m[s] == -INFINITY) m[s] = mt;
+        }
+        const float negm = m[s] == -INFINITY ? 0.f : -m[s];  // no finite score yet: every p is 0
+        float p[16], ts = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          p[i] = __builtin_amdgcn_exp2f(fmaf((float)bw[i >> 2][i & 3], kLog2e, fmaf(acc[i], c1, negm)));
+          ts += p[i];
+        }
+        lsum[s] += ts;
+        oacc[s] = mfma(vA0, pack8(p), oacc[s]);
+        oacc[s] = mfma(vA1, pack8(p + 8), oacc[s]);
       }
-      lsum += ts;
-      oacc = mfma(tr_operand_sw(vbuf, 0, lane), pack8(p), oacc);
-      oacc = mfma(tr_operand_sw(vbuf, 16, lane), pack8(p + 8), oacc);
     };
-    // the row's pass; returns the sum of p over all keys (both lane halves)
-    auto pass = [&](float &m, f32x16 &oacc) -> float {
-      oacc = (f32x16){};
-      float lsum = 0.f;
-      FwdTile A, B;
-      fetch(0, A);
-      for (int kt = 0; kt < nkt; kt += 2) {
-        fetch(kt + 1, B);
-        tile(kt, A, m, oacc, lsum);
-        fetch(kt + 2, A);
-        if (kt + 1 < nkt) tile(kt + 1, B, m, oacc, lsum);
-      }
-      return lsum + __shfl_xor(lsum, 32);
+    // the row's pass; lsum[s] = the sum of p over all keys (both lane halves)
+    auto pass = [&](float *m, f32x16 *oacc, float *lsum) {
+      oacc[0] = oacc[1] = (f32x16){};
+      lsum[0] = lsum[1] = 0.f;
+      FwdTile T;
+      fetch(0, T);
+      for (int kt = 0; kt < nkt; ++kt) tile(kt, T, m, oacc, lsum);
+      lsum[0] += __shfl_xor(lsum[0], 32);
+      lsum[1] += __shfl_xor(lsum[1], 32);
     };
 
-    float m = -INFINITY;  // reference maximum of the lane's query, in logit/alpha units
-    f32x16 oacc;
-    float lsum = pass(m, oacc);
-    bool bad = !isfinite(lsum);
+    float m[2] = {-INFINITY, -INFINITY};  // reference maxima of t for the lane's two queries
+    f32x16 oacc[2];
+    float lsum[2];
+    pass(m, oacc, lsum);
+    bool bad = !isfinite(lsum[0]) || !isfinite(lsum[1]);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) bad = bad || !isfinite(oacc[i]);
+    for (int i = 0; i < 16; ++i) bad = bad || !isfinite(oacc[0][i]) || !isfinite(oacc[1][i]);
     if (__ballot(bad) != 0ull) {
       // a probability left the fp32 range: take each query's true maximum over the
       // row, then run the pass again against it
-      m = -INFINITY;
+      m[0] = m[1] = -INFINITY;
       FwdTile T;
       for (int kt = 0; kt < nkt; ++kt) {
         fetch(kt, T);
         const unsigned valid = MASKED ? (unsigned)__ballot(T.m != 0u) : 0xffffffffu;
-        if (valid != 0u) {
-          *(u32x4 *)(kbuf + tile_off(vkey, vpart * 8)) = T.k0;
-          *(u32x4 *)(kbuf + tile_off(16 + vkey, vpart * 8)) = T.k1;
-          m = fmaxf(m, tile_max(scores(kt, T, valid)));
+        if (valid == 0u) continue;
+        stage_k(T);
+        for (int s = 0; s < (two ? 2 : 1); ++s) {
+          f16x4 bw[4];
+          bias_of(s, kt, bw);
+          m[s] = fmaxf(m[s], tile_max(qk(s, valid), bw));
         }
       }
-      lsum = pass(m, oacc);
+      pass(m, oacc, lsum);
     }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    const long long obase = base + (long long)(j0 + jl) * a.f.sQ;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      float ov[4], rv[4];
-      unsigned pk[2];
+    for (int s = 0; s < 2; ++s) {
+      if (s == 1 && !two) break;
+      const float inv = lsum[s] > 0.f ? 1.f / lsum[s] : 0.f;
+      const long long obase = base + (long long)(j0 + 32 * s + jl) * a.f.sQ;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ov[i] = oacc[4 * g + i] * inv;
-      pk[0] = pack_bf16(ov[0], ov[1]);
-      pk[1] = pack_bf16(ov[2], ov[3]);
-      rv[0] = ov[0] - bf_lo(pk[0]);
-      rv[1] = ov[1] - bf_hi(pk[0]);
-      rv[2] = ov[2] - bf_lo(pk[1]);
-      rv[3] = ov[3] - bf_hi(pk[1]);
-      const int c = 8 * g + 4 * hh;
-      *(u32x2 *)(a.o + obase + c) = (u32x2){pk[0], pk[1]};
-      if (a.res) *(f32x4 *)(a.res + obase + c) = (f32x4){rv[0], rv[1], rv[2], rv[3]};
-    }
-    if (hh == 0) {
-      const float L = lsum > 0.f ? a.alpha * m + logf(lsum) : INFINITY;
-      a.lse[(((long long)b * N + r) * a.H + h) * N + j0 + jl] = L;
+      for (int g = 0; g < 4; ++g) {
+        float ov[4], rv[4];
+        unsigned pk[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = oacc[s][4 * g + i] * inv;
+        pk[0] = pack_bf16(ov[0], ov[1]);
+        pk[1] = pack_bf16(ov[2], ov[3]);
+        rv[0] = ov[0] - bf_lo(pk[0]);
+        rv[1] = ov[1] - bf_hi(pk[0]);
+        rv[2] = ov[2] - bf_lo(pk[1]);
+        rv[3] = ov[3] - bf_hi(pk[1]);
+        const int c = 8 * g + 4 * hh;
+        *(u32x2 *)(a.o + obase + c) = (u32x2){pk[0], pk[1]};
+        if (a.res) *(f32x4 *)(a.res + obase + c) = (f32x4){rv[0], rv[1], rv[2], rv[3]};
+      }
+      if (hh == 0) {
+        // lse = ln(sum exp(logit)) = ln 2 * (m + log2(sum p))
+        const float L = lsum[s] > 0.f ? kLn2 * m[s] + logf(lsum[s]) : INFINITY;
+        a.lse[(((long long)b * N + r) * a.H + h) * N + j0 + 32 * s + jl] = L;
+      }
     }
   }
 }
@@ -957,16 +981,17 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
   a.B = (int)p.B;
   a.N = (int)p.N;
   a.H = (int)p.H;
-  a.alpha = alpha_of(problem);
-  a.inv_alpha = 1.f / a.alpha;
-  a.c1 = a.alpha * kLog2e;
-  a.n_jblocks = a.N / FWD_BJ;
+  a.c1 = alpha_of(problem) * kLog2e;
+  a.n_jblocks = (a.N + FWD_BJ - 1) / FWD_BJ;
+  // fp16 bias row stride with stride/2 = 2 (mod 32) 4-byte banks: the 8-byte reads of
+  // 16 lanes (16 rows) are then conflict-free
+  a.bstride = a.N + ((a.N & 63) ? 36 : 4);
   const int groups = a.B * a.H * a.n_jblocks;
   int chunks = (768 + groups - 1) / groups;  // about three rounds of one workgroup per CU
   if (chunks > a.N) chunks = a.N;
   a.rows_per_chunk = (a.N + chunks - 1) / chunks;
   a.n_chunks = (a.N + a.rows_per_chunk - 1) / a.rows_per_chunk;
-  const size_t lds = (size_t)FWD_BJ * (a.N + 4) * 4 + (size_t)FWD_WAVES * 2 * 32 * HD * 2;
+  const size_t lds = (size_t)FWD_BJ * a.bstride * 2 + (size_t)FWD_WAVES * 2 * 32 * HD * 2;
   const void *kern = mask ? (const void *)fwd_kernel<true> : (const void *)fwd_kernel<false>;
   if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
       hipSuccess)
