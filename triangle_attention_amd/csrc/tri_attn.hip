@@ -549,14 +549,17 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
     *(u32x4 *)(s_kv + BWD_BK * HD + tile_off(row, part * 8)) = vw;
   };
   // mask bytes of the lane's keys (bit 0: key k0 + ll, bit 8: key k0 + 32 + ll)
-  auto load_mask = [&](int r) -> unsigned {
-    unsigned m = 0x101u;
-    if (a.mask) {
-      const uint8_t *mr = a.mask + (long long)b * a.f.mB + (long long)r * a.f.mR;
-      m = mr[(long long)(k0 + ll) * a.f.mK] != 0 ? 1u : 0u;
-      if (nkt > 1 && mr[(long long)(k0 + 32 + ll) * a.f.mK] != 0) m |= 0x100u;
-    }
-    return m;
+  // mask bytes of the lane's keys k0 + ll and k0 + 32 + ll (a byte holding 1 when there
+  // is no mask; the first key's byte again when the second tile is absent).  The
+  // values are first looked at a row later.
+  const uint8_t *mask_base =
+      a.mask ? a.mask + (long long)b * a.f.mB + (long long)(k0 + ll) * a.f.mK : &kMaskAllValid;
+  const long long mask_rstride = a.mask ? a.f.mR : 0;
+  const long long mask_second = (a.mask && nkt > 1) ? 32 * a.f.mK : 0;
+  auto load_mask = [&](int r, unsigned &m0, unsigned &m1) {
+    const uint8_t *mp = mask_base + (long long)r * mask_rstride;
+    m0 = mp[0];
+    m1 = mp[mask_second];
   };
   // one query tile: the lane's q and dO row halves (A operands as loaded) and the
   // two per-query terms of the lane's query
@@ -575,11 +578,13 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
 
   // transposed pair-bias tile: s_bias[kk][j] = bias[b, h, j, k0 + kk]
   {
-    const uint16_t *src = a.bias + ((long long)b * a.H + h) * N * N + k0;
-    const int per_row = nkt * 4;  // 8-key chunks per query row
-    for (int idx = tid; idx < N * per_row; idx += BWD_WAVES * 64) {
-      const int j = idx / per_row, c8 = idx - j * per_row;
-      const u32x4 w = ld16(src + (long long)j * N + c8 * 8);
+    // all 64 key rows; at a ragged end the absent key tile gets the last key's
+    // (finite) values, which its masked scores never use
+    const uint16_t *src = a.bias + ((long long)b * a.H + h) * N * N;
+    for (int idx = tid; idx < N * 8; idx += BWD_WAVES * 64) {
+      const int j = idx >> 3, c8 = idx & 7;
+      const int kc = min(k0 + c8 * 8, N - 8);
+      const u32x4 w = ld16(src + (long long)j * N + kc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         s_bias[(c8 * 8 + 2 * i) * BSTR + j] = (_Float16)bf_lo(w[i]);
@@ -617,25 +622,23 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
   uint16_t *dq_part = a.dq_part + (long long)kb * E;
 
   // prologue: the first row's keys, values, key mask and first query tile
-  u32x4 nk = {}, nv = {};
-  unsigned nmask = 0x101u;
-  if (r0 < r1) {
-    load_kv(r0, nk, nv);
-    nmask = load_mask(r0);
-    if (wave < njt) load_qtile(r0, wave);
-  }
+  u32x4 nk, nv;
+  unsigned nm0, nm1;
+  const int rfirst = min(r0, N - 1);  // a chunk is never empty; clamped for safety
+  load_kv(rfirst, nk, nv);
+  load_mask(rfirst, nm0, nm1);
+  load_qtile(rfirst, min(wave, njt - 1));
   store_kv(nk, nv);
   lds_barrier();
 
   for (int r = r0; r < r1; ++r) {
     const bool has_next = r + 1 < r1;
-    const unsigned cmask = nmask;
-    if (has_next) {
-      load_kv(r + 1, nk, nv);
-      nmask = load_mask(r + 1);
-    }
-    // exp2 argument offset of the lane's key per key tile: 0, or -inf for a masked key
-    const float moff[2] = {(cmask & 0xffu) ? 0.f : -INFINITY, (cmask >> 8) ? 0.f : -INFINITY};
+    const int rn = has_next ? r + 1 : r;  // row whose operands are fetched next (this row's at the end)
+    // exp2 argument offset of the lane's key per key tile: 0, or -inf for a masked or
+    // absent key
+    const float moff[2] = {nm0 != 0u ? 0.f : -INFINITY, (nkt > 1 && nm1 != 0u) ? 0.f : -INFINITY};
+    load_kv(rn, nk, nv);
+    load_mask(rn, nm0, nm1);
     const long long base = rowbase(r);
 
     f32x16 dK[2], dV[2];
@@ -662,38 +665,36 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
       const bf16x8 qB0 = tr_operand_sw(wq, 0, lane), qB1 = tr_operand_sw(wq, 16, lane);
       const bf16x8 dB0 = tr_operand_sw(wdo, 0, lane), dB1 = tr_operand_sw(wdo, 16, lane);
 
-      f32x16 dqT = {};
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        if (kt >= nkt) break;  // absent key tile at a ragged end
+      // Both key tiles are processed (at a ragged end the second one is fully masked
+      // and contributes zeros), as one software-pipelined block: each stage's LDS
+      // reads are issued a stage before their use.
+      struct KOps { bf16x8 k0, k1, v0, v1; f16x4 bw[4]; };
+      auto read_ops = [&](int kt, KOps &o) {
         const int krow = 32 * kt + ll;
-        const bf16x8 kB0 = *(const bf16x8 *)(s_kv + tile_off(krow, 8 * hh));
-        const bf16x8 kB1 = *(const bf16x8 *)(s_kv + tile_off(krow, 16 + 8 * hh));
-        const bf16x8 vB0 = *(const bf16x8 *)(s_v + tile_off(krow, 8 * hh));
-        const bf16x8 vB1 = *(const bf16x8 *)(s_v + tile_off(krow, 16 + 8 * hh));
-        f32x16 s = mfma(lA, ones3, (f32x16){});  // -lse/alpha
-        s = mfma(qA0, kB0, s);
-        s = mfma(qA1, kB1, s);                    // q.k - lse/alpha
-        f32x16 dp = mfma(dlA, ones3, (f32x16){}); // -D
-        dp = mfma(dA0, vB0, dp);
-        dp = mfma(dA1, vB1, dp);                  // dP - D
-        if (kt == nkt - 1) {
-          // the tile's q, dO and per-query terms are consumed: fetch the next tile's
-          if (jt + BWD_WAVES < njt)
-            load_qtile(r, jt + BWD_WAVES);
-          else if (has_next)
-            load_qtile(r + 1, wave);
-        }
+        o.k0 = *(const bf16x8 *)(s_kv + tile_off(krow, 8 * hh));
+        o.k1 = *(const bf16x8 *)(s_kv + tile_off(krow, 16 + 8 * hh));
+        o.v0 = *(const bf16x8 *)(s_v + tile_off(krow, 8 * hh));
+        o.v1 = *(const bf16x8 *)(s_v + tile_off(krow, 16 + 8 * hh));
         const _Float16 *brow = s_bias + krow * BSTR + j0 + 4 * hh;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) o.bw[g] = *(const f16x4 *)(brow + 8 * g);
+      };
+      // score and dP products of one key tile
+      auto products = [&](const KOps &o, f32x16 &sv, f32x16 &dp) {
+        sv = mfma(lA, ones3, (f32x16){});  // -lse/alpha
+        sv = mfma(qA0, o.k0, sv);
+        sv = mfma(qA1, o.k1, sv);           // q.k - lse/alpha
+        dp = mfma(dlA, ones3, (f32x16){});  // -D
+        dp = mfma(dA0, o.v0, dp);
+        dp = mfma(dA1, o.v1, dp);           // dP - D
+      };
+      // probabilities and dS of one key tile, their dV, dK, dbias products, and dS^T
+      // into LDS for the dQ product
+      auto gradients = [&](int kt, const KOps &o, const f32x16 &sv, const f32x16 &dp) {
         float p[16], ds[16];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f16x4 bw = *(const f16x4 *)(brow + 8 * g);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            p[4 * g + i] =
-                __builtin_amdgcn_exp2f(fmaf((float)bw[i], kLog2e, fmaf(s[4 * g + i], c1, moff[kt])));
-        }
+        for (int i = 0; i < 16; ++i)
+          p[i] = __builtin_amdgcn_exp2f(fmaf((float)o.bw[i >> 2][i & 3], kLog2e, fmaf(sv[i], c1, moff[kt])));
 #pragma unroll
         for (int i = 0; i < 16; ++i) ds[i] = p[i] * dp[i];
         const bf16x8 pA0 = pack8(p), pA1 = pack8(p + 8);
@@ -704,15 +705,34 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
         dK[kt] = mfma(sA1, qB1, dK[kt]);
         dbias[jj][kt] = mfma(ident[0], sA0, dbias[jj][kt]);
         dbias[jj][kt] = mfma(ident[1], sA1, dbias[jj][kt]);
-        // dS^T rows of this key tile for the dQ product (rows = keys, columns = queries)
         const u32x4 s0 = __builtin_bit_cast(u32x4, sA0), s1 = __builtin_bit_cast(u32x4, sA1);
+        const int krow = 32 * kt + ll;
         *(u32x2 *)(wds + tile_off(krow, 4 * hh)) = (u32x2){s0[0], s0[1]};
         *(u32x2 *)(wds + tile_off(krow, 8 + 4 * hh)) = (u32x2){s0[2], s0[3]};
         *(u32x2 *)(wds + tile_off(krow, 16 + 4 * hh)) = (u32x2){s1[0], s1[1]};
         *(u32x2 *)(wds + tile_off(krow, 24 + 4 * hh)) = (u32x2){s1[2], s1[3]};
+      };
+      auto dq_product = [&](int kt, f32x16 &dqT) {
         dqT = mfma(tr_operand_sw(s_kv, 32 * kt, lane), tr_operand_sw(wds, 32 * kt, lane), dqT);
         dqT = mfma(tr_operand_sw(s_kv, 32 * kt + 16, lane), tr_operand_sw(wds, 32 * kt + 16, lane), dqT);
+      };
+
+      KOps o0, o1;
+      f32x16 sv0, dp0, sv1, dp1, dqT = {};
+      read_ops(0, o0);
+      products(o0, sv0, dp0);
+      read_ops(1, o1);
+      products(o1, sv1, dp1);
+      // the tile's q, dO and per-query terms are consumed: fetch the next tile's (this
+      // row's next one, or the next row's first)
+      {
+        const bool same_row = jt + BWD_WAVES < njt;
+        load_qtile(same_row ? r : rn, same_row ? jt + BWD_WAVES : wave);
       }
+      gradients(0, o0, sv0, dp0);
+      gradients(1, o1, sv1, dp1);
+      dq_product(0, dqT);
+      dq_product(1, dqT);
       // this key block's dQ partial, rounded to bf16 (summed in fp32 over the blocks);
       // a wave's four stores fill the tile's contiguous 2 KB of the partial
       uint16_t *qout = dq_part + ((((long long)b * N + r) * a.H + h) * N + j0 + ll) * HD + 4 * hh;
