@@ -11,7 +11,10 @@ backward products; exp and the bias-gradient additions are not counted).
 The JSON line also carries
   roofline     : the backward main kernel (the dominant one), timed with HIP
                  events recorded by the library on the launch stream, against
-                 the MI355X dense bf16 MFMA peak;
+                 the MI355X dense bf16 MFMA peak; its "traffic" is the HBM bytes
+                 per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary in
+                 profiles/ (calibrated against a plain device copy), or null when
+                 that summary was taken on a different kernel source;
   cpu_baseline : the FP64 oracle timed on this host on a bounded sample of the
                  same workload (sampled attention rows and bias-gradient rows),
                  scaled to the whole workload.
@@ -19,10 +22,13 @@ The JSON line also carries
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
+from pathlib import Path
 
 import torch
 
@@ -62,6 +68,28 @@ class HipEvents:
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+ROOT = Path(__file__).resolve().parent
+KERNEL_SOURCE = ROOT / "triangle_attention_amd" / "csrc" / "tri_attn.hip"
+
+
+def measured_traffic(workload: str, ending: bool):
+    """HBM bytes per launch of the backward main kernel from the committed rocprofv3
+    counter summary, if it was taken on this kernel source and workload."""
+    if ending:
+        return None
+    f = ROOT / "profiles" / f"traffic_bwd_main_{workload}.md"
+    if not f.exists():
+        return None
+    text = f.read_text()
+    sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not sha or not val:
+        return None
+    if sha.group(1) != hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest():
+        return None
+    return int(val.group(1))
 
 
 def cpu_baseline(inp, rows: int, dbias_rows: int):
@@ -104,9 +132,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="crop768")
     ap.add_argument("--ending", action="store_true", help="ending-node orientation")
-    ap.add_argument("--cpu-rows", type=int, default=48)
-    ap.add_argument("--cpu-dbias-rows", type=int, default=96)
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-dbias-rows", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="copy a 256 MiB device buffer once before the warmup (a known-size kernel "
+                         "that calibrates the rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -132,6 +163,12 @@ def main():
         return ta.tri_attn_bwd(g["q"], g["k"], g["v"], g["bias"], mask, o, res, lse, g["do"],
                                ending=args.ending, workspace=ws, main_events=events)
 
+    if args.calib_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
@@ -175,7 +212,8 @@ def main():
                    "mfma_peak_frac": round(value / MFMA_PEAK_BF16_TFLOPS, 4)},
         "roofline": {"kernel": "bwd_main_kernel", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / MFMA_PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name, args.ending),
                      "avg_ms": round(main_ms, 4)},
     }
     if not args.no_cpu_baseline:

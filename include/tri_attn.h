@@ -22,7 +22,12 @@
  * Layouts (row-major, last index fastest):
  *   q, k, v, o, d_o, dq, dk, dv : bf16 [B, N, N, H, D]  (D contiguous)
  *   o_residual                  : fp32 [B, N, N, H, D]
- *   bias, dbias                 : bf16 [B, H, N, N] (dbias fp32 with FLAG_DBIAS_FP32)
+ *   bias, dbias                 : bf16 [B, H, N, N] (dbias fp32 with FLAG_DBIAS_FP32);
+ *                                 bias values must lie in the fp16 range
+ *                                 (|bias| <= 65504, or -inf): the kernels hold the
+ *                                 bias as fp16, to which such a bf16 value converts
+ *                                 exactly when |bias| >= 2^-14 (smaller magnitudes
+ *                                 round to a multiple of 2^-24)
  *   mask                        : uint8 [B, N, N], nonzero = key attended; NULL = all
  *   lse                         : fp32 [B, N, H, N], indexed [b, r, h, q] by
  *                                 attention row r and query q (natural log)
