@@ -40,6 +40,7 @@
 namespace {
 
 constexpr int HD = 32;  // head dimension handled by this build
+constexpr int kNumCUs = 256;  // compute units of an MI355X: launch shapes are sized for one round
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
@@ -199,16 +200,21 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
       *(f16x8 *)(bias_s + row * bstride + c8 * 8) = hv;
     }
   }
-  __syncthreads();
-
+  // rows of the chunk are handed out one at a time: each wave starts on its own row
+  // and then takes the next untaken one, so the waves of the workgroup, which share
+  // SIMDs unevenly, finish within about one row of each other
+  __shared__ int s_next_row;
   const int r0 = chunk * a.rows_per_chunk;
   const int r1 = min(N, r0 + a.rows_per_chunk);
+  if (tid == 0) s_next_row = r0 + FWD_WAVES;
+  __syncthreads();
+
   const float c1 = a.c1;
   const int nkt = N / 32;
   const int vkey = lane >> 2, vpart = lane & 3;  // the lane's K and V chunks within a tile
   const long long mk = a.mask ? a.f.mK : 0;
   typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
-  for (int r = r0 + wave; r < r1; r += FWD_WAVES) {
+  for (int r = r0 + wave; r < r1;) {
     const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
     bf16x8 qB[2][2];
 #pragma unroll
@@ -260,8 +266,18 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) bw[g] = *(const f16x4 *)(brow + 8 * g);
     };
-    // maximum over the tile of t = c1 q.k + log2(e) bias (both lane halves)
-    auto tile_max = [&](const f32x16 &acc, const f16x4 *bw) {
+    // maximum over the tile of t = c1 q.k + log2(e) bias (both lane halves).  The bias
+    // values pass through an empty asm first: were they shared with the hot path, the
+    // compiler would convert them to fp32 once for both uses, and the hot path would
+    // then spend a conversion and a multiply-add per score instead of one
+    // mixed-precision multiply-add.
+    auto tile_max = [&](const f32x16 &acc, const f16x4 *bw_in) {
+      f16x4 bw[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bw[g] = bw_in[g];
+        __asm__ volatile("" : "+v"(bw[g]));
+      }
       float mt = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, fmaf((float)bw[i >> 2][i & 3], kLog2e, acc[i] * c1));
@@ -364,6 +380,9 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
         a.lse[(((long long)b * N + r) * a.H + h) * N + j0 + 32 * s + jl] = L;
       }
     }
+    int taken = 0;
+    if (lane == 0) taken = atomicAdd(&s_next_row, 1);
+    r = __builtin_amdgcn_readfirstlane(taken);
   }
 }
 
@@ -916,7 +935,7 @@ BwdPlan plan_bwd(const tri_attn_problem *p) {
   pl.T = (N + BWD_BK - 1) / BWD_BK;
   // one workgroup per CU (its LDS and registers fill one); one wave of workgroups
   const int groups = (int)(p->B * p->H * pl.T);
-  int C = 256 / groups;
+  int C = kNumCUs / groups;
   if (C < 1) C = 1;
   if (C > N) C = N;
   pl.rows_per_chunk = (N + C - 1) / C;
@@ -1006,8 +1025,11 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
   // fp16 bias row stride with stride/2 = 2 (mod 32) 4-byte banks: the 8-byte reads of
   // 16 lanes (16 rows) are then conflict-free
   a.bstride = a.N + ((a.N & 63) ? 36 : 4);
+  // one workgroup per CU (its LDS fills one) and, where the problem allows, a single
+  // round of workgroups: the block's bias is then staged once per CU
   const int groups = a.B * a.H * a.n_jblocks;
-  int chunks = (768 + groups - 1) / groups;  // about three rounds of one workgroup per CU
+  int chunks = kNumCUs / groups;
+  if (chunks < 1) chunks = 1;
   if (chunks > a.N) chunks = a.N;
   a.rows_per_chunk = (a.N + chunks - 1) / chunks;
   a.n_chunks = (a.N + a.rows_per_chunk - 1) / a.rows_per_chunk;
