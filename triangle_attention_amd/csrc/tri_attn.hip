@@ -170,7 +170,9 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
   _Float16 *bias_s = (_Float16 *)smem_f4;
   const int N = a.N;
   const int bstride = a.bstride;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index through readfirstlane: the compiler then knows it is uniform and
+  // keeps everything derived from it (rows, tile indices, addresses) in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int jl = lane & 31, hh = lane >> 5;
   int t = xcd_remap(blockIdx.x, gridDim.x);
   const int jb = t % a.n_jblocks; t /= a.n_jblocks;
@@ -529,7 +531,9 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
   __shared__ __attribute__((aligned(16))) uint16_t s_ds[BWD_WAVES * BWD_BK * HD];
 
   const int N = a.N;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index through readfirstlane, so that tile indices and addresses derived
+  // from it stay in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, ll = lane & 31;
   uint16_t *wq = s_qd + wave * 2 * 32 * HD;
   uint16_t *wdo = wq + 32 * HD;
