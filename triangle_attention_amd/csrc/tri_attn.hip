@@ -841,7 +841,8 @@ __global__ __launch_bounds__(256) void reduce_dq_kernel(ReduceArgs a) {
   if (e >= E) return;
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int t = 0; t < a.T; ++t) {
-    const u32x4 w = ld16(a.dq_part + (long long)t * E + e);
+    // each partial is read once: non-temporal loads keep them from displacing other lines
+    const u32x4 w = __builtin_nontemporal_load((const u32x4 *)(a.dq_part + (long long)t * E + e));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       s[2 * i] += bf_lo(w[i]);
