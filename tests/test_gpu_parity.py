@@ -229,6 +229,18 @@ def test_shapes_and_masks(ta, B, N, H, mask_kind, ending):
     check_full(ta, inp, ending=ending, tag=f"B{B}N{N}H{H}{mask_kind}")
 
 
+@pytest.mark.parametrize("B,N,H,mask_kind,ending", [
+    (1, 736, 2, "pad32", False),   # largest row tiling (6 query tiles per wave), last key block one 32-key tile
+    (1, 736, 2, "random", True),
+    (2, 352, 3, "random", False),  # B > 1 with a ragged key block at a mid size
+])
+def test_large_ragged_sampled(ta, B, N, H, mask_kind, ending):
+    inp = custom(B, N, H, 101 + N + H, mask_kind)
+    rows = sorted(set((b, r) for b in range(B) for (_, r) in sample_rows(N)))
+    sel = sorted(set((b, h, j) for b in range(B) for (_, h, j) in sample_dbias(N, H)))
+    check_sampled(ta, inp, ending, rows, sel, f"B{B}N{N}H{H}{mask_kind}")
+
+
 def test_fully_masked_rows_and_keys(ta):
     inp = custom(1, 64, 2, 11, "random")
     m = inp["mask"]
