@@ -21,7 +21,7 @@
  *
  * Layouts (row-major, last index fastest):
  *   q, k, v, o, d_o, dq, dk, dv : bf16 [B, N, N, H, D]  (D contiguous)
- *   o_residual                  : fp32 [B, N, N, H, D]
+ *   o_residual                  : bf16 [B, N, N, H, D]
  *   bias, dbias                 : bf16 [B, H, N, N] (dbias fp32 with FLAG_DBIAS_FP32);
  *                                 bias values must lie in the fp16 range
  *                                 (|bias| <= 65504, or -inf): the kernels hold the
@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define TRI_ATTN_ABI_VERSION 1
+#define TRI_ATTN_ABI_VERSION 2
 
 typedef enum {
     TRI_ATTN_SUCCESS = 0,
@@ -94,14 +94,17 @@ const char *tri_attn_status_string(int status);
  * the FP32-to-BF16 rounding residual of the output is kept for the backward).
  *   q, k, v, bias, mask : inputs as laid out above (mask may be NULL)
  *   o                   : bf16 output, round-to-nearest-even of the fp32 result O
- *   o_residual          : fp32 O - float(o), exactly; NULL = not saved
+ *   o_residual          : bf16 round-to-nearest-even of the fp32 residual O - float(o)
+ *                         (exact in fp32); float(o) + float(o_residual) restores O to
+ *                         within 2^-9 of the residual, i.e. about 2^-17 relative to O.
+ *                         NULL = not saved
  *   lse                 : fp32 log-sum-exp of every softmax row; +inf for a row
  *                         whose keys are all masked (its o and residual are 0)
  */
 tri_attn_status tri_attn_fwd(const tri_attn_problem *problem,
                              const void *q, const void *k, const void *v,
                              const void *bias, const uint8_t *mask,
-                             void *o, float *o_residual, float *lse,
+                             void *o, void *o_residual, float *lse,
                              hipStream_t stream);
 
 /* Device workspace (bytes) tri_attn_bwd needs for `problem`; 0 if the problem
@@ -128,7 +131,7 @@ size_t tri_attn_bwd_workspace_bytes(const tri_attn_problem *problem);
 tri_attn_status tri_attn_bwd(const tri_attn_problem *problem,
                              const void *q, const void *k, const void *v,
                              const void *bias, const uint8_t *mask,
-                             const void *o, const float *o_residual, const float *lse,
+                             const void *o, const void *o_residual, const float *lse,
                              const void *d_o,
                              void *dq, void *dk, void *dv, void *dbias,
                              void *workspace, size_t workspace_bytes,
@@ -144,7 +147,7 @@ tri_attn_status tri_attn_bwd(const tri_attn_problem *problem,
 tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem,
                                       const void *q, const void *k, const void *v,
                                       const void *bias, const uint8_t *mask,
-                                      const void *o, const float *o_residual,
+                                      const void *o, const void *o_residual,
                                       const float *lse, const void *d_o,
                                       void *dq, void *dk, void *dv, void *dbias,
                                       void *workspace, size_t workspace_bytes,

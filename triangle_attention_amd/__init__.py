@@ -21,7 +21,7 @@ import torch
 _HERE = Path(__file__).resolve().parent
 LIB_PATH = _HERE / "libtri_attn.so"
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 FLAG_ENDING_NODE = 1
 FLAG_DBIAS_FP32 = 2
 
@@ -115,12 +115,12 @@ def _check_inputs(q, k, v, bias, mask):
 
 
 def tri_attn_fwd(q, k, v, bias, mask=None, *, ending=False, scale=None, save_residual=True):
-    """Forward: returns (o bf16, o_residual fp32 or None, lse fp32 [B, N, H, N])."""
+    """Forward: returns (o bf16, o_residual bf16 or None, lse fp32 [B, N, H, N])."""
     B, N, H, D = _check_inputs(q, k, v, bias, mask)
     lib = load_library()
     prob = make_problem(B, N, H, D, ending=ending, scale=scale)
     o = torch.empty_like(q)
-    res = torch.empty(q.shape, dtype=torch.float32, device=q.device) if save_residual else None
+    res = torch.empty_like(q) if save_residual else None
     lse = torch.empty((B, N, H, N), dtype=torch.float32, device=q.device)
     st = lib.tri_attn_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask),
                           _ptr(o), _ptr(res), _ptr(lse), _stream(q.device))

@@ -149,7 +149,8 @@ struct FwdArgs {
   const uint16_t *q, *k, *v, *bias;
   const uint8_t *mask;
   uint16_t *o;
-  float *res, *lse;
+  uint16_t *res;  // bf16 rounding residual, may be null
+  float *lse;
   Frame f;
   int B, N, H;
   int n_jblocks, n_chunks, rows_per_chunk;
@@ -355,26 +356,35 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
       }
       pass(m, oacc, lsum);
     }
+    // o and its rounding residual (both bf16) leave through the wave's K/V LDS tiles
+    // (free between rows): written there in the accumulator layout and read back by
+    // query, so that every query's 64-byte segment of each is stored whole.  16-byte
+    // chunks are permuted by row bits so both LDS passes are free of bank conflicts.
+    auto o_off = [](int row, int chunk) { return row * HD + ((chunk ^ ((row >> 2) & 3)) << 3); };
+    uint16_t *ot = kbuf;  // [32 queries][32 channels] bf16: o
+    uint16_t *rt = vbuf;  // [32 queries][32 channels] bf16: residual
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (s == 1 && !two) break;
       const float inv = lsum[s] > 0.f ? 1.f / lsum[s] : 0.f;
-      const long long obase = base + (long long)(j0 + 32 * s + jl) * a.f.sQ;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        float ov[4], rv[4];
-        unsigned pk[2];
+        float ov[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ov[i] = oacc[s][4 * g + i] * inv;
-        pk[0] = pack_bf16(ov[0], ov[1]);
-        pk[1] = pack_bf16(ov[2], ov[3]);
-        rv[0] = ov[0] - bf_lo(pk[0]);
-        rv[1] = ov[1] - bf_hi(pk[0]);
-        rv[2] = ov[2] - bf_lo(pk[1]);
-        rv[3] = ov[3] - bf_hi(pk[1]);
-        const int c = 8 * g + 4 * hh;
-        *(u32x2 *)(a.o + obase + c) = (u32x2){pk[0], pk[1]};
-        if (a.res) *(f32x4 *)(a.res + obase + c) = (f32x4){rv[0], rv[1], rv[2], rv[3]};
+        const unsigned p0 = pack_bf16(ov[0], ov[1]), p1 = pack_bf16(ov[2], ov[3]);
+        // channels 8g + 4hh .. 8g + 4hh + 3 of query jl; the residual O - float(o) is
+        // exact in fp32 and rounded once more, to bf16
+        *(u32x2 *)(ot + o_off(jl, g) + 4 * hh) = (u32x2){p0, p1};
+        *(u32x2 *)(rt + o_off(jl, g) + 4 * hh) =
+            (u32x2){pack_bf16(ov[0] - bf_lo(p0), ov[1] - bf_hi(p0)), pack_bf16(ov[2] - bf_lo(p1), ov[3] - bf_hi(p1))};
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int row = (lane >> 2) + 16 * k, chunk = lane & 3;
+        const long long off = base + (long long)(j0 + 32 * s + row) * a.f.sQ + 8 * chunk;
+        *(u32x4 *)(a.o + off) = *(const u32x4 *)(ot + o_off(row, chunk));
+        if (a.res) *(u32x4 *)(a.res + off) = *(const u32x4 *)(rt + o_off(row, chunk));
       }
       if (hh == 0) {
         // lse = ln(sum exp(logit)) = ln 2 * (m + log2(sum p))
@@ -396,7 +406,8 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
 // residual when the residual is saved; the channel sum runs in a fixed order.
 struct PrepArgs {
   const uint16_t *o, *d_o;
-  const float *res, *lse;
+  const uint16_t *res;  // bf16 rounding residual of o, or null
+  const float *lse;
   float *stats;  // [B][N][H][2][N]: -lse/alpha, then -D
   Frame f;
   int B, N, H;
@@ -422,22 +433,22 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
     gw[i] = ld16(a.d_o + base + 8 * i);
     ow[i] = ld16(a.o + base + 8 * i);
   }
-  f32x4 rw[8];
+  u32x4 rw[4];
   if (a.res) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rw[i] = *(const f32x4 *)(a.res + base + 4 * i);
+    for (int i = 0; i < 4; ++i) rw[i] = ld16(a.res + base + 8 * i);
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rw[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) rw[i] = (u32x4){0u, 0u, 0u, 0u};
   }
   float acc = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const int c = 8 * i + 2 * w;  // channels c, c+1
-      const float o0 = bf_lo(ow[i][w]) + rw[c >> 2][c & 3];
-      const float o1 = bf_hi(ow[i][w]) + rw[(c + 1) >> 2][(c + 1) & 3];
+      // channels 8i + 2w and 8i + 2w + 1
+      const float o0 = bf_lo(ow[i][w]) + bf_lo(rw[i][w]);
+      const float o1 = bf_hi(ow[i][w]) + bf_hi(rw[i][w]);
       acc = fmaf(bf_lo(gw[i][w]), o0, acc);
       acc = fmaf(bf_hi(gw[i][w]), o1, acc);
     }
@@ -992,7 +1003,7 @@ const char *tri_attn_status_string(int status) {
 }
 
 tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, const void *k, const void *v,
-                             const void *bias, const uint8_t *mask, void *o, float *o_residual, float *lse,
+                             const void *bias, const uint8_t *mask, void *o, void *o_residual, float *lse,
                              hipStream_t stream) {
   tri_attn_status st = check_problem(problem);
   if (st != TRI_ATTN_SUCCESS) return st;
@@ -1003,7 +1014,7 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
   const size_t E = (size_t)p.B * p.N * p.N * p.H * p.D;
   const Range ins[] = {span(q, E * 2), span(k, E * 2), span(v, E * 2), span(bias, (size_t)p.B * p.H * p.N * p.N * 2),
                        span(mask, mask ? (size_t)p.B * p.N * p.N : 0)};
-  const Range outs[] = {span(o, E * 2), span(o_residual, o_residual ? E * 4 : 0),
+  const Range outs[] = {span(o, E * 2), span(o_residual, o_residual ? E * 2 : 0),
                         span(lse, (size_t)p.B * p.N * p.H * p.N * 4)};
   for (const Range &x : outs) {
     for (const Range &y : ins)
@@ -1019,7 +1030,7 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
   a.bias = (const uint16_t *)bias;
   a.mask = mask;
   a.o = (uint16_t *)o;
-  a.res = o_residual;
+  a.res = (uint16_t *)o_residual;
   a.lse = lse;
   a.f = make_frame(problem);
   a.B = (int)p.B;
@@ -1057,7 +1068,7 @@ size_t tri_attn_bwd_workspace_bytes(const tri_attn_problem *problem) {
 
 tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const void *q, const void *k,
                                       const void *v, const void *bias, const uint8_t *mask, const void *o,
-                                      const float *o_residual, const float *lse, const void *d_o, void *dq,
+                                      const void *o_residual, const float *lse, const void *d_o, void *dq,
                                       void *dk, void *dv, void *dbias, void *workspace, size_t workspace_bytes,
                                       hipEvent_t main_start, hipEvent_t main_stop, hipStream_t stream) {
   tri_attn_status st = check_problem(problem);
@@ -1078,7 +1089,7 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
                        span(bias, nb * 2),
                        span(mask, mask ? (size_t)p.B * p.N * p.N : 0),
                        span(o, E * 2),
-                       span(o_residual, o_residual ? E * 4 : 0),
+                       span(o_residual, o_residual ? E * 2 : 0),
                        span(lse, (size_t)p.B * p.N * p.H * p.N * 4),
                        span(d_o, E * 2)};
   const Range outs[] = {span(dq, E * 2), span(dk, E * 2), span(dv, E * 2),
@@ -1101,7 +1112,7 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
   PrepArgs pa;
   pa.o = (const uint16_t *)o;
   pa.d_o = (const uint16_t *)d_o;
-  pa.res = o_residual;
+  pa.res = (const uint16_t *)o_residual;
   pa.lse = lse;
   pa.stats = stats;
   pa.inv_alpha = 1.f / alpha;
@@ -1161,7 +1172,7 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
 }
 
 tri_attn_status tri_attn_bwd(const tri_attn_problem *problem, const void *q, const void *k, const void *v,
-                             const void *bias, const uint8_t *mask, const void *o, const float *o_residual,
+                             const void *bias, const uint8_t *mask, const void *o, const void *o_residual,
                              const float *lse, const void *d_o, void *dq, void *dk, void *dv, void *dbias,
                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
   return tri_attn_bwd_profiled(problem, q, k, v, bias, mask, o, o_residual, lse, d_o, dq, dk, dv, dbias,
