@@ -848,27 +848,29 @@ struct ReduceArgs {
 // block order, times alpha, rounded to bf16 in the caller's frame
 __global__ __launch_bounds__(256) void reduce_dq_kernel(ReduceArgs a) {
   const long long E = (long long)a.B * a.N * a.N * a.H * HD;
+  // thread -> 8 channels of output element (b, r, q, h, c), heads inside positions, so
+  // that a wave writes whole multi-head position segments
   const long long e = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (e >= E) return;
+  const int c = (int)(e % HD);
+  long long u = e / HD;
+  const int h = (int)(u % a.H);
+  u /= a.H;
+  const int q = (int)(u % a.N);
+  u /= a.N;
+  const int r = (int)(u % a.N);
+  const int b = (int)(u / a.N);
+  const long long pe = ((((long long)b * a.N + r) * a.H + h) * a.N + q) * HD + c;  // partial element
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int t = 0; t < a.T; ++t) {
     // each partial is read once: non-temporal loads keep them from displacing other lines
-    const u32x4 w = __builtin_nontemporal_load((const u32x4 *)(a.dq_part + (long long)t * E + e));
+    const u32x4 w = __builtin_nontemporal_load((const u32x4 *)(a.dq_part + (long long)t * E + pe));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       s[2 * i] += bf_lo(w[i]);
       s[2 * i + 1] += bf_hi(w[i]);
     }
   }
-  // partial element (b, r, h, q, c) -> caller's frame
-  const int c = (int)(e % HD);
-  long long u = e / HD;
-  const int q = (int)(u % a.N);
-  u /= a.N;
-  const int h = (int)(u % a.H);
-  u /= a.H;
-  const int r = (int)(u % a.N);
-  const int b = (int)(u / a.N);
   const long long off = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)q * a.f.sQ + h * HD + c;
   *(u32x4 *)(a.dq + off) = (u32x4){pack_bf16(s[0] * a.alpha, s[1] * a.alpha), pack_bf16(s[2] * a.alpha, s[3] * a.alpha),
                                    pack_bf16(s[4] * a.alpha, s[5] * a.alpha), pack_bf16(s[6] * a.alpha, s[7] * a.alpha)};
