@@ -532,12 +532,14 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int JT>
+template <int JT, bool MASKED>
 __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) {
   constexpr int NMAX = 32 * BWD_WAVES * JT;
   constexpr int BSTR = NMAX + 4;  // fp16 row stride of the bias tile: conflict-free 8-byte reads
   __shared__ __attribute__((aligned(16))) _Float16 s_bias[BWD_BK * BSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t s_kv[2 * BWD_BK * HD];
+  // keys and values of the block for two rows: the current one and the next one, which
+  // is staged early in the current row
+  __shared__ __attribute__((aligned(16))) uint16_t s_kv[2][2 * BWD_BK * HD];
   __shared__ __attribute__((aligned(16))) uint16_t s_qd[BWD_WAVES * 2 * 32 * HD];
   __shared__ __attribute__((aligned(16))) uint16_t s_ds[BWD_WAVES * BWD_BK * HD];
 
@@ -549,7 +551,6 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
   uint16_t *wq = s_qd + wave * 2 * 32 * HD;
   uint16_t *wdo = wq + 32 * HD;
   uint16_t *wds = s_ds + wave * BWD_BK * HD;
-  const uint16_t *s_v = s_kv + BWD_BK * HD;
 
   int t = xcd_remap(blockIdx.x, gridDim.x);
   const int kb = t % a.n_kblocks; t /= a.n_kblocks;
@@ -577,28 +578,45 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
     kw = ld16(a.k + off);
     vw = ld16(a.v + off);
   };
-  auto store_kv = [&](u32x4 kw, u32x4 vw) {
+  auto store_kv = [&](u32x4 kw, u32x4 vw, int buf) {
     const int row = tid >> 2, part = tid & 3;
-    *(u32x4 *)(s_kv + tile_off(row, part * 8)) = kw;
-    *(u32x4 *)(s_kv + BWD_BK * HD + tile_off(row, part * 8)) = vw;
+    *(u32x4 *)(s_kv[buf] + tile_off(row, part * 8)) = kw;
+    *(u32x4 *)(s_kv[buf] + BWD_BK * HD + tile_off(row, part * 8)) = vw;
   };
-  // mask bytes of the lane's keys (bit 0: key k0 + ll, bit 8: key k0 + 32 + ll)
-  // mask bytes of the lane's keys k0 + ll and k0 + 32 + ll (a byte holding 1 when there
-  // is no mask; the first key's byte again when the second tile is absent).  The
-  // values are first looked at a row later.
-  const uint8_t *mask_base =
-      a.mask ? a.mask + (long long)b * a.f.mB + (long long)(k0 + ll) * a.f.mK : &kMaskAllValid;
-  const long long mask_rstride = a.mask ? a.f.mR : 0;
-  const long long mask_second = (a.mask && nkt > 1) ? 32 * a.f.mK : 0;
+  // mask bytes of the lane's keys k0 + ll and k0 + 32 + ll (the first key's byte again
+  // when the second tile is absent), looked at a row later; the unmasked variant loads
+  // none and takes every key as attended
+  const uint8_t *mask_base = MASKED ? a.mask + (long long)b * a.f.mB + (long long)(k0 + ll) * a.f.mK : nullptr;
+  const long long mask_second = nkt > 1 ? 32 * a.f.mK : 0;
   auto load_mask = [&](int r, unsigned &m0, unsigned &m1) {
-    const uint8_t *mp = mask_base + (long long)r * mask_rstride;
-    m0 = mp[0];
-    m1 = mp[mask_second];
+    if constexpr (MASKED) {
+      const uint8_t *mp = mask_base + (long long)r * a.f.mR;
+      m0 = mp[0];
+      m1 = mp[mask_second];
+    } else {
+      m0 = m1 = 1u;
+    }
   };
   // one query tile: the lane's q and dO row halves (A operands as loaded) and the
   // two per-query terms of the lane's query
   u32x4 tq0, tq1, td0, td1;
   float tl = 0.f, tdl = 0.f;
+  // the loaded tile's q and dO rows into the wave's LDS tiles, for the transposed B
+  // operands of the dK and dV products; the empty asm makes the per-query terms count as
+  // consumed here too, so the tile that uses them waits for nothing
+  auto stage_qtile = [&]() {
+    *(u32x4 *)(wq + tile_off(ll, 8 * hh)) = tq0;
+    *(u32x4 *)(wq + tile_off(ll, 16 + 8 * hh)) = tq1;
+    *(u32x4 *)(wdo + tile_off(ll, 8 * hh)) = td0;
+    *(u32x4 *)(wdo + tile_off(ll, 16 + 8 * hh)) = td1;
+    __asm__ volatile("" ::"v"(tl), "v"(tdl));
+  };
+  // exp2 argument offsets of the lane's keys from their mask bytes: 0, or -inf for a
+  // masked or absent key
+  auto mask_offsets = [&](unsigned m0, unsigned m1, float *mo) {
+    mo[0] = m0 != 0u ? 0.f : -INFINITY;
+    mo[1] = (nkt > 1 && m1 != 0u) ? 0.f : -INFINITY;
+  };
   auto load_qtile = [&](int r, int jt) {
     const long long off = rowbase(r) + (long long)(jt * 32 + ll) * a.f.sQ + 8 * hh;
     tq0 = ld16(a.q + off);
@@ -662,15 +680,20 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
   load_kv(rfirst, nk, nv);
   load_mask(rfirst, nm0, nm1);
   load_qtile(rfirst, min(wave, njt - 1));
-  store_kv(nk, nv);
+  store_kv(nk, nv, 0);
+  stage_qtile();
+  float moff[2];
+  mask_offsets(nm0, nm1, moff);
   lds_barrier();
 
   for (int r = r0; r < r1; ++r) {
+    // this row's keys and values; the next row's go to the other buffer during the
+    // row's first tile, where waiting for their loads does not also wait for stores
+    const int cur = (r - r0) & 1;
+    const uint16_t *s_k = s_kv[cur], *s_v = s_kv[cur] + BWD_BK * HD;
     const bool has_next = r + 1 < r1;
     const int rn = has_next ? r + 1 : r;  // row whose operands are fetched next (this row's at the end)
-    // exp2 argument offset of the lane's key per key tile: 0, or -inf for a masked or
-    // absent key
-    const float moff[2] = {nm0 != 0u ? 0.f : -INFINITY, (nkt > 1 && nm1 != 0u) ? 0.f : -INFINITY};
+    float next_moff[2] = {0.f, 0.f};
     load_kv(rn, nk, nv);
     load_mask(rn, nm0, nm1);
     const long long base = rowbase(r);
@@ -692,10 +715,9 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
       const bf16x8 qA0 = as_bf16x8(tq0), qA1 = as_bf16x8(tq1);
       const bf16x8 dA0 = as_bf16x8(td0), dA1 = as_bf16x8(td1);
       const bf16x8 lA = split3_operand(tl, hh), dlA = split3_operand(tdl, hh);
-      *(u32x4 *)(wq + tile_off(ll, 8 * hh)) = tq0;
-      *(u32x4 *)(wq + tile_off(ll, 16 + 8 * hh)) = tq1;
-      *(u32x4 *)(wdo + tile_off(ll, 8 * hh)) = td0;
-      *(u32x4 *)(wdo + tile_off(ll, 16 + 8 * hh)) = td1;
+      // the row's first tile was staged at the end of the previous row (or before the
+      // first): waiting for its loads here would also wait for that row's stores
+      if (jj > 0) stage_qtile();
       const bf16x8 qB0 = tr_operand_sw(wq, 0, lane), qB1 = tr_operand_sw(wq, 16, lane);
       const bf16x8 dB0 = tr_operand_sw(wdo, 0, lane), dB1 = tr_operand_sw(wdo, 16, lane);
 
@@ -705,8 +727,8 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
       struct KOps { bf16x8 k0, k1, v0, v1; f16x4 bw[4]; };
       auto read_ops = [&](int kt, KOps &o) {
         const int krow = 32 * kt + ll;
-        o.k0 = *(const bf16x8 *)(s_kv + tile_off(krow, 8 * hh));
-        o.k1 = *(const bf16x8 *)(s_kv + tile_off(krow, 16 + 8 * hh));
+        o.k0 = *(const bf16x8 *)(s_k + tile_off(krow, 8 * hh));
+        o.k1 = *(const bf16x8 *)(s_k + tile_off(krow, 16 + 8 * hh));
         o.v0 = *(const bf16x8 *)(s_v + tile_off(krow, 8 * hh));
         o.v1 = *(const bf16x8 *)(s_v + tile_off(krow, 16 + 8 * hh));
         const _Float16 *brow = s_bias + krow * BSTR + j0 + 4 * hh;
@@ -747,8 +769,8 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
         *(u32x2 *)(wds + tile_off(krow, 24 + 4 * hh)) = (u32x2){s1[2], s1[3]};
       };
       auto dq_product = [&](int kt, f32x16 &dqT) {
-        dqT = mfma(tr_operand_sw(s_kv, 32 * kt, lane), tr_operand_sw(wds, 32 * kt, lane), dqT);
-        dqT = mfma(tr_operand_sw(s_kv, 32 * kt + 16, lane), tr_operand_sw(wds, 32 * kt + 16, lane), dqT);
+        dqT = mfma(tr_operand_sw(s_k, 32 * kt, lane), tr_operand_sw(wds, 32 * kt, lane), dqT);
+        dqT = mfma(tr_operand_sw(s_k, 32 * kt + 16, lane), tr_operand_sw(wds, 32 * kt + 16, lane), dqT);
       };
 
       KOps o0, o1;
@@ -763,6 +785,15 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
         const bool same_row = jt + BWD_WAVES < njt;
         load_qtile(same_row ? r : rn, same_row ? jt + BWD_WAVES : wave);
       }
+      if (jj == 0) {
+        // kept here (not hoisted next to the loads at the row start): waiting for the
+        // loads at this point leaves the stores issued since in flight
+        __builtin_amdgcn_sched_barrier(0);
+        store_kv(nk, nv, cur ^ 1);
+        unsigned m0 = nm0, m1 = nm1;
+        __asm__ volatile("" : "+v"(m0), "+v"(m1));  // not merged with the copy below
+        mask_offsets(m0, m1, next_moff);
+      }
       gradients(0, o0, sv0, dp0);
       gradients(1, o1, sv1, dp1);
       dq_product(0, dqT);
@@ -774,6 +805,11 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
       for (int g = 0; g < 4; ++g)
         *(u32x2 *)(qout + 8 * g) =
             (u32x2){pack_bf16(dqT[4 * g], dqT[4 * g + 1]), pack_bf16(dqT[4 * g + 2], dqT[4 * g + 3])};
+    }
+
+    if (wave >= njt) {  // a wave without query tiles in this row
+      store_kv(nk, nv, cur ^ 1);
+      mask_offsets(nm0, nm1, next_moff);
     }
 
     // fixed-order cross-wave reduction of dV then dK for this row.  Each wave's
@@ -793,8 +829,6 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
         for (int i = 0; i < 16; ++i) red_ptr(wave, 32 * kt + 8 * (i >> 2) + 4 * hh + (i & 3))[ll] = acc[i];
       }
       lds_barrier();
-      // every wave is past its last read of this row's keys and values: stage the next row's
-      if (!which) store_kv(nk, nv);
       const float scale = which ? a.alpha : 1.f;
       uint16_t *dst = which ? a.dk : a.dv;
 #pragma unroll
@@ -810,7 +844,10 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
         *(u32x2 *)(dst + off) = (u32x2){pack_bf16(sum[0], sum[1]), pack_bf16(sum[2], sum[3])};
       }
     }
-    lds_barrier();  // partials read, next row's keys and values in LDS
+    lds_barrier();  // partials read; the next row's keys and values are visible
+    stage_qtile();  // the next row's first query tile (the wave's own LDS tiles)
+    moff[0] = next_moff[0];
+    moff[1] = next_moff[1];
   }
 
   // dbias partial of this row chunk for the block's keys and every query
@@ -969,7 +1006,7 @@ BwdPlan plan_bwd(const tri_attn_problem *p) {
 
 template <int JT>
 hipError_t launch_main(const BwdArgs &args, int grid, size_t lds, hipStream_t stream) {
-  auto kern = bwd_main_kernel<JT>;
+  auto kern = args.mask ? bwd_main_kernel<JT, true> : bwd_main_kernel<JT, false>;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(BWD_WAVES * 64), lds, stream, args);
   return hipGetLastError();
 }
