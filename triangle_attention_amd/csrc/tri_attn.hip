@@ -175,11 +175,16 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
   // keeps everything derived from it (rows, tile indices, addresses) in scalar registers
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int jl = lane & 31, hh = lane >> 5;
+  // tile order (fastest first): head within a head pair, query block, row chunk, head
+  // pair, batch.  The two heads of a pair share every 128-byte line of q, k and v, and
+  // their workgroups run at the same time on the same XCD.
   int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int hw = a.H & 1 ? 1 : 2;  // heads per pair (1 for an odd head count)
+  const int hp = t % hw; t /= hw;
   const int jb = t % a.n_jblocks; t /= a.n_jblocks;
   const int chunk = t % a.n_chunks; t /= a.n_chunks;
-  const int h = t % a.H;
-  const int b = t / a.H;
+  const int h = (t % (a.H / hw)) * hw + hp;
+  const int b = t / (a.H / hw);
   const int j0 = jb * FWD_BJ;
   const bool two = j0 + 32 < N;  // second 32-query half present (N % 64 == 32: not in the last block)
   uint16_t *kbuf = (uint16_t *)(bias_s + FWD_BJ * bstride) + wave * (2 * 32 * HD);
@@ -552,11 +557,16 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
   uint16_t *wdo = wq + 32 * HD;
   uint16_t *wds = s_ds + wave * BWD_BK * HD;
 
+  // tile order (fastest first): head within a head pair, key block, row chunk, head
+  // pair, batch.  The two heads of a pair share every 128-byte line of q, k, v and dO,
+  // and their workgroups run at the same time on the same XCD.
   int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int hw = a.H & 1 ? 1 : 2;  // heads per pair (1 for an odd head count)
+  const int hp = t % hw; t /= hw;
   const int kb = t % a.n_kblocks; t /= a.n_kblocks;
   const int chunk = t % a.n_chunks; t /= a.n_chunks;
-  const int h = t % a.H;
-  const int b = t / a.H;
+  const int h = (t % (a.H / hw)) * hw + hp;
+  const int b = t / (a.H / hw);
   const int k0 = kb * BWD_BK;
   const int nkt = min(2, (N - k0) / 32);  // key tiles present in this block (1 at a ragged end)
   const int njt = N / 32;
