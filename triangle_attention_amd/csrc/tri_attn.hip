@@ -545,6 +545,7 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
   // keys and values of the block for two rows: the current one and the next one, which
   // is staged early in the current row
   __shared__ __attribute__((aligned(16))) uint16_t s_kv[2][2 * BWD_BK * HD];
+  __shared__ uint8_t s_mask[2][BWD_BK];  // the two rows' key mask bytes (masked variant)
   __shared__ __attribute__((aligned(16))) uint16_t s_qd[BWD_WAVES * 2 * 32 * HD];
   __shared__ __attribute__((aligned(16))) uint16_t s_ds[BWD_WAVES * BWD_BK * HD];
 
@@ -588,24 +589,19 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
     kw = ld16(a.k + off);
     vw = ld16(a.v + off);
   };
-  auto store_kv = [&](u32x4 kw, u32x4 vw, int buf) {
+  // masked variant: thread tid fetches the mask byte of key k0 + tid % 64 (clamped at
+  // a ragged end, where the absent tile's keys are masked anyway) with the keys and
+  // values; the first wave stores the 64 bytes to LDS with them
+  const uint8_t *mask_thr =
+      MASKED ? a.mask + (long long)b * a.f.mB + (long long)min(k0 + (tid & 63), N - 1) * a.f.mK : nullptr;
+  auto load_mask = [&](int r, uint8_t &m) {
+    if constexpr (MASKED) m = mask_thr[(long long)r * a.f.mR];
+  };
+  auto store_kv = [&](u32x4 kw, u32x4 vw, uint8_t m, int buf) {
     const int row = tid >> 2, part = tid & 3;
     *(u32x4 *)(s_kv[buf] + tile_off(row, part * 8)) = kw;
     *(u32x4 *)(s_kv[buf] + BWD_BK * HD + tile_off(row, part * 8)) = vw;
-  };
-  // mask bytes of the lane's keys k0 + ll and k0 + 32 + ll (the first key's byte again
-  // when the second tile is absent), looked at a row later; the unmasked variant loads
-  // none and takes every key as attended
-  const uint8_t *mask_base = MASKED ? a.mask + (long long)b * a.f.mB + (long long)(k0 + ll) * a.f.mK : nullptr;
-  const long long mask_second = nkt > 1 ? 32 * a.f.mK : 0;
-  auto load_mask = [&](int r, unsigned &m0, unsigned &m1) {
-    if constexpr (MASKED) {
-      const uint8_t *mp = mask_base + (long long)r * a.f.mR;
-      m0 = mp[0];
-      m1 = mp[mask_second];
-    } else {
-      m0 = m1 = 1u;
-    }
+    if (MASKED && wave == 0) s_mask[buf][lane] = m;
   };
   // one query tile: the lane's q and dO row halves (A operands as loaded) and the
   // two per-query terms of the lane's query
@@ -621,11 +617,13 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
     *(u32x4 *)(wdo + tile_off(ll, 16 + 8 * hh)) = td1;
     __asm__ volatile("" ::"v"(tl), "v"(tdl));
   };
-  // exp2 argument offsets of the lane's keys from their mask bytes: 0, or -inf for a
-  // masked or absent key
-  auto mask_offsets = [&](unsigned m0, unsigned m1, float *mo) {
-    mo[0] = m0 != 0u ? 0.f : -INFINITY;
-    mo[1] = (nkt > 1 && m1 != 0u) ? 0.f : -INFINITY;
+  // exp2 argument offsets of the lane's keys k0 + ll and k0 + 32 + ll in a row staged to
+  // buffer buf: 0, or -inf for a masked or absent key
+  auto mask_offsets = [&](int buf, float *mo) {
+    const bool v0 = MASKED ? s_mask[buf][ll] != 0 : true;
+    const bool v1 = nkt > 1 && (MASKED ? s_mask[buf][32 + ll] != 0 : true);
+    mo[0] = v0 ? 0.f : -INFINITY;
+    mo[1] = v1 ? 0.f : -INFINITY;
   };
   auto load_qtile = [&](int r, int jt) {
     const long long off = rowbase(r) + (long long)(jt * 32 + ll) * a.f.sQ + 8 * hh;
@@ -685,15 +683,13 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
 
   // prologue: the first row's keys, values, key mask and first query tile
   u32x4 nk, nv;
-  unsigned nm0, nm1;
+  uint8_t nm = 1;
   const int rfirst = min(r0, N - 1);  // a chunk is never empty; clamped for safety
   load_kv(rfirst, nk, nv);
-  load_mask(rfirst, nm0, nm1);
+  load_mask(rfirst, nm);
   load_qtile(rfirst, min(wave, njt - 1));
-  store_kv(nk, nv, 0);
+  store_kv(nk, nv, nm, 0);
   stage_qtile();
-  float moff[2];
-  mask_offsets(nm0, nm1, moff);
   lds_barrier();
 
   for (int r = r0; r < r1; ++r) {
@@ -703,9 +699,10 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
     const uint16_t *s_k = s_kv[cur], *s_v = s_kv[cur] + BWD_BK * HD;
     const bool has_next = r + 1 < r1;
     const int rn = has_next ? r + 1 : r;  // row whose operands are fetched next (this row's at the end)
-    float next_moff[2] = {0.f, 0.f};
+    float moff[2];
+    mask_offsets(cur, moff);
     load_kv(rn, nk, nv);
-    load_mask(rn, nm0, nm1);
+    load_mask(rn, nm);
     const long long base = rowbase(r);
 
     f32x16 dK[2], dV[2];
@@ -799,10 +796,7 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
         // kept here (not hoisted next to the loads at the row start): waiting for the
         // loads at this point leaves the stores issued since in flight
         __builtin_amdgcn_sched_barrier(0);
-        store_kv(nk, nv, cur ^ 1);
-        unsigned m0 = nm0, m1 = nm1;
-        __asm__ volatile("" : "+v"(m0), "+v"(m1));  // not merged with the copy below
-        mask_offsets(m0, m1, next_moff);
+        store_kv(nk, nv, nm, cur ^ 1);
       }
       gradients(0, o0, sv0, dp0);
       gradients(1, o1, sv1, dp1);
@@ -817,10 +811,7 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
             (u32x2){pack_bf16(dqT[4 * g], dqT[4 * g + 1]), pack_bf16(dqT[4 * g + 2], dqT[4 * g + 3])};
     }
 
-    if (wave >= njt) {  // a wave without query tiles in this row
-      store_kv(nk, nv, cur ^ 1);
-      mask_offsets(nm0, nm1, next_moff);
-    }
+    if (wave >= njt) store_kv(nk, nv, nm, cur ^ 1);  // a wave without query tiles in this row
 
     // fixed-order cross-wave reduction of dV then dK for this row.  Each wave's
     // 64 x 32 fp32 partial goes to its own staging: key rows 0-31 to the dS^T
@@ -856,8 +847,6 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
     }
     lds_barrier();  // partials read; the next row's keys and values are visible
     stage_qtile();  // the next row's first query tile (the wave's own LDS tiles)
-    moff[0] = next_moff[0];
-    moff[1] = next_moff[1];
   }
 
   // dbias partial of this row chunk for the block's keys and every query
