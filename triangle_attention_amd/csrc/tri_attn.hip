@@ -802,13 +802,32 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
       gradients(1, o1, sv1, dp1);
       dq_product(0, dqT);
       dq_product(1, dqT);
-      // this key block's dQ partial, rounded to bf16 (summed in fp32 over the blocks);
-      // a wave's four stores fill the tile's contiguous 2 KB of the partial
-      uint16_t *qout = dq_part + ((((long long)b * N + r) * a.H + h) * N + j0 + ll) * HD + 4 * hh;
+      // this key block's dQ partial, rounded to bf16 (summed in fp32 over the blocks).
+      // The lane halves trade channel groups (lanes l and l + 32 hold the same query),
+      // so that each lane stores two 16-byte runs: a wave's two stores fill the tile's
+      // contiguous 2 KB of the partial.  Before the swaps, lane l < 32 holds channels
+      // 8g..8g+3 of group g and lane l + 32 channels 8g+4..8g+7 of query ll; swapping
+      // groups 0 with 1 and 2 with 3 across the halves leaves lane l with channels 0-7
+      // and 16-23 and lane l + 32 with channels 8-15 and 24-31.
+      uint16_t *qout = dq_part + ((((long long)b * N + r) * a.H + h) * N + j0 + ll) * HD + 8 * hh;
+      {
+        unsigned w[4][2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *(u32x2 *)(qout + 8 * g) =
-            (u32x2){pack_bf16(dqT[4 * g], dqT[4 * g + 1]), pack_bf16(dqT[4 * g + 2], dqT[4 * g + 3])};
+        for (int g = 0; g < 4; ++g) {
+          w[g][0] = pack_bf16(dqT[4 * g], dqT[4 * g + 1]);
+          w[g][1] = pack_bf16(dqT[4 * g + 2], dqT[4 * g + 3]);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; g += 2)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(w[g][e], w[g + 1][e], false, false);
+            w[g][e] = sw[0];
+            w[g + 1][e] = sw[1];
+          }
+        *(u32x4 *)qout = (u32x4){w[0][0], w[0][1], w[1][0], w[1][1]};
+        *(u32x4 *)(qout + 16) = (u32x4){w[2][0], w[2][1], w[3][0], w[3][1]};
+      }
     }
 
     if (wave >= njt) store_kv(nk, nv, nm, cur ^ 1);  // a wave without query tiles in this row
@@ -832,17 +851,23 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
       lds_barrier();
       const float scale = which ? a.alpha : 1.f;
       uint16_t *dst = which ? a.dk : a.dv;
+      {
+        // thread tid: channels 8 (tid % 4) .. + 7 of key row tid / 4
+        const int kr = tid >> 2, c = 8 * (tid & 3);
+        if (k0 + kr < N) {
+          f32x4 s0 = *(const f32x4 *)(red_ptr(0, kr) + c);
+          f32x4 s1 = *(const f32x4 *)(red_ptr(0, kr) + c + 4);
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = 4 * (tid + 256 * u);
-        const int kr = e / HD, c = e - kr * HD;
-        if (k0 + kr >= N) continue;
-        f32x4 sum = *(const f32x4 *)(red_ptr(0, kr) + c);
-#pragma unroll
-        for (int w = 1; w < BWD_WAVES; ++w) sum += *(const f32x4 *)(red_ptr(w, kr) + c);
-        sum *= scale;
-        const long long off = base + (long long)(k0 + kr) * a.f.sQ + c;
-        *(u32x2 *)(dst + off) = (u32x2){pack_bf16(sum[0], sum[1]), pack_bf16(sum[2], sum[3])};
+          for (int w = 1; w < BWD_WAVES; ++w) {
+            s0 += *(const f32x4 *)(red_ptr(w, kr) + c);
+            s1 += *(const f32x4 *)(red_ptr(w, kr) + c + 4);
+          }
+          s0 *= scale;
+          s1 *= scale;
+          const long long off = base + (long long)(k0 + kr) * a.f.sQ + c;
+          *(u32x4 *)(dst + off) = (u32x4){pack_bf16(s0[0], s0[1]), pack_bf16(s0[2], s0[3]),
+                                           pack_bf16(s1[0], s1[1]), pack_bf16(s1[2], s1[3])};
+        }
       }
     }
     lds_barrier();  // partials read; the next row's keys and values are visible
