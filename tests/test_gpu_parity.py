@@ -224,6 +224,8 @@ def custom(B, N, H, seed, mask_kind="none", bias_std=1.0):
     (2, 96, 3, "random", True),
     (1, 160, 2, "pad32", True),
     (1, 128, 5, "random", False),
+    (1, 64, 8, "random", False),        # more heads: 8 and 16 (head pairs across workgroups)
+    (1, 64, 16, "none", True),
 ])
 def test_shapes_and_masks(ta, B, N, H, mask_kind, ending):
     inp = custom(B, N, H, 7 + N + H, mask_kind)
