@@ -17,7 +17,11 @@ The JSON line also carries
                  that summary was taken on a different kernel source;
   cpu_baseline : the FP64 oracle timed on this host on a bounded sample of the
                  same workload (sampled attention rows and bias-gradient rows),
-                 scaled to the whole workload.
+                 scaled to the whole workload;
+  phases       : median and 90th-percentile forward, backward and step times over
+                 the timed steps (events on the launch stream), the algorithmic
+                 bytes of one step and the rate they imply, and whether the outputs
+                 of the first and last timed steps are bitwise identical.
 """
 from __future__ import annotations
 
@@ -26,6 +30,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 from pathlib import Path
@@ -90,6 +95,20 @@ def measured_traffic(workload: str, ending: bool):
     if sha.group(1) != hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest():
         return None
     return int(val.group(1))
+
+
+def algorithmic_bytes(B: int, N: int, H: int, D: int, masked: bool) -> int:
+    """Bytes one fwd+bwd step must move: the forward reads q, k, v, bias (and the
+    mask) and writes o, its bf16 residual and lse; the backward reads q, k, v, o,
+    the residual, dO, lse, bias (and the mask) and writes dq, dk, dv and dbias."""
+    E = B * N * N * H * D
+    return 28 * E + 14 * B * H * N * N + (2 * B * N * N if masked else 0)
+
+
+def quantiles(xs):
+    xs = sorted(xs)
+    pick = lambda q: xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
+    return {"median": round(pick(0.5), 4), "p90": round(pick(0.9), 4)}
 
 
 def cpu_baseline(inp, rows: int, dbias_rows: int):
@@ -158,10 +177,15 @@ def main():
     ws = torch.empty(ta.bwd_workspace_bytes(w.B, w.N, w.H, w.D, ending=args.ending),
                      dtype=torch.uint8, device=dev)
 
-    def step(events=None):
-        o, res, lse = ta.tri_attn_fwd(g["q"], g["k"], g["v"], g["bias"], mask, ending=args.ending)
+    def fwd():
+        return ta.tri_attn_fwd(g["q"], g["k"], g["v"], g["bias"], mask, ending=args.ending)
+
+    def bwd(o, res, lse, events=None):
         return ta.tri_attn_bwd(g["q"], g["k"], g["v"], g["bias"], mask, o, res, lse, g["do"],
                                ending=args.ending, workspace=ws, main_events=events)
+
+    def step(events=None):
+        return bwd(*fwd(), events=events)
 
     if args.calib_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
@@ -176,11 +200,19 @@ def main():
 
     hip = HipEvents()
     ev = [(hip.create(), hip.create()) for _ in range(args.steps)]
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
+    outs = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(ev[i])
+        marks[i][0].record()
+        fo = fwd()
+        marks[i][1].record()
+        grads = bwd(*fo, events=ev[i])
+        marks[i][2].record()
+        if i == 0 or i == args.steps - 1:
+            outs.append(fo + tuple(grads))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
@@ -190,6 +222,13 @@ def main():
         hip.destroy(b)
     log(f"{ms:.3f} ms/step, backward main kernel {main_ms:.3f} ms")
 
+    fwd_ms = [m[0].elapsed_time(m[1]) for m in marks]
+    bwd_ms = [m[1].elapsed_time(m[2]) for m in marks]
+    step_ms = [m[0].elapsed_time(m[2]) for m in marks]
+    same = all(torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32))
+               for x, y in zip(outs[0], outs[-1]))
+    nbytes = algorithmic_bytes(w.B, w.N, w.H, w.D, w.mask != "none")
     flops = si.flop_count(w.B, w.N, w.H, w.D, inp["mask"])
     value = flops / (ms * 1e-3) / 1e12
     bwd_main_flops = flops * 10 / 14   # S, dP, dV, dK, dQ products of the backward
@@ -215,6 +254,10 @@ def main():
                      "frac": round(achieved / MFMA_PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(w.name, args.ending),
                      "avg_ms": round(main_ms, 4)},
+        "phases": {"fwd_ms": quantiles(fwd_ms), "bwd_ms": quantiles(bwd_ms), "step_ms": quantiles(step_ms),
+                   "algorithmic_bytes_per_step": nbytes,
+                   "algorithmic_GBps": round(nbytes / (statistics.median(step_ms) * 1e-3) / 1e9, 1),
+                   "deterministic_first_vs_last_step": bool(same)},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)")
