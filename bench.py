@@ -14,7 +14,7 @@ The JSON line also carries
                  the MI355X dense bf16 MFMA peak; its "traffic" is the HBM bytes
                  per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary in
                  profiles/ (calibrated against a plain device copy), or null when
-                 that summary was taken on a different kernel source;
+                 that summary was taken on a different kernel source or build flags;
   cpu_baseline : the FP64 oracle timed on this host on a bounded sample of the
                  same workload (sampled attention rows and bias-gradient rows),
                  scaled to the whole workload;
@@ -79,20 +79,27 @@ ROOT = Path(__file__).resolve().parent
 KERNEL_SOURCE = ROOT / "triangle_attention_amd" / "csrc" / "tri_attn.hip"
 
 
+def build_hash() -> str:
+    """sha256 of the kernel source and the compiler flags it is built with."""
+    from triangle_attention_amd.build import FLAGS
+    return hashlib.sha256(KERNEL_SOURCE.read_bytes() + " ".join(FLAGS).encode()).hexdigest()
+
+
 def measured_traffic(workload: str, ending: bool):
     """HBM bytes per launch of the backward main kernel from the committed rocprofv3
-    counter summary, if it was taken on this kernel source and workload."""
+    counter summary, if it was taken on this kernel source, these build flags and
+    this workload."""
     if ending:
         return None
     f = ROOT / "profiles" / f"traffic_bwd_main_{workload}.md"
     if not f.exists():
         return None
     text = f.read_text()
-    sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    sha = re.search(r"build_sha256:\s*([0-9a-f]{64})", text)
     val = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
     if not sha or not val:
         return None
-    if sha.group(1) != hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest():
+    if sha.group(1) != build_hash():
         return None
     return int(val.group(1))
 

@@ -15,10 +15,14 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 VALU forms are disabled for all device code (-packed-fp32-ops).
 # MFMA results start in architectural VGPRs (-amdgpu-mfma-vgpr-form): the
 # per-tile score, dP and dQ products are read by VALU code, and only the
-# long-lived backward accumulators (dbias, dK, dV) end up in AGPRs.
+# long-lived backward accumulators (dbias, dK, dV) end up in AGPRs.  The
+# iterative ILP machine-scheduling strategy orders the backward main kernel's
+# single wave (one per SIMD, so nothing else hides its latencies) better than the
+# default occupancy-driven one: 3-5 % less backward time at N = 384..768.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-mllvm", "-amdgpu-mfma-vgpr-form",
+         "-mllvm", "-amdgpu-sched-strategy=iterative-ilp",
          "-Wno-unused-command-line-argument"]
 
 
