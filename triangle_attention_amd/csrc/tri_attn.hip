@@ -6,18 +6,21 @@
 // dim 32) whose logits also get a pair bias shared by all rows and a key mask.
 //
 // Kernels
-//   fwd       flash-style forward: S^T = K Q^T on MFMA with the scaled pair bias
-//             as the accumulator's initial value, online softmax in fp32, O^T =
-//             V^T P^T on MFMA; writes bf16 o, its exact fp32 rounding residual
-//             and the fp32 log-sum-exp.
+//   fwd       flash-style forward: S^T = K Q^T on MFMA, the pair bias added in
+//             fp32 (fp16 operand of a mixed-precision multiply-add), exponentials
+//             against a per-row reference maximum (recomputed against the true
+//             maximum only if a value leaves the fp32 range), O^T = V^T P^T on
+//             MFMA; writes bf16 o, the bf16-rounded remainder O - float(o) and the
+//             fp32 log-sum-exp.
 //   bwd_prep  D = rowsum(dO * (o + residual)) in fp32, fixed channel order.
 //   bwd_main  key-block-parallel backward: one workgroup owns a block of keys
 //             for a chunk of rows and every query; each probability tile is
 //             recomputed once from the saved log-sum-exp and feeds dV, dK, dQ
 //             and dbias.  dK/dV are reduced across waves in a fixed order, dbias
-//             accumulates over the chunk's rows in registers, dQ leaves one fp32
+//             accumulates over the chunk's rows in registers, dQ leaves one bf16
 //             partial per key block.
-//   bwd_reduce fixed-order sums of the dQ partials (over key blocks) and the
+//   reduce_dq, reduce_dbias
+//             fixed-order fp32 sums of the dQ partials (over key blocks) and the
 //             dbias partials (over row chunks).
 // No floating-point atomics are used anywhere, so results are bitwise
 // reproducible (Lambda post, third point of "Как работает TurboPairFormer").
@@ -90,8 +93,13 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t *tile, int base_row,
 }
 
 // Offset of element (row, col) of a [rows][32] bf16 LDS tile whose 16-byte chunks
-// are permuted by bits 1 and 2 of the row, so that 16-byte row reads by 32 lanes
-// (one row each) and transposing reads are free of bank conflicts.
+// are permuted by bits 1 and 2 of the row.  With the MI355X LDS (64 four-byte banks,
+// 16-byte reads served 16 lanes at a time) the transposing reads and the 16-byte
+// row writes are then conflict-free, while 16-byte row reads of 16 consecutive rows
+// and 8-byte row writes see two-way conflicts (SQ_LDS_BANK_CONFLICT on probe
+// kernels).  A permutation that also frees the row reads (row bits 2-3 XOR bit 1)
+// measured no faster in the forward and slower in the backward, whose transposed
+// K reads then need two addresses.
 __device__ __forceinline__ int tile_off(int row, int col) {
   const int sw = (row & 2) | ((row >> 2) & 1);
   return row * HD + (((col >> 3) ^ sw) << 3) + (col & 7);
@@ -479,7 +487,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
 //   dV, dK       += P^T dO, dS^T Q        (MFMA, per-wave partials for the row)
 //   dbias        += I * dS                (MFMA against an identity; fp32 accumulators
 //                                          held over the chunk's rows)
-//   dQ^T          = K^T dS^T over 64 keys (MFMA, one fp32 partial per key block)
+//   dQ^T          = K^T dS^T over 64 keys (MFMA, one bf16 partial per key block)
 // At the end of a row the four waves' dK/dV partials are summed in LDS in wave
 // order; dbias leaves the kernel as one partial per row chunk.
 //
@@ -493,8 +501,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
 // into registers while the current row runs.  Query and dO tiles go through a
 // per-wave LDS tile only for the transposed operands of the dK and dV products.
 // The 64-byte rows of LDS tiles have their 16-byte chunks permuted per row
-// (tile_off) so that row reads of MFMA operands and transposing reads are free of
-// bank conflicts.
+// (tile_off); see there for which accesses that keeps free of bank conflicts.
 constexpr int BWD_WAVES = 4;
 constexpr int BWD_BK = 64;
 
