@@ -58,6 +58,11 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Fourth word of a raw (stride 0) buffer descriptor on gfx9-family GPUs: 32-bit
+// data format, no swizzle; loads through it are bounds-checked against the
+// descriptor's byte count.
+constexpr int kBufferWord3 = 0x00020000;
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -241,22 +246,27 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
     }
     const uint8_t *mrow = a.mask ? a.mask + (long long)b * a.f.mB + (long long)r * a.f.mR : &kMaskAllValid;
 
-    // per-lane addresses of tile 0; tile kt is a uniform offset away
-    const uint16_t *kl = a.k + base + (long long)vkey * a.f.sQ + vpart * 8;
-    const uint16_t *vl = a.v + base + (long long)vkey * a.f.sQ + vpart * 8;
+    // K and V of the row through buffer descriptors: the lane's byte offset is fixed
+    // for the row and tile kt is a scalar byte offset away, so no per-tile address
+    // math.  A row spans N * sQ * 2 < 2^32 bytes (N <= 768, H <= 64, D = 32), so the
+    // offsets are unsigned 32-bit values.
+    const unsigned row_bytes = (unsigned)((long long)N * a.f.sQ * 2);
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + base), (short)0, row_bytes, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + base), (short)0, row_bytes, kBufferWord3);
+    const unsigned lane_off = (unsigned)(((long long)vkey * a.f.sQ + vpart * 8) * 2);
+    const unsigned tstep_b = (unsigned)(32 * a.f.sQ * 2), vhalf_b = (unsigned)(16 * a.f.sQ * 2);
     const uint8_t *ml = mrow + (long long)jl * mk;
-    const long long tstep = 32 * a.f.sQ, vhalf = 16 * a.f.sQ, mstep = 32 * mk;
+    const long long mstep = 32 * mk;
     // every fetch is unconditional (a tile past the end refetches the last one, which
     // is then not processed): a load under a branch makes the compiler wait for all
     // outstanding memory operations where the paths merge
     auto fetch = [&](int kt, FwdTile &T) {
       kt = min(kt, nkt - 1);
-      const uint16_t *kp = kl + kt * tstep;
-      const uint16_t *vp = vl + kt * tstep;
-      T.k0 = ld16(kp);
-      T.k1 = ld16(kp + vhalf);
-      T.v0 = ld16(vp);
-      T.v1 = ld16(vp + vhalf);
+      const unsigned so = (unsigned)kt * tstep_b;
+      T.k0 = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)lane_off, (int)so, 0);
+      T.k1 = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)lane_off, (int)(so + vhalf_b), 0);
+      T.v0 = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)lane_off, (int)so, 0);
+      T.v1 = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)lane_off, (int)(so + vhalf_b), 0);
       T.m = MASKED ? (unsigned)ml[kt * mstep] : 1u;
     };
     auto stage_k = [&](const FwdTile &T) {
