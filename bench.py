@@ -85,11 +85,11 @@ def build_hash() -> str:
     return hashlib.sha256(KERNEL_SOURCE.read_bytes() + " ".join(FLAGS).encode()).hexdigest()
 
 
-def measured_traffic(workload: str, ending: bool):
+def measured_traffic(workload: str, ending: bool, residual: str = "bf16"):
     """HBM bytes per launch of the backward main kernel from the committed rocprofv3
     counter summary, if it was taken on this kernel source, these build flags and
     this workload."""
-    if ending:
+    if ending or residual != "bf16":
         return None
     f = ROOT / "profiles" / f"traffic_bwd_main_{workload}.md"
     if not f.exists():
@@ -104,12 +104,12 @@ def measured_traffic(workload: str, ending: bool):
     return int(val.group(1))
 
 
-def algorithmic_bytes(B: int, N: int, H: int, D: int, masked: bool) -> int:
+def algorithmic_bytes(B: int, N: int, H: int, D: int, masked: bool, residual_bytes: int = 2) -> int:
     """Bytes one fwd+bwd step must move: the forward reads q, k, v, bias (and the
-    mask) and writes o, its bf16 residual and lse; the backward reads q, k, v, o,
-    the residual, dO, lse, bias (and the mask) and writes dq, dk, dv and dbias."""
+    mask) and writes o, its residual and lse; the backward reads q, k, v, o, the
+    residual, dO, lse, bias (and the mask) and writes dq, dk, dv and dbias."""
     E = B * N * N * H * D
-    return 28 * E + 14 * B * H * N * N + (2 * B * N * N if masked else 0)
+    return (24 + 2 * residual_bytes) * E + 14 * B * H * N * N + (2 * B * N * N if masked else 0)
 
 
 def quantiles(xs):
@@ -158,6 +158,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="crop768")
     ap.add_argument("--ending", action="store_true", help="ending-node orientation")
+    ap.add_argument("--residual", choices=("bf16", "fp32"), default="bf16",
+                    help="precision of the saved rounding residual of o")
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--cpu-dbias-rows", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -185,7 +187,8 @@ def main():
                      dtype=torch.uint8, device=dev)
 
     def fwd():
-        return ta.tri_attn_fwd(g["q"], g["k"], g["v"], g["bias"], mask, ending=args.ending)
+        return ta.tri_attn_fwd(g["q"], g["k"], g["v"], g["bias"], mask, ending=args.ending,
+                               residual_fp32=args.residual == "fp32")
 
     def bwd(o, res, lse, events=None):
         return ta.tri_attn_bwd(g["q"], g["k"], g["v"], g["bias"], mask, o, res, lse, g["do"],
@@ -235,7 +238,7 @@ def main():
     same = all(torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
                            y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32))
                for x, y in zip(outs[0], outs[-1]))
-    nbytes = algorithmic_bytes(w.B, w.N, w.H, w.D, w.mask != "none")
+    nbytes = algorithmic_bytes(w.B, w.N, w.H, w.D, w.mask != "none", 4 if args.residual == "fp32" else 2)
     flops = si.flop_count(w.B, w.N, w.H, w.D, inp["mask"])
     value = flops / (ms * 1e-3) / 1e12
     bwd_main_flops = flops * 10 / 14   # S, dP, dV, dK, dQ products of the backward
@@ -255,11 +258,12 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name} ({w.description})", "B": w.B, "N": w.N, "H": w.H,
                    "D": w.D, "orientation": "ending" if args.ending else "starting",
+                   "residual": args.residual,
                    "mfma_peak_frac": round(value / MFMA_PEAK_BF16_TFLOPS, 4)},
         "roofline": {"kernel": "bwd_main_kernel", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name, args.ending),
+                     "traffic": measured_traffic(w.name, args.ending, args.residual),
                      "avg_ms": round(main_ms, 4)},
         "phases": {"fwd_ms": quantiles(fwd_ms), "bwd_ms": quantiles(bwd_ms), "step_ms": quantiles(step_ms),
                    "algorithmic_bytes_per_step": nbytes,

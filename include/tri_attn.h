@@ -21,7 +21,7 @@
  *
  * Layouts (row-major, last index fastest):
  *   q, k, v, o, d_o, dq, dk, dv : bf16 [B, N, N, H, D]  (D contiguous)
- *   o_residual                  : bf16 [B, N, N, H, D]
+ *   o_residual                  : bf16 [B, N, N, H, D] (fp32 with FLAG_RESIDUAL_FP32)
  *   bias, dbias                 : bf16 [B, H, N, N] (dbias fp32 with FLAG_DBIAS_FP32);
  *                                 bias values must lie in the fp16 range
  *                                 (|bias| <= 65504, or -inf): the kernels hold the
@@ -69,8 +69,9 @@ typedef enum {
 } tri_attn_status;
 
 enum {
-    TRI_ATTN_FLAG_ENDING_NODE = 1 << 0, /* attend along the first pair axis (see above) */
-    TRI_ATTN_FLAG_DBIAS_FP32 = 1 << 1   /* dbias is written as fp32 instead of bf16 */
+    TRI_ATTN_FLAG_ENDING_NODE = 1 << 0,   /* attend along the first pair axis (see above) */
+    TRI_ATTN_FLAG_DBIAS_FP32 = 1 << 1,    /* dbias is written as fp32 instead of bf16 */
+    TRI_ATTN_FLAG_RESIDUAL_FP32 = 1 << 2  /* o_residual is the exact fp32 residual (both passes) */
 };
 
 typedef struct {
@@ -94,10 +95,12 @@ const char *tri_attn_status_string(int status);
  * the FP32-to-BF16 rounding residual of the output is kept for the backward).
  *   q, k, v, bias, mask : inputs as laid out above (mask may be NULL)
  *   o                   : bf16 output, round-to-nearest-even of the fp32 result O
- *   o_residual          : bf16 round-to-nearest-even of the fp32 residual O - float(o)
- *                         (exact in fp32); float(o) + float(o_residual) restores O to
- *                         within 2^-9 of the residual, i.e. about 2^-17 relative to O.
- *                         NULL = not saved
+ *   o_residual          : the fp32 residual O - float(o) (exact in fp32), stored as
+ *                         its bf16 round-to-nearest-even by default: float(o) +
+ *                         float(o_residual) then restores O to within 2^-9 of the
+ *                         residual, i.e. about 2^-17 relative to O.  With
+ *                         TRI_ATTN_FLAG_RESIDUAL_FP32 it is stored as fp32 (twice
+ *                         the bytes) and restores O exactly.  NULL = not saved
  *   lse                 : fp32 log-sum-exp of every softmax row; +inf for a row
  *                         whose keys are all masked (its o and residual are 0)
  */
@@ -119,8 +122,9 @@ size_t tri_attn_bwd_workspace_bytes(const tri_attn_problem *problem);
  * key, value, query and pair-bias gradients are reduced in a fixed order and
  * the full score gradient is never stored.
  *   q, k, v, bias, mask, o, lse : the forward's inputs and outputs
- *   o_residual : the forward's residual; NULL = uncompensated correction
- *                D = rowsum(dO * float(o))
+ *   o_residual : the forward's residual (bf16, or fp32 with the same
+ *                TRI_ATTN_FLAG_RESIDUAL_FP32 as the forward); NULL = uncompensated
+ *                correction D = rowsum(dO * float(o))
  *   d_o        : bf16 upstream gradient of o
  *   dq, dk, dv : bf16 gradients, [B,N,N,H,D]
  *   dbias      : [B,H,N,N] gradient of the pair bias (bf16, or fp32 with

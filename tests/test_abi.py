@@ -76,7 +76,7 @@ def test_null_problem_is_invalid(lib):
     ("abi_version", ta.ABI_VERSION + 1, ABI), ("B", 0, INVALID), ("N", 0, INVALID), ("H", 0, INVALID),
     ("D", 64, UNSUPPORTED), ("D", 16, UNSUPPORTED), ("N", 48, UNSUPPORTED),
     ("N", 800, UNSUPPORTED), ("N", 1024, UNSUPPORTED), ("H", 65, UNSUPPORTED),
-    ("flags", 4, UNSUPPORTED), ("softmax_scale", -1.0, INVALID),
+    ("flags", 8, UNSUPPORTED), ("softmax_scale", -1.0, INVALID),
     ("softmax_scale", float("inf"), INVALID), ("softmax_scale", float("nan"), INVALID),
 ])
 def test_problem_validation(lib, field, value, expect):

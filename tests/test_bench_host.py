@@ -1,0 +1,47 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU refusal, the algorithmic byte
+count of a step and the gate on the measured-traffic summary."""
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=bench.ROOT,
+                         capture_output=True, text=True, timeout=300)
+    assert res.returncode == 2
+    assert "one GPU" in res.stdout
+
+
+@pytest.mark.parametrize("masked", [False, True])
+@pytest.mark.parametrize("residual_bytes", [2, 4])
+def test_algorithmic_bytes_counts_every_tensor_once_per_pass(masked, residual_bytes):
+    B, N, H, D = 2, 96, 3, 32
+    pair = B * N * N * H * D          # elements of q, k, v, o, dO and the gradients
+    bias = B * H * N * N              # elements of bias, dbias and lse
+    mask = B * N * N if masked else 0
+    forward_reads = {"q": 2 * pair, "k": 2 * pair, "v": 2 * pair, "bias": 2 * bias, "mask": mask}
+    forward_writes = {"o": 2 * pair, "residual": residual_bytes * pair, "lse": 4 * bias}
+    backward_reads = {"q": 2 * pair, "k": 2 * pair, "v": 2 * pair, "o": 2 * pair,
+                      "residual": residual_bytes * pair, "dO": 2 * pair, "lse": 4 * bias,
+                      "bias": 2 * bias, "mask": mask}
+    backward_writes = {"dq": 2 * pair, "dk": 2 * pair, "dv": 2 * pair, "dbias": 2 * bias}
+    total = sum(sum(d.values()) for d in (forward_reads, forward_writes, backward_reads, backward_writes))
+    assert bench.algorithmic_bytes(B, N, H, D, masked, residual_bytes) == total
+
+
+def test_traffic_is_reported_only_for_a_matching_build(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    monkeypatch.setattr(bench, "ROOT", tmp_path)
+    assert bench.measured_traffic("crop768", False) is None          # no summary
+    (prof / "traffic_bwd_main_crop768.md").write_text(
+        f"traffic_bytes_per_launch: 123\nbuild_sha256: {bench.build_hash()}\n")
+    assert bench.measured_traffic("crop768", False) == 123
+    assert bench.measured_traffic("crop768", True) is None           # other orientation
+    assert bench.measured_traffic("crop768", False, "fp32") is None  # other residual
+    (prof / "traffic_bwd_main_crop768.md").write_text(
+        "traffic_bytes_per_launch: 123\nbuild_sha256: " + "0" * 64 + "\n")
+    assert bench.measured_traffic("crop768", False) is None          # other source or flags

@@ -50,12 +50,12 @@ def to_np(t):
     return t.detach().float().cpu().double().numpy()
 
 
-def run_gpu(ta, inp, ending=False, compensated=True, scale=None, dbias_fp32=False):
+def run_gpu(ta, inp, ending=False, compensated=True, scale=None, dbias_fp32=False, residual_fp32=False):
     dev = torch.device("cuda:0")
     g = {k: v.to(dev) for k, v in inp.items()}
     mask = g["mask"] if inp.get("mask") is not None else None
     o, res, lse = ta.tri_attn_fwd(g["q"], g["k"], g["v"], g["bias"], mask, ending=ending,
-                                  scale=scale, save_residual=True)
+                                  scale=scale, save_residual=True, residual_fp32=residual_fp32)
     dq, dk, dv, db = ta.tri_attn_bwd(g["q"], g["k"], g["v"], g["bias"], mask, o,
                                      res if compensated else None, lse, g["do"],
                                      ending=ending, scale=scale, dbias_fp32=dbias_fp32)
@@ -166,6 +166,44 @@ def test_residual_is_the_rounding_remainder(ta):
     # what remains of the error of o + r comes from the bf16 probabilities fed to the
     # PV product, so the gain is bounded (about 2x)
     assert e_fp < 0.75 * e_bf
+
+
+@pytest.mark.parametrize("ending", [False, True])
+def test_fp32_residual(ta, ending):
+    """With the fp32-residual flag the forward saves O - float(o) itself: its bf16
+    rounding is exactly the default residual, o + r restores the kernel's fp32
+    output, and the backward (flag on) meets the gradient criteria with the exact
+    compensation, next to the bf16-residual and uncompensated corrections."""
+    inp = si.make_workload("pad256")
+    out32 = run_gpu(ta, inp, ending=ending, residual_fp32=True)
+    out16 = run_gpu(ta, inp, ending=ending)
+    unc = run_gpu(ta, inp, ending=ending, compensated=False)
+    r32 = out32["res"]
+    assert r32.dtype == torch.float32 and out16["res"].dtype == torch.bfloat16
+    assert torch.equal(out32["o"], out16["o"]) and torch.equal(out32["lse"], out16["lse"])
+    assert torch.equal(r32.to(torch.bfloat16).view(torch.int16), out16["res"].view(torch.int16))
+    o = out32["o"].float()
+    ulp_half = torch.where(o == 0, torch.zeros_like(o),
+                           torch.ldexp(torch.ones_like(o), torch.frexp(o.abs()).exponent - 9))
+    bad = r32.abs() > ulp_half + 1e-30
+    if bool(bad.any()):
+        idx = bad.nonzero()[:5]
+        for ix in idx:
+            t = tuple(int(x) for x in ix)
+            say(f"[fp32 residual] at {t}: o={o[t]!r} r={r32[t]!r} half ulp={ulp_half[t]!r} "
+                f"r16={out16['res'][t]!r}")
+    assert not bool(bad.any())
+    ref = oracle.forward_backward(inp["q"], inp["k"], inp["v"], inp["bias"], inp["mask"], inp["do"],
+                                  ending=ending)
+    assert rel_rmse(to_np(o + r32), ref["o"]) <= rel_rmse(to_np(o + out16["res"].float()), ref["o"]) * 1.01
+    for n in ("dq", "dk", "dv", "dbias"):
+        e32 = rel_rmse(to_np(out32[n]), ref[n])
+        e16 = rel_rmse(to_np(out16[n]), ref[n])
+        eu = rel_rmse(to_np(unc[n]), ref[n])
+        say(f"[fp32 residual] ending={ending} {n}: fp32 residual {e32:.3e}, bf16 residual {e16:.3e}, "
+            f"uncompensated {eu:.3e}")
+        assert e32 <= GRAD_REL_RMSE
+    assert torch.equal(out32["dv"].view(torch.int16), out16["dv"].view(torch.int16))
 
 
 @pytest.mark.parametrize("name,reps", [("tiny64", 3), ("pad256", 3), ("crop640", 3),

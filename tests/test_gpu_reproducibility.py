@@ -6,8 +6,8 @@ passes only if the gradients of q, k, v and the pair bias are bitwise identical
 over the five runs.  Here the forward outputs (o, its residual, lse) are compared
 too.  The cases are small (N <= 128) and drawn from a fixed seed over batch size,
 N, head count, key-mask kind (none given as no mask at all, a ones mask, padded
-keys, random keys), orientation, compensated or uncompensated D, softmax scale and
-bf16 or fp32 dbias.
+keys, random keys), orientation, compensated or uncompensated D, softmax scale,
+bf16 or fp32 dbias and bf16 or fp32 saved residual.
 """
 import sys
 
@@ -49,17 +49,19 @@ def test_reproducibility_sweep(ta):
         compensated = bool(rng.integers(0, 2))
         scale = None if rng.integers(0, 2) else float(rng.uniform(0.1, 0.4))
         dbias_fp32 = bool(rng.integers(0, 2))
+        residual_fp32 = bool(rng.integers(0, 2))
         inp = si.make_problem(B, N, H, 32, 20000 + case, mask="none" if kind == "absent" else kind)
         g = {k: v.to(dev) for k, v in inp.items()}
         mask = None if kind == "absent" else g["mask"]
         if case % 100 == 0:
             print(f"[reproducibility] case {case}: B={B} N={N} H={H} mask={kind} ending={ending} "
-                  f"compensated={compensated} scale={scale} dbias_fp32={dbias_fp32}", flush=True)
+                  f"compensated={compensated} scale={scale} dbias_fp32={dbias_fp32} "
+                  f"residual_fp32={residual_fp32}", flush=True)
             sys.stdout.flush()
         first = None
         for _ in range(N_RUNS):
             o, res, lse = ta.tri_attn_fwd(g["q"], g["k"], g["v"], g["bias"], mask, ending=ending,
-                                          scale=scale, save_residual=True)
+                                          scale=scale, save_residual=True, residual_fp32=residual_fp32)
             grads = ta.tri_attn_bwd(g["q"], g["k"], g["v"], g["bias"], mask, o,
                                     res if compensated else None, lse, g["do"], ending=ending,
                                     scale=scale, dbias_fp32=dbias_fp32)

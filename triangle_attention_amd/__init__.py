@@ -24,6 +24,7 @@ LIB_PATH = _HERE / "libtri_attn.so"
 ABI_VERSION = 2
 FLAG_ENDING_NODE = 1
 FLAG_DBIAS_FP32 = 2
+FLAG_RESIDUAL_FP32 = 4
 
 STATUS_NAMES = {
     0: "TRI_ATTN_SUCCESS",
@@ -85,9 +86,10 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     return lib
 
 
-def make_problem(B, N, H, D, *, ending=False, dbias_fp32=False, scale=None,
+def make_problem(B, N, H, D, *, ending=False, dbias_fp32=False, scale=None, residual_fp32=False,
                  abi_version=ABI_VERSION) -> Problem:
-    flags = (FLAG_ENDING_NODE if ending else 0) | (FLAG_DBIAS_FP32 if dbias_fp32 else 0)
+    flags = ((FLAG_ENDING_NODE if ending else 0) | (FLAG_DBIAS_FP32 if dbias_fp32 else 0)
+             | (FLAG_RESIDUAL_FP32 if residual_fp32 else 0))
     return Problem(abi_version, flags, B, N, H, D, float(scale or 0.0))
 
 
@@ -114,13 +116,16 @@ def _check_inputs(q, k, v, bias, mask):
     return B, N, H, D
 
 
-def tri_attn_fwd(q, k, v, bias, mask=None, *, ending=False, scale=None, save_residual=True):
-    """Forward: returns (o bf16, o_residual bf16 or None, lse fp32 [B, N, H, N])."""
+def tri_attn_fwd(q, k, v, bias, mask=None, *, ending=False, scale=None, save_residual=True,
+                 residual_fp32=False):
+    """Forward: returns (o bf16, o_residual or None, lse fp32 [B, N, H, N]); the residual
+    is bf16, or the exact fp32 residual with residual_fp32=True."""
     B, N, H, D = _check_inputs(q, k, v, bias, mask)
     lib = load_library()
-    prob = make_problem(B, N, H, D, ending=ending, scale=scale)
+    prob = make_problem(B, N, H, D, ending=ending, scale=scale, residual_fp32=residual_fp32)
     o = torch.empty_like(q)
-    res = torch.empty_like(q) if save_residual else None
+    res = (torch.empty(q.shape, dtype=torch.float32 if residual_fp32 else torch.bfloat16, device=q.device)
+           if save_residual else None)
     lse = torch.empty((B, N, H, N), dtype=torch.float32, device=q.device)
     st = lib.tri_attn_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask),
                           _ptr(o), _ptr(res), _ptr(lse), _stream(q.device))
@@ -138,11 +143,16 @@ def bwd_workspace_bytes(B, N, H, D, *, ending=False, dbias_fp32=False, scale=Non
 def tri_attn_bwd(q, k, v, bias, mask, o, o_residual, lse, d_o, *, ending=False, scale=None,
                  dbias_fp32=False, workspace=None, main_events=None):
     """Backward: returns (dq, dk, dv, dbias).  o_residual=None selects the
-    uncompensated softmax correction rowsum(dO * float(o)).  main_events, a pair
-    of raw hipEvent_t handles (ints), is recorded around the main kernel."""
+    uncompensated softmax correction rowsum(dO * float(o)); an fp32 o_residual is
+    passed with the fp32-residual flag.  main_events, a pair of raw hipEvent_t
+    handles (ints), is recorded around the main kernel."""
     B, N, H, D = _check_inputs(q, k, v, bias, mask)
     lib = load_library()
-    prob = make_problem(B, N, H, D, ending=ending, dbias_fp32=dbias_fp32, scale=scale)
+    if o_residual is not None and o_residual.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("o_residual must be bf16 or fp32")
+    residual_fp32 = o_residual is not None and o_residual.dtype == torch.float32
+    prob = make_problem(B, N, H, D, ending=ending, dbias_fp32=dbias_fp32, scale=scale,
+                        residual_fp32=residual_fp32)
     nbytes = int(lib.tri_attn_bwd_workspace_bytes(ctypes.byref(prob)))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)

@@ -162,7 +162,7 @@ struct FwdArgs {
   const uint16_t *q, *k, *v, *bias;
   const uint8_t *mask;
   uint16_t *o;
-  uint16_t *res;  // bf16 rounding residual, may be null
+  void *res;      // rounding residual (bf16, or fp32 in the RES32 kernels), may be null
   float *lse;
   Frame f;
   int B, N, H;
@@ -178,7 +178,7 @@ struct FwdTile {
   unsigned m;
 };
 
-template <bool MASKED>
+template <bool MASKED, bool RES32>
 __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
   extern __shared__ float4 smem_f4[];
   _Float16 *bias_s = (_Float16 *)smem_f4;
@@ -379,9 +379,10 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
       }
       pass(m, oacc, lsum);
     }
-    // o and its rounding residual (both bf16) leave through the wave's K/V LDS tiles
-    // (free between rows): written there in the accumulator layout and read back by
-    // query, so that every query's 64-byte segment of each is stored whole.  16-byte
+    // o and its bf16 rounding residual leave through the wave's K/V LDS tiles (free
+    // between rows): written there in the accumulator layout and read back by query,
+    // so that every query's 64-byte segment of each is stored whole (an fp32
+    // residual goes out directly: the lane's four channels are 16 contiguous bytes).  16-byte
     // chunks are permuted by row bits so both LDS passes are free of bank conflicts.
     auto o_off = [](int row, int chunk) { return row * HD + ((chunk ^ ((row >> 2) & 3)) << 3); };
     uint16_t *ot = kbuf;  // [32 queries][32 channels] bf16: o
@@ -392,6 +393,9 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
       const float inv = lsum[s] > 0.f ? 1.f / lsum[s] : 0.f;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        // no contraction here: fused into an fma, O - float(o) would be taken from the
+        // unrounded product and could exceed half a bf16 ulp of o
+#pragma clang fp contract(off)
         float ov[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) ov[i] = oacc[s][4 * g + i] * inv;
@@ -399,15 +403,23 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
         // channels 8g + 4hh .. 8g + 4hh + 3 of query jl; the residual O - float(o) is
         // exact in fp32 and rounded once more, to bf16
         *(u32x2 *)(ot + o_off(jl, g) + 4 * hh) = (u32x2){p0, p1};
-        *(u32x2 *)(rt + o_off(jl, g) + 4 * hh) =
-            (u32x2){pack_bf16(ov[0] - bf_lo(p0), ov[1] - bf_hi(p0)), pack_bf16(ov[2] - bf_lo(p1), ov[3] - bf_hi(p1))};
+        const f32x4 rv = {ov[0] - bf_lo(p0), ov[1] - bf_hi(p0), ov[2] - bf_lo(p1), ov[3] - bf_hi(p1)};
+        if (RES32) {
+          // fp32 residual: the lane's four channels are 16 contiguous bytes
+          if (a.res) {
+            const long long off = base + (long long)(j0 + 32 * s + jl) * a.f.sQ + 8 * g + 4 * hh;
+            *(f32x4 *)((float *)a.res + off) = rv;
+          }
+        } else {
+          *(u32x2 *)(rt + o_off(jl, g) + 4 * hh) = (u32x2){pack_bf16(rv[0], rv[1]), pack_bf16(rv[2], rv[3])};
+        }
       }
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
         const int row = (lane >> 2) + 16 * k, chunk = lane & 3;
         const long long off = base + (long long)(j0 + 32 * s + row) * a.f.sQ + 8 * chunk;
         *(u32x4 *)(a.o + off) = *(const u32x4 *)(ot + o_off(row, chunk));
-        if (a.res) *(u32x4 *)(a.res + off) = *(const u32x4 *)(rt + o_off(row, chunk));
+        if (!RES32 && a.res) *(u32x4 *)((uint16_t *)a.res + off) = *(const u32x4 *)(rt + o_off(row, chunk));
       }
       if (hh == 0) {
         // lse = ln(sum exp(logit)) = ln 2 * (m + log2(sum p))
@@ -429,7 +441,8 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
 // residual when the residual is saved; the channel sum runs in a fixed order.
 struct PrepArgs {
   const uint16_t *o, *d_o;
-  const uint16_t *res;  // bf16 rounding residual of o, or null
+  const void *res;  // rounding residual of o (bf16, or fp32 when res_fp32), or null
+  int res_fp32;
   const float *lse;
   float *stats;  // [B][N][H][2][N]: -lse/alpha, then -D
   Frame f;
@@ -456,13 +469,31 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
     gw[i] = ld16(a.d_o + base + 8 * i);
     ow[i] = ld16(a.o + base + 8 * i);
   }
-  u32x4 rw[4];
-  if (a.res) {
+  // the residual of channels 8i + 2w, 8i + 2w + 1 as fp32
+  float rf[4][4][2];
+  if (a.res && a.res_fp32) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rw[i] = ld16(a.res + base + 8 * i);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int hlf = 0; hlf < 2; ++hlf) {
+        const f32x4 x = *(const f32x4 *)((const float *)a.res + base + 8 * i + 4 * hlf);
+        rf[i][2 * hlf][0] = x[0];
+        rf[i][2 * hlf][1] = x[1];
+        rf[i][2 * hlf + 1][0] = x[2];
+        rf[i][2 * hlf + 1][1] = x[3];
+      }
   } else {
+    u32x4 rw[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rw[i] = (u32x4){0u, 0u, 0u, 0u};
+    for (int i = 0; i < 4; ++i)
+      rw[i] = a.res ? ld16((const uint16_t *)a.res + base + 8 * i) : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        rf[i][w][0] = bf_lo(rw[i][w]);
+        rf[i][w][1] = bf_hi(rw[i][w]);
+      }
   }
   float acc = 0.f;
 #pragma unroll
@@ -470,8 +501,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       // channels 8i + 2w and 8i + 2w + 1
-      const float o0 = bf_lo(ow[i][w]) + bf_lo(rw[i][w]);
-      const float o1 = bf_hi(ow[i][w]) + bf_hi(rw[i][w]);
+      const float o0 = bf_lo(ow[i][w]) + rf[i][w][0];
+      const float o1 = bf_hi(ow[i][w]) + rf[i][w][1];
       acc = fmaf(bf_lo(gw[i][w]), o0, acc);
       acc = fmaf(bf_hi(gw[i][w]), o1, acc);
     }
@@ -986,7 +1017,8 @@ tri_attn_status check_problem(const tri_attn_problem *p) {
   if (p->abi_version != TRI_ATTN_ABI_VERSION) return TRI_ATTN_ERROR_ABI_MISMATCH;
   if (p->B < 1 || p->N < 1 || p->H < 1 || p->D < 1) return TRI_ATTN_ERROR_INVALID_VALUE;
   if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale)) return TRI_ATTN_ERROR_INVALID_VALUE;
-  if (p->flags & ~(TRI_ATTN_FLAG_ENDING_NODE | TRI_ATTN_FLAG_DBIAS_FP32)) return TRI_ATTN_ERROR_NOT_SUPPORTED;
+  if (p->flags & ~(TRI_ATTN_FLAG_ENDING_NODE | TRI_ATTN_FLAG_DBIAS_FP32 | TRI_ATTN_FLAG_RESIDUAL_FP32))
+    return TRI_ATTN_ERROR_NOT_SUPPORTED;
   if (p->D != HD || p->N % 32 != 0 || p->N > kMaxN || p->H > kMaxH) return TRI_ATTN_ERROR_NOT_SUPPORTED;
   if (p->B * p->N * p->N * p->H * p->D > (int64_t)1 << 40) return TRI_ATTN_ERROR_NOT_SUPPORTED;
   return TRI_ATTN_SUCCESS;
@@ -1094,7 +1126,8 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
   const size_t E = (size_t)p.B * p.N * p.N * p.H * p.D;
   const Range ins[] = {span(q, E * 2), span(k, E * 2), span(v, E * 2), span(bias, (size_t)p.B * p.H * p.N * p.N * 2),
                        span(mask, mask ? (size_t)p.B * p.N * p.N : 0)};
-  const Range outs[] = {span(o, E * 2), span(o_residual, o_residual ? E * 2 : 0),
+  const size_t res_bytes = (p.flags & TRI_ATTN_FLAG_RESIDUAL_FP32) ? E * 4 : E * 2;
+  const Range outs[] = {span(o, E * 2), span(o_residual, o_residual ? res_bytes : 0),
                         span(lse, (size_t)p.B * p.N * p.H * p.N * 4)};
   for (const Range &x : outs) {
     for (const Range &y : ins)
@@ -1110,7 +1143,7 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
   a.bias = (const uint16_t *)bias;
   a.mask = mask;
   a.o = (uint16_t *)o;
-  a.res = (uint16_t *)o_residual;
+  a.res = o_residual;
   a.lse = lse;
   a.f = make_frame(problem);
   a.B = (int)p.B;
@@ -1130,14 +1163,13 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
   a.rows_per_chunk = (a.N + chunks - 1) / chunks;
   a.n_chunks = (a.N + a.rows_per_chunk - 1) / a.rows_per_chunk;
   const size_t lds = (size_t)FWD_BJ * a.bstride * 2 + (size_t)FWD_WAVES * 2 * 32 * HD * 2;
-  const void *kern = mask ? (const void *)fwd_kernel<true> : (const void *)fwd_kernel<false>;
-  if (hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+  const bool res32 = (p.flags & TRI_ATTN_FLAG_RESIDUAL_FP32) != 0;
+  void (*kern)(FwdArgs) = mask ? (res32 ? fwd_kernel<true, true> : fwd_kernel<true, false>)
+                               : (res32 ? fwd_kernel<false, true> : fwd_kernel<false, false>);
+  if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
       hipSuccess)
     return TRI_ATTN_ERROR_LAUNCH_FAILED;
-  if (mask)
-    hipLaunchKernelGGL(fwd_kernel<true>, dim3(groups * a.n_chunks), dim3(FWD_WAVES * 64), lds, stream, a);
-  else
-    hipLaunchKernelGGL(fwd_kernel<false>, dim3(groups * a.n_chunks), dim3(FWD_WAVES * 64), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3(groups * a.n_chunks), dim3(FWD_WAVES * 64), lds, stream, a);
   return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH_FAILED;
 }
 
@@ -1169,7 +1201,7 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
                        span(bias, nb * 2),
                        span(mask, mask ? (size_t)p.B * p.N * p.N : 0),
                        span(o, E * 2),
-                       span(o_residual, o_residual ? E * 2 : 0),
+                       span(o_residual, o_residual ? ((p.flags & TRI_ATTN_FLAG_RESIDUAL_FP32) ? E * 4 : E * 2) : 0),
                        span(lse, (size_t)p.B * p.N * p.H * p.N * 4),
                        span(d_o, E * 2)};
   const Range outs[] = {span(dq, E * 2), span(dk, E * 2), span(dv, E * 2),
@@ -1192,7 +1224,8 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
   PrepArgs pa;
   pa.o = (const uint16_t *)o;
   pa.d_o = (const uint16_t *)d_o;
-  pa.res = (const uint16_t *)o_residual;
+  pa.res = o_residual;
+  pa.res_fp32 = (p.flags & TRI_ATTN_FLAG_RESIDUAL_FP32) ? 1 : 0;
   pa.lse = lse;
   pa.stats = stats;
   pa.inv_alpha = 1.f / alpha;
