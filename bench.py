@@ -85,11 +85,11 @@ def build_hash() -> str:
     return hashlib.sha256(KERNEL_SOURCE.read_bytes() + " ".join(FLAGS).encode()).hexdigest()
 
 
-def measured_traffic(workload: str, ending: bool, residual: str = "bf16"):
+def measured_traffic(workload: str, ending: bool, residual: str = "fp32"):
     """HBM bytes per launch of the backward main kernel from the committed rocprofv3
     counter summary, if it was taken on this kernel source, these build flags and
     this workload."""
-    if ending or residual != "bf16":
+    if ending or residual != "fp32":
         return None
     f = ROOT / "profiles" / f"traffic_bwd_main_{workload}.md"
     if not f.exists():
@@ -104,7 +104,7 @@ def measured_traffic(workload: str, ending: bool, residual: str = "bf16"):
     return int(val.group(1))
 
 
-def algorithmic_bytes(B: int, N: int, H: int, D: int, masked: bool, residual_bytes: int = 2) -> int:
+def algorithmic_bytes(B: int, N: int, H: int, D: int, masked: bool, residual_bytes: int = 4) -> int:
     """Bytes one fwd+bwd step must move: the forward reads q, k, v, bias (and the
     mask) and writes o, its residual and lse; the backward reads q, k, v, o, the
     residual, dO, lse, bias (and the mask) and writes dq, dk, dv and dbias."""
@@ -158,7 +158,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="crop768")
     ap.add_argument("--ending", action="store_true", help="ending-node orientation")
-    ap.add_argument("--residual", choices=("bf16", "fp32"), default="bf16",
+    ap.add_argument("--residual", choices=("fp32", "bf16"), default="fp32",
                     help="precision of the saved rounding residual of o")
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--cpu-dbias-rows", type=int, default=512)
@@ -188,7 +188,7 @@ def main():
 
     def fwd():
         return ta.tri_attn_fwd(g["q"], g["k"], g["v"], g["bias"], mask, ending=args.ending,
-                               residual_fp32=args.residual == "fp32")
+                               residual=args.residual)
 
     def bwd(o, res, lse, events=None):
         return ta.tri_attn_bwd(g["q"], g["k"], g["v"], g["bias"], mask, o, res, lse, g["do"],

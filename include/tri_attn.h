@@ -21,7 +21,7 @@
  *
  * Layouts (row-major, last index fastest):
  *   q, k, v, o, d_o, dq, dk, dv : bf16 [B, N, N, H, D]  (D contiguous)
- *   o_residual                  : bf16 [B, N, N, H, D] (fp32 with FLAG_RESIDUAL_FP32)
+ *   o_residual                  : fp32 [B, N, N, H, D] (bf16 with FLAG_RESIDUAL_BF16)
  *   bias, dbias                 : bf16 [B, H, N, N] (dbias fp32 with FLAG_DBIAS_FP32);
  *                                 bias values must lie in the fp16 range
  *                                 (|bias| <= 65504, or -inf): the kernels hold the
@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define TRI_ATTN_ABI_VERSION 2
+#define TRI_ATTN_ABI_VERSION 3
 
 typedef enum {
     TRI_ATTN_SUCCESS = 0,
@@ -71,7 +71,7 @@ typedef enum {
 enum {
     TRI_ATTN_FLAG_ENDING_NODE = 1 << 0,   /* attend along the first pair axis (see above) */
     TRI_ATTN_FLAG_DBIAS_FP32 = 1 << 1,    /* dbias is written as fp32 instead of bf16 */
-    TRI_ATTN_FLAG_RESIDUAL_FP32 = 1 << 2  /* o_residual is the exact fp32 residual (both passes) */
+    TRI_ATTN_FLAG_RESIDUAL_BF16 = 1 << 2  /* o_residual is stored as bf16 instead of fp32 (both passes) */
 };
 
 typedef struct {
@@ -95,12 +95,12 @@ const char *tri_attn_status_string(int status);
  * the FP32-to-BF16 rounding residual of the output is kept for the backward).
  *   q, k, v, bias, mask : inputs as laid out above (mask may be NULL)
  *   o                   : bf16 output, round-to-nearest-even of the fp32 result O
- *   o_residual          : the fp32 residual O - float(o) (exact in fp32), stored as
- *                         its bf16 round-to-nearest-even by default: float(o) +
- *                         float(o_residual) then restores O to within 2^-9 of the
- *                         residual, i.e. about 2^-17 relative to O.  With
- *                         TRI_ATTN_FLAG_RESIDUAL_FP32 it is stored as fp32 (twice
- *                         the bytes) and restores O exactly.  NULL = not saved
+ *   o_residual          : the fp32 residual O - float(o), exact in fp32, so that
+ *                         float(o) + o_residual is O bitwise.  With
+ *                         TRI_ATTN_FLAG_RESIDUAL_BF16 it is stored as its bf16
+ *                         round-to-nearest-even instead (half the bytes): float(o)
+ *                         + float(o_residual) then restores O to within 2^-9 of the
+ *                         residual, about 2^-17 relative to O.  NULL = not saved
  *   lse                 : fp32 log-sum-exp of every softmax row; +inf for a row
  *                         whose keys are all masked (its o and residual are 0)
  */
@@ -122,8 +122,8 @@ size_t tri_attn_bwd_workspace_bytes(const tri_attn_problem *problem);
  * key, value, query and pair-bias gradients are reduced in a fixed order and
  * the full score gradient is never stored.
  *   q, k, v, bias, mask, o, lse : the forward's inputs and outputs
- *   o_residual : the forward's residual (bf16, or fp32 with the same
- *                TRI_ATTN_FLAG_RESIDUAL_FP32 as the forward); NULL = uncompensated
+ *   o_residual : the forward's residual (fp32, or bf16 with the same
+ *                TRI_ATTN_FLAG_RESIDUAL_BF16 as the forward); NULL = uncompensated
  *                correction D = rowsum(dO * float(o))
  *   d_o        : bf16 upstream gradient of o
  *   dq, dk, dv : bf16 gradients, [B,N,N,H,D]

@@ -41,7 +41,7 @@ def test_traffic_is_reported_only_for_a_matching_build(tmp_path, monkeypatch):
         f"traffic_bytes_per_launch: 123\nbuild_sha256: {bench.build_hash()}\n")
     assert bench.measured_traffic("crop768", False) == 123
     assert bench.measured_traffic("crop768", True) is None           # other orientation
-    assert bench.measured_traffic("crop768", False, "fp32") is None  # other residual
+    assert bench.measured_traffic("crop768", False, "bf16") is None  # other residual
     (prof / "traffic_bwd_main_crop768.md").write_text(
         "traffic_bytes_per_launch: 123\nbuild_sha256: " + "0" * 64 + "\n")
     assert bench.measured_traffic("crop768", False) is None          # other source or flags

@@ -50,12 +50,12 @@ def to_np(t):
     return t.detach().float().cpu().double().numpy()
 
 
-def run_gpu(ta, inp, ending=False, compensated=True, scale=None, dbias_fp32=False, residual_fp32=False):
+def run_gpu(ta, inp, ending=False, compensated=True, scale=None, dbias_fp32=False, residual="fp32"):
     dev = torch.device("cuda:0")
     g = {k: v.to(dev) for k, v in inp.items()}
     mask = g["mask"] if inp.get("mask") is not None else None
     o, res, lse = ta.tri_attn_fwd(g["q"], g["k"], g["v"], g["bias"], mask, ending=ending,
-                                  scale=scale, save_residual=True, residual_fp32=residual_fp32)
+                                  scale=scale, save_residual=True, residual=residual)
     dq, dk, dv, db = ta.tri_attn_bwd(g["q"], g["k"], g["v"], g["bias"], mask, o,
                                      res if compensated else None, lse, g["do"],
                                      ending=ending, scale=scale, dbias_fp32=dbias_fp32)
@@ -152,13 +152,12 @@ def test_residual_is_the_rounding_remainder(ta):
     out = run_gpu(ta, inp)
     o = out["o"].float()
     r = out["res"]
-    assert r.dtype == torch.bfloat16
-    r = r.float()
-    # r is the bf16 rounding of O - float(o), so |r| is at most half an ulp of o
+    assert r.dtype == torch.float32
+    # r is O - float(o) for the round-to-nearest-even o, so |r| is at most half an ulp of o
     ulp_half = torch.where(o == 0, torch.zeros_like(o),
                            torch.ldexp(torch.ones_like(o), torch.frexp(o.abs()).exponent - 9))
     assert bool((r.abs() <= ulp_half + 1e-30).all())
-    full = o + r  # the kernel's fp32 output to about 16 significant bits
+    full = o + r  # the kernel's fp32 output, exactly
     ref = oracle.forward(inp["q"], inp["k"], inp["v"], inp["bias"], inp["mask"])[0]
     e_bf = rel_rmse(to_np(out["o"]), ref)
     e_fp = rel_rmse(to_np(full), ref)
@@ -169,14 +168,14 @@ def test_residual_is_the_rounding_remainder(ta):
 
 
 @pytest.mark.parametrize("ending", [False, True])
-def test_fp32_residual(ta, ending):
-    """With the fp32-residual flag the forward saves O - float(o) itself: its bf16
-    rounding is exactly the default residual, o + r restores the kernel's fp32
-    output, and the backward (flag on) meets the gradient criteria with the exact
-    compensation, next to the bf16-residual and uncompensated corrections."""
+def test_bf16_residual(ta, ending):
+    """With the bf16-residual flag the forward saves the bf16 rounding of the fp32
+    residual O - float(o), bitwise; o and lse do not change, and the backward (flag
+    on) meets the gradient criteria, next to the fp32-residual and uncompensated
+    corrections."""
     inp = si.make_workload("pad256")
-    out32 = run_gpu(ta, inp, ending=ending, residual_fp32=True)
-    out16 = run_gpu(ta, inp, ending=ending)
+    out32 = run_gpu(ta, inp, ending=ending)
+    out16 = run_gpu(ta, inp, ending=ending, residual="bf16")
     unc = run_gpu(ta, inp, ending=ending, compensated=False)
     r32 = out32["res"]
     assert r32.dtype == torch.float32 and out16["res"].dtype == torch.bfloat16
@@ -200,9 +199,9 @@ def test_fp32_residual(ta, ending):
         e32 = rel_rmse(to_np(out32[n]), ref[n])
         e16 = rel_rmse(to_np(out16[n]), ref[n])
         eu = rel_rmse(to_np(unc[n]), ref[n])
-        say(f"[fp32 residual] ending={ending} {n}: fp32 residual {e32:.3e}, bf16 residual {e16:.3e}, "
+        say(f"[residual] ending={ending} {n}: fp32 residual {e32:.3e}, bf16 residual {e16:.3e}, "
             f"uncompensated {eu:.3e}")
-        assert e32 <= GRAD_REL_RMSE
+        assert e32 <= GRAD_REL_RMSE and e16 <= GRAD_REL_RMSE
     assert torch.equal(out32["dv"].view(torch.int16), out16["dv"].view(torch.int16))
 
 

@@ -49,19 +49,19 @@ def test_reproducibility_sweep(ta):
         compensated = bool(rng.integers(0, 2))
         scale = None if rng.integers(0, 2) else float(rng.uniform(0.1, 0.4))
         dbias_fp32 = bool(rng.integers(0, 2))
-        residual_fp32 = bool(rng.integers(0, 2))
+        residual = "fp32" if rng.integers(0, 2) else "bf16"
         inp = si.make_problem(B, N, H, 32, 20000 + case, mask="none" if kind == "absent" else kind)
         g = {k: v.to(dev) for k, v in inp.items()}
         mask = None if kind == "absent" else g["mask"]
         if case % 100 == 0:
             print(f"[reproducibility] case {case}: B={B} N={N} H={H} mask={kind} ending={ending} "
                   f"compensated={compensated} scale={scale} dbias_fp32={dbias_fp32} "
-                  f"residual_fp32={residual_fp32}", flush=True)
+                  f"residual={residual}", flush=True)
             sys.stdout.flush()
         first = None
         for _ in range(N_RUNS):
             o, res, lse = ta.tri_attn_fwd(g["q"], g["k"], g["v"], g["bias"], mask, ending=ending,
-                                          scale=scale, save_residual=True, residual_fp32=residual_fp32)
+                                          scale=scale, save_residual=True, residual=residual)
             grads = ta.tri_attn_bwd(g["q"], g["k"], g["v"], g["bias"], mask, o,
                                     res if compensated else None, lse, g["do"], ending=ending,
                                     scale=scale, dbias_fp32=dbias_fp32)

@@ -21,10 +21,11 @@ import torch
 _HERE = Path(__file__).resolve().parent
 LIB_PATH = _HERE / "libtri_attn.so"
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 FLAG_ENDING_NODE = 1
 FLAG_DBIAS_FP32 = 2
-FLAG_RESIDUAL_FP32 = 4
+FLAG_RESIDUAL_BF16 = 4
+RESIDUAL_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}
 
 STATUS_NAMES = {
     0: "TRI_ATTN_SUCCESS",
@@ -86,10 +87,12 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     return lib
 
 
-def make_problem(B, N, H, D, *, ending=False, dbias_fp32=False, scale=None, residual_fp32=False,
+def make_problem(B, N, H, D, *, ending=False, dbias_fp32=False, scale=None, residual="fp32",
                  abi_version=ABI_VERSION) -> Problem:
+    if residual not in RESIDUAL_DTYPES:
+        raise ValueError("residual must be 'fp32' or 'bf16'")
     flags = ((FLAG_ENDING_NODE if ending else 0) | (FLAG_DBIAS_FP32 if dbias_fp32 else 0)
-             | (FLAG_RESIDUAL_FP32 if residual_fp32 else 0))
+             | (FLAG_RESIDUAL_BF16 if residual == "bf16" else 0))
     return Problem(abi_version, flags, B, N, H, D, float(scale or 0.0))
 
 
@@ -117,15 +120,14 @@ def _check_inputs(q, k, v, bias, mask):
 
 
 def tri_attn_fwd(q, k, v, bias, mask=None, *, ending=False, scale=None, save_residual=True,
-                 residual_fp32=False):
+                 residual="fp32"):
     """Forward: returns (o bf16, o_residual or None, lse fp32 [B, N, H, N]); the residual
-    is bf16, or the exact fp32 residual with residual_fp32=True."""
+    O - float(o) is fp32 (exact), or its bf16 rounding with residual="bf16"."""
     B, N, H, D = _check_inputs(q, k, v, bias, mask)
     lib = load_library()
-    prob = make_problem(B, N, H, D, ending=ending, scale=scale, residual_fp32=residual_fp32)
+    prob = make_problem(B, N, H, D, ending=ending, scale=scale, residual=residual)
     o = torch.empty_like(q)
-    res = (torch.empty(q.shape, dtype=torch.float32 if residual_fp32 else torch.bfloat16, device=q.device)
-           if save_residual else None)
+    res = torch.empty(q.shape, dtype=RESIDUAL_DTYPES[residual], device=q.device) if save_residual else None
     lse = torch.empty((B, N, H, N), dtype=torch.float32, device=q.device)
     st = lib.tri_attn_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask),
                           _ptr(o), _ptr(res), _ptr(lse), _stream(q.device))
@@ -143,16 +145,16 @@ def bwd_workspace_bytes(B, N, H, D, *, ending=False, dbias_fp32=False, scale=Non
 def tri_attn_bwd(q, k, v, bias, mask, o, o_residual, lse, d_o, *, ending=False, scale=None,
                  dbias_fp32=False, workspace=None, main_events=None):
     """Backward: returns (dq, dk, dv, dbias).  o_residual=None selects the
-    uncompensated softmax correction rowsum(dO * float(o)); an fp32 o_residual is
-    passed with the fp32-residual flag.  main_events, a pair of raw hipEvent_t
+    uncompensated softmax correction rowsum(dO * float(o)); a bf16 o_residual is
+    passed with the bf16-residual flag.  main_events, a pair of raw hipEvent_t
     handles (ints), is recorded around the main kernel."""
     B, N, H, D = _check_inputs(q, k, v, bias, mask)
     lib = load_library()
     if o_residual is not None and o_residual.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("o_residual must be bf16 or fp32")
-    residual_fp32 = o_residual is not None and o_residual.dtype == torch.float32
+    residual = "bf16" if o_residual is not None and o_residual.dtype == torch.bfloat16 else "fp32"
     prob = make_problem(B, N, H, D, ending=ending, dbias_fp32=dbias_fp32, scale=scale,
-                        residual_fp32=residual_fp32)
+                        residual=residual)
     nbytes = int(lib.tri_attn_bwd_workspace_bytes(ctypes.byref(prob)))
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)

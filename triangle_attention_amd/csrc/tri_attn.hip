@@ -1017,7 +1017,7 @@ tri_attn_status check_problem(const tri_attn_problem *p) {
   if (p->abi_version != TRI_ATTN_ABI_VERSION) return TRI_ATTN_ERROR_ABI_MISMATCH;
   if (p->B < 1 || p->N < 1 || p->H < 1 || p->D < 1) return TRI_ATTN_ERROR_INVALID_VALUE;
   if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale)) return TRI_ATTN_ERROR_INVALID_VALUE;
-  if (p->flags & ~(TRI_ATTN_FLAG_ENDING_NODE | TRI_ATTN_FLAG_DBIAS_FP32 | TRI_ATTN_FLAG_RESIDUAL_FP32))
+  if (p->flags & ~(TRI_ATTN_FLAG_ENDING_NODE | TRI_ATTN_FLAG_DBIAS_FP32 | TRI_ATTN_FLAG_RESIDUAL_BF16))
     return TRI_ATTN_ERROR_NOT_SUPPORTED;
   if (p->D != HD || p->N % 32 != 0 || p->N > kMaxN || p->H > kMaxH) return TRI_ATTN_ERROR_NOT_SUPPORTED;
   if (p->B * p->N * p->N * p->H * p->D > (int64_t)1 << 40) return TRI_ATTN_ERROR_NOT_SUPPORTED;
@@ -1126,7 +1126,7 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
   const size_t E = (size_t)p.B * p.N * p.N * p.H * p.D;
   const Range ins[] = {span(q, E * 2), span(k, E * 2), span(v, E * 2), span(bias, (size_t)p.B * p.H * p.N * p.N * 2),
                        span(mask, mask ? (size_t)p.B * p.N * p.N : 0)};
-  const size_t res_bytes = (p.flags & TRI_ATTN_FLAG_RESIDUAL_FP32) ? E * 4 : E * 2;
+  const size_t res_bytes = (p.flags & TRI_ATTN_FLAG_RESIDUAL_BF16) ? E * 2 : E * 4;
   const Range outs[] = {span(o, E * 2), span(o_residual, o_residual ? res_bytes : 0),
                         span(lse, (size_t)p.B * p.N * p.H * p.N * 4)};
   for (const Range &x : outs) {
@@ -1163,7 +1163,7 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
   a.rows_per_chunk = (a.N + chunks - 1) / chunks;
   a.n_chunks = (a.N + a.rows_per_chunk - 1) / a.rows_per_chunk;
   const size_t lds = (size_t)FWD_BJ * a.bstride * 2 + (size_t)FWD_WAVES * 2 * 32 * HD * 2;
-  const bool res32 = (p.flags & TRI_ATTN_FLAG_RESIDUAL_FP32) != 0;
+  const bool res32 = (p.flags & TRI_ATTN_FLAG_RESIDUAL_BF16) == 0;
   void (*kern)(FwdArgs) = mask ? (res32 ? fwd_kernel<true, true> : fwd_kernel<true, false>)
                                : (res32 ? fwd_kernel<false, true> : fwd_kernel<false, false>);
   if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
@@ -1201,7 +1201,7 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
                        span(bias, nb * 2),
                        span(mask, mask ? (size_t)p.B * p.N * p.N : 0),
                        span(o, E * 2),
-                       span(o_residual, o_residual ? ((p.flags & TRI_ATTN_FLAG_RESIDUAL_FP32) ? E * 4 : E * 2) : 0),
+                       span(o_residual, o_residual ? ((p.flags & TRI_ATTN_FLAG_RESIDUAL_BF16) ? E * 2 : E * 4) : 0),
                        span(lse, (size_t)p.B * p.N * p.H * p.N * 4),
                        span(d_o, E * 2)};
   const Range outs[] = {span(dq, E * 2), span(dk, E * 2), span(dv, E * 2),
@@ -1225,7 +1225,7 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
   pa.o = (const uint16_t *)o;
   pa.d_o = (const uint16_t *)d_o;
   pa.res = o_residual;
-  pa.res_fp32 = (p.flags & TRI_ATTN_FLAG_RESIDUAL_FP32) ? 1 : 0;
+  pa.res_fp32 = (p.flags & TRI_ATTN_FLAG_RESIDUAL_BF16) ? 0 : 1;
   pa.lse = lse;
   pa.stats = stats;
   pa.inv_alpha = 1.f / alpha;
