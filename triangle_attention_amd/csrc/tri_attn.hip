@@ -379,18 +379,21 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
       }
       pass(m, oacc, lsum);
     }
-    // o and its bf16 rounding residual leave through the wave's K/V LDS tiles (free
-    // between rows): written there in the accumulator layout and read back by query,
-    // so that every query's 64-byte segment of each is stored whole (an fp32
-    // residual goes out directly: the lane's four channels are 16 contiguous bytes).  16-byte
-    // chunks are permuted by row bits so both LDS passes are free of bank conflicts.
+    // o and its rounding residual leave through the wave's K/V LDS tiles (free between
+    // rows, 4 KB): written there in the accumulator layout and read back by query, so
+    // that every query's segment of each (64 bytes of o, 128 bytes of an fp32 or 64 of a
+    // bf16 residual) is stored whole.  16-byte chunks are permuted by row bits so both
+    // LDS passes are free of bank conflicts.  An fp32 residual tile fills all 4 KB: it
+    // goes first, and o follows once its rows have been read back.
     auto o_off = [](int row, int chunk) { return row * HD + ((chunk ^ ((row >> 2) & 3)) << 3); };
+    auto r32_off = [](int row, int c16) { return row * HD + ((c16 ^ ((row >> 1) & 7)) << 2); };
     uint16_t *ot = kbuf;  // [32 queries][32 channels] bf16: o
     uint16_t *rt = vbuf;  // [32 queries][32 channels] bf16: residual
+    float *r32t = (float *)kbuf;  // [32 queries][32 channels] fp32: residual (kbuf and vbuf)
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (s == 1 && !two) break;
-      const float inv = lsum[s] > 0.f ? 1.f / lsum[s] : 0.f;
+      float inv = lsum[s] > 0.f ? 1.f / lsum[s] : 0.f;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         // no contraction here: fused into an fma, O - float(o) would be taken from the
@@ -401,17 +404,37 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
         for (int i = 0; i < 4; ++i) ov[i] = oacc[s][4 * g + i] * inv;
         const unsigned p0 = pack_bf16(ov[0], ov[1]), p1 = pack_bf16(ov[2], ov[3]);
         // channels 8g + 4hh .. 8g + 4hh + 3 of query jl; the residual O - float(o) is
-        // exact in fp32 and rounded once more, to bf16
-        *(u32x2 *)(ot + o_off(jl, g) + 4 * hh) = (u32x2){p0, p1};
+        // exact in fp32 (and rounded once more, to bf16, for a bf16 residual)
         const f32x4 rv = {ov[0] - bf_lo(p0), ov[1] - bf_hi(p0), ov[2] - bf_lo(p1), ov[3] - bf_hi(p1)};
         if (RES32) {
-          // fp32 residual: the lane's four channels are 16 contiguous bytes
-          if (a.res) {
-            const long long off = base + (long long)(j0 + 32 * s + jl) * a.f.sQ + 8 * g + 4 * hh;
-            *(f32x4 *)((float *)a.res + off) = rv;
-          }
+          *(f32x4 *)(r32t + r32_off(jl, 2 * g + hh)) = rv;
         } else {
+          *(u32x2 *)(ot + o_off(jl, g) + 4 * hh) = (u32x2){p0, p1};
           *(u32x2 *)(rt + o_off(jl, g) + 4 * hh) = (u32x2){pack_bf16(rv[0], rv[1]), pack_bf16(rv[2], rv[3])};
+        }
+      }
+      if (RES32) {
+        // the residual rows (eight lanes per query's 128 bytes), then o into the freed
+        // tile, converted again rather than held.  The lane index passes through an
+        // empty asm: otherwise the compiler hoists these stores' address arithmetic out
+        // of the row loop and the tile loop spills.
+        if (a.res) {
+          int ln = lane;
+          __asm__ volatile("" : "+v"(ln));
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int row = 8 * k + (ln >> 3), c16 = ln & 7;
+            const long long off = base + (long long)(j0 + 32 * s + row) * a.f.sQ + 4 * c16;
+            *(f32x4 *)((float *)a.res + off) = *(const f32x4 *)(r32t + r32_off(row, c16));
+          }
+        }
+        __asm__ volatile("" : "+v"(inv));
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+#pragma clang fp contract(off)
+          const f32x16 &ac = oacc[s];
+          *(u32x2 *)(ot + o_off(jl, g) + 4 * hh) =
+              (u32x2){pack_bf16(ac[4 * g] * inv, ac[4 * g + 1] * inv), pack_bf16(ac[4 * g + 2] * inv, ac[4 * g + 3] * inv)};
         }
       }
 #pragma unroll
@@ -453,64 +476,49 @@ struct PrepArgs {
 // One thread per (b, r, q, h), heads fastest so that a wave reads whole
 // 256-byte (position, all heads) segments.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
+  // four lanes per (b, r, q, h): lane j takes channels 8j .. 8j + 7, so that the lanes
+  // of a wave read contiguous runs of o, dO and the residual
   const long long total = (long long)a.B * a.N * a.N * a.H;
-  const long long idx = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= total) return;
+  const long long idx = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 2;
+  const int j = threadIdx.x & 3;
+  if (idx >= total) return;  // whole groups of four leave together
   const int h = (int)(idx % a.H);
   long long t = idx / a.H;
   const int q = (int)(t % a.N);
   t /= a.N;
   const int r = (int)(t % a.N);
   const int b = (int)(t / a.N);
-  const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)q * a.f.sQ + h * HD;
-  u32x4 gw[4], ow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    gw[i] = ld16(a.d_o + base + 8 * i);
-    ow[i] = ld16(a.o + base + 8 * i);
-  }
-  // the residual of channels 8i + 2w, 8i + 2w + 1 as fp32
-  float rf[4][4][2];
+  const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)q * a.f.sQ + h * HD + 8 * j;
+  const u32x4 gw = ld16(a.d_o + base), ow = ld16(a.o + base);
+  // the residual of channels 8j + 2w, 8j + 2w + 1 as fp32
+  float rf[4][2];
   if (a.res && a.res_fp32) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int hlf = 0; hlf < 2; ++hlf) {
-        const f32x4 x = *(const f32x4 *)((const float *)a.res + base + 8 * i + 4 * hlf);
-        rf[i][2 * hlf][0] = x[0];
-        rf[i][2 * hlf][1] = x[1];
-        rf[i][2 * hlf + 1][0] = x[2];
-        rf[i][2 * hlf + 1][1] = x[3];
-      }
+    const f32x4 x0 = *(const f32x4 *)((const float *)a.res + base);
+    const f32x4 x1 = *(const f32x4 *)((const float *)a.res + base + 4);
+    rf[0][0] = x0[0]; rf[0][1] = x0[1]; rf[1][0] = x0[2]; rf[1][1] = x0[3];
+    rf[2][0] = x1[0]; rf[2][1] = x1[1]; rf[3][0] = x1[2]; rf[3][1] = x1[3];
   } else {
-    u32x4 rw[4];
+    const u32x4 rw = a.res ? ld16((const uint16_t *)a.res + base) : (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      rw[i] = a.res ? ld16((const uint16_t *)a.res + base + 8 * i) : (u32x4){0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        rf[i][w][0] = bf_lo(rw[i][w]);
-        rf[i][w][1] = bf_hi(rw[i][w]);
-      }
+    for (int w = 0; w < 4; ++w) {
+      rf[w][0] = bf_lo(rw[w]);
+      rf[w][1] = bf_hi(rw[w]);
+    }
   }
   float acc = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // channels 8i + 2w and 8i + 2w + 1
-      const float o0 = bf_lo(ow[i][w]) + rf[i][w][0];
-      const float o1 = bf_hi(ow[i][w]) + rf[i][w][1];
-      acc = fmaf(bf_lo(gw[i][w]), o0, acc);
-      acc = fmaf(bf_hi(gw[i][w]), o1, acc);
-    }
+  for (int w = 0; w < 4; ++w) {
+    const float o0 = bf_lo(ow[w]) + rf[w][0];
+    const float o1 = bf_hi(ow[w]) + rf[w][1];
+    acc = fmaf(bf_lo(gw[w]), o0, acc);
+    acc = fmaf(bf_hi(gw[w]), o1, acc);
   }
+  // (l0 + l1) + (l2 + l3) on every lane of the group: a fixed order
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
   const long long row = ((long long)b * a.N + r) * a.H + h;
-  const float L = a.lse[row * a.N + q];
-  a.stats[row * 2 * a.N + q] = -L * a.inv_alpha;
-  a.stats[row * 2 * a.N + a.N + q] = -acc;
+  if (j == 0) a.stats[row * 2 * a.N + q] = -a.lse[row * a.N + q] * a.inv_alpha;
+  if (j == 1) a.stats[row * 2 * a.N + a.N + q] = -acc;
 }
 
 // ------------------------------------------------------------------------------------
@@ -1234,7 +1242,7 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
   pa.N = (int)p.N;
   pa.H = (int)p.H;
   const long long nrows = (long long)p.B * p.N * p.N * p.H;
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((nrows + 255) / 256)), dim3(256), 0, stream, pa);
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((4 * nrows + 255) / 256)), dim3(256), 0, stream, pa);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
 
   BwdArgs ba;
