@@ -83,11 +83,6 @@ def check_full(ta, inp, ending=False, scale=None, tag=""):
     return out, ref
 
 
-def frame_rows(x, ending):
-    """[B,N,N,...] caller-frame array -> attended frame (row axis first)."""
-    return np.swapaxes(x, 1, 2) if ending else x
-
-
 def check_sampled(ta, inp, ending, rows, sel, tag, reps=1):
     say(f"[parity] {tag} ending={ending} sampled rows={rows} dbias rows={sel}")
     out = run_gpu(ta, inp, ending=ending)
@@ -95,16 +90,22 @@ def check_sampled(ta, inp, ending, rows, sel, tag, reps=1):
                        ending=ending)
     ref = p.rows(rows)
     refb = p.dbias(sel)
-    got = {n: frame_rows(to_np(out[n]), ending) for n in ("o", "dq", "dk", "dv")}
-    lse = to_np(out["lse"])
-    cat = {n: (np.stack([got[n][b, r] for (b, r) in rows]), ref[n]) for n in got}
+
+    # the sampled rows are cut out on the device, so that only they are copied back
+    def row_of(t, b, r):
+        return t[b, :, r] if ending else t[b, r]   # attended-frame row r of a caller-frame tensor
+
+    cat = {n: (np.stack([to_np(row_of(out[n], b, r)) for (b, r) in rows]), ref[n])
+           for n in ("o", "dq", "dk", "dv")}
     o_g, o_r = cat["o"]
     assert np.max(np.abs(o_g - o_r)) <= FWD_MAX_ABS, tag
     assert rel_rmse(o_g, o_r) <= FWD_REL_RMSE, tag
-    lse_g = np.stack([lse[b, r] for (b, r) in rows])
-    assert np.max(np.abs(lse_g - ref["lse"])) <= LSE_ABS, tag
-    db = to_np(out["dbias"])
-    db_g = np.stack([db[b, h, j] for (b, h, j) in sel])
+    lse_g = np.stack([to_np(out["lse"][b, r]) for (b, r) in rows])
+    fin = np.isfinite(ref["lse"])  # a row without attended keys has lse = +inf on both sides
+    assert np.array_equal(np.isfinite(lse_g), fin), tag
+    if fin.any():
+        assert np.max(np.abs(lse_g[fin] - ref["lse"][fin])) <= LSE_ABS, tag
+    db_g = np.stack([to_np(out["dbias"][b, h, j]) for (b, h, j) in sel])
     errs = {n: rel_rmse(*cat[n]) for n in ("dq", "dk", "dv")}
     errs["dbias"] = rel_rmse(db_g, refb)
     say(f"[parity] {tag} o_rmse={rel_rmse(o_g, o_r):.2e} grads={errs}")
@@ -279,6 +280,27 @@ def test_large_ragged_sampled(ta, B, N, H, mask_kind, ending):
     rows = sorted(set((b, r) for b in range(B) for (_, r) in sample_rows(N)))
     sel = sorted(set((b, h, j) for b in range(B) for (_, h, j) in sample_dbias(N, H)))
     check_sampled(ta, inp, ending, rows, sel, f"B{B}N{N}H{H}{mask_kind}")
+
+
+@pytest.mark.parametrize("B,N,H,mask_kind,ending", [
+    (3, 128, 64, "random", False),  # 384 workgroups in both passes: more than one round, one row chunk
+    (2, 256, 33, "pad32", True),    # an odd head count above 32 (no head pairs), 264 workgroups
+])
+def test_multi_round_grids_sampled(ta, B, N, H, mask_kind, ending):
+    inp = custom(B, N, H, 211 + N + H, mask_kind)
+    rows = sorted(set((b, r) for b in range(B) for (_, r) in sample_rows(N)))
+    sel = sorted(set((b, h, j) for b in range(B) for (_, h, j) in sample_dbias(N, H)))
+    check_sampled(ta, inp, ending, rows, sel, f"B{B}N{N}H{H}{mask_kind}")
+
+
+def test_maximum_size_sampled(ta):
+    """N = 768 with H = 64, the largest problem the library accepts (1.2e9 elements per
+    tensor): element offsets of the dQ partials and of the outputs pass 2^32, and the
+    backward runs three rounds of workgroups."""
+    say("[parity] maximum size: generating inputs")
+    inp = custom(1, 768, 64, 97, "ragged512")
+    check_sampled(ta, inp, False, [(0, 0), (0, 383), (0, 767)],
+                  [(0, 0, 5), (0, 31, 400), (0, 63, 767)], "B1N768H64ragged512")
 
 
 def test_fully_masked_rows_and_keys(ta):
