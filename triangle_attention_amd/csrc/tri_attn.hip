@@ -10,9 +10,10 @@
 //             fp32 (fp16 operand of a mixed-precision multiply-add), exponentials
 //             against a per-row reference maximum (recomputed against the true
 //             maximum only if a value leaves the fp32 range), O^T = V^T P^T on
-//             MFMA; writes bf16 o, the bf16-rounded remainder O - float(o) and the
-//             fp32 log-sum-exp.
-//   bwd_prep  D = rowsum(dO * (o + residual)) in fp32, fixed channel order.
+//             MFMA; writes bf16 o, the remainder O - float(o) (exact in fp32; or
+//             rounded to bf16 in the bf16-residual variant) and the fp32
+//             log-sum-exp.
+//   bwd_prep  D = rowsum(dO * (o + residual)) in fp32, fixed summation order.
 //   bwd_main  key-block-parallel backward: one workgroup owns a block of keys
 //             for a chunk of rows and every query; each probability tile is
 //             recomputed once from the saved log-sum-exp and feeds dV, dK, dQ
