@@ -19,9 +19,12 @@ The JSON line also carries
                  same workload (sampled attention rows and bias-gradient rows),
                  scaled to the whole workload;
   phases       : median and 90th-percentile forward, backward and step times over
-                 the timed steps (events on the launch stream), the algorithmic
-                 bytes of one step and the rate they imply, and whether the outputs
-                 of the first and last timed steps are bitwise identical.
+                 the timed steps (events on the launch stream), the same for each
+                 of the backward's four kernels (events the library records
+                 between them), the algorithmic bytes of one step and the rate they
+                 imply, the pair-bias and bias-gradient bytes of a step with the
+                 measured rate of the dbias reduction, and whether the outputs of
+                 the first and last timed steps are bitwise identical.
 """
 from __future__ import annotations
 
@@ -112,6 +115,30 @@ def algorithmic_bytes(B: int, N: int, H: int, D: int, masked: bool, residual_byt
     return (24 + 2 * residual_bytes) * E + 14 * B * H * N * N + (2 * B * N * N if masked else 0)
 
 
+def row_chunks(groups: int, N: int, cus: int = 256) -> int:
+    """Row chunks per (batch, head, block) in the library's launch plan: one round of
+    workgroups over the MI355X's 256 compute units (at least one chunk, at most N)."""
+    c = max(1, min(N, cus // groups))
+    per = -(-N // c)
+    return -(-N // per)
+
+
+def bias_dbias_bytes(B: int, N: int, H: int, dbias_bytes: int = 2) -> dict:
+    """Pair-bias and bias-gradient HBM bytes of one step.  Every forward workgroup
+    (b, h, 64-query block, row chunk) and every backward workgroup (b, h, 64-key
+    block, row chunk) stages its bias block once; the backward main kernel writes
+    one fp32 dbias partial per row chunk, which the dbias reduction reads back
+    before writing dbias."""
+    nb = B * H * N * N
+    blocks = -(-N // 64)
+    c_fwd = row_chunks(B * H * blocks, N)
+    c_bwd = row_chunks(B * H * blocks, N)
+    return {"bias_tensor_bytes": 2 * nb,
+            "bias_staged_bytes": (c_fwd + c_bwd) * 2 * nb,
+            "dbias_partial_bytes": c_bwd * 4 * nb,
+            "dbias_reduction_bytes": c_bwd * 4 * nb + dbias_bytes * nb}
+
+
 def quantiles(xs):
     xs = sorted(xs)
     pick = lambda q: xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
@@ -192,7 +219,7 @@ def main():
 
     def bwd(o, res, lse, events=None):
         return ta.tri_attn_bwd(g["q"], g["k"], g["v"], g["bias"], mask, o, res, lse, g["do"],
-                               ending=args.ending, workspace=ws, main_events=events)
+                               ending=args.ending, workspace=ws, kernel_events=events)
 
     def step(events=None):
         return bwd(*fwd(), events=events)
@@ -209,7 +236,9 @@ def main():
     torch.cuda.synchronize()
 
     hip = HipEvents()
-    ev = [(hip.create(), hip.create()) for _ in range(args.steps)]
+    # five events per step around the backward's four kernels (statistics, main, dQ
+    # reduction, dbias reduction), recorded by the library on the launch stream
+    ev = [[hip.create() for _ in range(5)] for _ in range(args.steps)]
     marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     outs = []
@@ -226,10 +255,12 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
-    main_ms = sum(hip.elapsed_ms(a, b) for a, b in ev) / args.steps
-    for a, b in ev:
-        hip.destroy(a)
-        hip.destroy(b)
+    kern = {name: [hip.elapsed_ms(e[i], e[i + 1]) for e in ev]
+            for i, name in enumerate(("bwd_prep", "bwd_main", "reduce_dq", "reduce_dbias"))}
+    main_ms = statistics.mean(kern["bwd_main"])
+    for e in ev:
+        for x in e:
+            hip.destroy(x)
     log(f"{ms:.3f} ms/step, backward main kernel {main_ms:.3f} ms")
 
     fwd_ms = [m[0].elapsed_time(m[1]) for m in marks]
@@ -243,6 +274,11 @@ def main():
     value = flops / (ms * 1e-3) / 1e12
     bwd_main_flops = flops * 10 / 14   # S, dP, dV, dK, dQ products of the backward
     achieved = bwd_main_flops / (main_ms * 1e-3) / 1e12
+    bd = bias_dbias_bytes(w.B, w.N, w.H)
+    red_ms = statistics.median(kern["reduce_dbias"])
+    bd["reduce_dbias_ms"] = round(red_ms, 4)
+    bd["reduce_dbias_GBps"] = round(bd["dbias_reduction_bytes"] / (red_ms * 1e-3) / 1e9, 1)
+    bd["bias_and_dbias_bytes_per_step"] = bd["bias_staged_bytes"] + 2 * bd["dbias_partial_bytes"] + 2 * w.B * w.H * w.N * w.N
     line = {
         "metric": "triangle-attn fwd+bwd TFLOP/s at N=768 bf16; % of MFMA peak",
         "value": round(value, 2),
@@ -266,6 +302,8 @@ def main():
                      "traffic": measured_traffic(w.name, args.ending, args.residual),
                      "avg_ms": round(main_ms, 4)},
         "phases": {"fwd_ms": quantiles(fwd_ms), "bwd_ms": quantiles(bwd_ms), "step_ms": quantiles(step_ms),
+                   "bwd_kernels_ms": {n: quantiles(v) for n, v in kern.items()},
+                   "bias_dbias": bd,
                    "algorithmic_bytes_per_step": nbytes,
                    "algorithmic_GBps": round(nbytes / (statistics.median(step_ms) * 1e-3) / 1e9, 1),
                    "deterministic_first_vs_last_step": bool(same)},

@@ -158,6 +158,25 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem,
                                       hipEvent_t main_start, hipEvent_t main_stop,
                                       hipStream_t stream);
 
+/*
+ * Same as tri_attn_bwd, with every kernel of the backward bracketed by events
+ * so a caller can time each one with hipEventElapsedTime.  events points to
+ * five caller-owned hipEvent_t (an entry may be NULL: not recorded), recorded on
+ * `stream` before the statistics kernel (0), after it (1), after the main
+ * kernel (2), after the dQ reduction (3) and after the dbias reduction (4).
+ * events == NULL returns TRI_ATTN_ERROR_INVALID_VALUE.  The dbias reduction
+ * (events 3 to 4) is the backward's bias-gradient traffic: C fp32 partials of
+ * B*H*N*N values read, the bf16 (or fp32) dbias written.
+ */
+tri_attn_status tri_attn_bwd_timed(const tri_attn_problem *problem,
+                                   const void *q, const void *k, const void *v,
+                                   const void *bias, const uint8_t *mask,
+                                   const void *o, const void *o_residual,
+                                   const float *lse, const void *d_o,
+                                   void *dq, void *dk, void *dv, void *dbias,
+                                   void *workspace, size_t workspace_bytes,
+                                   const hipEvent_t *events, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

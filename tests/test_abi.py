@@ -143,3 +143,16 @@ def test_workspace_grows_with_problem(lib):
     sizes = [lib.tri_attn_bwd_workspace_bytes(ctypes.byref(ta.make_problem(1, n, 4, 32)))
              for n in (64, 256, 768)]
     assert sizes[0] < sizes[1] < sizes[2]
+
+
+def test_bwd_timed_validates_before_any_hip_call(lib):
+    """tri_attn_bwd_timed needs its event array, and otherwise validates exactly as
+    tri_attn_bwd (five NULL events: nothing is recorded)."""
+    prob = ta.make_problem(1, 64, 4, 32)
+    need = lib.tri_attn_bwd_workspace_bytes(ctypes.byref(prob))
+    nulls = (ctypes.c_void_p * 5)()
+    assert lib.tri_attn_bwd_timed(ctypes.byref(prob), *fake_ptrs(14), need, None, None) == INVALID
+    ptrs = fake_ptrs(14)
+    ptrs[0] = None
+    assert lib.tri_attn_bwd_timed(ctypes.byref(prob), *ptrs, need, nulls, None) == INVALID
+    assert lib.tri_attn_bwd_timed(ctypes.byref(prob), *fake_ptrs(14), need - 1, nulls, None) == WORKSPACE

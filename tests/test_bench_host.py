@@ -45,3 +45,20 @@ def test_traffic_is_reported_only_for_a_matching_build(tmp_path, monkeypatch):
     (prof / "traffic_bwd_main_crop768.md").write_text(
         "traffic_bytes_per_launch: 123\nbuild_sha256: " + "0" * 64 + "\n")
     assert bench.measured_traffic("crop768", False) is None          # other source or flags
+
+
+def test_row_chunks_follow_one_round_of_workgroups():
+    assert bench.row_chunks(48, 768) == 5     # crop768, H = 4: 240 of 256 compute units
+    assert bench.row_chunks(384, 128) == 1    # more groups than compute units: one chunk
+    assert bench.row_chunks(16, 64) == 16
+    assert bench.row_chunks(2, 96) == 96      # never more chunks than rows
+    assert bench.row_chunks(40, 640) == 6     # 107 rows per chunk: 6 chunks cover 640
+
+
+def test_bias_dbias_bytes_at_crop768():
+    d = bench.bias_dbias_bytes(1, 768, 4)
+    nb = 4 * 768 * 768
+    assert d["bias_tensor_bytes"] == 2 * nb
+    assert d["bias_staged_bytes"] == 10 * 2 * nb        # five row chunks in each pass
+    assert d["dbias_partial_bytes"] == 5 * 4 * nb
+    assert d["dbias_reduction_bytes"] == 5 * 4 * nb + 2 * nb

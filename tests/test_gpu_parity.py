@@ -350,6 +350,30 @@ def test_autograd_wrapper(ta):
         assert rel_rmse(to_np(t.grad), ref[n]) <= GRAD_REL_RMSE, n
 
 
+def test_timed_backward_matches_and_times_each_kernel(ta):
+    """tri_attn_bwd_timed gives the same bits as tri_attn_bwd and brackets each of
+    the four backward kernels with an event."""
+    import bench
+    inp = custom(1, 128, 4, 23, "pad32")
+    dev = torch.device("cuda:0")
+    g = {k: v.to(dev) for k, v in inp.items()}
+    o, res, lse = ta.tri_attn_fwd(g["q"], g["k"], g["v"], g["bias"], g["mask"])
+    plain = ta.tri_attn_bwd(g["q"], g["k"], g["v"], g["bias"], g["mask"], o, res, lse, g["do"])
+    hip = bench.HipEvents()
+    ev = [hip.create() for _ in range(5)]
+    timed = ta.tri_attn_bwd(g["q"], g["k"], g["v"], g["bias"], g["mask"], o, res, lse, g["do"],
+                            kernel_events=ev)
+    torch.cuda.synchronize()
+    for a, b in zip(plain, timed):
+        assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                           b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+    ms = [hip.elapsed_ms(ev[i], ev[i + 1]) for i in range(4)]
+    for e in ev:
+        hip.destroy(e)
+    say(f"[timed] statistics, main, dQ reduction, dbias reduction: {ms} ms")
+    assert all(t > 0 for t in ms)
+
+
 def test_rejects_unsupported_on_device(ta):
     dev = torch.device("cuda:0")
     q = torch.zeros((1, 48, 48, 1, 32), dtype=torch.bfloat16, device=dev)

@@ -37,7 +37,8 @@ STATUS_NAMES = {
 }
 
 EXPORTED_SYMBOLS = ("tri_attn_abi_version", "tri_attn_status_string", "tri_attn_fwd",
-                    "tri_attn_bwd_workspace_bytes", "tri_attn_bwd", "tri_attn_bwd_profiled")
+                    "tri_attn_bwd_workspace_bytes", "tri_attn_bwd", "tri_attn_bwd_profiled",
+                    "tri_attn_bwd_timed")
 
 
 class Problem(ctypes.Structure):
@@ -80,6 +81,8 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.tri_attn_bwd.restype = i32
     lib.tri_attn_bwd_profiled.argtypes = [pp] + [vp] * 14 + [ctypes.c_size_t, vp, vp, vp]
     lib.tri_attn_bwd_profiled.restype = i32
+    lib.tri_attn_bwd_timed.argtypes = [pp] + [vp] * 14 + [ctypes.c_size_t, ctypes.POINTER(vp), vp]
+    lib.tri_attn_bwd_timed.restype = i32
     if lib.tri_attn_abi_version() != ABI_VERSION:
         raise RuntimeError("libtri_attn.so ABI version mismatch")
     if path is None:
@@ -143,11 +146,12 @@ def bwd_workspace_bytes(B, N, H, D, *, ending=False, dbias_fp32=False, scale=Non
 
 
 def tri_attn_bwd(q, k, v, bias, mask, o, o_residual, lse, d_o, *, ending=False, scale=None,
-                 dbias_fp32=False, workspace=None, main_events=None):
+                 dbias_fp32=False, workspace=None, main_events=None, kernel_events=None):
     """Backward: returns (dq, dk, dv, dbias).  o_residual=None selects the
     uncompensated softmax correction rowsum(dO * float(o)); a bf16 o_residual is
     passed with the bf16-residual flag.  main_events, a pair of raw hipEvent_t
-    handles (ints), is recorded around the main kernel."""
+    handles (ints), is recorded around the main kernel; kernel_events, five raw
+    handles, around each of the four backward kernels (tri_attn_bwd_timed)."""
     B, N, H, D = _check_inputs(q, k, v, bias, mask)
     lib = load_library()
     if o_residual is not None and o_residual.dtype not in (torch.bfloat16, torch.float32):
@@ -164,7 +168,12 @@ def tri_attn_bwd(q, k, v, bias, mask, o, o_residual, lse, d_o, *, ending=False, 
     args = (ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask),
             _ptr(o), _ptr(o_residual), _ptr(lse), _ptr(d_o.contiguous()),
             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), _ptr(workspace), workspace.numel())
-    if main_events is None:
+    if kernel_events is not None:
+        if len(kernel_events) != 5:
+            raise ValueError("kernel_events must hold five hipEvent_t handles")
+        evs = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(e) for e in kernel_events])
+        st = lib.tri_attn_bwd_timed(*args, evs, _stream(q.device))
+    elif main_events is None:
         st = lib.tri_attn_bwd(*args, _stream(q.device))
     else:
         ev = [ctypes.c_void_p(e) for e in main_events]

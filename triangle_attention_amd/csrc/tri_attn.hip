@@ -1187,11 +1187,13 @@ size_t tri_attn_bwd_workspace_bytes(const tri_attn_problem *problem) {
   return plan_bwd(problem).total;
 }
 
-tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const void *q, const void *k,
-                                      const void *v, const void *bias, const uint8_t *mask, const void *o,
-                                      const void *o_residual, const float *lse, const void *d_o, void *dq,
-                                      void *dk, void *dv, void *dbias, void *workspace, size_t workspace_bytes,
-                                      hipEvent_t main_start, hipEvent_t main_stop, hipStream_t stream) {
+// The backward's four launches; marks[0..4] (each may be null) are recorded before the
+// statistics kernel, between consecutive kernels and after the dbias reduction.
+static tri_attn_status bwd_run(const tri_attn_problem *problem, const void *q, const void *k, const void *v,
+                               const void *bias, const uint8_t *mask, const void *o, const void *o_residual,
+                               const float *lse, const void *d_o, void *dq, void *dk, void *dv, void *dbias,
+                               void *workspace, size_t workspace_bytes, const hipEvent_t *marks,
+                               hipStream_t stream) {
   tri_attn_status st = check_problem(problem);
   if (st != TRI_ATTN_SUCCESS) return st;
   const tri_attn_problem &p = *problem;
@@ -1242,6 +1244,8 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
   pa.B = (int)p.B;
   pa.N = (int)p.N;
   pa.H = (int)p.H;
+  auto mark = [&](int i) { return !marks[i] || hipEventRecord(marks[i], stream) == hipSuccess; };
+  if (!mark(0)) return TRI_ATTN_ERROR_LAUNCH_FAILED;
   const long long nrows = (long long)p.B * p.N * p.N * p.H;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((4 * nrows + 255) / 256)), dim3(256), 0, stream, pa);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
@@ -1268,10 +1272,10 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
   ba.alpha = alpha;
   ba.c1 = alpha * kLog2e;
   const int grid = ba.B * ba.H * pl.T * pl.C;
-  if (main_start && hipEventRecord(main_start, stream) != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  if (!mark(1)) return TRI_ATTN_ERROR_LAUNCH_FAILED;
   const hipError_t e = dispatch_main(pl.JT, ba, grid, pl.lds_bytes, stream);
   if (e != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
-  if (main_stop && hipEventRecord(main_stop, stream) != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  if (!mark(2)) return TRI_ATTN_ERROR_LAUNCH_FAILED;
 
   ReduceArgs ra;
   ra.dq_part = dq_part;
@@ -1287,18 +1291,39 @@ tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const voi
   ra.dbias_fp32 = (p.flags & TRI_ATTN_FLAG_DBIAS_FP32) ? 1 : 0;
   ra.alpha = alpha;
   hipLaunchKernelGGL(reduce_dq_kernel, dim3((unsigned)((E / 8 + 255) / 256)), dim3(256), 0, stream, ra);
-  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  if (hipGetLastError() != hipSuccess || !mark(3)) return TRI_ATTN_ERROR_LAUNCH_FAILED;
   hipLaunchKernelGGL(reduce_dbias_kernel, dim3((unsigned)((nb / 4 + 255) / 256)), dim3(256), 0, stream, ra);
-  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  if (hipGetLastError() != hipSuccess || !mark(4)) return TRI_ATTN_ERROR_LAUNCH_FAILED;
   return TRI_ATTN_SUCCESS;
+}
+
+tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const void *q, const void *k,
+                                      const void *v, const void *bias, const uint8_t *mask, const void *o,
+                                      const void *o_residual, const float *lse, const void *d_o, void *dq,
+                                      void *dk, void *dv, void *dbias, void *workspace, size_t workspace_bytes,
+                                      hipEvent_t main_start, hipEvent_t main_stop, hipStream_t stream) {
+  const hipEvent_t marks[5] = {nullptr, main_start, main_stop, nullptr, nullptr};
+  return bwd_run(problem, q, k, v, bias, mask, o, o_residual, lse, d_o, dq, dk, dv, dbias, workspace,
+                 workspace_bytes, marks, stream);
+}
+
+tri_attn_status tri_attn_bwd_timed(const tri_attn_problem *problem, const void *q, const void *k, const void *v,
+                                   const void *bias, const uint8_t *mask, const void *o, const void *o_residual,
+                                   const float *lse, const void *d_o, void *dq, void *dk, void *dv, void *dbias,
+                                   void *workspace, size_t workspace_bytes, const hipEvent_t *events,
+                                   hipStream_t stream) {
+  if (!events) return TRI_ATTN_ERROR_INVALID_VALUE;
+  return bwd_run(problem, q, k, v, bias, mask, o, o_residual, lse, d_o, dq, dk, dv, dbias, workspace,
+                 workspace_bytes, events, stream);
 }
 
 tri_attn_status tri_attn_bwd(const tri_attn_problem *problem, const void *q, const void *k, const void *v,
                              const void *bias, const uint8_t *mask, const void *o, const void *o_residual,
                              const float *lse, const void *d_o, void *dq, void *dk, void *dv, void *dbias,
                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  return tri_attn_bwd_profiled(problem, q, k, v, bias, mask, o, o_residual, lse, d_o, dq, dk, dv, dbias,
-                               workspace, workspace_bytes, nullptr, nullptr, stream);
+  const hipEvent_t marks[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  return bwd_run(problem, q, k, v, bias, mask, o, o_residual, lse, d_o, dq, dk, dv, dbias, workspace,
+                 workspace_bytes, marks, stream);
 }
 
 }  // extern "C"
