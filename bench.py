@@ -17,7 +17,11 @@ The JSON line also carries
                  that summary was taken on a different kernel source or build flags;
   cpu_baseline : the FP64 oracle timed on this host on a bounded sample of the
                  same workload (sampled attention rows and bias-gradient rows),
-                 scaled to the whole workload;
+                 scaled to the whole workload, with the host's thread count and
+                 CPU model;
+  mfma_probe   : the sustained bf16 matrix-core rate this device reaches with
+                 independent back-to-back 32x32x16 products, and the backward main
+                 kernel's and the whole step's fractions of it;
   phases       : median and 90th-percentile forward, backward and step times over
                  the timed steps (events on the launch stream), the same for each
                  of the backward's four kernels (events the library records
@@ -139,10 +143,50 @@ def bias_dbias_bytes(B: int, N: int, H: int, dbias_bytes: int = 2) -> dict:
             "dbias_reduction_bytes": c_bwd * 4 * nb + dbias_bytes * nb}
 
 
+def mfma_probe_tflops(blocks: int = 1024, iters: int = 20000) -> float:
+    """Sustained bf16 matrix-core rate of this device: `blocks` workgroups of four
+    waves (four per SIMD at 1024) issuing independent 32x32x16 products back to
+    back (libmfma_probe.so, built with the library), timed with events on the
+    current stream."""
+    import ctypes
+    from triangle_attention_amd.build import PROBE_LIB
+    if not PROBE_LIB.exists():
+        raise RuntimeError(f"{PROBE_LIB} is missing: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(str(PROBE_LIB))
+    lib.mfma_probe_launch.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.mfma_probe_launch.restype = ctypes.c_int
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda:0")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launch(n):
+        if lib.mfma_probe_launch(ctypes.c_void_p(out.data_ptr()), blocks, n, stream) != 0:
+            raise RuntimeError("mfma probe launch failed")
+
+    launch(iters // 10)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    launch(iters)
+    e1.record()
+    torch.cuda.synchronize()
+    flops = blocks * 4 * iters * 4 * 32768
+    return flops / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+
 def quantiles(xs):
     xs = sorted(xs)
     pick = lambda q: xs[min(len(xs) - 1, int(round(q * (len(xs) - 1))))]
     return {"median": round(pick(0.5), 4), "p90": round(pick(0.9), 4)}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(inp, rows: int, dbias_rows: int):
@@ -172,6 +216,7 @@ def cpu_baseline(inp, rows: int, dbias_rows: int):
         "unit": "TFLOP/s",
         "cores": int(os.environ.get("OMP_NUM_THREADS", threads)),
         "kind": "oracle",
+        "cpu": cpu_model(),
         "sample": (f"{len(sel_rows)} of {B * N} attention rows (forward and q/k/v gradients, "
                    f"{t1 - t0:.1f} s) and {len(sel_db)} of {B * H * N} bias-gradient rows "
                    f"({t2 - t1:.1f} s), scaled to the whole workload; est. {t_full:.0f} s"),
@@ -181,8 +226,8 @@ def cpu_baseline(inp, rows: int, dbias_rows: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="crop768")
     ap.add_argument("--ending", action="store_true", help="ending-node orientation")
     ap.add_argument("--residual", choices=("fp32", "bf16"), default="fp32",
@@ -308,6 +353,13 @@ def main():
                    "algorithmic_GBps": round(nbytes / (statistics.median(step_ms) * 1e-3) / 1e9, 1),
                    "deterministic_first_vs_last_step": bool(same)},
     }
+    log("matrix-core probe")
+    probe = mfma_probe_tflops()
+    line["mfma_probe"] = {"TFLOPs": round(probe, 1),
+                          "what": "sustained v_mfma_f32_32x32x16_bf16 rate of this device "
+                                  "(four waves per SIMD, independent accumulators)",
+                          "bwd_main_frac": round(achieved / probe, 4),
+                          "step_frac": round(value / probe, 4)}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle sample)")
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows, args.cpu_dbias_rows)

@@ -156,3 +156,17 @@ def test_bwd_timed_validates_before_any_hip_call(lib):
     ptrs[0] = None
     assert lib.tri_attn_bwd_timed(ctypes.byref(prob), *ptrs, need, nulls, None) == INVALID
     assert lib.tri_attn_bwd_timed(ctypes.byref(prob), *fake_ptrs(14), need - 1, nulls, None) == WORKSPACE
+
+
+def test_mfma_probe_library_validates_arguments():
+    """The matrix-core probe bench.py reports is built with the library; invalid
+    arguments are rejected before any HIP call."""
+    from triangle_attention_amd import build
+    if not build.PROBE_LIB.exists():
+        build.build()
+    probe = ctypes.CDLL(str(build.PROBE_LIB))
+    probe.mfma_probe_launch.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    probe.mfma_probe_launch.restype = ctypes.c_int
+    assert probe.mfma_probe_launch(None, 4, 10, None) == 1
+    assert probe.mfma_probe_launch(ctypes.c_void_p(ADDR), 0, 10, None) == 1
+    assert probe.mfma_probe_launch(ctypes.c_void_p(ADDR), 4, 0, None) == 1

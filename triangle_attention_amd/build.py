@@ -10,6 +10,9 @@ HERE = Path(__file__).resolve().parent
 ROOT = HERE.parent
 SRC = HERE / "csrc" / "tri_attn.hip"
 LIB = HERE / "libtri_attn.so"
+# the matrix-core rate probe bench.py reports next to the published peak
+PROBE_SRC = HERE / "csrc" / "mfma_probe.hip"
+PROBE_LIB = HERE / "libmfma_probe.so"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU forms are disabled for all device code (-packed-fp32-ops).
@@ -26,16 +29,22 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Wno-unused-command-line-argument"]
 
 
-def build(verbose: bool = False) -> Path:
-    tmp = LIB.with_suffix(".so.tmp")
-    cmd = [HIPCC, *FLAGS, "-I", str(ROOT / "include"), "-o", str(tmp), str(SRC)]
+def _compile(src: Path, lib: Path, verbose: bool) -> None:
+    tmp = lib.with_suffix(".so.tmp")
+    cmd = [HIPCC, *FLAGS, "-I", str(ROOT / "include"), "-o", str(tmp), str(src)]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed building {SRC}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"hipcc failed building {src}")
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> Path:
+    """Compile the library and the matrix-core probe; returns the library's path."""
+    _compile(SRC, LIB, verbose)
+    _compile(PROBE_SRC, PROBE_LIB, verbose)
     return LIB
 
 
