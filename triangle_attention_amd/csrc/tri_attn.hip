@@ -477,18 +477,22 @@ struct PrepArgs {
 // One thread per (b, r, q, h), heads fastest so that a wave reads whole
 // 256-byte (position, all heads) segments.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
-  // four lanes per (b, r, q, h): lane j takes channels 8j .. 8j + 7, so that the lanes
-  // of a wave read contiguous runs of o, dO and the residual
+  // four lanes per (b, position, h): lane j takes channels 8j .. 8j + 7.  Groups run
+  // in the caller's memory order (b, first pair axis, second pair axis, h), so that the
+  // lanes of a wave read contiguous runs of o, dO and the residual in both
+  // orientations; the attended frame's row and query follow from the strides.
   const long long total = (long long)a.B * a.N * a.N * a.H;
   const long long idx = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 2;
   const int j = threadIdx.x & 3;
   if (idx >= total) return;  // whole groups of four leave together
   const int h = (int)(idx % a.H);
   long long t = idx / a.H;
-  const int q = (int)(t % a.N);
+  const int p2 = (int)(t % a.N);
   t /= a.N;
-  const int r = (int)(t % a.N);
+  const int p1 = (int)(t % a.N);
   const int b = (int)(t / a.N);
+  const bool starting = a.f.sR > a.f.sQ;  // rows along the first pair axis
+  const int r = starting ? p1 : p2, q = starting ? p2 : p1;
   const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)q * a.f.sQ + h * HD + 8 * j;
   const u32x4 gw = ld16(a.d_o + base), ow = ld16(a.o + base);
   // the residual of channels 8j + 2w, 8j + 2w + 1 as fp32
