@@ -81,8 +81,9 @@ typedef struct {
     float softmax_scale;  /* alpha; 0 selects 1/sqrt(D) */
 } tri_attn_problem;
 
-/* Supported sizes of this build: D == 32, N a multiple of 32 with
- * 32 <= N <= 768, B >= 1, 1 <= H <= 64. */
+/* Supported sizes of this build: D == 32 or D == 16, N a multiple of 32 with
+ * 32 <= N <= 768, B >= 1, 1 <= H <= 64.  D == 16 runs the same kernels with the
+ * tiles' channels 16..31 held at zero. */
 
 /* Returns TRI_ATTN_ABI_VERSION of the loaded library. */
 int tri_attn_abi_version(void);

@@ -55,6 +55,8 @@ WORKLOADS = {
                  "B=1 N=640 H=4 d=32, bias ~ N(0, 4^2), seeded valid length in [512, 640]"),
         Workload("crop768", 5, 1, 768, 4, 32, 1.0, "none",
                  "B=1 N=768 H=4 d=32, all keys valid (starting and ending node)"),
+        Workload("crop768_h8d16", 6, 1, 768, 8, 16, 1.0, "none",
+                 "B=1 N=768 H=8 d=16 (the same 128 pair channels as H=4 d=32), all keys valid"),
     ]
 }
 

@@ -74,7 +74,7 @@ def test_null_problem_is_invalid(lib):
 
 @pytest.mark.parametrize("field,value,expect", [
     ("abi_version", ta.ABI_VERSION + 1, ABI), ("B", 0, INVALID), ("N", 0, INVALID), ("H", 0, INVALID),
-    ("D", 64, UNSUPPORTED), ("D", 16, UNSUPPORTED), ("N", 48, UNSUPPORTED),
+    ("D", 64, UNSUPPORTED), ("D", 8, UNSUPPORTED), ("N", 48, UNSUPPORTED),
     ("N", 800, UNSUPPORTED), ("N", 1024, UNSUPPORTED), ("H", 65, UNSUPPORTED),
     ("flags", 8, UNSUPPORTED), ("softmax_scale", -1.0, INVALID),
     ("softmax_scale", float("inf"), INVALID), ("softmax_scale", float("nan"), INVALID),

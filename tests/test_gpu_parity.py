@@ -206,7 +206,7 @@ def test_bf16_residual(ta, ending):
     assert torch.equal(out32["dv"].view(torch.int16), out16["dv"].view(torch.int16))
 
 
-@pytest.mark.parametrize("name,reps", [("tiny64", 3), ("pad256", 3), ("crop640", 3),
+@pytest.mark.parametrize("name,reps", [("tiny64", 3), ("pad256", 3), ("crop640", 3), ("crop768_h8d16", 3),
                                        ("crop768", 5)])
 def test_bitwise_determinism(ta, name, reps):
     inp = si.make_workload(name)
@@ -252,8 +252,8 @@ def test_compensation(ta, name):
         assert ec <= GRAD_REL_RMSE and eu <= GRAD_REL_RMSE
 
 
-def custom(B, N, H, seed, mask_kind="none", bias_std=1.0):
-    return si.make_problem(B, N, H, 32, seed, bias_std=bias_std, mask=mask_kind)
+def custom(B, N, H, seed, mask_kind="none", bias_std=1.0, D=32):
+    return si.make_problem(B, N, H, D, seed, bias_std=bias_std, mask=mask_kind)
 
 
 @pytest.mark.parametrize("B,N,H,mask_kind,ending", [
@@ -301,6 +301,27 @@ def test_maximum_size_sampled(ta):
     inp = custom(1, 768, 64, 97, "ragged512")
     check_sampled(ta, inp, False, [(0, 0), (0, 383), (0, 767)],
                   [(0, 0, 5), (0, 31, 400), (0, 63, 767)], "B1N768H64ragged512")
+
+
+@pytest.mark.parametrize("B,N,H,mask_kind,ending", [
+    (1, 64, 4, "none", False),
+    (2, 96, 3, "random", True),
+    (1, 256, 8, "pad32", False),
+    (1, 160, 2, "pad32", True),
+])
+def test_head_dim16_full(ta, B, N, H, mask_kind, ending):
+    """Head dimension 16: the kernels run the 32-channel tiles with channels 16..31 at
+    zero and store only the caller's 16."""
+    inp = custom(B, N, H, 301 + N + H, mask_kind, D=16)
+    out, ref = check_full(ta, inp, ending=ending, tag=f"D16 B{B}N{N}H{H}{mask_kind}")
+    assert out["res"].shape[-1] == 16
+
+
+@pytest.mark.parametrize("ending", [False, True])
+def test_head_dim16_crop768_sampled(ta, ending):
+    w = si.WORKLOADS["crop768_h8d16"]
+    check_sampled(ta, si.make_workload("crop768_h8d16"), ending, sample_rows(w.N),
+                  sample_dbias(w.N, w.H), "crop768_h8d16")
 
 
 def test_fully_masked_rows_and_keys(ta):

@@ -7,7 +7,7 @@ over the five runs.  Here the forward outputs (o, its residual, lse) are compare
 too.  The cases are small (N <= 128) and drawn from a fixed seed over batch size,
 N, head count, key-mask kind (none given as no mask at all, a ones mask, padded
 keys, random keys), orientation, compensated or uncompensated D, softmax scale,
-bf16 or fp32 dbias and bf16 or fp32 saved residual.
+bf16 or fp32 dbias, bf16 or fp32 saved residual and head dimension 16 or 32.
 """
 import sys
 
@@ -50,11 +50,12 @@ def test_reproducibility_sweep(ta):
         scale = None if rng.integers(0, 2) else float(rng.uniform(0.1, 0.4))
         dbias_fp32 = bool(rng.integers(0, 2))
         residual = "fp32" if rng.integers(0, 2) else "bf16"
-        inp = si.make_problem(B, N, H, 32, 20000 + case, mask="none" if kind == "absent" else kind)
+        D = int(rng.choice([16, 32]))
+        inp = si.make_problem(B, N, H, D, 20000 + case, mask="none" if kind == "absent" else kind)
         g = {k: v.to(dev) for k, v in inp.items()}
         mask = None if kind == "absent" else g["mask"]
         if case % 100 == 0:
-            print(f"[reproducibility] case {case}: B={B} N={N} H={H} mask={kind} ending={ending} "
+            print(f"[reproducibility] case {case}: B={B} N={N} H={H} D={D} mask={kind} ending={ending} "
                   f"compensated={compensated} scale={scale} dbias_fp32={dbias_fp32} "
                   f"residual={residual}", flush=True)
             sys.stdout.flush()

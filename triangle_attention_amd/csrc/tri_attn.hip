@@ -179,7 +179,10 @@ struct FwdTile {
   unsigned m;
 };
 
-template <bool MASKED, bool RES32>
+// DIN: the head dimension of the caller's tensors (32, or 16: channels 16..31 are
+// then zero in every tile and never stored; the second contraction slice of q.k is
+// skipped)
+template <bool MASKED, bool RES32, int DIN>
 __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
   extern __shared__ float4 smem_f4[];
   _Float16 *bias_s = (_Float16 *)smem_f4;
@@ -237,24 +240,28 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
   const long long mk = a.mask ? a.f.mK : 0;
   typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
   for (int r = r0 + wave; r < r1;) {
-    const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
+    const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * DIN;
     bf16x8 qB[2][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const uint16_t *qp = a.q + base + (long long)(j0 + (two ? 32 * s : 0) + jl) * a.f.sQ;
       qB[s][0] = as_bf16x8(ld16(qp + 8 * hh));
-      qB[s][1] = as_bf16x8(ld16(qp + 16 + 8 * hh));
+      qB[s][1] = DIN == 32 ? as_bf16x8(ld16(qp + 16 + 8 * hh)) : as_bf16x8((u32x4){0u, 0u, 0u, 0u});
     }
     const uint8_t *mrow = a.mask ? a.mask + (long long)b * a.f.mB + (long long)r * a.f.mR : &kMaskAllValid;
 
     // K and V of the row through buffer descriptors: the lane's byte offset is fixed
     // for the row and tile kt is a scalar byte offset away, so no per-tile address
-    // math.  A row spans N * sQ * 2 < 2^32 bytes (N <= 768, H <= 64, D = 32), so the
-    // offsets are unsigned 32-bit values.
+    // math.  A row spans N * sQ * 2 < 2^32 bytes (N <= 768, H <= 64, D <= 32), so the
+    // offsets are unsigned 32-bit values.  With D = 16 a row spans less than 2^31
+    // bytes and the lanes of channels 16..31 get the offset 2^31, past the row (with
+    // any tile's scalar offset still below 2^32): out-of-range buffer loads return
+    // zeros.
     const unsigned row_bytes = (unsigned)((long long)N * a.f.sQ * 2);
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + base), (short)0, row_bytes, kBufferWord3);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + base), (short)0, row_bytes, kBufferWord3);
-    const unsigned lane_off = (unsigned)(((long long)vkey * a.f.sQ + vpart * 8) * 2);
+    const unsigned lane_off = (DIN == 16 && vpart >= 2) ? 0x80000000u
+                                                        : (unsigned)(((long long)vkey * a.f.sQ + vpart * 8) * 2);
     const unsigned tstep_b = (unsigned)(32 * a.f.sQ * 2), vhalf_b = (unsigned)(16 * a.f.sQ * 2);
     const uint8_t *ml = mrow + (long long)jl * mk;
     const long long mstep = 32 * mk;
@@ -277,7 +284,7 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
     // q.k of query half s against the staged key tile (masked keys at -inf)
     auto qk = [&](int s, unsigned valid) -> f32x16 {
       f32x16 acc = mfma(*(const bf16x8 *)(kbuf + tile_off(jl, 8 * hh)), qB[s][0], (f32x16){});
-      acc = mfma(*(const bf16x8 *)(kbuf + tile_off(jl, 16 + 8 * hh)), qB[s][1], acc);
+      if constexpr (DIN == 32) acc = mfma(*(const bf16x8 *)(kbuf + tile_off(jl, 16 + 8 * hh)), qB[s][1], acc);
       if (__builtin_expect(valid != 0xffffffffu, 0)) {  // a partly masked tile
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -426,7 +433,7 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
           for (int k = 0; k < 4; ++k) {
             const int row = 8 * k + (ln >> 3), c16 = ln & 7;
             const long long off = base + (long long)(j0 + 32 * s + row) * a.f.sQ + 4 * c16;
-            *(f32x4 *)((float *)a.res + off) = *(const f32x4 *)(r32t + r32_off(row, c16));
+            if (DIN == 32 || c16 < 4) *(f32x4 *)((float *)a.res + off) = *(const f32x4 *)(r32t + r32_off(row, c16));
           }
         }
         __asm__ volatile("" : "+v"(inv));
@@ -442,8 +449,10 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
       for (int k = 0; k < 2; ++k) {
         const int row = (lane >> 2) + 16 * k, chunk = lane & 3;
         const long long off = base + (long long)(j0 + 32 * s + row) * a.f.sQ + 8 * chunk;
-        *(u32x4 *)(a.o + off) = *(const u32x4 *)(ot + o_off(row, chunk));
-        if (!RES32 && a.res) *(u32x4 *)((uint16_t *)a.res + off) = *(const u32x4 *)(rt + o_off(row, chunk));
+        if (DIN == 32 || chunk < 2) {
+          *(u32x4 *)(a.o + off) = *(const u32x4 *)(ot + o_off(row, chunk));
+          if (!RES32 && a.res) *(u32x4 *)((uint16_t *)a.res + off) = *(const u32x4 *)(rt + o_off(row, chunk));
+        }
       }
       if (hh == 0) {
         // lse = ln(sum exp(logit)) = ln 2 * (m + log2(sum p))
@@ -470,17 +479,18 @@ struct PrepArgs {
   const float *lse;
   float *stats;  // [B][N][H][2][N]: -lse/alpha, then -D
   Frame f;
-  int B, N, H;
+  int B, N, H, D;
   float inv_alpha;
 };
 
 // One thread per (b, r, q, h), heads fastest so that a wave reads whole
 // 256-byte (position, all heads) segments.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
-  // four lanes per (b, position, h): lane j takes channels 8j .. 8j + 7.  Groups run
-  // in the caller's memory order (b, first pair axis, second pair axis, h), so that the
-  // lanes of a wave read contiguous runs of o, dO and the residual in both
-  // orientations; the attended frame's row and query follow from the strides.
+  // four lanes per (b, position, h): lane j takes channels 8j .. 8j + 7 (with D = 16
+  // lanes 2 and 3 hold none and add zero).  Groups run in the caller's memory order
+  // (b, first pair axis, second pair axis, h), so that the lanes of a wave read
+  // contiguous runs of o, dO and the residual in both orientations; the attended
+  // frame's row and query follow from the strides.
   const long long total = (long long)a.B * a.N * a.N * a.H;
   const long long idx = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 2;
   const int j = threadIdx.x & 3;
@@ -493,17 +503,21 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
   const int b = (int)(t / a.N);
   const bool starting = a.f.sR > a.f.sQ;  // rows along the first pair axis
   const int r = starting ? p1 : p2, q = starting ? p2 : p1;
-  const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)q * a.f.sQ + h * HD + 8 * j;
-  const u32x4 gw = ld16(a.d_o + base), ow = ld16(a.o + base);
+  const bool has = 8 * j < a.D;
+  const long long base =
+      (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)q * a.f.sQ + h * a.D + 8 * (has ? j : 0);
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const u32x4 gw = has ? ld16(a.d_o + base) : zero, ow = has ? ld16(a.o + base) : zero;
   // the residual of channels 8j + 2w, 8j + 2w + 1 as fp32
   float rf[4][2];
   if (a.res && a.res_fp32) {
-    const f32x4 x0 = *(const f32x4 *)((const float *)a.res + base);
-    const f32x4 x1 = *(const f32x4 *)((const float *)a.res + base + 4);
+    const f32x4 fz = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 x0 = has ? *(const f32x4 *)((const float *)a.res + base) : fz;
+    const f32x4 x1 = has ? *(const f32x4 *)((const float *)a.res + base + 4) : fz;
     rf[0][0] = x0[0]; rf[0][1] = x0[1]; rf[1][0] = x0[2]; rf[1][1] = x0[3];
     rf[2][0] = x1[0]; rf[2][1] = x1[1]; rf[3][0] = x1[2]; rf[3][1] = x1[3];
   } else {
-    const u32x4 rw = a.res ? ld16((const uint16_t *)a.res + base) : (u32x4){0u, 0u, 0u, 0u};
+    const u32x4 rw = (a.res && has) ? ld16((const uint16_t *)a.res + base) : zero;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       rf[w][0] = bf_lo(rw[w]);
@@ -598,7 +612,10 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int JT, bool MASKED>
+// DIN: the head dimension of the caller's tensors (32, or 16: channels 16..31 of the
+// tiles are zero, the second contraction slice of the score and dP products is
+// skipped, and only channels 0..15 of dK, dV and the dQ partials are stored)
+template <int JT, bool MASKED, int DIN>
 __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) {
   constexpr int NMAX = 32 * BWD_WAVES * JT;
   constexpr int BSTR = NMAX + 4;  // fp16 row stride of the bias tile: conflict-free 8-byte reads
@@ -638,7 +655,7 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
 
   // row r of head h of batch b: q, k, v, dO (element offset) and the statistics row
   auto rowbase = [&](int r) -> long long {
-    return (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * HD;
+    return (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * DIN;
   };
   auto stats_of = [&](int r) -> const float * {
     return a.stats + (((long long)b * N + r) * a.H + h) * 2 * N;
@@ -646,9 +663,11 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
   // keys and values of the block: thread tid carries 16 bytes of each (key tid/4, part tid%4)
   auto load_kv = [&](int r, u32x4 &kw, u32x4 &vw) {
     const int key = min(k0 + (tid >> 2), N - 1);
-    const long long off = rowbase(r) + (long long)key * a.f.sQ + (tid & 3) * 8;
+    const int part = DIN == 32 ? (tid & 3) : (tid & 1);  // D = 16: parts 2, 3 are zero
+    const long long off = rowbase(r) + (long long)key * a.f.sQ + part * 8;
     kw = ld16(a.k + off);
     vw = ld16(a.v + off);
+    if (DIN == 16 && (tid & 2)) kw = vw = (u32x4){0u, 0u, 0u, 0u};
   };
   // masked variant: thread tid fetches the mask byte of key k0 + tid % 64 (clamped at
   // a ragged end, where the absent tile's keys are masked anyway) with the keys and
@@ -688,10 +707,11 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
   };
   auto load_qtile = [&](int r, int jt) {
     const long long off = rowbase(r) + (long long)(jt * 32 + ll) * a.f.sQ + 8 * hh;
+    const u32x4 zero = {0u, 0u, 0u, 0u};  // channels 16..31 when D = 16
     tq0 = ld16(a.q + off);
-    tq1 = ld16(a.q + off + 16);
+    tq1 = DIN == 32 ? ld16(a.q + off + 16) : zero;
     td0 = ld16(a.d_o + off);
-    td1 = ld16(a.d_o + off + 16);
+    td1 = DIN == 32 ? ld16(a.d_o + off + 16) : zero;
     const float *sp = stats_of(r) + jt * 32 + ll;
     tl = sp[0];
     tdl = sp[N];
@@ -739,7 +759,7 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) dbias[jj][kt] = (f32x16){};
 
-  const long long E = (long long)a.B * N * N * a.H * HD;
+  const long long E = (long long)a.B * N * N * a.H * DIN;
   uint16_t *dq_part = a.dq_part + (long long)kb * E;
 
   // prologue: the first row's keys, values, key mask and first query tile
@@ -807,10 +827,10 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
       auto products = [&](const KOps &o, f32x16 &sv, f32x16 &dp) {
         sv = mfma(lA, ones3, (f32x16){});  // -lse/alpha
         sv = mfma(qA0, o.k0, sv);
-        sv = mfma(qA1, o.k1, sv);           // q.k - lse/alpha
+        if constexpr (DIN == 32) sv = mfma(qA1, o.k1, sv);  // q.k - lse/alpha
         dp = mfma(dlA, ones3, (f32x16){});  // -D
         dp = mfma(dA0, o.v0, dp);
-        dp = mfma(dA1, o.v1, dp);           // dP - D
+        if constexpr (DIN == 32) dp = mfma(dA1, o.v1, dp);  // dP - D
       };
       // probabilities and dS of one key tile, their dV, dK, dbias products, and dS^T
       // into LDS for the dQ product
@@ -869,8 +889,9 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
       // contiguous 2 KB of the partial.  Before the swaps, lane l < 32 holds channels
       // 8g..8g+3 of group g and lane l + 32 channels 8g+4..8g+7 of query ll; swapping
       // groups 0 with 1 and 2 with 3 across the halves leaves lane l with channels 0-7
-      // and 16-23 and lane l + 32 with channels 8-15 and 24-31.
-      uint16_t *qout = dq_part + ((((long long)b * N + r) * a.H + h) * N + j0 + ll) * HD + 8 * hh;
+      // and 16-23 and lane l + 32 with channels 8-15 and 24-31 (with D = 16 only the
+      // first run of each lane is stored: the 32-byte partial of the query).
+      uint16_t *qout = dq_part + ((((long long)b * N + r) * a.H + h) * N + j0 + ll) * DIN + 8 * hh;
       {
         unsigned w[4][2];
 #pragma unroll
@@ -887,7 +908,7 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
             w[g + 1][e] = sw[1];
           }
         *(u32x4 *)qout = (u32x4){w[0][0], w[0][1], w[1][0], w[1][1]};
-        *(u32x4 *)(qout + 16) = (u32x4){w[2][0], w[2][1], w[3][0], w[3][1]};
+        if constexpr (DIN == 32) *(u32x4 *)(qout + 16) = (u32x4){w[2][0], w[2][1], w[3][0], w[3][1]};
       }
     }
 
@@ -915,7 +936,7 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
       {
         // thread tid: channels 8 (tid % 4) .. + 7 of key row tid / 4
         const int kr = tid >> 2, c = 8 * (tid & 3);
-        if (k0 + kr < N) {
+        if (k0 + kr < N && c < DIN) {
           f32x4 s0 = *(const f32x4 *)(red_ptr(0, kr) + c);
           f32x4 s1 = *(const f32x4 *)(red_ptr(0, kr) + c + 4);
 #pragma unroll
@@ -962,27 +983,29 @@ struct ReduceArgs {
   uint16_t *dq;
   void *dbias;
   Frame f;
-  int B, N, H, T, C, dbias_fp32;
+  int B, N, H, D, T, C, dbias_fp32;
   float alpha;
 };
 
 // one thread per 8 channels: the bf16 partials of the key blocks summed in fp32 in
 // block order, times alpha, rounded to bf16 in the caller's frame
 __global__ __launch_bounds__(256) void reduce_dq_kernel(ReduceArgs a) {
-  const long long E = (long long)a.B * a.N * a.N * a.H * HD;
+  // partials and output hold D channels (32 or 16)
+  const long long E = (long long)a.B * a.N * a.N * a.H * a.D;
   // thread -> 8 channels of output element (b, r, q, h, c), heads inside positions, so
   // that a wave writes whole multi-head position segments
   const long long e = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (e >= E) return;
-  const int c = (int)(e % HD);
-  long long u = e / HD;
+  const int dsh = a.D == 32 ? 5 : 4;  // D is 32 or 16
+  const int c = (int)(e & (a.D - 1));
+  long long u = e >> dsh;
   const int h = (int)(u % a.H);
   u /= a.H;
   const int q = (int)(u % a.N);
   u /= a.N;
   const int r = (int)(u % a.N);
   const int b = (int)(u / a.N);
-  const long long pe = ((((long long)b * a.N + r) * a.H + h) * a.N + q) * HD + c;  // partial element
+  const long long pe = ((((long long)b * a.N + r) * a.H + h) * a.N + q) * a.D + c;  // partial element
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int t = 0; t < a.T; ++t) {
     // each partial is read once: non-temporal loads keep them from displacing other lines
@@ -993,7 +1016,7 @@ __global__ __launch_bounds__(256) void reduce_dq_kernel(ReduceArgs a) {
       s[2 * i + 1] += bf_hi(w[i]);
     }
   }
-  const long long off = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)q * a.f.sQ + h * HD + c;
+  const long long off = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)q * a.f.sQ + h * a.D + c;
   *(u32x4 *)(a.dq + off) = (u32x4){pack_bf16(s[0] * a.alpha, s[1] * a.alpha), pack_bf16(s[2] * a.alpha, s[3] * a.alpha),
                                    pack_bf16(s[4] * a.alpha, s[5] * a.alpha), pack_bf16(s[6] * a.alpha, s[7] * a.alpha)};
 }
@@ -1032,24 +1055,24 @@ tri_attn_status check_problem(const tri_attn_problem *p) {
   if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale)) return TRI_ATTN_ERROR_INVALID_VALUE;
   if (p->flags & ~(TRI_ATTN_FLAG_ENDING_NODE | TRI_ATTN_FLAG_DBIAS_FP32 | TRI_ATTN_FLAG_RESIDUAL_BF16))
     return TRI_ATTN_ERROR_NOT_SUPPORTED;
-  if (p->D != HD || p->N % 32 != 0 || p->N > kMaxN || p->H > kMaxH) return TRI_ATTN_ERROR_NOT_SUPPORTED;
+  if ((p->D != HD && p->D != 16) || p->N % 32 != 0 || p->N > kMaxN || p->H > kMaxH) return TRI_ATTN_ERROR_NOT_SUPPORTED;
   if (p->B * p->N * p->N * p->H * p->D > (int64_t)1 << 40) return TRI_ATTN_ERROR_NOT_SUPPORTED;
   return TRI_ATTN_SUCCESS;
 }
 
 Frame make_frame(const tri_attn_problem *p) {
   Frame f;
-  const long long N = p->N, H = p->H;
-  f.sB = N * N * H * HD;
+  const long long N = p->N, H = p->H, D = p->D;
+  f.sB = N * N * H * D;
   f.mB = N * N;
   if (p->flags & TRI_ATTN_FLAG_ENDING_NODE) {
-    f.sR = H * HD;
-    f.sQ = N * H * HD;
+    f.sR = H * D;
+    f.sQ = N * H * D;
     f.mR = 1;
     f.mK = N;
   } else {
-    f.sR = N * H * HD;
-    f.sQ = H * HD;
+    f.sR = N * H * D;
+    f.sQ = H * D;
     f.mR = N;
     f.mK = 1;
   }
@@ -1085,26 +1108,27 @@ BwdPlan plan_bwd(const tri_attn_problem *p) {
   const size_t B = p->B, NN = (size_t)N * N, H = p->H;
   pl.off_stats = 0;
   pl.off_dq = align256(B * N * H * 2 * N * 4);
-  pl.off_db = pl.off_dq + align256((size_t)pl.T * B * NN * H * HD * 2);
+  pl.off_db = pl.off_dq + align256((size_t)pl.T * B * NN * H * p->D * 2);
   pl.total = pl.off_db + align256((size_t)pl.C * B * H * NN * 4);
   return pl;
 }
 
 template <int JT>
-hipError_t launch_main(const BwdArgs &args, int grid, size_t lds, hipStream_t stream) {
-  auto kern = args.mask ? bwd_main_kernel<JT, true> : bwd_main_kernel<JT, false>;
+hipError_t launch_main(const BwdArgs &args, int D, int grid, size_t lds, hipStream_t stream) {
+  auto kern = D == 32 ? (args.mask ? bwd_main_kernel<JT, true, 32> : bwd_main_kernel<JT, false, 32>)
+                      : (args.mask ? bwd_main_kernel<JT, true, 16> : bwd_main_kernel<JT, false, 16>);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(BWD_WAVES * 64), lds, stream, args);
   return hipGetLastError();
 }
 
-hipError_t dispatch_main(int JT, const BwdArgs &args, int grid, size_t lds, hipStream_t stream) {
+hipError_t dispatch_main(int JT, const BwdArgs &args, int D, int grid, size_t lds, hipStream_t stream) {
   switch (JT) {
-    case 1: return launch_main<1>(args, grid, lds, stream);
-    case 2: return launch_main<2>(args, grid, lds, stream);
-    case 3: return launch_main<3>(args, grid, lds, stream);
-    case 4: return launch_main<4>(args, grid, lds, stream);
-    case 5: return launch_main<5>(args, grid, lds, stream);
-    case 6: return launch_main<6>(args, grid, lds, stream);
+    case 1: return launch_main<1>(args, D, grid, lds, stream);
+    case 2: return launch_main<2>(args, D, grid, lds, stream);
+    case 3: return launch_main<3>(args, D, grid, lds, stream);
+    case 4: return launch_main<4>(args, D, grid, lds, stream);
+    case 5: return launch_main<5>(args, D, grid, lds, stream);
+    case 6: return launch_main<6>(args, D, grid, lds, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1177,8 +1201,13 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
   a.n_chunks = (a.N + a.rows_per_chunk - 1) / a.rows_per_chunk;
   const size_t lds = (size_t)FWD_BJ * a.bstride * 2 + (size_t)FWD_WAVES * 2 * 32 * HD * 2;
   const bool res32 = (p.flags & TRI_ATTN_FLAG_RESIDUAL_BF16) == 0;
-  void (*kern)(FwdArgs) = mask ? (res32 ? fwd_kernel<true, true> : fwd_kernel<true, false>)
-                               : (res32 ? fwd_kernel<false, true> : fwd_kernel<false, false>);
+  void (*kern)(FwdArgs);
+  if (p.D == 32)
+    kern = mask ? (res32 ? fwd_kernel<true, true, 32> : fwd_kernel<true, false, 32>)
+                : (res32 ? fwd_kernel<false, true, 32> : fwd_kernel<false, false, 32>);
+  else
+    kern = mask ? (res32 ? fwd_kernel<true, true, 16> : fwd_kernel<true, false, 16>)
+                : (res32 ? fwd_kernel<false, true, 16> : fwd_kernel<false, false, 16>);
   if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
       hipSuccess)
     return TRI_ATTN_ERROR_LAUNCH_FAILED;
@@ -1248,6 +1277,7 @@ static tri_attn_status bwd_run(const tri_attn_problem *problem, const void *q, c
   pa.B = (int)p.B;
   pa.N = (int)p.N;
   pa.H = (int)p.H;
+  pa.D = (int)p.D;
   auto mark = [&](int i) { return !marks[i] || hipEventRecord(marks[i], stream) == hipSuccess; };
   if (!mark(0)) return TRI_ATTN_ERROR_LAUNCH_FAILED;
   const long long nrows = (long long)p.B * p.N * p.N * p.H;
@@ -1277,7 +1307,7 @@ static tri_attn_status bwd_run(const tri_attn_problem *problem, const void *q, c
   ba.c1 = alpha * kLog2e;
   const int grid = ba.B * ba.H * pl.T * pl.C;
   if (!mark(1)) return TRI_ATTN_ERROR_LAUNCH_FAILED;
-  const hipError_t e = dispatch_main(pl.JT, ba, grid, pl.lds_bytes, stream);
+  const hipError_t e = dispatch_main(pl.JT, ba, (int)p.D, grid, pl.lds_bytes, stream);
   if (e != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
   if (!mark(2)) return TRI_ATTN_ERROR_LAUNCH_FAILED;
 
@@ -1290,6 +1320,7 @@ static tri_attn_status bwd_run(const tri_attn_problem *problem, const void *q, c
   ra.B = (int)p.B;
   ra.N = (int)p.N;
   ra.H = (int)p.H;
+  ra.D = (int)p.D;
   ra.T = pl.T;
   ra.C = pl.C;
   ra.dbias_fp32 = (p.flags & TRI_ATTN_FLAG_DBIAS_FP32) ? 1 : 0;
