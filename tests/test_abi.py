@@ -170,3 +170,15 @@ def test_mfma_probe_library_validates_arguments():
     assert probe.mfma_probe_launch(None, 4, 10, None) == 1
     assert probe.mfma_probe_launch(ctypes.c_void_p(ADDR), 0, 10, None) == 1
     assert probe.mfma_probe_launch(ctypes.c_void_p(ADDR), 4, 0, None) == 1
+
+
+def test_head_dim16_is_accepted_with_a_smaller_workspace(lib):
+    """D = 16 passes host validation; its dQ partials hold 16 channels, so the
+    workspace is smaller than at D = 32 (same N, H)."""
+    w32 = lib.tri_attn_bwd_workspace_bytes(ctypes.byref(ta.make_problem(1, 256, 4, 32)))
+    w16 = lib.tri_attn_bwd_workspace_bytes(ctypes.byref(ta.make_problem(1, 256, 4, 16)))
+    assert 0 < w16 < w32
+    prob = ta.make_problem(1, 64, 4, 16)
+    ptrs = fake_ptrs(7)
+    ptrs[0] = None  # validation reaches the pointer checks: the size itself is accepted
+    assert call_fwd(lib, prob, ptrs) == INVALID
