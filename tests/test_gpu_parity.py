@@ -360,13 +360,15 @@ def test_custom_scale_and_fp32_dbias(ta):
     assert e32 <= e16
 
 
-def test_autograd_wrapper(ta):
-    inp = custom(1, 64, 2, 17, "pad32")
+@pytest.mark.parametrize("D,ending", [(32, False), (16, True)])
+def test_autograd_wrapper(ta, D, ending):
+    inp = custom(1, 64, 2, 17, "pad32", D=D)
     dev = torch.device("cuda:0")
     q, k, v, bias = (inp[n].to(dev).requires_grad_(True) for n in ("q", "k", "v", "bias"))
-    o = ta.tri_attn(q, k, v, bias, inp["mask"].to(dev))
+    o = ta.tri_attn(q, k, v, bias, inp["mask"].to(dev), ending=ending)
     o.backward(inp["do"].to(dev))
-    ref = oracle.forward_backward(inp["q"], inp["k"], inp["v"], inp["bias"], inp["mask"], inp["do"])
+    ref = oracle.forward_backward(inp["q"], inp["k"], inp["v"], inp["bias"], inp["mask"], inp["do"],
+                                  ending=ending)
     for t, n in ((q, "dq"), (k, "dk"), (v, "dv"), (bias, "dbias")):
         assert rel_rmse(to_np(t.grad), ref[n]) <= GRAD_REL_RMSE, n
 
