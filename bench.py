@@ -223,48 +223,28 @@ def cpu_baseline(inp, rows: int, dbias_rows: int):
     }
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="crop768")
-    ap.add_argument("--ending", action="store_true", help="ending-node orientation")
-    ap.add_argument("--residual", choices=("fp32", "bf16"), default="fp32",
-                    help="precision of the saved rounding residual of o")
-    ap.add_argument("--cpu-rows", type=int, default=256)
-    ap.add_argument("--cpu-dbias-rows", type=int, default=512)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--calib-copy", action="store_true",
-                    help="copy a 256 MiB device buffer once before the warmup (a known-size kernel "
-                         "that calibrates the rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
-                                   "supported (use --gpus 1)", "n_gpus": args.gpus}))
-        sys.exit(2)
-
+def run_workload(args, workload: str, ending: bool, with_cpu_baseline: bool) -> dict:
+    """Time fwd+bwd steps of one workload and return its JSON line as a dict."""
     import seeded_inputs as si
     import triangle_attention_amd as ta
 
-    w = si.WORKLOADS[args.workload]
+    w = si.WORKLOADS[workload]
     dev = torch.device("cuda:0")
     log(f"workload {w.name}: {w.description}")
     inp = si.make_workload(w.name)
     g = {k: v.to(dev) for k, v in inp.items()}
     mask = g["mask"] if w.mask != "none" else None
     ta.load_library()
-    ws = torch.empty(ta.bwd_workspace_bytes(w.B, w.N, w.H, w.D, ending=args.ending),
+    ws = torch.empty(ta.bwd_workspace_bytes(w.B, w.N, w.H, w.D, ending=ending),
                      dtype=torch.uint8, device=dev)
 
     def fwd():
-        return ta.tri_attn_fwd(g["q"], g["k"], g["v"], g["bias"], mask, ending=args.ending,
+        return ta.tri_attn_fwd(g["q"], g["k"], g["v"], g["bias"], mask, ending=ending,
                                residual=args.residual)
 
     def bwd(o, res, lse, events=None):
         return ta.tri_attn_bwd(g["q"], g["k"], g["v"], g["bias"], mask, o, res, lse, g["do"],
-                               ending=args.ending, workspace=ws, kernel_events=events)
+                               ending=ending, workspace=ws, kernel_events=events)
 
     def step(events=None):
         return bwd(*fwd(), events=events)
@@ -338,13 +318,13 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{w.name} ({w.description})", "B": w.B, "N": w.N, "H": w.H,
-                   "D": w.D, "orientation": "ending" if args.ending else "starting",
+                   "D": w.D, "orientation": "ending" if ending else "starting",
                    "residual": args.residual,
                    "mfma_peak_frac": round(value / MFMA_PEAK_BF16_TFLOPS, 4)},
         "roofline": {"kernel": "bwd_main_kernel", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name, args.ending, args.residual),
+                     "traffic": measured_traffic(w.name, ending, args.residual),
                      "avg_ms": round(main_ms, 4)},
         "phases": {"fwd_ms": quantiles(fwd_ms), "bwd_ms": quantiles(bwd_ms), "step_ms": quantiles(step_ms),
                    "bwd_kernels_ms": {n: quantiles(v) for n, v in kern.items()},
@@ -360,9 +340,44 @@ def main():
                                   "(four waves per SIMD, independent accumulators)",
                           "bwd_main_frac": round(achieved / probe, 4),
                           "step_frac": round(value / probe, 4)}
-    if not args.no_cpu_baseline:
+    if with_cpu_baseline:
         log("cpu baseline (oracle sample)")
         line["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows, args.cpu_dbias_rows)
+    return line
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="crop768")
+    ap.add_argument("--ending", action="store_true", help="ending-node orientation")
+    ap.add_argument("--residual", choices=("fp32", "bf16"), default="fp32",
+                    help="precision of the saved rounding residual of o")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-dbias-rows", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all", action="store_true",
+                    help="one JSON line per workload: crop384, crop640, crop768 starting and ending node")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="copy a 256 MiB device buffer once before the warmup (a known-size kernel "
+                         "that calibrates the rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU runs are not "
+                                   "supported (use --gpus 1)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    if args.all:
+        # one line per workload the reporting plan names: crops 384, 640 and 768, the
+        # last in both orientations; the oracle baseline with the crop768 line only
+        for wl, ending in (("crop384", False), ("crop640", False), ("crop768", False), ("crop768", True)):
+            line = run_workload(args, wl, ending, not args.no_cpu_baseline and wl == "crop768" and not ending)
+            print(json.dumps(line), flush=True)
+        return
+    line = run_workload(args, args.workload, args.ending, not args.no_cpu_baseline)
     print(json.dumps(line), flush=True)
 
 
