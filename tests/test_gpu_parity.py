@@ -206,14 +206,15 @@ def test_bf16_residual(ta, ending):
     assert torch.equal(out32["dv"].view(torch.int16), out16["dv"].view(torch.int16))
 
 
-@pytest.mark.parametrize("name,reps", [("tiny64", 3), ("pad256", 3), ("crop640", 3), ("crop768_h8d16", 3),
-                                       ("crop768", 5)])
-def test_bitwise_determinism(ta, name, reps):
+@pytest.mark.parametrize("name,reps,ending", [("tiny64", 3, False), ("pad256", 3, False),
+                                              ("crop640", 3, False), ("crop768_h8d16", 3, False),
+                                              ("crop768", 5, False), ("crop768", 5, True)])
+def test_bitwise_determinism(ta, name, reps, ending):
     inp = si.make_workload(name)
-    say(f"[determinism] {name} x{reps}")
-    first = run_gpu(ta, inp)
+    say(f"[determinism] {name} ending={ending} x{reps}")
+    first = run_gpu(ta, inp, ending=ending)
     for _ in range(reps - 1):
-        again = run_gpu(ta, inp)
+        again = run_gpu(ta, inp, ending=ending)
         for n in ("o", "res", "lse", "dq", "dk", "dv", "dbias"):
             a, b = first[n], again[n]
             assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
