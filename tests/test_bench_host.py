@@ -62,3 +62,22 @@ def test_bias_dbias_bytes_at_crop768():
     assert d["bias_staged_bytes"] == 10 * 2 * nb        # five row chunks in each pass
     assert d["dbias_partial_bytes"] == 5 * 4 * nb
     assert d["dbias_reduction_bytes"] == 5 * 4 * nb + 2 * nb
+
+
+@pytest.mark.parametrize("B,N,H,D", [(1, 768, 4, 32), (1, 640, 4, 32), (1, 384, 4, 32), (2, 352, 3, 32),
+                                     (1, 768, 8, 16), (3, 128, 64, 32), (1, 96, 1, 16)])
+def test_row_chunks_match_the_library_plan(B, N, H, D):
+    """The library's backward workspace is the statistics, the dQ partials (one per
+    64-key block) and one fp32 dbias partial per row chunk, each 256-byte aligned:
+    rebuilt from bench.row_chunks it must equal tri_attn_bwd_workspace_bytes."""
+    import ctypes
+    import triangle_attention_amd as ta
+    lib = ta.load_library()
+    got = lib.tri_attn_bwd_workspace_bytes(ctypes.byref(ta.make_problem(B, N, H, D)))
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+    T = -(-N // 64)
+    C = bench.row_chunks(B * H * T, N)
+    want = a256(B * N * H * 2 * N * 4) + a256(T * B * N * N * H * D * 2) + a256(C * B * H * N * N * 4)
+    assert got == want
