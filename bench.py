@@ -15,10 +15,9 @@ The JSON line also carries
                  per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary in
                  profiles/ (calibrated against a plain device copy), or null when
                  that summary was taken on a different kernel source or build flags;
-  cpu_baseline : the FP64 oracle timed on this host on a bounded sample of the
-                 same workload (sampled attention rows and bias-gradient rows),
-                 scaled to the whole workload, with the host's thread count and
-                 CPU model;
+  cpu_baseline : the FP64 oracle run on the whole crop768 problem on this host's
+                 cores (one timed forward and backward, ~40 s on 16 threads), with
+                 the thread count and CPU model;
   mfma_probe   : the sustained bf16 matrix-core rate this device reaches with
                  independent back-to-back 32x32x16 products, and the backward main
                  kernel's and the whole step's fractions of it;
@@ -28,7 +27,17 @@ The JSON line also carries
                  between them), the algorithmic bytes of one step and the rate they
                  imply, the pair-bias and bias-gradient bytes of a step with the
                  measured rate of the dbias reduction, and whether the outputs of
-                 the first and last timed steps are bitwise identical.
+                 the first and last timed steps are bitwise identical;
+  workloads    : the other reported crop sizes (384 and 640, and 768 in the ending
+                 node orientation), each timed over fewer steps: median time per
+                 step, forward and backward, TFLOP/s and fraction of the MFMA peak;
+  accuracy     : the crop768 outputs of the last timed step against the FP64 oracle
+                 run on the whole problem (forward max-abs and rel-RMSE, lse max-abs,
+                 and the rel-RMSE of each gradient with the residual-compensated
+                 correction next to the uncompensated one, the latter from one more
+                 backward without the residual), and the same gradient comparison at
+                 crop640 (peaked rows) on sampled rows.
+The whole-problem oracle run is the cpu_baseline's timed work.
 """
 from __future__ import annotations
 
@@ -189,48 +198,96 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(inp, rows: int, dbias_rows: int):
-    """Oracle time on `rows` attention rows (o, lse, dq, dk, dv) plus `dbias_rows`
-    bias-gradient rows, scaled to the full problem."""
+def rel_rmse(x, ref) -> float:
     import numpy as np
+    den = float(np.linalg.norm(ref))
+    return float(np.linalg.norm(np.asarray(x, np.float64) - ref) / (den if den > 0 else 1.0))
+
+
+def to_np(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def oracle_whole(inp):
+    """The FP64 oracle on the whole problem (forward, then every row's gradients, then
+    every pair-bias-gradient row), timed on this host: (reference dict, cpu_baseline)."""
     import oracle
     import seeded_inputs as si
 
     B, N, _, H, D = inp["q"].shape
     threads = len(os.sched_getaffinity(0))
     os.environ.setdefault("OMP_NUM_THREADS", str(threads))
-    p = oracle.Problem(inp["q"], inp["k"], inp["v"], inp["bias"], inp["mask"], inp["do"])
-    rng = np.random.default_rng(0)
-    sel_rows = [(0, int(r)) for r in rng.choice(N, size=min(rows, N), replace=False)]
-    sel_db = [(0, int(h), int(j)) for h, j in zip(rng.integers(0, H, dbias_rows),
-                                                  rng.integers(0, N, dbias_rows))]
     t0 = time.perf_counter()
-    p.rows(sel_rows)
-    t1 = time.perf_counter()
-    p.dbias(sel_db)
-    t2 = time.perf_counter()
-    t_full = (t1 - t0) * (B * N / len(sel_rows)) + (t2 - t1) * (B * H * N / len(sel_db))
+    ref = oracle.forward_backward(inp["q"], inp["k"], inp["v"], inp["bias"], inp["mask"], inp["do"])
+    t = time.perf_counter() - t0
     flops = si.flop_count(B, N, H, D, inp["mask"])
-    return {
-        "value": flops / t_full / 1e12,
+    base = {
+        "value": flops / t / 1e12,
         "unit": "TFLOP/s",
         "cores": int(os.environ.get("OMP_NUM_THREADS", threads)),
         "kind": "oracle",
         "cpu": cpu_model(),
-        "sample": (f"{len(sel_rows)} of {B * N} attention rows (forward and q/k/v gradients, "
-                   f"{t1 - t0:.1f} s) and {len(sel_db)} of {B * H * N} bias-gradient rows "
-                   f"({t2 - t1:.1f} s), scaled to the whole workload; est. {t_full:.0f} s"),
+        "sample": (f"the whole workload: all {B * N} attention rows (forward, lse and q/k/v gradients) "
+                   f"and all {B * H * N} pair-bias-gradient rows, {t:.1f} s"),
     }
+    return ref, base
 
 
-def run_workload(args, workload: str, ending: bool, with_cpu_baseline: bool) -> dict:
-    """Time fwd+bwd steps of one workload and return its JSON line as a dict."""
+def accuracy_whole(out, unc, ref) -> dict:
+    """Forward errors and per-gradient rel-RMSE (compensated / uncompensated) of one
+    step's outputs against the whole-problem oracle."""
+    import numpy as np
+    o = to_np(out["o"])
+    lse = to_np(out["lse"])
+    fin = np.isfinite(ref["lse"])
+    acc = {"reference": "FP64 oracle, whole problem",
+           "o_max_abs": float(np.max(np.abs(o - ref["o"]))),
+           "o_rel_rmse": rel_rmse(o, ref["o"]),
+           "lse_max_abs": float(np.max(np.abs(lse[fin] - ref["lse"][fin]))) if fin.any() else 0.0,
+           "grad_rel_rmse": {}}
+    del o, lse
+    for n in ("dq", "dk", "dv", "dbias"):
+        acc["grad_rel_rmse"][n] = {"compensated": rel_rmse(to_np(out[n]), ref[n]),
+                                   "uncompensated": rel_rmse(to_np(unc[n]), ref[n])}
+    acc["bounds"] = {"o_max_abs": 2e-2, "o_rel_rmse": 1e-2, "grad_rel_rmse": 2e-2}
+    return acc
+
+
+def accuracy_sampled(out, unc, inp, rows: int, dbias_rows: int) -> dict:
+    """Per-gradient rel-RMSE, compensated and uncompensated, on `rows` sampled attention
+    rows and `dbias_rows` sampled pair-bias-gradient rows."""
+    import numpy as np
+    import oracle
+    B, N, _, H, D = inp["q"].shape
+    rng = np.random.default_rng(1)
+    sel_rows = sorted((0, int(r)) for r in rng.choice(N, size=min(rows, N), replace=False))
+    sel_db = sorted({(0, int(h), int(j)) for h, j in zip(rng.integers(0, H, dbias_rows),
+                                                         rng.integers(0, N, dbias_rows))})
+    p = oracle.Problem(inp["q"], inp["k"], inp["v"], inp["bias"], inp["mask"], inp["do"])
+    ref = p.rows(sel_rows)
+    ref["dbias"] = p.dbias(sel_db)
+
+    def pick(x, n):
+        if n == "dbias":
+            return np.stack([to_np(x[b, h, j]) for (b, h, j) in sel_db])
+        return np.stack([to_np(x[b, r]) for (b, r) in sel_rows])
+    acc = {"reference": f"FP64 oracle, {len(sel_rows)} sampled attention rows and {len(sel_db)} "
+                        "sampled pair-bias-gradient rows",
+           "o_rel_rmse": rel_rmse(pick(out["o"], "o"), ref["o"]), "grad_rel_rmse": {}}
+    for n in ("dq", "dk", "dv", "dbias"):
+        acc["grad_rel_rmse"][n] = {"compensated": rel_rmse(pick(out[n], n), ref[n]),
+                                   "uncompensated": rel_rmse(pick(unc[n], n), ref[n])}
+    return acc
+
+
+def time_workload(args, workload: str, ending: bool, steps: int, warmup: int, keep_outputs: bool = False):
+    """Time `steps` fwd+bwd steps of one workload after `warmup` untimed ones."""
     import seeded_inputs as si
     import triangle_attention_amd as ta
 
     w = si.WORKLOADS[workload]
     dev = torch.device("cuda:0")
-    log(f"workload {w.name}: {w.description}")
+    log(f"workload {w.name}{' (ending node)' if ending else ''}: {w.description}")
     inp = si.make_workload(w.name)
     g = {k: v.to(dev) for k, v in inp.items()}
     mask = g["mask"] if w.mask != "none" else None
@@ -246,56 +303,72 @@ def run_workload(args, workload: str, ending: bool, with_cpu_baseline: bool) -> 
         return ta.tri_attn_bwd(g["q"], g["k"], g["v"], g["bias"], mask, o, res, lse, g["do"],
                                ending=ending, workspace=ws, kernel_events=events)
 
-    def step(events=None):
-        return bwd(*fwd(), events=events)
-
     if args.calib_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    log(f"warmup {args.warmup}")
-    for _ in range(args.warmup):
-        step()
+    log(f"warmup {warmup}")
+    for _ in range(warmup):
+        bwd(*fwd())
     torch.cuda.synchronize()
 
     hip = HipEvents()
     # five events per step around the backward's four kernels (statistics, main, dQ
     # reduction, dbias reduction), recorded by the library on the launch stream
-    ev = [[hip.create() for _ in range(5)] for _ in range(args.steps)]
-    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    log(f"timing {args.steps} steps")
+    ev = [[hip.create() for _ in range(5)] for _ in range(steps)]
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    log(f"timing {steps} steps")
     outs = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         marks[i][0].record()
         fo = fwd()
         marks[i][1].record()
         grads = bwd(*fo, events=ev[i])
         marks[i][2].record()
-        if i == 0 or i == args.steps - 1:
+        if i == 0 or i == steps - 1:
             outs.append(fo + tuple(grads))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
+    ms = (t1 - t0) * 1e3 / steps
     kern = {name: [hip.elapsed_ms(e[i], e[i + 1]) for e in ev]
             for i, name in enumerate(("bwd_prep", "bwd_main", "reduce_dq", "reduce_dbias"))}
-    main_ms = statistics.mean(kern["bwd_main"])
     for e in ev:
         for x in e:
             hip.destroy(x)
-    log(f"{ms:.3f} ms/step, backward main kernel {main_ms:.3f} ms")
+    res = {
+        "w": w, "inp": inp, "ms": ms,
+        "fwd_ms": [m[0].elapsed_time(m[1]) for m in marks],
+        "bwd_ms": [m[1].elapsed_time(m[2]) for m in marks],
+        "step_ms": [m[0].elapsed_time(m[2]) for m in marks],
+        "kern": kern,
+        "same": all(torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
+                                y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32))
+                    for x, y in zip(outs[0], outs[-1])),
+        "flops": si.flop_count(w.B, w.N, w.H, w.D, inp["mask"]),
+    }
+    if keep_outputs:
+        o, r, lse, dq, dk, dv, db = outs[-1]
+        res["out"] = {"o": o, "res": r, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "dbias": db}
+        # one more backward without the residual: the uncompensated correction
+        udq, udk, udv, udb = bwd(o, None, lse)
+        torch.cuda.synchronize()
+        res["unc"] = {"dq": udq, "dk": udk, "dv": udv, "dbias": udb}
+    del g, ws, outs
+    log(f"{ms:.3f} ms/step, backward main kernel {statistics.mean(kern['bwd_main']):.3f} ms")
+    return res
 
-    fwd_ms = [m[0].elapsed_time(m[1]) for m in marks]
-    bwd_ms = [m[1].elapsed_time(m[2]) for m in marks]
-    step_ms = [m[0].elapsed_time(m[2]) for m in marks]
-    same = all(torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
-                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32))
-               for x, y in zip(outs[0], outs[-1]))
+
+def run_workload(args, workload: str, ending: bool, with_extras: bool) -> dict:
+    """Time fwd+bwd steps of one workload and return its JSON line as a dict."""
+    t = time_workload(args, workload, ending, args.steps, args.warmup, keep_outputs=with_extras)
+    w, kern, flops = t["w"], t["kern"], t["flops"]
+    ms = t["ms"]
+    main_ms = statistics.mean(kern["bwd_main"])
     nbytes = algorithmic_bytes(w.B, w.N, w.H, w.D, w.mask != "none", 4 if args.residual == "fp32" else 2)
-    flops = si.flop_count(w.B, w.N, w.H, w.D, inp["mask"])
     value = flops / (ms * 1e-3) / 1e12
     bwd_main_flops = flops * 10 / 14   # S, dP, dV, dK, dQ products of the backward
     achieved = bwd_main_flops / (main_ms * 1e-3) / 1e12
@@ -326,13 +399,38 @@ def run_workload(args, workload: str, ending: bool, with_cpu_baseline: bool) -> 
                      "frac": round(achieved / MFMA_PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(w.name, ending, args.residual),
                      "avg_ms": round(main_ms, 4)},
-        "phases": {"fwd_ms": quantiles(fwd_ms), "bwd_ms": quantiles(bwd_ms), "step_ms": quantiles(step_ms),
+        "phases": {"fwd_ms": quantiles(t["fwd_ms"]), "bwd_ms": quantiles(t["bwd_ms"]),
+                   "step_ms": quantiles(t["step_ms"]),
                    "bwd_kernels_ms": {n: quantiles(v) for n, v in kern.items()},
                    "bias_dbias": bd,
                    "algorithmic_bytes_per_step": nbytes,
-                   "algorithmic_GBps": round(nbytes / (statistics.median(step_ms) * 1e-3) / 1e9, 1),
-                   "deterministic_first_vs_last_step": bool(same)},
+                   "algorithmic_GBps": round(nbytes / (statistics.median(t["step_ms"]) * 1e-3) / 1e9, 1),
+                   "deterministic_first_vs_last_step": bool(t["same"])},
     }
+    if not with_extras:
+        return line
+    out, unc, inp = t.pop("out"), t.pop("unc"), t["inp"]
+    del t
+    # the other reported workloads: crop 384 and 640, and 768 in the ending orientation
+    others = {}
+    for wl, end in (("crop384", False), ("crop640", False), ("crop768", True)):
+        o = time_workload(args, wl, end, args.other_steps, min(args.warmup, 3),
+                          keep_outputs=(wl == "crop640"))
+        v = o["flops"] / (statistics.median(o["step_ms"]) * 1e-3) / 1e12
+        key = f"{wl}_ending" if end else wl
+        others[key] = {"ms_per_step": round(statistics.median(o["step_ms"]), 4),
+                       "fwd_ms": round(statistics.median(o["fwd_ms"]), 4),
+                       "bwd_ms": round(statistics.median(o["bwd_ms"]), 4),
+                       "bwd_main_ms": round(statistics.median(o["kern"]["bwd_main"]), 4),
+                       "TFLOPs": round(v, 2), "mfma_peak_frac": round(v / MFMA_PEAK_BF16_TFLOPS, 4),
+                       "steps": args.other_steps,
+                       "deterministic_first_vs_last_step": bool(o["same"])}
+        if wl == "crop640":
+            log("accuracy at crop640 (sampled oracle rows)")
+            acc640 = accuracy_sampled(o["out"], o["unc"], o["inp"], args.acc_rows, args.acc_dbias_rows)
+        del o
+        torch.cuda.empty_cache()
+    line["workloads"] = others
     log("matrix-core probe")
     probe = mfma_probe_tflops()
     line["mfma_probe"] = {"TFLOPs": round(probe, 1),
@@ -340,9 +438,13 @@ def run_workload(args, workload: str, ending: bool, with_cpu_baseline: bool) -> 
                                   "(four waves per SIMD, independent accumulators)",
                           "bwd_main_frac": round(achieved / probe, 4),
                           "step_frac": round(value / probe, 4)}
-    if with_cpu_baseline:
-        log("cpu baseline (oracle sample)")
-        line["cpu_baseline"] = cpu_baseline(inp, args.cpu_rows, args.cpu_dbias_rows)
+    if not args.no_cpu_baseline:
+        log("cpu baseline: the FP64 oracle on the whole workload")
+        ref, base = oracle_whole(inp)
+        line["cpu_baseline"] = base
+        log("accuracy against the oracle")
+        line["accuracy"] = accuracy_whole(out, unc, ref)
+        line["accuracy"]["crop640_sampled"] = acc640
     return line
 
 
@@ -355,9 +457,16 @@ def main():
     ap.add_argument("--ending", action="store_true", help="ending-node orientation")
     ap.add_argument("--residual", choices=("fp32", "bf16"), default="fp32",
                     help="precision of the saved rounding residual of o")
-    ap.add_argument("--cpu-rows", type=int, default=256)
-    ap.add_argument("--cpu-dbias-rows", type=int, default=512)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--other-steps", type=int, default=20,
+                    help="timed steps of each of the other reported workloads")
+    ap.add_argument("--acc-rows", type=int, default=64,
+                    help="sampled attention rows of the crop640 accuracy comparison")
+    ap.add_argument("--acc-dbias-rows", type=int, default=256,
+                    help="sampled pair-bias-gradient rows of the crop640 accuracy comparison")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the whole-problem oracle run (and with it the crop768 accuracy block)")
+    ap.add_argument("--quick", action="store_true",
+                    help="only the timed workload: no other workloads, probe, oracle or accuracy")
     ap.add_argument("--all", action="store_true",
                     help="one JSON line per workload: crop384, crop640, crop768 starting and ending node")
     ap.add_argument("--calib-copy", action="store_true",
@@ -374,10 +483,11 @@ def main():
         # one line per workload the reporting plan names: crops 384, 640 and 768, the
         # last in both orientations; the oracle baseline with the crop768 line only
         for wl, ending in (("crop384", False), ("crop640", False), ("crop768", False), ("crop768", True)):
-            line = run_workload(args, wl, ending, not args.no_cpu_baseline and wl == "crop768" and not ending)
+            line = run_workload(args, wl, ending, False)
             print(json.dumps(line), flush=True)
         return
-    line = run_workload(args, args.workload, args.ending, not args.no_cpu_baseline)
+    extras = not args.quick and args.workload == "crop768" and not args.ending
+    line = run_workload(args, args.workload, args.ending, extras)
     print(json.dumps(line), flush=True)
 
 

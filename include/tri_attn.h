@@ -22,12 +22,18 @@
  * Layouts (row-major, last index fastest):
  *   q, k, v, o, d_o, dq, dk, dv : bf16 [B, N, N, H, D]  (D contiguous)
  *   o_residual                  : fp32 [B, N, N, H, D] (bf16 with FLAG_RESIDUAL_BF16)
- *   bias, dbias                 : bf16 [B, H, N, N] (dbias fp32 with FLAG_DBIAS_FP32);
- *                                 bias values must lie in the fp16 range
- *                                 (|bias| <= 65504, or -inf): the kernels hold the
- *                                 bias as fp16, to which such a bf16 value converts
- *                                 exactly when |bias| >= 2^-14 (smaller magnitudes
- *                                 round to a multiple of 2^-24)
+ *   bias, dbias                 : bf16 [B, H, N, N] (dbias fp32 with FLAG_DBIAS_FP32).
+ *                                 The kernels hold the bias as fp16: a bf16 value
+ *                                 with 2^-14 <= |bias| <= 65504 converts exactly,
+ *                                 smaller magnitudes round to a multiple of 2^-24,
+ *                                 finite values beyond +-65504 saturate to +-65504
+ *                                 and +-inf stay infinite.  Saturation keeps the
+ *                                 exact softmax when such values mask keys (a key at
+ *                                 -65504 gets zero weight next to any in-range
+ *                                 logit) or shift every key of a query alike (a
+ *                                 -1e9 masking bias on a whole query row); it
+ *                                 differs only where one query's keys carry several
+ *                                 different out-of-range values
  *   mask                        : uint8 [B, N, N], nonzero = key attended; NULL = all
  *   lse                         : fp32 [B, N, H, N], indexed [b, r, h, q] by
  *                                 attention row r and query q (natural log)
@@ -44,7 +50,10 @@
  *   - Results are bitwise deterministic for a fixed problem, build and device:
  *     every reduction runs in a fixed order and no floating-point atomics are
  *     used (Lambda post, "Как работает TurboPairFormer", third point).
- *   - No global mutable state: calls from several threads are safe.
+ *   - The only global state is a per-device cache, held in atomics, of the
+ *     device's compute-unit count (which sizes the launch plans and the backward
+ *     workspace; 256, the MI355X's count, when no device can be queried) and of
+ *     kernel attributes set once: calls from several threads are safe.
  */
 #ifndef TRI_ATTN_H
 #define TRI_ATTN_H
@@ -85,10 +94,23 @@ typedef struct {
  * 32 <= N <= 768, B >= 1, 1 <= H <= 64.  D == 16 runs the same kernels with the
  * tiles' channels 16..31 held at zero. */
 
-/* Returns TRI_ATTN_ABI_VERSION of the loaded library. */
+/*
+ * Returns TRI_ATTN_ABI_VERSION of the loaded library (biocloudservice page,
+ * "当前可用环境非常窄，先做兼容性预检": the loader checks the binary it found
+ * against what it was built for and stops with an error instead of compiling or
+ * falling back at run time).  The Python binding refuses a library whose version
+ * differs from its own, and every call refuses a problem whose abi_version field
+ * differs (TRI_ATTN_ERROR_ABI_MISMATCH).  Never fails.
+ */
 int tri_attn_abi_version(void);
 
-/* Static, human-readable name of a status code (never NULL). */
+/*
+ * Static, human-readable name of a status code; "unknown status" for a code this
+ * library does not return; never NULL and never to be freed (biocloudservice
+ * page, "一个可执行的验收清单", first point: a caller must be able to tell the fast
+ * path ran, so an unsupported request is reported by name, never served by a
+ * fallback).
+ */
 const char *tri_attn_status_string(int status);
 
 /*
@@ -111,8 +133,18 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem,
                              void *o, void *o_residual, float *lse,
                              hipStream_t stream);
 
-/* Device workspace (bytes) tri_attn_bwd needs for `problem`; 0 if the problem
- * is invalid or unsupported. */
+/*
+ * Device workspace (bytes) tri_attn_bwd needs for `problem` on the current device;
+ * 0 if the problem is invalid or unsupported (biocloudservice page, "它优化了什么，
+ * 而不是只“少存一点张量”": the backward never writes the full score gradient
+ * out).  The workspace holds the per-query statistics (-lse/alpha and -D, fp32,
+ * 2*B*N*H*N values), one bf16 dQ partial per 64-key block (ceil(N/64)*B*N*N*H*D
+ * values) and one fp32 pair-bias-gradient partial per row chunk (C*B*H*N*N values,
+ * C = the number of row chunks the launch plan uses on this device), each
+ * 256-byte aligned.  At N = 768, H = 4, D = 32 that is 1.87 GB against the 3.6 GB
+ * of one bf16 score gradient (N^3*H values).  Host-only; no HIP call except the
+ * cached compute-unit query.
+ */
 size_t tri_attn_bwd_workspace_bytes(const tri_attn_problem *problem);
 
 /*
@@ -143,25 +175,11 @@ tri_attn_status tri_attn_bwd(const tri_attn_problem *problem,
                              hipStream_t stream);
 
 /*
- * Same as tri_attn_bwd.  In addition, when main_start and main_stop are not
- * NULL, they are recorded on `stream` immediately before and after the launch
- * of the backward's main kernel (the key-block-parallel recomputation that
- * dominates the run time), so a caller can time that kernel alone with
- * hipEventElapsedTime.  The events are owned by the caller.
- */
-tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem,
-                                      const void *q, const void *k, const void *v,
-                                      const void *bias, const uint8_t *mask,
-                                      const void *o, const void *o_residual,
-                                      const float *lse, const void *d_o,
-                                      void *dq, void *dk, void *dv, void *dbias,
-                                      void *workspace, size_t workspace_bytes,
-                                      hipEvent_t main_start, hipEvent_t main_stop,
-                                      hipStream_t stream);
-
-/*
- * Same as tri_attn_bwd, with every kernel of the backward bracketed by events
- * so a caller can time each one with hipEventElapsedTime.  events points to
+ * Same as tri_attn_bwd (same validation, kernels and bits), with every kernel of
+ * the backward bracketed by events so a caller can time each one with
+ * hipEventElapsedTime (Lambda post, "Результаты тестирования", and the
+ * biocloudservice page, "crop size不是一个普通参数": time is reported per crop
+ * size, and here also per kernel).  events points to
  * five caller-owned hipEvent_t (an entry may be NULL: not recorded), recorded on
  * `stream` before the statistics kernel (0), after it (1), after the main
  * kernel (2), after the dQ reduction (3) and after the dbias reduction (4).

@@ -38,6 +38,26 @@ def test_header_declares_the_exported_set():
     assert declared_functions() == sorted(ta.EXPORTED_SYMBOLS)
 
 
+def declaration_comments():
+    """The comment block directly above each declared call in the header."""
+    text = HEADER.read_text()
+    out = {}
+    for m in re.finditer(r"/\*((?:(?!\*/).)*)\*/\s*(?:[A-Za-z_][A-Za-z_0-9 ]*\*?\s*)(tri_attn_[a-z_]+)\s*\(",
+                         text, flags=re.S):
+        out[m.group(2)] = re.sub(r"\s*\n\s*\*?\s*", " ", m.group(1))   # one line, no leading '*'
+    return out
+
+
+def test_every_declared_call_cites_the_pages():
+    """Each entry point's comment names the page passage that defines it: the Lambda
+    post (dev48.org translation) or the biocloudservice page, with a section."""
+    comments = declaration_comments()
+    assert sorted(comments) == declared_functions()
+    for name, c in comments.items():
+        assert ("Lambda post" in c) or ("biocloudservice page" in c), name
+        assert re.search(r'"[^"]+"', c), name   # a quoted section title
+
+
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
@@ -182,3 +202,78 @@ def test_head_dim16_is_accepted_with_a_smaller_workspace(lib):
     ptrs = fake_ptrs(7)
     ptrs[0] = None  # validation reaches the pointer checks: the size itself is accepted
     assert call_fwd(lib, prob, ptrs) == INVALID
+
+
+# ---- the Python binding's argument checks (host only: nothing reaches the library) ----
+
+import torch  # noqa: E402
+
+
+def test_check_tensor_rejects_each_mismatch():
+    dev = torch.device("cpu")
+    good = torch.zeros((1, 64, 4, 64), dtype=torch.float32)
+    ta._check_tensor("lse", good, (1, 64, 4, 64), (torch.float32,), dev)
+    with pytest.raises(ValueError, match="shape"):
+        ta._check_tensor("lse", torch.zeros((1, 64, 4, 32)), (1, 64, 4, 64), (torch.float32,), dev)
+    with pytest.raises(ValueError, match="dtype"):
+        ta._check_tensor("lse", good.double(), (1, 64, 4, 64), (torch.float32,), dev)
+    with pytest.raises(ValueError, match="contiguous"):
+        ta._check_tensor("lse", torch.zeros((1, 64, 64, 4)).transpose(2, 3), (1, 64, 4, 64),
+                         (torch.float32,), dev)
+    with pytest.raises(ValueError, match="device"):
+        ta._check_tensor("lse", good, (1, 64, 4, 64), (torch.float32,), torch.device("meta"))
+    with pytest.raises(ValueError, match="tensor"):
+        ta._check_tensor("lse", None, (1, 64, 4, 64), (torch.float32,), dev)
+
+
+@pytest.fixture
+def host_only_binding(monkeypatch):
+    """The binding with its device checks of q, k, v, bias bypassed and no library:
+    any call that got past the argument checks would raise RuntimeError."""
+    def no_lib(*a, **k):
+        raise RuntimeError("library reached")
+    monkeypatch.setattr(ta, "load_library", no_lib)
+    monkeypatch.setattr(ta, "_check_inputs", lambda q, k, v, bias, mask: tuple(
+        q.shape[i] for i in (0, 1, 3, 4)))
+    B, N, H, D = 1, 64, 2, 32
+    t = {"q": torch.zeros((B, N, N, H, D), dtype=torch.bfloat16)}
+    t.update(k=t["q"], v=t["q"], bias=torch.zeros((B, H, N, N), dtype=torch.bfloat16),
+             o=torch.zeros_like(t["q"]), res=torch.zeros((B, N, N, H, D), dtype=torch.float32),
+             lse=torch.zeros((B, N, H, N), dtype=torch.float32), do=torch.zeros_like(t["q"]))
+    return t
+
+
+@pytest.mark.parametrize("name,bad,match", [
+    ("o", lambda t: t["o"].float(), "o must be of dtype"),
+    ("o", lambda t: t["o"][:, :32], "o must have shape"),
+    ("res", lambda t: t["res"].double(), "o_residual must be of dtype"),
+    ("res", lambda t: t["res"][..., :16], "o_residual must have shape"),
+    ("lse", lambda t: t["lse"][:, :32], "lse must have shape"),
+    ("lse", lambda t: t["lse"].to(torch.bfloat16), "lse must be of dtype"),
+    ("lse", lambda t: t["lse"].transpose(1, 3), "lse must"),
+    ("do", lambda t: t["do"].float(), "d_o must be of dtype"),
+    ("do", lambda t: t["do"][:, :, :32], "d_o must have shape"),
+    ("do", lambda t: t["do"].transpose(1, 2), "d_o must be contiguous"),
+])
+def test_backward_rejects_mismatched_saved_tensors(host_only_binding, name, bad, match):
+    t = dict(host_only_binding)
+    t[name] = bad(t)
+    with pytest.raises(ValueError, match=match):
+        ta.tri_attn_bwd(t["q"], t["k"], t["v"], t["bias"], None, t["o"], t["res"], t["lse"], t["do"])
+
+
+def test_backward_checks_pass_on_matching_tensors(host_only_binding):
+    t = host_only_binding
+    with pytest.raises(RuntimeError, match="library reached"):
+        ta.tri_attn_bwd(t["q"], t["k"], t["v"], t["bias"], None, t["o"], t["res"], t["lse"], t["do"])
+    with pytest.raises(RuntimeError, match="library reached"):   # uncompensated: no residual
+        ta.tri_attn_bwd(t["q"], t["k"], t["v"], t["bias"], None, t["o"], None, t["lse"], t["do"])
+
+
+def test_forward_rejects_mismatched_outputs(host_only_binding):
+    t = host_only_binding
+    with pytest.raises(ValueError, match="lse must have shape"):
+        ta.tri_attn_fwd(t["q"], t["k"], t["v"], t["bias"], None, out=(t["o"], t["res"], t["lse"][:, :8]))
+    with pytest.raises(ValueError, match="o_residual must be of dtype"):
+        ta.tri_attn_fwd(t["q"], t["k"], t["v"], t["bias"], None, residual="bf16",
+                        out=(t["o"], t["res"], t["lse"]))

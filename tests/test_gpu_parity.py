@@ -4,11 +4,17 @@ Every GPU call goes through the C ABI (via the thin binding).  Criteria:
   forward o       : max |o - o_ref| <= 2e-2 and rel-RMSE <= 1e-2
   lse             : max |lse - lse_ref| <= 1e-4 (fp32 log-sum-exp)
   dq, dk, dv, dbias: rel-RMSE <= 2e-2 each
-with rel-RMSE(x) = ||x - x_ref||_2 / ||x_ref||_2 over all compared elements.
+with rel-RMSE(x) = ||x - x_ref||_2 / ||x_ref||_2 over all compared elements, and
+the same 2e-2 (1e-2 for o) on every tile of the kernels' tiling on its own: each
+(attention row, head, 32 positions) of o, dq, dk, dv and each (head, 32 queries)
+block of dbias over all keys, or each sampled dbias row (tests/parity_checks.py).
 The oracle runs on the whole problem at N = 64 and N = 256; at N = 384, 640 and
 768 it runs on sampled attention rows (o, lse, dq, dk, dv of those rows) and
 sampled pair-bias-gradient rows dbias[b, h, j, :], each an exact sum over all
-rows, so every sampled value is checked one by one at full size.
+rows, so every sampled value is checked one by one at full size.  The sampled
+rows include the first, second and last row of every row chunk of the launch
+plan.  Outputs and the backward workspace are filled with NaN before each call,
+so a value the kernels never write fails the comparison.
 """
 import math
 import os
@@ -18,12 +24,16 @@ import numpy as np
 import pytest
 import torch
 
+import bench
 import oracle
 import seeded_inputs as si
+from parity_checks import (dbias_row_tile_errors, dbias_tile_errors, full_tile_errors, rel_rmse,
+                           row_tile_errors, worst)
 
 pytestmark = pytest.mark.gpu
 
 FWD_MAX_ABS, FWD_REL_RMSE, GRAD_REL_RMSE, LSE_ABS = 2e-2, 1e-2, 2e-2, 1e-4
+NAN_FILL = 0xFF  # every byte 0xff: NaN in bf16 and fp32
 
 
 def say(*a):
@@ -40,52 +50,90 @@ def ta():
     return mod
 
 
-def rel_rmse(x, ref):
-    x, ref = np.asarray(x, np.float64), np.asarray(ref, np.float64)
-    den = np.linalg.norm(ref)
-    return float(np.linalg.norm(x - ref) / (den if den > 0 else 1.0))
-
-
 def to_np(t):
     return t.detach().float().cpu().double().numpy()
 
 
-def run_gpu(ta, inp, ending=False, compensated=True, scale=None, dbias_fp32=False, residual="fp32"):
+def filled(shape, dtype, dev, byte):
+    t = torch.empty(shape, dtype=dtype, device=dev)
+    t.view(torch.uint8).fill_(byte)
+    return t
+
+
+def mask_arg(g, inp, use_mask):
+    """The mask passed to the library: None (the unmasked kernels) for an all-ones
+    mask unless use_mask is True; the given mask otherwise."""
+    m = inp.get("mask")
+    if m is None:
+        return None
+    if use_mask is None:
+        use_mask = not bool(torch.all(m != 0))
+    return g["mask"] if use_mask else None
+
+
+def run_gpu(ta, inp, ending=False, compensated=True, scale=None, dbias_fp32=False, residual="fp32",
+            use_mask=None, fill=NAN_FILL):
+    """One forward and backward through the C ABI into outputs and a workspace
+    whose every byte is `fill` beforehand."""
     dev = torch.device("cuda:0")
     g = {k: v.to(dev) for k, v in inp.items()}
-    mask = g["mask"] if inp.get("mask") is not None else None
+    mask = mask_arg(g, inp, use_mask)
+    B, N, _, H, D = inp["q"].shape
+    shp = tuple(inp["q"].shape)
+    fo = (filled(shp, torch.bfloat16, dev, fill), filled(shp, ta.RESIDUAL_DTYPES[residual], dev, fill),
+          filled((B, N, H, N), torch.float32, dev, fill))
     o, res, lse = ta.tri_attn_fwd(g["q"], g["k"], g["v"], g["bias"], mask, ending=ending,
-                                  scale=scale, save_residual=True, residual=residual)
+                                  scale=scale, residual=residual, out=fo)
+    ws = filled((ta.bwd_workspace_bytes(B, N, H, D, ending=ending, dbias_fp32=dbias_fp32, scale=scale),),
+                torch.uint8, dev, fill)
+    bo = tuple(filled(shp, torch.bfloat16, dev, fill) for _ in range(3)) + (
+        filled((B, H, N, N), torch.float32 if dbias_fp32 else torch.bfloat16, dev, fill),)
     dq, dk, dv, db = ta.tri_attn_bwd(g["q"], g["k"], g["v"], g["bias"], mask, o,
                                      res if compensated else None, lse, g["do"],
-                                     ending=ending, scale=scale, dbias_fp32=dbias_fp32)
+                                     ending=ending, scale=scale, dbias_fp32=dbias_fp32,
+                                     workspace=ws, out=bo)
     torch.cuda.synchronize()
     return {"o": o, "res": res, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "dbias": db}
 
 
-def check_full(ta, inp, ending=False, scale=None, tag=""):
+def assert_tiles(errs, bound, tag, name):
+    e, idx = worst(errs)
+    assert e <= bound, (tag, name, "worst tile", idx, e)
+    return e
+
+
+def check_full(ta, inp, ending=False, scale=None, tag="", use_mask=None, lse_ok=None):
+    """Whole-problem comparison with the oracle.  lse_ok, if given, is a boolean
+    [B, N, H, N] array of the lse entries to compare (the others are skipped)."""
     say(f"[parity] {tag} ending={ending} full oracle")
-    out = run_gpu(ta, inp, ending=ending, scale=scale)
+    out = run_gpu(ta, inp, ending=ending, scale=scale, use_mask=use_mask)
     ref = oracle.forward_backward(inp["q"], inp["k"], inp["v"], inp["bias"], inp["mask"],
                                   inp["do"], scale=scale, ending=ending)
     o = to_np(out["o"])
     assert np.max(np.abs(o - ref["o"])) <= FWD_MAX_ABS, tag
     assert rel_rmse(o, ref["o"]) <= FWD_REL_RMSE, tag
+    assert_tiles(full_tile_errors(o, ref["o"], ending), FWD_REL_RMSE, tag, "o")
     lse, lref = to_np(out["lse"]), ref["lse"]
+    sel = np.ones(lref.shape, bool) if lse_ok is None else lse_ok
     fin = np.isfinite(lref)
-    assert np.array_equal(np.isfinite(lse), fin), tag
-    if fin.any():
-        assert np.max(np.abs(lse[fin] - lref[fin])) <= LSE_ABS, tag
-    errs = {n: rel_rmse(to_np(out[n]), ref[n]) for n in ("dq", "dk", "dv", "dbias")}
-    say(f"[parity] {tag} o_rmse={rel_rmse(o, ref['o']):.2e} grads={errs}")
+    assert np.array_equal(np.isfinite(lse)[sel], fin[sel]), tag
+    if (fin & sel).any():
+        assert np.max(np.abs(lse[fin & sel] - lref[fin & sel])) <= LSE_ABS, tag
+    errs, tiles = {}, {}
+    for n in ("dq", "dk", "dv", "dbias"):
+        x = to_np(out[n])
+        errs[n] = rel_rmse(x, ref[n])
+        te = dbias_tile_errors(x, ref[n]) if n == "dbias" else full_tile_errors(x, ref[n], ending)
+        tiles[n] = assert_tiles(te, GRAD_REL_RMSE, tag, n)
+    say(f"[parity] {tag} o_rmse={rel_rmse(o, ref['o']):.2e} grads={errs} worst tiles={tiles}")
     for n, e in errs.items():
         assert e <= GRAD_REL_RMSE, (tag, n, e)
     return out, ref
 
 
-def check_sampled(ta, inp, ending, rows, sel, tag, reps=1):
+def check_sampled(ta, inp, ending, rows, sel, tag, use_mask=None, **kw):
     say(f"[parity] {tag} ending={ending} sampled rows={rows} dbias rows={sel}")
-    out = run_gpu(ta, inp, ending=ending)
+    out = run_gpu(ta, inp, ending=ending, use_mask=use_mask, **kw)
     p = oracle.Problem(inp["q"], inp["k"], inp["v"], inp["bias"], inp["mask"], inp["do"],
                        ending=ending)
     ref = p.rows(rows)
@@ -100,6 +148,7 @@ def check_sampled(ta, inp, ending, rows, sel, tag, reps=1):
     o_g, o_r = cat["o"]
     assert np.max(np.abs(o_g - o_r)) <= FWD_MAX_ABS, tag
     assert rel_rmse(o_g, o_r) <= FWD_REL_RMSE, tag
+    assert_tiles(row_tile_errors(o_g, o_r), FWD_REL_RMSE, tag, "o")
     lse_g = np.stack([to_np(out["lse"][b, r]) for (b, r) in rows])
     fin = np.isfinite(ref["lse"])  # a row without attended keys has lse = +inf on both sides
     assert np.array_equal(np.isfinite(lse_g), fin), tag
@@ -108,7 +157,9 @@ def check_sampled(ta, inp, ending, rows, sel, tag, reps=1):
     db_g = np.stack([to_np(out["dbias"][b, h, j]) for (b, h, j) in sel])
     errs = {n: rel_rmse(*cat[n]) for n in ("dq", "dk", "dv")}
     errs["dbias"] = rel_rmse(db_g, refb)
-    say(f"[parity] {tag} o_rmse={rel_rmse(o_g, o_r):.2e} grads={errs}")
+    tiles = {n: assert_tiles(row_tile_errors(*cat[n]), GRAD_REL_RMSE, tag, n) for n in ("dq", "dk", "dv")}
+    tiles["dbias"] = assert_tiles(dbias_row_tile_errors(db_g, refb), GRAD_REL_RMSE, tag, "dbias")
+    say(f"[parity] {tag} o_rmse={rel_rmse(o_g, o_r):.2e} grads={errs} worst tiles={tiles}")
     for n, e in errs.items():
         assert e <= GRAD_REL_RMSE, (tag, n, e)
     return out
@@ -124,14 +175,28 @@ def test_pad256_full(ta, ending):
     check_full(ta, si.make_workload("pad256"), ending=ending, tag="pad256")
 
 
-def sample_rows(N, L=None):
-    rows = [0, 1, N // 2, N - 1, 37 % N, (N * 5) // 7]
-    return [(0, r) for r in sorted(set(rows))]
+def chunk_rows(B, N, H):
+    """First, second and last row of every row chunk of the launch plan (one round of
+    workgroups of 64 queries or keys; the same chunking in both passes)."""
+    C = bench.row_chunks(B * H * -(-N // 64), N)
+    per = -(-N // C)
+    rows = set()
+    for c in range(C):
+        r0, r1 = c * per, min(N, (c + 1) * per)
+        rows.update({r0, min(r0 + 1, r1 - 1), r1 - 1})
+    return rows
+
+
+def sample_rows(N, H=4, B=1):
+    rows = {0, 1, N // 2, N - 1, 37 % N, (N * 5) // 7} | chunk_rows(B, N, H)
+    return [(0, r) for r in sorted(rows)]
 
 
 def sample_dbias(N, H):
     sel = [(0, 0, 0), (0, 1 % H, N // 3), (0, 2 % H, N - 1), (0, 3 % H, 17), (0, 0, N // 2),
            (0, H - 1, (N * 3) // 4)]
+    # one query of every 32-query tile, heads in turn
+    sel += [(0, t % H, 32 * t + (7 * t) % 32) for t in range(N // 32)]
     return sorted(set(sel))
 
 
@@ -143,9 +208,30 @@ def test_crop_sampled(ta, name):
 
 @pytest.mark.parametrize("ending", [False, True])
 def test_crop768_sampled(ta, ending):
+    """The timed workload: no mask (the unmasked kernel variants), rows from every row
+    chunk of both passes."""
     w = si.WORKLOADS["crop768"]
-    check_sampled(ta, si.make_workload("crop768"), ending, sample_rows(w.N),
-                  sample_dbias(w.N, w.H), "crop768")
+    rows = sample_rows(w.N, w.H)
+    assert len({r * 5 // w.N for _, r in rows}) == 5   # every fifth of the rows is sampled
+    check_sampled(ta, si.make_workload("crop768"), ending, rows, sample_dbias(w.N, w.H), "crop768",
+                  use_mask=False)
+
+
+@pytest.mark.parametrize("name,ending", [("tiny64", False), ("tiny64", True), ("crop384", False),
+                                         ("crop768", True)])
+def test_absent_mask_equals_all_ones_mask(ta, name, ending):
+    """mask = NULL selects compile-time unmasked kernels; an all-ones mask the masked
+    ones.  Both must give the same bits."""
+    inp = si.make_workload(name)
+    a = run_gpu(ta, inp, ending=ending, use_mask=False)
+    b = run_gpu(ta, inp, ending=ending, use_mask=True, fill=0x00)
+    for n in ("o", "res", "lse", "dq", "dk", "dv", "dbias"):
+        assert torch.equal(bits(a[n]), bits(b[n])), (name, n)
+
+
+@pytest.mark.parametrize("ending", [False, True])
+def test_tiny64_full_with_explicit_ones_mask(ta, ending):
+    check_full(ta, si.make_workload("tiny64"), ending=ending, tag="tiny64-ones-mask", use_mask=True)
 
 
 def test_residual_is_the_rounding_remainder(ta):
@@ -206,19 +292,29 @@ def test_bf16_residual(ta, ending):
     assert torch.equal(out32["dv"].view(torch.int16), out16["dv"].view(torch.int16))
 
 
+def bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+# byte patterns the outputs and the workspace are filled with before each rerun: NaN
+# first, then patterns that differ from each other, so that any value the kernels read
+# without writing it first (or never write) differs between reruns
+RERUN_FILLS = (0xFF, 0x00, 0x7F, 0xA5, 0x5A)
+
+
 @pytest.mark.parametrize("name,reps,ending", [("tiny64", 3, False), ("pad256", 3, False),
                                               ("crop640", 3, False), ("crop768_h8d16", 3, False),
                                               ("crop768", 5, False), ("crop768", 5, True)])
 def test_bitwise_determinism(ta, name, reps, ending):
     inp = si.make_workload(name)
     say(f"[determinism] {name} ending={ending} x{reps}")
-    first = run_gpu(ta, inp, ending=ending)
-    for _ in range(reps - 1):
-        again = run_gpu(ta, inp, ending=ending)
+    first = run_gpu(ta, inp, ending=ending, fill=RERUN_FILLS[0])
+    for n in ("o", "res", "lse", "dq", "dk", "dv", "dbias"):
+        assert not bool(torch.isnan(first[n].float()).any()), (name, n)
+    for rep in range(1, reps):
+        again = run_gpu(ta, inp, ending=ending, fill=RERUN_FILLS[rep])
         for n in ("o", "res", "lse", "dq", "dk", "dv", "dbias"):
-            a, b = first[n], again[n]
-            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
-                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), n
+            assert torch.equal(bits(first[n]), bits(again[n])), (name, rep, n)
         del again
 
 
@@ -294,14 +390,16 @@ def test_multi_round_grids_sampled(ta, B, N, H, mask_kind, ending):
     check_sampled(ta, inp, ending, rows, sel, f"B{B}N{N}H{H}{mask_kind}")
 
 
-def test_maximum_size_sampled(ta):
+@pytest.mark.parametrize("ending", [False, True])
+def test_maximum_size_sampled(ta, ending):
     """N = 768 with H = 64, the largest problem the library accepts (1.2e9 elements per
-    tensor): element offsets of the dQ partials and of the outputs pass 2^32, and the
-    backward runs three rounds of workgroups."""
-    say("[parity] maximum size: generating inputs")
+    tensor): element offsets of the dQ partials and of the outputs pass 2^32, the
+    backward runs three rounds of workgroups, and in the ending orientation one
+    attention row spans 2.4e9 bytes (its key tiles lie more than 2^31 bytes apart)."""
+    say(f"[parity] maximum size ending={ending}: generating inputs")
     inp = custom(1, 768, 64, 97, "ragged512")
-    check_sampled(ta, inp, False, [(0, 0), (0, 383), (0, 767)],
-                  [(0, 0, 5), (0, 31, 400), (0, 63, 767)], "B1N768H64ragged512")
+    check_sampled(ta, inp, ending, [(0, 0), (0, 383), (0, 767)],
+                  [(0, 0, 5), (0, 31, 400), (0, 63, 767)], f"B1N768H64ragged512-end{int(ending)}")
 
 
 @pytest.mark.parametrize("B,N,H,mask_kind,ending", [
@@ -346,6 +444,28 @@ def test_forward_probability_overflow(ta):
     inp["bias"][:, :, :, 64:] += 150.0   # keys 64..95: logits about 150 above the rest
     out, ref = check_full(ta, inp, tag="overflow")
     assert torch.isfinite(out["o"].float()).all() and torch.isfinite(out["lse"]).all()
+
+
+def test_bias_beyond_the_fp16_range(ta):
+    """The kernels hold the bias as fp16 and saturate finite values beyond +-65504.
+    That keeps the exact softmax where such values mask keys or shift every key of
+    a query alike: -1e9 on every key of one query row, +7e4 on one key of a query
+    (which then takes all the weight), -7e4 on some keys of a query (zero weight).
+    The lse of the queries whose bias saturates is that of the saturated logits and
+    is not compared; everything else is."""
+    inp = custom(1, 64, 2, 29, "none")
+    big = inp["bias"].float()
+    big[0, 0, 5, :] = -1e9          # every key of query 5, head 0
+    big[0, 1, 9, 30] = 7.0e4        # one key of query 9, head 1
+    big[0, 1, 12, 3:40] = -7.0e4    # keys 3..39 of query 12, head 1
+    big[0, 0, 20, 50] = -3.0e5      # one key of query 20, head 0
+    inp["bias"] = big.to(torch.bfloat16)
+    lse_ok = np.ones((1, 64, 2, 64), bool)
+    lse_ok[0, :, 0, 5] = False
+    lse_ok[0, :, 1, 9] = False
+    for ending in (False, True):
+        out, ref = check_full(ta, inp, ending=ending, tag=f"large-bias-end{int(ending)}", lse_ok=lse_ok)
+        assert torch.isfinite(out["o"].float()).all()
 
 
 def test_custom_scale_and_fp32_dbias(ta):

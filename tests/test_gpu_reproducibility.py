@@ -8,6 +8,9 @@ too.  The cases are small (N <= 128) and drawn from a fixed seed over batch size
 N, head count, key-mask kind (none given as no mask at all, a ones mask, padded
 keys, random keys), orientation, compensated or uncompensated D, softmax scale,
 bf16 or fp32 dbias, bf16 or fp32 saved residual and head dimension 16 or 32.
+Before every run the outputs and the backward workspace are filled with a byte
+pattern (NaN in the first run, other patterns after), so that a value the kernels
+read before writing it, or never write, would differ between the runs.
 """
 import sys
 
@@ -31,8 +34,17 @@ def ta():
     return mod
 
 
+FILLS = (0xFF, 0x00, 0x7F, 0xA5, 0x5A)  # 0xff bytes: NaN in bf16 and fp32
+
+
 def bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def filled(shape, dtype, dev, byte):
+    t = torch.empty(shape, dtype=dtype, device=dev)
+    t.view(torch.uint8).fill_(byte)
+    return t
 
 
 def test_reproducibility_sweep(ta):
@@ -60,12 +72,23 @@ def test_reproducibility_sweep(ta):
                   f"residual={residual}", flush=True)
             sys.stdout.flush()
         first = None
-        for _ in range(N_RUNS):
+        shp = tuple(inp["q"].shape)
+        ws_bytes = ta.bwd_workspace_bytes(B, N, H, D, ending=ending, dbias_fp32=dbias_fp32, scale=scale)
+        for run in range(N_RUNS):
+            # outputs and workspace start as NaN in the first run and as other byte
+            # patterns in the later ones: a value read before it is written, or never
+            # written, then differs between runs
+            fill = FILLS[run]
+            fo = (filled(shp, torch.bfloat16, dev, fill), filled(shp, ta.RESIDUAL_DTYPES[residual], dev, fill),
+                  filled((B, N, H, N), torch.float32, dev, fill))
             o, res, lse = ta.tri_attn_fwd(g["q"], g["k"], g["v"], g["bias"], mask, ending=ending,
-                                          scale=scale, save_residual=True, residual=residual)
+                                          scale=scale, residual=residual, out=fo)
+            bo = tuple(filled(shp, torch.bfloat16, dev, fill) for _ in range(3)) + (
+                filled((B, H, N, N), torch.float32 if dbias_fp32 else torch.bfloat16, dev, fill),)
+            ws = filled((ws_bytes,), torch.uint8, dev, fill)
             grads = ta.tri_attn_bwd(g["q"], g["k"], g["v"], g["bias"], mask, o,
                                     res if compensated else None, lse, g["do"], ending=ending,
-                                    scale=scale, dbias_fp32=dbias_fp32)
+                                    scale=scale, dbias_fp32=dbias_fp32, workspace=ws, out=bo)
             out = dict(zip(names, (o, res, lse) + tuple(grads)))
             if first is None:
                 first = out

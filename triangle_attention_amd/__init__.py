@@ -37,8 +37,7 @@ STATUS_NAMES = {
 }
 
 EXPORTED_SYMBOLS = ("tri_attn_abi_version", "tri_attn_status_string", "tri_attn_fwd",
-                    "tri_attn_bwd_workspace_bytes", "tri_attn_bwd", "tri_attn_bwd_profiled",
-                    "tri_attn_bwd_timed")
+                    "tri_attn_bwd_workspace_bytes", "tri_attn_bwd", "tri_attn_bwd_timed")
 
 
 class Problem(ctypes.Structure):
@@ -79,8 +78,6 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.tri_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.tri_attn_bwd.argtypes = [pp] + [vp] * 14 + [ctypes.c_size_t, vp]
     lib.tri_attn_bwd.restype = i32
-    lib.tri_attn_bwd_profiled.argtypes = [pp] + [vp] * 14 + [ctypes.c_size_t, vp, vp, vp]
-    lib.tri_attn_bwd_profiled.restype = i32
     lib.tri_attn_bwd_timed.argtypes = [pp] + [vp] * 14 + [ctypes.c_size_t, ctypes.POINTER(vp), vp]
     lib.tri_attn_bwd_timed.restype = i32
     if lib.tri_attn_abi_version() != ABI_VERSION:
@@ -119,19 +116,47 @@ def _check_inputs(q, k, v, bias, mask):
     if mask is not None and (mask.dtype != torch.uint8 or tuple(mask.shape) != (B, N, N)
                              or not mask.is_contiguous() or not mask.is_cuda):
         raise ValueError("mask must be a contiguous uint8 CUDA tensor [B, N, N]")
+    for name, t in (("k", k), ("v", v), ("bias", bias), ("mask", mask)):
+        if t is not None and t.device != q.device:
+            raise ValueError(f"{name} must be on the device of q")
     return B, N, H, D
 
 
+def _check_tensor(name, t, shape, dtypes, device):
+    """A tensor the library reads or writes: exact shape, dtype, device, contiguity."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be of dtype {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device} (the device of q)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def tri_attn_fwd(q, k, v, bias, mask=None, *, ending=False, scale=None, save_residual=True,
-                 residual="fp32"):
+                 residual="fp32", out=None):
     """Forward: returns (o bf16, o_residual or None, lse fp32 [B, N, H, N]); the residual
-    O - float(o) is fp32 (exact), or its bf16 rounding with residual="bf16"."""
+    O - float(o) is fp32 (exact), or its bf16 rounding with residual="bf16".  `out`, if
+    given, is a tuple (o, o_residual, lse) of preallocated outputs written in place
+    (o_residual may be None, which then also means save_residual=False)."""
     B, N, H, D = _check_inputs(q, k, v, bias, mask)
+    if residual not in RESIDUAL_DTYPES:
+        raise ValueError("residual must be 'fp32' or 'bf16'")
+    if out is not None:
+        o, res, lse = out
+        _check_tensor("o", o, q.shape, (torch.bfloat16,), q.device)
+        if res is not None:
+            _check_tensor("o_residual", res, q.shape, (RESIDUAL_DTYPES[residual],), q.device)
+        _check_tensor("lse", lse, (B, N, H, N), (torch.float32,), q.device)
     lib = load_library()
     prob = make_problem(B, N, H, D, ending=ending, scale=scale, residual=residual)
-    o = torch.empty_like(q)
-    res = torch.empty(q.shape, dtype=RESIDUAL_DTYPES[residual], device=q.device) if save_residual else None
-    lse = torch.empty((B, N, H, N), dtype=torch.float32, device=q.device)
+    if out is None:
+        o = torch.empty_like(q)
+        res = torch.empty(q.shape, dtype=RESIDUAL_DTYPES[residual], device=q.device) if save_residual else None
+        lse = torch.empty((B, N, H, N), dtype=torch.float32, device=q.device)
     st = lib.tri_attn_fwd(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask),
                           _ptr(o), _ptr(res), _ptr(lse), _stream(q.device))
     if st != 0:
@@ -146,38 +171,50 @@ def bwd_workspace_bytes(B, N, H, D, *, ending=False, dbias_fp32=False, scale=Non
 
 
 def tri_attn_bwd(q, k, v, bias, mask, o, o_residual, lse, d_o, *, ending=False, scale=None,
-                 dbias_fp32=False, workspace=None, main_events=None, kernel_events=None):
+                 dbias_fp32=False, workspace=None, kernel_events=None, out=None):
     """Backward: returns (dq, dk, dv, dbias).  o_residual=None selects the
     uncompensated softmax correction rowsum(dO * float(o)); a bf16 o_residual is
-    passed with the bf16-residual flag.  main_events, a pair of raw hipEvent_t
-    handles (ints), is recorded around the main kernel; kernel_events, five raw
-    handles, around each of the four backward kernels (tri_attn_bwd_timed)."""
+    passed with the bf16-residual flag.  o, o_residual, lse and d_o must match the
+    problem of q exactly (shape, dtype, device, contiguity): the kernels read them
+    without bounds.  kernel_events, five raw hipEvent_t handles (ints), are recorded
+    around each of the four backward kernels (tri_attn_bwd_timed).  `out`, if given,
+    is a tuple (dq, dk, dv, dbias) of preallocated outputs written in place;
+    `workspace` a uint8 device tensor of at least bwd_workspace_bytes bytes."""
     B, N, H, D = _check_inputs(q, k, v, bias, mask)
+    _check_tensor("o", o, q.shape, (torch.bfloat16,), q.device)
+    if o_residual is not None:
+        _check_tensor("o_residual", o_residual, q.shape, (torch.bfloat16, torch.float32), q.device)
+    _check_tensor("lse", lse, (B, N, H, N), (torch.float32,), q.device)
+    _check_tensor("d_o", d_o, q.shape, (torch.bfloat16,), q.device)
     lib = load_library()
-    if o_residual is not None and o_residual.dtype not in (torch.bfloat16, torch.float32):
-        raise ValueError("o_residual must be bf16 or fp32")
     residual = "bf16" if o_residual is not None and o_residual.dtype == torch.bfloat16 else "fp32"
     prob = make_problem(B, N, H, D, ending=ending, dbias_fp32=dbias_fp32, scale=scale,
                         residual=residual)
     nbytes = int(lib.tri_attn_bwd_workspace_bytes(ctypes.byref(prob)))
-    if workspace is None or workspace.numel() < nbytes:
+    if workspace is None:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    dbias = torch.empty(bias.shape, dtype=torch.float32 if dbias_fp32 else torch.bfloat16,
-                        device=q.device)
+    elif (workspace.dtype != torch.uint8 or workspace.device != q.device or not workspace.is_contiguous()
+          or workspace.numel() < nbytes):
+        raise ValueError(f"workspace must be a contiguous uint8 tensor of at least {nbytes} bytes on {q.device}")
+    db_dtype = torch.float32 if dbias_fp32 else torch.bfloat16
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        dbias = torch.empty(bias.shape, dtype=db_dtype, device=q.device)
+    else:
+        dq, dk, dv, dbias = out
+        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+            _check_tensor(name, t, q.shape, (torch.bfloat16,), q.device)
+        _check_tensor("dbias", dbias, bias.shape, (db_dtype,), q.device)
     args = (ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask),
-            _ptr(o), _ptr(o_residual), _ptr(lse), _ptr(d_o.contiguous()),
+            _ptr(o), _ptr(o_residual), _ptr(lse), _ptr(d_o),
             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), _ptr(workspace), workspace.numel())
     if kernel_events is not None:
         if len(kernel_events) != 5:
             raise ValueError("kernel_events must hold five hipEvent_t handles")
         evs = (ctypes.c_void_p * 5)(*[ctypes.c_void_p(e) for e in kernel_events])
         st = lib.tri_attn_bwd_timed(*args, evs, _stream(q.device))
-    elif main_events is None:
-        st = lib.tri_attn_bwd(*args, _stream(q.device))
     else:
-        ev = [ctypes.c_void_p(e) for e in main_events]
-        st = lib.tri_attn_bwd_profiled(*args, ev[0], ev[1], _stream(q.device))
+        st = lib.tri_attn_bwd(*args, _stream(q.device))
     if st != 0:
         raise TriAttnError(st, "tri_attn_bwd")
     return dq, dk, dv, dbias
@@ -198,7 +235,7 @@ class TriAttnFunction(torch.autograd.Function):
     def backward(ctx, d_o):
         q, k, v, bias, mask, o, res, lse = ctx.saved_tensors
         dq, dk, dv, dbias = tri_attn_bwd(q, k, v, bias, mask, o, res, lse,
-                                         d_o.to(torch.bfloat16), ending=ctx.ending,
+                                         d_o.to(torch.bfloat16).contiguous(), ending=ctx.ending,
                                          scale=ctx.scale)
         return dq, dk, dv, dbias, None, None, None
 

@@ -37,6 +37,7 @@
 #include <stdint.h>
 #include <string.h>
 #include <math.h>
+#include <atomic>
 #include <type_traits>
 
 #include "tri_attn.h"
@@ -44,7 +45,6 @@
 namespace {
 
 constexpr int HD = 32;  // head dimension handled by this build
-constexpr int kNumCUs = 256;  // compute units of an MI355X: launch shapes are sized for one round
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
@@ -79,6 +79,15 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
 __device__ __forceinline__ bf16x8 pack8(const float *x) {
   u32x4 w = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
   return as_bf16x8(w);
+}
+// fp16 copy of a bf16 pair-bias value.  bf16 values with 2^-14 <= |x| <= 65504
+// convert exactly; finite values beyond the fp16 range saturate to +-65504 (rather
+// than becoming infinite), and +-inf and NaN pass through.  A saturated value still
+// masks a key next to any in-range logit (exp(-65504 - m) = 0) and shifts every key
+// of a query alike when all of them carry it, so a masking bias of, say, -1e9 gives
+// the exact softmax.
+__device__ __forceinline__ _Float16 bias_f16(float x) {
+  return (_Float16)(__builtin_isfinite(x) ? __builtin_amdgcn_fmed3f(x, -65504.f, 65504.f) : x);
 }
 // Two transposing LDS reads forming one 8-element MFMA operand.
 __device__ __forceinline__ bf16x8 tr_read(const uint16_t *p0, const uint16_t *p1) {
@@ -219,8 +228,8 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
       f16x8 hv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        hv[2 * i] = (_Float16)bf_lo(w[i]);
-        hv[2 * i + 1] = (_Float16)bf_hi(w[i]);
+        hv[2 * i] = bias_f16(bf_lo(w[i]));
+        hv[2 * i + 1] = bias_f16(bf_hi(w[i]));
       }
       *(f16x8 *)(bias_s + row * bstride + c8 * 8) = hv;
     }
@@ -250,19 +259,17 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
     }
     const uint8_t *mrow = a.mask ? a.mask + (long long)b * a.f.mB + (long long)r * a.f.mR : &kMaskAllValid;
 
-    // K and V of the row through buffer descriptors: the lane's byte offset is fixed
-    // for the row and tile kt is a scalar byte offset away, so no per-tile address
-    // math.  A row spans N * sQ * 2 < 2^32 bytes (N <= 768, H <= 64, D <= 32), so the
-    // offsets are unsigned 32-bit values.  With D = 16 a row spans less than 2^31
-    // bytes and the lanes of channels 16..31 get the offset 2^31, past the row (with
-    // any tile's scalar offset still below 2^32): out-of-range buffer loads return
-    // zeros.
-    const unsigned row_bytes = (unsigned)((long long)N * a.f.sQ * 2);
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void *)(a.k + base), (short)0, row_bytes, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void *)(a.v + base), (short)0, row_bytes, kBufferWord3);
-    const unsigned lane_off = (DIN == 16 && vpart >= 2) ? 0x80000000u
-                                                        : (unsigned)(((long long)vkey * a.f.sQ + vpart * 8) * 2);
-    const unsigned tstep_b = (unsigned)(32 * a.f.sQ * 2), vhalf_b = (unsigned)(16 * a.f.sQ * 2);
+    // K and V tiles through buffer descriptors based at the tile (scalar registers):
+    // the lane's byte offset is fixed for the row, so no per-tile vector address
+    // math.  A tile spans 32 * sQ * 2 < 2^27 bytes (N <= 768, H <= 64, D <= 32, in
+    // either orientation), so every offset is far below 2^31.  With D = 16 the lanes
+    // of channels 16..31 get the offset 2^31, past the tile: out-of-range buffer loads
+    // return zeros.
+    const uint16_t *krow = a.k + base, *vrow = a.v + base;
+    const long long tstep = 32 * a.f.sQ;  // elements from one key tile to the next
+    const int tile_bytes = (int)(tstep * 2);
+    const int lane_off = (DIN == 16 && vpart >= 2) ? (int)0x80000000u : (int)(((long long)vkey * a.f.sQ + vpart * 8) * 2);
+    const int vhalf_b = (int)(16 * a.f.sQ * 2);
     const uint8_t *ml = mrow + (long long)jl * mk;
     const long long mstep = 32 * mk;
     // every fetch is unconditional (a tile past the end refetches the last one, which
@@ -270,11 +277,14 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
     // outstanding memory operations where the paths merge
     auto fetch = [&](int kt, FwdTile &T) {
       kt = min(kt, nkt - 1);
-      const unsigned so = (unsigned)kt * tstep_b;
-      T.k0 = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)lane_off, (int)so, 0);
-      T.k1 = __builtin_amdgcn_raw_buffer_load_b128(krs, (int)lane_off, (int)(so + vhalf_b), 0);
-      T.v0 = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)lane_off, (int)so, 0);
-      T.v1 = __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)lane_off, (int)(so + vhalf_b), 0);
+      const __amdgpu_buffer_rsrc_t krs =
+          __builtin_amdgcn_make_buffer_rsrc((void *)(krow + kt * tstep), (short)0, tile_bytes, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t vrs =
+          __builtin_amdgcn_make_buffer_rsrc((void *)(vrow + kt * tstep), (short)0, tile_bytes, kBufferWord3);
+      T.k0 = __builtin_amdgcn_raw_buffer_load_b128(krs, lane_off, 0, 0);
+      T.k1 = __builtin_amdgcn_raw_buffer_load_b128(krs, lane_off, vhalf_b, 0);
+      T.v0 = __builtin_amdgcn_raw_buffer_load_b128(vrs, lane_off, 0, 0);
+      T.v1 = __builtin_amdgcn_raw_buffer_load_b128(vrs, lane_off, vhalf_b, 0);
       T.m = MASKED ? (unsigned)ml[kt * mstep] : 1u;
     };
     auto stage_k = [&](const FwdTile &T) {
@@ -728,8 +738,8 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
       const u32x4 w = ld16(src + (long long)j * N + kc);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        s_bias[(c8 * 8 + 2 * i) * BSTR + j] = (_Float16)bf_lo(w[i]);
-        s_bias[(c8 * 8 + 2 * i + 1) * BSTR + j] = (_Float16)bf_hi(w[i]);
+        s_bias[(c8 * 8 + 2 * i) * BSTR + j] = bias_f16(bf_lo(w[i]));
+        s_bias[(c8 * 8 + 2 * i + 1) * BSTR + j] = bias_f16(bf_hi(w[i]));
       }
     }
   }
@@ -1040,6 +1050,36 @@ __global__ __launch_bounds__(256) void reduce_dbias_kernel(ReduceArgs a) {
 constexpr int64_t kMaxN = 768;
 constexpr int64_t kMaxH = 64;
 
+// Compute units of the current device, which size the launch plans (one round of
+// workgroups, one per CU).  Read once per device with hipDeviceGetAttribute and
+// cached; where no device can be queried (host-only validation, e.g. a workspace
+// size asked for on a machine without a GPU) the MI355X's 256 is used.
+constexpr int kDefaultCUs = 256;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kDefaultCUs;
+  }
+  int cus = g_cus[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) {
+    (void)hipGetLastError();
+    return kDefaultCUs;
+  }
+  g_cus[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// forward kernels (bit per variant, per device) whose dynamic LDS limit is raised
+std::atomic<unsigned> g_fwd_lds_set[kMaxDevices];
+// the forward's largest dynamic LDS: the fp16 bias block at the widest row stride
+// (N + 36 for N <= kMaxN) and the waves' K/V tiles
+constexpr size_t kFwdMaxLds = (size_t)FWD_BJ * (kMaxN + 36) * 2 + (size_t)FWD_WAVES * 2 * 32 * HD * 2;
+
 bool aligned16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
 
 struct Range {
@@ -1091,7 +1131,7 @@ struct BwdPlan {
   size_t off_stats, off_dq, off_db, total;
 };
 
-BwdPlan plan_bwd(const tri_attn_problem *p) {
+BwdPlan plan_bwd(const tri_attn_problem *p, int cus) {
   BwdPlan pl;
   const int N = (int)p->N;
   const int njt = N / 32;
@@ -1099,7 +1139,7 @@ BwdPlan plan_bwd(const tri_attn_problem *p) {
   pl.T = (N + BWD_BK - 1) / BWD_BK;
   // one workgroup per CU (its LDS and registers fill one); one wave of workgroups
   const int groups = (int)(p->B * p->H * pl.T);
-  int C = kNumCUs / groups;
+  int C = cus / groups;
   if (C < 1) C = 1;
   if (C > N) C = N;
   pl.rows_per_chunk = (N + C - 1) / C;
@@ -1194,30 +1234,36 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
   // one workgroup per CU (its LDS fills one) and, where the problem allows, a single
   // round of workgroups: the block's bias is then staged once per CU
   const int groups = a.B * a.H * a.n_jblocks;
-  int chunks = kNumCUs / groups;
+  int chunks = device_cus() / groups;
   if (chunks < 1) chunks = 1;
   if (chunks > a.N) chunks = a.N;
   a.rows_per_chunk = (a.N + chunks - 1) / chunks;
   a.n_chunks = (a.N + a.rows_per_chunk - 1) / a.rows_per_chunk;
   const size_t lds = (size_t)FWD_BJ * a.bstride * 2 + (size_t)FWD_WAVES * 2 * 32 * HD * 2;
   const bool res32 = (p.flags & TRI_ATTN_FLAG_RESIDUAL_BF16) == 0;
-  void (*kern)(FwdArgs);
-  if (p.D == 32)
-    kern = mask ? (res32 ? fwd_kernel<true, true, 32> : fwd_kernel<true, false, 32>)
-                : (res32 ? fwd_kernel<false, true, 32> : fwd_kernel<false, false, 32>);
-  else
-    kern = mask ? (res32 ? fwd_kernel<true, true, 16> : fwd_kernel<true, false, 16>)
-                : (res32 ? fwd_kernel<false, true, 16> : fwd_kernel<false, false, 16>);
-  if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
-      hipSuccess)
-    return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  void (*const kernels[8])(FwdArgs) = {fwd_kernel<false, false, 32>, fwd_kernel<false, true, 32>,
+                                        fwd_kernel<true, false, 32>,  fwd_kernel<true, true, 32>,
+                                        fwd_kernel<false, false, 16>, fwd_kernel<false, true, 16>,
+                                        fwd_kernel<true, false, 16>,  fwd_kernel<true, true, 16>};
+  const int variant = (p.D == 16 ? 4 : 0) | (mask ? 2 : 0) | (res32 ? 1 : 0);
+  void (*kern)(FwdArgs) = kernels[variant];
+  // the kernel's dynamic LDS limit, raised once per device and variant to the largest
+  // size any accepted problem uses
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  if (!(g_fwd_lds_set[dev].load(std::memory_order_acquire) & (1u << variant))) {
+    if (hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFwdMaxLds) !=
+        hipSuccess)
+      return TRI_ATTN_ERROR_LAUNCH_FAILED;
+    g_fwd_lds_set[dev].fetch_or(1u << variant, std::memory_order_acq_rel);
+  }
   hipLaunchKernelGGL(kern, dim3(groups * a.n_chunks), dim3(FWD_WAVES * 64), lds, stream, a);
   return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH_FAILED;
 }
 
 size_t tri_attn_bwd_workspace_bytes(const tri_attn_problem *problem) {
   if (check_problem(problem) != TRI_ATTN_SUCCESS) return 0;
-  return plan_bwd(problem).total;
+  return plan_bwd(problem, device_cus()).total;
 }
 
 // The backward's four launches; marks[0..4] (each may be null) are recorded before the
@@ -1235,7 +1281,7 @@ static tri_attn_status bwd_run(const tri_attn_problem *problem, const void *q, c
     if (!aligned16(x)) return TRI_ATTN_ERROR_INVALID_VALUE;
   if (o_residual && !aligned16(o_residual)) return TRI_ATTN_ERROR_INVALID_VALUE;
   if (!workspace || ((uintptr_t)workspace & 255u)) return TRI_ATTN_ERROR_INVALID_VALUE;
-  const BwdPlan pl = plan_bwd(problem);
+  const BwdPlan pl = plan_bwd(problem, device_cus());
   if (workspace_bytes < pl.total) return TRI_ATTN_ERROR_INSUFFICIENT_WORKSPACE;
   const size_t E = (size_t)p.B * p.N * p.N * p.H * p.D;
   const size_t nb = (size_t)p.B * p.H * p.N * p.N;
@@ -1330,16 +1376,6 @@ static tri_attn_status bwd_run(const tri_attn_problem *problem, const void *q, c
   hipLaunchKernelGGL(reduce_dbias_kernel, dim3((unsigned)((nb / 4 + 255) / 256)), dim3(256), 0, stream, ra);
   if (hipGetLastError() != hipSuccess || !mark(4)) return TRI_ATTN_ERROR_LAUNCH_FAILED;
   return TRI_ATTN_SUCCESS;
-}
-
-tri_attn_status tri_attn_bwd_profiled(const tri_attn_problem *problem, const void *q, const void *k,
-                                      const void *v, const void *bias, const uint8_t *mask, const void *o,
-                                      const void *o_residual, const float *lse, const void *d_o, void *dq,
-                                      void *dk, void *dv, void *dbias, void *workspace, size_t workspace_bytes,
-                                      hipEvent_t main_start, hipEvent_t main_stop, hipStream_t stream) {
-  const hipEvent_t marks[5] = {nullptr, main_start, main_stop, nullptr, nullptr};
-  return bwd_run(problem, q, k, v, bias, mask, o, o_residual, lse, d_o, dq, dk, dv, dbias, workspace,
-                 workspace_bytes, marks, stream);
 }
 
 tri_attn_status tri_attn_bwd_timed(const tri_attn_problem *problem, const void *q, const void *k, const void *v,
