@@ -42,8 +42,9 @@
  *   - All tensor pointers are device pointers owned by the caller.  The library
  *     allocates nothing, frees nothing and keeps no pointer after returning.
  *   - Work is enqueued on `stream`; the call returns without synchronising.
- *   - Arguments are validated on the host before any HIP call.  On an error
- *     nothing is enqueued and no output is touched.  Unsupported sizes return
+ *   - Arguments are validated on the host before anything is enqueued (the only
+ *     HIP calls before that query the current device).  On an error nothing is
+ *     enqueued and no output is touched.  Unsupported sizes return
  *     TRI_ATTN_ERROR_NOT_SUPPORTED; there is no silent fallback path.
  *   - Tensor base pointers must be 16-byte aligned and outputs must not overlap
  *     inputs.
@@ -195,6 +196,36 @@ tri_attn_status tri_attn_bwd_timed(const tri_attn_problem *problem,
                                    void *dq, void *dk, void *dv, void *dbias,
                                    void *workspace, size_t workspace_bytes,
                                    const hipEvent_t *events, hipStream_t stream);
+
+/* Size of the library's fixed device buffer used by tri_attn_bwd_noalloc: 128 MiB. */
+#define TRI_ATTN_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+
+/*
+ * Allocation-free backward, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels and bits as tri_attn_bwd without the workspace: the
+ * workspace lives in a fixed device buffer of TRI_ATTN_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every device it runs on, from module load until the process
+ * ends.  The call allocates and frees nothing; the caller still provides every
+ * input and output.
+ *   - Problems whose workspace (tri_attn_bwd_workspace_bytes) exceeds the buffer
+ *     return TRI_ATTN_ERROR_INSUFFICIENT_WORKSPACE (with this build, B = 1, H = 4 and
+ *     D = 32 on a 256-CU device: N <= 288).
+ *   - The buffer keeps the last call's contents; every byte the kernels read is
+ *     written earlier in the same call, so nothing needs clearing between calls.
+ *   - All calls on one device share that device's buffer: calls that overlap in
+ *     time on one device (other streams, other threads) race and must be
+ *     serialised by the caller.
+ *   - The first call on a device looks up the buffer's device address
+ *     (hipGetSymbolAddress) and caches it; TRI_ATTN_ERROR_LAUNCH_FAILED if that fails.
+ */
+tri_attn_status tri_attn_bwd_noalloc(const tri_attn_problem *problem,
+                                     const void *q, const void *k, const void *v,
+                                     const void *bias, const uint8_t *mask,
+                                     const void *o, const void *o_residual, const float *lse,
+                                     const void *d_o,
+                                     void *dq, void *dk, void *dv, void *dbias,
+                                     hipStream_t stream);
 
 #ifdef __cplusplus
 }

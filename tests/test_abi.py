@@ -48,14 +48,46 @@ def declaration_comments():
     return out
 
 
+# the allocation-free variant of the backward: its comment names the callers it is
+# for (those that cannot allocate) instead of a page passage
+NO_ALLOC_VARIANT = "tri_attn_bwd_noalloc"
+
+
 def test_every_declared_call_cites_the_pages():
     """Each entry point's comment names the page passage that defines it: the Lambda
     post (dev48.org translation) or the biocloudservice page, with a section."""
     comments = declaration_comments()
     assert sorted(comments) == declared_functions()
     for name, c in comments.items():
+        if name == NO_ALLOC_VARIANT:
+            assert "cannot allocate" in c and "graph capture" in c, name
+            continue
         assert ("Lambda post" in c) or ("biocloudservice page" in c), name
         assert re.search(r'"[^"]+"', c), name   # a quoted section title
+
+
+def test_noalloc_validates_and_rejects_oversized_problems(lib):
+    """Host-side checks of the allocation-free backward run before the fixed
+    buffer's address is looked up: invalid problems and problems whose workspace
+    exceeds the buffer are rejected (no HIP device needed)."""
+    lib.tri_attn_bwd_noalloc.argtypes = [ctypes.c_void_p] + [ctypes.c_void_p] * 14
+    p = fake_ptrs(13)
+    bad = ta.make_problem(1, 64, 4, 32)
+    bad.N = 0
+    assert lib.tri_attn_bwd_noalloc(ctypes.byref(bad), *p, None) == INVALID
+    unsupported = ta.make_problem(1, 64, 4, 64)
+    assert lib.tri_attn_bwd_noalloc(ctypes.byref(unsupported), *p, None) == UNSUPPORTED
+    big = ta.make_problem(1, 768, 4, 32)
+    assert lib.tri_attn_bwd_workspace_bytes(ctypes.byref(big)) > ta.NOALLOC_SCRATCH_BYTES
+    assert lib.tri_attn_bwd_noalloc(ctypes.byref(big), *p, None) == WORKSPACE
+    small = ta.make_problem(1, 256, 4, 32)
+    assert lib.tri_attn_bwd_workspace_bytes(ctypes.byref(small)) <= ta.NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_buffer_size_matches_the_header():
+    text = HEADER.read_text()
+    m = re.search(r"#define TRI_ATTN_NOALLOC_SCRATCH_BYTES \((\d+)u \* 1024u \* 1024u\)", text)
+    assert m and int(m.group(1)) * 1024 * 1024 == ta.NOALLOC_SCRATCH_BYTES
 
 
 def test_library_exports_every_declared_symbol(lib):

@@ -37,7 +37,9 @@ STATUS_NAMES = {
 }
 
 EXPORTED_SYMBOLS = ("tri_attn_abi_version", "tri_attn_status_string", "tri_attn_fwd",
-                    "tri_attn_bwd_workspace_bytes", "tri_attn_bwd", "tri_attn_bwd_timed")
+                    "tri_attn_bwd_workspace_bytes", "tri_attn_bwd", "tri_attn_bwd_timed",
+                    "tri_attn_bwd_noalloc")
+NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024   # TRI_ATTN_NOALLOC_SCRATCH_BYTES
 
 
 class Problem(ctypes.Structure):
@@ -80,6 +82,8 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.tri_attn_bwd.restype = i32
     lib.tri_attn_bwd_timed.argtypes = [pp] + [vp] * 14 + [ctypes.c_size_t, ctypes.POINTER(vp), vp]
     lib.tri_attn_bwd_timed.restype = i32
+    lib.tri_attn_bwd_noalloc.argtypes = [pp] + [vp] * 13 + [vp]
+    lib.tri_attn_bwd_noalloc.restype = i32
     if lib.tri_attn_abi_version() != ABI_VERSION:
         raise RuntimeError("libtri_attn.so ABI version mismatch")
     if path is None:
@@ -220,6 +224,34 @@ def tri_attn_bwd(q, k, v, bias, mask, o, o_residual, lse, d_o, *, ending=False, 
     return dq, dk, dv, dbias
 
 
+def tri_attn_bwd_noalloc(q, k, v, bias, mask, o, o_residual, lse, d_o, out, *, ending=False,
+                         scale=None, dbias_fp32=False):
+    """tri_attn_bwd_noalloc: the backward with its workspace in the library's fixed
+    device buffer, for callers that cannot allocate.  `out` = (dq, dk, dv, dbias) must
+    be preallocated; nothing is allocated here.  Problems whose workspace exceeds
+    NOALLOC_SCRATCH_BYTES raise TriAttnError (TRI_ATTN_ERROR_INSUFFICIENT_WORKSPACE)."""
+    B, N, H, D = _check_inputs(q, k, v, bias, mask)
+    _check_tensor("o", o, q.shape, (torch.bfloat16,), q.device)
+    if o_residual is not None:
+        _check_tensor("o_residual", o_residual, q.shape, (torch.bfloat16, torch.float32), q.device)
+    _check_tensor("lse", lse, (B, N, H, N), (torch.float32,), q.device)
+    _check_tensor("d_o", d_o, q.shape, (torch.bfloat16,), q.device)
+    dq, dk, dv, dbias = out
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, q.shape, (torch.bfloat16,), q.device)
+    _check_tensor("dbias", dbias, bias.shape, (torch.float32 if dbias_fp32 else torch.bfloat16,), q.device)
+    lib = load_library()
+    residual = "bf16" if o_residual is not None and o_residual.dtype == torch.bfloat16 else "fp32"
+    prob = make_problem(B, N, H, D, ending=ending, dbias_fp32=dbias_fp32, scale=scale,
+                        residual=residual)
+    st = lib.tri_attn_bwd_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask),
+                                  _ptr(o), _ptr(o_residual), _ptr(lse), _ptr(d_o),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), _stream(q.device))
+    if st != 0:
+        raise TriAttnError(st, "tri_attn_bwd_noalloc")
+    return dq, dk, dv, dbias
+
+
 class TriAttnFunction(torch.autograd.Function):
     """Autograd wrapper: the forward saves o, its residual and lse; the backward
     recomputes every probability tile once inside the HIP kernels."""
@@ -245,6 +277,7 @@ def tri_attn(q, k, v, bias, mask=None, ending=False, scale=None):
     return TriAttnFunction.apply(q, k, v, bias, mask, ending, scale)
 
 
-__all__ = ["tri_attn", "tri_attn_fwd", "tri_attn_bwd", "bwd_workspace_bytes", "load_library",
+__all__ = ["tri_attn", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_bwd_noalloc", "bwd_workspace_bytes",
+           "load_library", "NOALLOC_SCRATCH_BYTES",
            "make_problem", "Problem", "TriAttnError", "TriAttnFunction", "LIB_PATH",
            "EXPORTED_SYMBOLS"]

@@ -42,6 +42,9 @@
 
 #include "tri_attn.h"
 
+// the allocation-free backward's workspace (see kScratchBytes below)
+static __device__ __align__(256) unsigned char scratch[TRI_ATTN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int HD = 32;  // head dimension handled by this build
@@ -1080,6 +1083,16 @@ std::atomic<unsigned> g_fwd_lds_set[kMaxDevices];
 // (N + 36 for N <= kMaxN) and the waves' K/V tiles
 constexpr size_t kFwdMaxLds = (size_t)FWD_BJ * (kMaxN + 36) * 2 + (size_t)FWD_WAVES * 2 * 32 * HD * 2;
 
+// Fixed device buffer of the allocation-free backward (tri_attn_bwd_noalloc): its
+// workspace (per-query statistics, dQ and dbias partials) lives here instead of in
+// caller memory.  Each device the library runs on holds one copy from module load
+// until the process ends.  In host code `scratch` only names the symbol: its device
+// address comes from hipGetSymbolAddress, taken once per device (with that device
+// current) and cached in g_scratch_ptr.
+constexpr size_t kScratchBytes = (size_t)TRI_ATTN_NOALLOC_SCRATCH_BYTES;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+
 bool aligned16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
 
 struct Range {
@@ -1171,6 +1184,23 @@ hipError_t dispatch_main(int JT, const BwdArgs &args, int D, int grid, size_t ld
     case 6: return launch_main<6>(args, D, grid, lds, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+// Device address of `scratch` on the current device (null on failure).
+void *scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
 }
 
 }  // namespace
@@ -1386,6 +1416,22 @@ tri_attn_status tri_attn_bwd_timed(const tri_attn_problem *problem, const void *
   if (!events) return TRI_ATTN_ERROR_INVALID_VALUE;
   return bwd_run(problem, q, k, v, bias, mask, o, o_residual, lse, d_o, dq, dk, dv, dbias, workspace,
                  workspace_bytes, events, stream);
+}
+
+tri_attn_status tri_attn_bwd_noalloc(const tri_attn_problem *problem, const void *q, const void *k,
+                                     const void *v, const void *bias, const uint8_t *mask, const void *o,
+                                     const void *o_residual, const float *lse, const void *d_o, void *dq,
+                                     void *dk, void *dv, void *dbias, hipStream_t stream) {
+  // host-side checks first: a problem whose workspace exceeds the fixed buffer is
+  // rejected before the buffer's address is even looked up
+  tri_attn_status st = check_problem(problem);
+  if (st != TRI_ATTN_SUCCESS) return st;
+  if (plan_bwd(problem, device_cus()).total > kScratchBytes) return TRI_ATTN_ERROR_INSUFFICIENT_WORKSPACE;
+  void *ws = scratch_address();
+  if (!ws) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  const hipEvent_t marks[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};
+  return bwd_run(problem, q, k, v, bias, mask, o, o_residual, lse, d_o, dq, dk, dv, dbias, ws, kScratchBytes,
+                 marks, stream);
 }
 
 tri_attn_status tri_attn_bwd(const tri_attn_problem *problem, const void *q, const void *k, const void *v,
