@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define TRI_ATTN_ABI_VERSION 3
+#define TRI_ATTN_ABI_VERSION 4
 
 typedef enum {
     TRI_ATTN_SUCCESS = 0,
@@ -89,6 +89,18 @@ typedef struct {
     int32_t flags;        /* TRI_ATTN_FLAG_* */
     int64_t B, N, H, D;   /* batch, pair length (I = J = K = N), heads, head dim */
     float softmax_scale;  /* alpha; 0 selects 1/sqrt(D) */
+    /* Attention rows of this call: [row_begin, row_end), 0 <= row_begin < row_end <= N,
+     * or 0, 0 for all N rows (anything else: TRI_ATTN_ERROR_INVALID_VALUE).  Rows are
+     * those of the attended frame (the second pair index for the ending node).  A call
+     * on a range computes o, o_residual, lse (forward) and dq, dk, dv (backward) of
+     * those rows only and leaves the other rows of these buffers untouched; dbias is
+     * then the range's unreduced partial sum over its rows, sum_{i in range} dS_i, to
+     * be added to the other ranges' partials by the caller (with
+     * TRI_ATTN_FLAG_DBIAS_FP32, so that the partials are not rounded to bf16).  This is
+     * one GPU's share of a row-sharded triangle attention; the sum over ranges of the
+     * partials is the dbias of the whole problem (same fixed-order guarantee per
+     * range, the cross-range order being the caller's). */
+    int64_t row_begin, row_end;
 } tri_attn_problem;
 
 /* Supported sizes of this build: D == 32 or D == 16, N a multiple of 32 with

@@ -309,3 +309,33 @@ def test_forward_rejects_mismatched_outputs(host_only_binding):
     with pytest.raises(ValueError, match="o_residual must be of dtype"):
         ta.tri_attn_fwd(t["q"], t["k"], t["v"], t["bias"], None, residual="bf16",
                         out=(t["o"], t["res"], t["lse"]))
+
+
+# ---- attention-row ranges (one GPU's share of a row-sharded problem) ----
+
+@pytest.mark.parametrize("rows,ok", [((0, 0), True), ((0, 64), True), ((10, 20), True), ((63, 64), True),
+                                     ((-1, 5), False), ((5, 5), False), ((20, 10), False),
+                                     ((0, 65), False), ((64, 64), False)])
+def test_row_range_validation(lib, rows, ok):
+    prob = ta.make_problem(1, 64, 4, 32, rows=rows)
+    need = lib.tri_attn_bwd_workspace_bytes(ctypes.byref(prob))
+    assert (need > 0) == ok
+    if not ok:
+        assert call_fwd(lib, prob) == INVALID
+        assert call_bwd(lib, prob, ws_bytes=1 << 40) == INVALID
+
+
+def test_row_range_workspace_follows_the_range_plan(lib):
+    """The dbias partials of a range call are one per row chunk of the range: a
+    range of 32 rows (H = 4, N = 256: 16 groups of workgroups, at most 16 chunks)
+    needs the same statistics and dQ partials as the whole problem but no more
+    dbias partials than chunks of its own rows."""
+    import bench
+    full = lib.tri_attn_bwd_workspace_bytes(ctypes.byref(ta.make_problem(1, 256, 4, 32)))
+    part = lib.tri_attn_bwd_workspace_bytes(ctypes.byref(ta.make_problem(1, 256, 4, 32, rows=(100, 132))))
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+    base = a256(256 * 4 * 2 * 256 * 4) + a256(4 * 256 * 256 * 4 * 32 * 2)
+    assert full == base + a256(bench.row_chunks(16, 256) * 4 * 256 * 256 * 4)
+    assert part == base + a256(bench.row_chunks(16, 32) * 4 * 256 * 256 * 4)

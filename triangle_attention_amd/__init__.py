@@ -21,7 +21,7 @@ import torch
 _HERE = Path(__file__).resolve().parent
 LIB_PATH = _HERE / "libtri_attn.so"
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 FLAG_ENDING_NODE = 1
 FLAG_DBIAS_FP32 = 2
 FLAG_RESIDUAL_BF16 = 4
@@ -46,7 +46,8 @@ class Problem(ctypes.Structure):
     """Mirror of ``tri_attn_problem``."""
     _fields_ = [("abi_version", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("B", ctypes.c_int64), ("N", ctypes.c_int64), ("H", ctypes.c_int64),
-                ("D", ctypes.c_int64), ("softmax_scale", ctypes.c_float)]
+                ("D", ctypes.c_int64), ("softmax_scale", ctypes.c_float),
+                ("row_begin", ctypes.c_int64), ("row_end", ctypes.c_int64)]
 
 
 class TriAttnError(RuntimeError):
@@ -92,12 +93,14 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
 
 
 def make_problem(B, N, H, D, *, ending=False, dbias_fp32=False, scale=None, residual="fp32",
-                 abi_version=ABI_VERSION) -> Problem:
+                 rows=None, abi_version=ABI_VERSION) -> Problem:
+    """rows = (row_begin, row_end): the attention rows of the call (None: all rows)."""
     if residual not in RESIDUAL_DTYPES:
         raise ValueError("residual must be 'fp32' or 'bf16'")
     flags = ((FLAG_ENDING_NODE if ending else 0) | (FLAG_DBIAS_FP32 if dbias_fp32 else 0)
              | (FLAG_RESIDUAL_BF16 if residual == "bf16" else 0))
-    return Problem(abi_version, flags, B, N, H, D, float(scale or 0.0))
+    r0, r1 = (0, 0) if rows is None else (int(rows[0]), int(rows[1]))
+    return Problem(abi_version, flags, B, N, H, D, float(scale or 0.0), r0, r1)
 
 
 def _ptr(t):
@@ -141,11 +144,13 @@ def _check_tensor(name, t, shape, dtypes, device):
 
 
 def tri_attn_fwd(q, k, v, bias, mask=None, *, ending=False, scale=None, save_residual=True,
-                 residual="fp32", out=None):
+                 residual="fp32", out=None, rows=None):
     """Forward: returns (o bf16, o_residual or None, lse fp32 [B, N, H, N]); the residual
     O - float(o) is fp32 (exact), or its bf16 rounding with residual="bf16".  `out`, if
     given, is a tuple (o, o_residual, lse) of preallocated outputs written in place
-    (o_residual may be None, which then also means save_residual=False)."""
+    (o_residual may be None, which then also means save_residual=False).  rows =
+    (row_begin, row_end) computes only those attention rows; the other rows of the
+    outputs are left as they are (uninitialised when the outputs are allocated here)."""
     B, N, H, D = _check_inputs(q, k, v, bias, mask)
     if residual not in RESIDUAL_DTYPES:
         raise ValueError("residual must be 'fp32' or 'bf16'")
@@ -156,7 +161,7 @@ def tri_attn_fwd(q, k, v, bias, mask=None, *, ending=False, scale=None, save_res
             _check_tensor("o_residual", res, q.shape, (RESIDUAL_DTYPES[residual],), q.device)
         _check_tensor("lse", lse, (B, N, H, N), (torch.float32,), q.device)
     lib = load_library()
-    prob = make_problem(B, N, H, D, ending=ending, scale=scale, residual=residual)
+    prob = make_problem(B, N, H, D, ending=ending, scale=scale, residual=residual, rows=rows)
     if out is None:
         o = torch.empty_like(q)
         res = torch.empty(q.shape, dtype=RESIDUAL_DTYPES[residual], device=q.device) if save_residual else None
@@ -168,14 +173,14 @@ def tri_attn_fwd(q, k, v, bias, mask=None, *, ending=False, scale=None, save_res
     return o, res, lse
 
 
-def bwd_workspace_bytes(B, N, H, D, *, ending=False, dbias_fp32=False, scale=None) -> int:
+def bwd_workspace_bytes(B, N, H, D, *, ending=False, dbias_fp32=False, scale=None, rows=None) -> int:
     lib = load_library()
-    prob = make_problem(B, N, H, D, ending=ending, dbias_fp32=dbias_fp32, scale=scale)
+    prob = make_problem(B, N, H, D, ending=ending, dbias_fp32=dbias_fp32, scale=scale, rows=rows)
     return int(lib.tri_attn_bwd_workspace_bytes(ctypes.byref(prob)))
 
 
 def tri_attn_bwd(q, k, v, bias, mask, o, o_residual, lse, d_o, *, ending=False, scale=None,
-                 dbias_fp32=False, workspace=None, kernel_events=None, out=None):
+                 dbias_fp32=False, workspace=None, kernel_events=None, out=None, rows=None):
     """Backward: returns (dq, dk, dv, dbias).  o_residual=None selects the
     uncompensated softmax correction rowsum(dO * float(o)); a bf16 o_residual is
     passed with the bf16-residual flag.  o, o_residual, lse and d_o must match the
@@ -183,7 +188,9 @@ def tri_attn_bwd(q, k, v, bias, mask, o, o_residual, lse, d_o, *, ending=False, 
     without bounds.  kernel_events, five raw hipEvent_t handles (ints), are recorded
     around each of the four backward kernels (tri_attn_bwd_timed).  `out`, if given,
     is a tuple (dq, dk, dv, dbias) of preallocated outputs written in place;
-    `workspace` a uint8 device tensor of at least bwd_workspace_bytes bytes."""
+    `workspace` a uint8 device tensor of at least bwd_workspace_bytes bytes.  rows =
+    (row_begin, row_end): gradients of those attention rows only, and dbias the
+    range's unreduced partial sum over its rows."""
     B, N, H, D = _check_inputs(q, k, v, bias, mask)
     _check_tensor("o", o, q.shape, (torch.bfloat16,), q.device)
     if o_residual is not None:
@@ -193,7 +200,7 @@ def tri_attn_bwd(q, k, v, bias, mask, o, o_residual, lse, d_o, *, ending=False, 
     lib = load_library()
     residual = "bf16" if o_residual is not None and o_residual.dtype == torch.bfloat16 else "fp32"
     prob = make_problem(B, N, H, D, ending=ending, dbias_fp32=dbias_fp32, scale=scale,
-                        residual=residual)
+                        residual=residual, rows=rows)
     nbytes = int(lib.tri_attn_bwd_workspace_bytes(ctypes.byref(prob)))
     if workspace is None:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=q.device)
@@ -225,7 +232,7 @@ def tri_attn_bwd(q, k, v, bias, mask, o, o_residual, lse, d_o, *, ending=False, 
 
 
 def tri_attn_bwd_noalloc(q, k, v, bias, mask, o, o_residual, lse, d_o, out, *, ending=False,
-                         scale=None, dbias_fp32=False):
+                         scale=None, dbias_fp32=False, rows=None):
     """tri_attn_bwd_noalloc: the backward with its workspace in the library's fixed
     device buffer, for callers that cannot allocate.  `out` = (dq, dk, dv, dbias) must
     be preallocated; nothing is allocated here.  Problems whose workspace exceeds
@@ -243,7 +250,7 @@ def tri_attn_bwd_noalloc(q, k, v, bias, mask, o, o_residual, lse, d_o, out, *, e
     lib = load_library()
     residual = "bf16" if o_residual is not None and o_residual.dtype == torch.bfloat16 else "fp32"
     prob = make_problem(B, N, H, D, ending=ending, dbias_fp32=dbias_fp32, scale=scale,
-                        residual=residual)
+                        residual=residual, rows=rows)
     st = lib.tri_attn_bwd_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(bias), _ptr(mask),
                                   _ptr(o), _ptr(o_residual), _ptr(lse), _ptr(d_o),
                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), _stream(q.device))

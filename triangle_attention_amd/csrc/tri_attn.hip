@@ -180,6 +180,7 @@ struct FwdArgs {
   Frame f;
   int B, N, H;
   int n_jblocks, n_chunks, rows_per_chunk;
+  int row_begin, row_end;  // attention rows computed: [row_begin, row_end)
   int bstride;  // fp16 row stride of the bias tile
   float c1;     // alpha * log2(e)
 };
@@ -241,8 +242,8 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
   // and then takes the next untaken one, so the waves of the workgroup, which share
   // SIMDs unevenly, finish within about one row of each other
   __shared__ int s_next_row;
-  const int r0 = chunk * a.rows_per_chunk;
-  const int r1 = min(N, r0 + a.rows_per_chunk);
+  const int r0 = a.row_begin + chunk * a.rows_per_chunk;
+  const int r1 = min(a.row_end, r0 + a.rows_per_chunk);
   if (tid == 0) s_next_row = r0 + FWD_WAVES;
   __syncthreads();
 
@@ -493,6 +494,7 @@ struct PrepArgs {
   float *stats;  // [B][N][H][2][N]: -lse/alpha, then -D
   Frame f;
   int B, N, H, D;
+  int row_begin, R;  // attention rows [row_begin, row_begin + R)
   float inv_alpha;
 };
 
@@ -504,17 +506,21 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
   // (b, first pair axis, second pair axis, h), so that the lanes of a wave read
   // contiguous runs of o, dO and the residual in both orientations; the attended
   // frame's row and query follow from the strides.
-  const long long total = (long long)a.B * a.N * a.N * a.H;
+  // (only the attention rows of the range: along the first pair axis for the starting
+  // node, the second for the ending node, so the order stays the memory order)
+  const long long total = (long long)a.B * a.R * a.N * a.H;
   const long long idx = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 2;
   const int j = threadIdx.x & 3;
   if (idx >= total) return;  // whole groups of four leave together
+  const bool starting = a.f.sR > a.f.sQ;  // rows along the first pair axis
   const int h = (int)(idx % a.H);
   long long t = idx / a.H;
-  const int p2 = (int)(t % a.N);
-  t /= a.N;
-  const int p1 = (int)(t % a.N);
-  const int b = (int)(t / a.N);
-  const bool starting = a.f.sR > a.f.sQ;  // rows along the first pair axis
+  const int n2 = starting ? a.N : a.R;  // extent of the second pair axis in the walk
+  const int n1 = starting ? a.R : a.N;
+  const int p2 = (int)(t % n2) + (starting ? 0 : a.row_begin);
+  t /= n2;
+  const int p1 = (int)(t % n1) + (starting ? a.row_begin : 0);
+  const int b = (int)(t / n1);
   const int r = starting ? p1 : p2, q = starting ? p2 : p1;
   const bool has = 8 * j < a.D;
   const long long base =
@@ -612,6 +618,7 @@ struct BwdArgs {
   Frame f;
   int B, N, H;
   int n_kblocks, n_chunks, rows_per_chunk;
+  int row_begin, row_end;  // attention rows computed: [row_begin, row_end)
   float alpha, c1;
 };
 
@@ -662,8 +669,8 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
   const int k0 = kb * BWD_BK;
   const int nkt = min(2, (N - k0) / 32);  // key tiles present in this block (1 at a ragged end)
   const int njt = N / 32;
-  const int r0 = chunk * a.rows_per_chunk;
-  const int r1 = min(N, r0 + a.rows_per_chunk);
+  const int r0 = a.row_begin + chunk * a.rows_per_chunk;
+  const int r1 = min(a.row_end, r0 + a.rows_per_chunk);
   const float c1 = a.c1;
 
   // row r of head h of batch b: q, k, v, dO (element offset) and the statistics row
@@ -997,6 +1004,7 @@ struct ReduceArgs {
   void *dbias;
   Frame f;
   int B, N, H, D, T, C, dbias_fp32;
+  int row_begin, R;  // attention rows [row_begin, row_begin + R) of dq
   float alpha;
 };
 
@@ -1005,10 +1013,10 @@ struct ReduceArgs {
 __global__ __launch_bounds__(256) void reduce_dq_kernel(ReduceArgs a) {
   // partials and output hold D channels (32 or 16)
   const long long E = (long long)a.B * a.N * a.N * a.H * a.D;
-  // thread -> 8 channels of output element (b, r, q, h, c), heads inside positions, so
-  // that a wave writes whole multi-head position segments
+  // thread -> 8 channels of output element (b, r, q, h, c), r in the row range, heads
+  // inside positions, so that a wave writes whole multi-head position segments
   const long long e = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 8;
-  if (e >= E) return;
+  if (e >= (long long)a.B * a.R * a.N * a.H * a.D) return;
   const int dsh = a.D == 32 ? 5 : 4;  // D is 32 or 16
   const int c = (int)(e & (a.D - 1));
   long long u = e >> dsh;
@@ -1016,8 +1024,8 @@ __global__ __launch_bounds__(256) void reduce_dq_kernel(ReduceArgs a) {
   u /= a.H;
   const int q = (int)(u % a.N);
   u /= a.N;
-  const int r = (int)(u % a.N);
-  const int b = (int)(u / a.N);
+  const int r = (int)(u % a.R) + a.row_begin;
+  const int b = (int)(u / a.R);
   const long long pe = ((((long long)b * a.N + r) * a.H + h) * a.N + q) * a.D + c;  // partial element
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int t = 0; t < a.T; ++t) {
@@ -1110,7 +1118,23 @@ tri_attn_status check_problem(const tri_attn_problem *p) {
     return TRI_ATTN_ERROR_NOT_SUPPORTED;
   if ((p->D != HD && p->D != 16) || p->N % 32 != 0 || p->N > kMaxN || p->H > kMaxH) return TRI_ATTN_ERROR_NOT_SUPPORTED;
   if (p->B * p->N * p->N * p->H * p->D > (int64_t)1 << 40) return TRI_ATTN_ERROR_NOT_SUPPORTED;
+  // attention rows: [row_begin, row_end) with 0 <= row_begin < row_end <= N, or
+  // 0, 0 for all rows
+  if (!(p->row_begin == 0 && p->row_end == 0) &&
+      !(p->row_begin >= 0 && p->row_begin < p->row_end && p->row_end <= p->N))
+    return TRI_ATTN_ERROR_INVALID_VALUE;
   return TRI_ATTN_SUCCESS;
+}
+
+// The attention rows a call computes (after check_problem).
+void row_range(const tri_attn_problem *p, int &i0, int &i1) {
+  if (p->row_begin == 0 && p->row_end == 0) {
+    i0 = 0;
+    i1 = (int)p->N;
+  } else {
+    i0 = (int)p->row_begin;
+    i1 = (int)p->row_end;
+  }
 }
 
 Frame make_frame(const tri_attn_problem *p) {
@@ -1151,12 +1175,16 @@ BwdPlan plan_bwd(const tri_attn_problem *p, int cus) {
   pl.JT = (njt + BWD_WAVES - 1) / BWD_WAVES;
   pl.T = (N + BWD_BK - 1) / BWD_BK;
   // one workgroup per CU (its LDS and registers fill one); one wave of workgroups
+  // over the call's R attention rows
+  int i0, i1;
+  row_range(p, i0, i1);
+  const int R = i1 - i0;
   const int groups = (int)(p->B * p->H * pl.T);
   int C = cus / groups;
   if (C < 1) C = 1;
-  if (C > N) C = N;
-  pl.rows_per_chunk = (N + C - 1) / C;
-  pl.C = (N + pl.rows_per_chunk - 1) / pl.rows_per_chunk;
+  if (C > R) C = R;
+  pl.rows_per_chunk = (R + C - 1) / C;
+  pl.C = (R + pl.rows_per_chunk - 1) / pl.rows_per_chunk;
   pl.lds_bytes = 0;  // static LDS, sized by the JT instantiation
   const size_t B = p->B, NN = (size_t)N * N, H = p->H;
   pl.off_stats = 0;
@@ -1263,12 +1291,14 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
   a.bstride = a.N + ((a.N & 63) ? 36 : 4);
   // one workgroup per CU (its LDS fills one) and, where the problem allows, a single
   // round of workgroups: the block's bias is then staged once per CU
+  row_range(problem, a.row_begin, a.row_end);
+  const int R = a.row_end - a.row_begin;
   const int groups = a.B * a.H * a.n_jblocks;
   int chunks = device_cus() / groups;
   if (chunks < 1) chunks = 1;
-  if (chunks > a.N) chunks = a.N;
-  a.rows_per_chunk = (a.N + chunks - 1) / chunks;
-  a.n_chunks = (a.N + a.rows_per_chunk - 1) / a.rows_per_chunk;
+  if (chunks > R) chunks = R;
+  a.rows_per_chunk = (R + chunks - 1) / chunks;
+  a.n_chunks = (R + a.rows_per_chunk - 1) / a.rows_per_chunk;
   const size_t lds = (size_t)FWD_BJ * a.bstride * 2 + (size_t)FWD_WAVES * 2 * 32 * HD * 2;
   const bool res32 = (p.flags & TRI_ATTN_FLAG_RESIDUAL_BF16) == 0;
   void (*const kernels[8])(FwdArgs) = {fwd_kernel<false, false, 32>, fwd_kernel<false, true, 32>,
@@ -1354,9 +1384,13 @@ static tri_attn_status bwd_run(const tri_attn_problem *problem, const void *q, c
   pa.N = (int)p.N;
   pa.H = (int)p.H;
   pa.D = (int)p.D;
+  int i0, i1;
+  row_range(problem, i0, i1);
+  pa.row_begin = i0;
+  pa.R = i1 - i0;
   auto mark = [&](int i) { return !marks[i] || hipEventRecord(marks[i], stream) == hipSuccess; };
   if (!mark(0)) return TRI_ATTN_ERROR_LAUNCH_FAILED;
-  const long long nrows = (long long)p.B * p.N * p.N * p.H;
+  const long long nrows = (long long)p.B * pa.R * p.N * p.H;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((4 * nrows + 255) / 256)), dim3(256), 0, stream, pa);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
 
@@ -1379,6 +1413,8 @@ static tri_attn_status bwd_run(const tri_attn_problem *problem, const void *q, c
   ba.n_kblocks = pl.T;
   ba.n_chunks = pl.C;
   ba.rows_per_chunk = pl.rows_per_chunk;
+  ba.row_begin = i0;
+  ba.row_end = i1;
   ba.alpha = alpha;
   ba.c1 = alpha * kLog2e;
   const int grid = ba.B * ba.H * pl.T * pl.C;
@@ -1401,7 +1437,10 @@ static tri_attn_status bwd_run(const tri_attn_problem *problem, const void *q, c
   ra.C = pl.C;
   ra.dbias_fp32 = (p.flags & TRI_ATTN_FLAG_DBIAS_FP32) ? 1 : 0;
   ra.alpha = alpha;
-  hipLaunchKernelGGL(reduce_dq_kernel, dim3((unsigned)((E / 8 + 255) / 256)), dim3(256), 0, stream, ra);
+  ra.row_begin = i0;
+  ra.R = i1 - i0;
+  const size_t E_rows = (size_t)p.B * ra.R * p.N * p.H * p.D;  // dq elements of the row range
+  hipLaunchKernelGGL(reduce_dq_kernel, dim3((unsigned)((E_rows / 8 + 255) / 256)), dim3(256), 0, stream, ra);
   if (hipGetLastError() != hipSuccess || !mark(3)) return TRI_ATTN_ERROR_LAUNCH_FAILED;
   hipLaunchKernelGGL(reduce_dbias_kernel, dim3((unsigned)((nb / 4 + 255) / 256)), dim3(256), 0, stream, ra);
   if (hipGetLastError() != hipSuccess || !mark(4)) return TRI_ATTN_ERROR_LAUNCH_FAILED;
