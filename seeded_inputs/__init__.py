@@ -22,7 +22,7 @@ import torch
 
 # tensor tags: each tensor of a workload draws from its own generator,
 # seeded with seed * 16 + tag
-_TAG = {"q": 0, "k": 1, "v": 2, "do": 3, "bias": 4, "length": 5}
+_TAG = {"q": 0, "k": 1, "v": 2, "do": 3, "bias": 4, "length": 5, "tm_a": 6, "tm_b": 7, "tm_g": 8}
 
 
 @dataclass(frozen=True)
@@ -129,3 +129,48 @@ def flop_count(B: int, N: int, H: int, D: int, mask: torch.Tensor | None) -> int
     adds are not counted)."""
     valid = N * N * B if mask is None else int(mask.to(torch.int64).sum())
     return 14 * D * H * N * valid
+
+
+# Triangle multiplicative update's contraction: the projected factors a, b and the
+# upstream gradient g, channel-major [B, C, N, N] bf16, N(0, 1) entries.  The crop
+# sizes are those of the attention workloads, with C = 128 channels.
+@dataclass(frozen=True)
+class TriMulWorkload:
+    name: str
+    index: int
+    B: int
+    N: int
+    C: int
+    description: str
+
+    @property
+    def seed(self) -> int:
+        return 2000 + self.index
+
+
+TRIMUL_WORKLOADS = {
+    w.name: w
+    for w in [
+        TriMulWorkload("trimul_tiny64", 1, 1, 64, 16, "B=1 N=64 C=16"),
+        TriMulWorkload("trimul_crop384", 2, 1, 384, 128, "B=1 N=384 C=128"),
+        TriMulWorkload("trimul_crop640", 3, 1, 640, 128, "B=1 N=640 C=128"),
+        TriMulWorkload("trimul_crop768", 4, 1, 768, 128, "B=1 N=768 C=128"),
+    ]
+}
+
+
+def make_trimul(B: int, N: int, C: int, seed: int) -> dict:
+    """Seeded bf16 factors a, b and upstream gradient g, each [B, C, N, N] (CPU)."""
+    shp = (B, C, N, N)
+    return {"a": _randn_bf16(shp, seed, "tm_a"), "b": _randn_bf16(shp, seed, "tm_b"),
+            "g": _randn_bf16(shp, seed, "tm_g")}
+
+
+def make_trimul_workload(name: str) -> dict:
+    w = TRIMUL_WORKLOADS[name]
+    return make_trimul(w.B, w.N, w.C, w.seed)
+
+
+def trimul_flop_count(B: int, N: int, C: int) -> int:
+    """Forward + backward flops of the contraction: three N^3 products per channel."""
+    return 3 * 2 * B * C * N ** 3

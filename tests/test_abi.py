@@ -15,6 +15,7 @@ import triangle_attention_amd as ta
 
 ROOT = Path(__file__).resolve().parents[1]
 HEADER = ROOT / "include" / "tri_attn.h"
+HEADERS = (HEADER, ROOT / "include" / "tri_mul.h")
 
 OK, INVALID, UNSUPPORTED, WORKSPACE, LAUNCH, ABI = 0, 1, 2, 3, 4, 5
 ADDR = 1 << 40  # fake, 256-byte-aligned device address
@@ -29,9 +30,11 @@ def lib():
 
 
 def declared_functions():
-    text = HEADER.read_text()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tri_attn_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", h.read_text(), flags=re.S)
+        names |= set(re.findall(r"\b(tri_(?:attn|mul)_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_exported_set():
@@ -39,12 +42,13 @@ def test_header_declares_the_exported_set():
 
 
 def declaration_comments():
-    """The comment block directly above each declared call in the header."""
-    text = HEADER.read_text()
+    """The comment block directly above each declared call in the headers."""
     out = {}
-    for m in re.finditer(r"/\*((?:(?!\*/).)*)\*/\s*(?:[A-Za-z_][A-Za-z_0-9 ]*\*?\s*)(tri_attn_[a-z_]+)\s*\(",
-                         text, flags=re.S):
-        out[m.group(2)] = re.sub(r"\s*\n\s*\*?\s*", " ", m.group(1))   # one line, no leading '*'
+    for h in HEADERS:
+        text = h.read_text()
+        for m in re.finditer(r"/\*((?:(?!\*/).)*)\*/\s*(?:[A-Za-z_][A-Za-z_0-9 ]*\*?\s*)(tri_(?:attn|mul)_[a-z_]+)\s*\(",
+                             text, flags=re.S):
+            out[m.group(2)] = re.sub(r"\s*\n\s*\*?\s*", " ", m.group(1))   # one line, no leading '*'
     return out
 
 
@@ -339,3 +343,55 @@ def test_row_range_workspace_follows_the_range_plan(lib):
     base = a256(256 * 4 * 2 * 256 * 4) + a256(4 * 256 * 256 * 4 * 32 * 2)
     assert full == base + a256(bench.row_chunks(16, 256) * 4 * 256 * 256 * 4)
     assert part == base + a256(bench.row_chunks(16, 32) * 4 * 256 * 256 * 4)
+
+
+# ---- the triangle multiplicative update's contraction (include/tri_mul.h) ----
+
+def call_mul_fwd(lib, prob, ptrs=None):
+    a, b, z = ptrs or fake_ptrs(3)
+    return lib.tri_mul_fwd(ctypes.byref(prob) if prob is not None else None, a, b, z, None)
+
+
+def call_mul_bwd(lib, prob, ptrs=None):
+    a, b, g, da, db = ptrs or fake_ptrs(5)
+    return lib.tri_mul_bwd(ctypes.byref(prob), a, b, g, da, db, None)
+
+
+def test_tri_mul_abi_version(lib):
+    assert lib.tri_mul_abi_version() == ta.TRI_MUL_ABI_VERSION
+
+
+@pytest.mark.parametrize("field,value,expect", [
+    ("abi_version", ta.TRI_MUL_ABI_VERSION + 1, ABI), ("B", 0, INVALID), ("N", 0, INVALID), ("C", 0, INVALID),
+    ("N", 48, UNSUPPORTED), ("N", 1056, UNSUPPORTED), ("flags", 2, UNSUPPORTED), ("C", 70000, UNSUPPORTED),
+])
+def test_tri_mul_problem_validation(lib, field, value, expect):
+    prob = ta.make_trimul_problem(1, 64, 8)
+    setattr(prob, field, value)
+    assert call_mul_fwd(lib, prob) == expect
+    assert call_mul_bwd(lib, prob) == expect
+
+
+def test_tri_mul_rejects_null_misaligned_and_aliased_pointers(lib):
+    prob = ta.make_trimul_problem(1, 64, 8)
+    assert call_mul_fwd(lib, None) == INVALID
+    for which in range(3):
+        p = fake_ptrs(3)
+        p[which] = None
+        assert call_mul_fwd(lib, prob, p) == INVALID
+        p = fake_ptrs(3)
+        p[which] = ctypes.c_void_p(p[which].value + 2)
+        assert call_mul_fwd(lib, prob, p) == INVALID
+    p = fake_ptrs(3)
+    p[2] = ctypes.c_void_p(p[0].value + 64)   # z inside a
+    assert call_mul_fwd(lib, prob, p) == INVALID
+    for which in range(5):
+        p = fake_ptrs(5)
+        p[which] = None
+        assert call_mul_bwd(lib, prob, p) == INVALID
+    p = fake_ptrs(5)
+    p[4] = p[3]   # db == da
+    assert call_mul_bwd(lib, prob, p) == INVALID
+    p = fake_ptrs(5)
+    p[3] = p[2]   # da == dz
+    assert call_mul_bwd(lib, prob, p) == INVALID

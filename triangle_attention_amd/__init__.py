@@ -38,7 +38,9 @@ STATUS_NAMES = {
 
 EXPORTED_SYMBOLS = ("tri_attn_abi_version", "tri_attn_status_string", "tri_attn_fwd",
                     "tri_attn_bwd_workspace_bytes", "tri_attn_bwd", "tri_attn_bwd_timed",
-                    "tri_attn_bwd_noalloc")
+                    "tri_attn_bwd_noalloc", "tri_mul_abi_version", "tri_mul_fwd", "tri_mul_bwd")
+TRI_MUL_ABI_VERSION = 1
+TRI_MUL_FLAG_INCOMING = 1
 NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024   # TRI_ATTN_NOALLOC_SCRATCH_BYTES
 
 
@@ -48,6 +50,12 @@ class Problem(ctypes.Structure):
                 ("B", ctypes.c_int64), ("N", ctypes.c_int64), ("H", ctypes.c_int64),
                 ("D", ctypes.c_int64), ("softmax_scale", ctypes.c_float),
                 ("row_begin", ctypes.c_int64), ("row_end", ctypes.c_int64)]
+
+
+class TriMulProblem(ctypes.Structure):
+    """Mirror of ``tri_mul_problem``."""
+    _fields_ = [("abi_version", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("B", ctypes.c_int64), ("N", ctypes.c_int64), ("C", ctypes.c_int64)]
 
 
 class TriAttnError(RuntimeError):
@@ -85,7 +93,14 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.tri_attn_bwd_timed.restype = i32
     lib.tri_attn_bwd_noalloc.argtypes = [pp] + [vp] * 13 + [vp]
     lib.tri_attn_bwd_noalloc.restype = i32
-    if lib.tri_attn_abi_version() != ABI_VERSION:
+    tp = ctypes.POINTER(TriMulProblem)
+    lib.tri_mul_abi_version.argtypes = []
+    lib.tri_mul_abi_version.restype = i32
+    lib.tri_mul_fwd.argtypes = [tp, vp, vp, vp, vp]
+    lib.tri_mul_fwd.restype = i32
+    lib.tri_mul_bwd.argtypes = [tp, vp, vp, vp, vp, vp, vp]
+    lib.tri_mul_bwd.restype = i32
+    if lib.tri_attn_abi_version() != ABI_VERSION or lib.tri_mul_abi_version() != TRI_MUL_ABI_VERSION:
         raise RuntimeError("libtri_attn.so ABI version mismatch")
     if path is None:
         _lib = lib
@@ -259,6 +274,51 @@ def tri_attn_bwd_noalloc(q, k, v, bias, mask, o, o_residual, lse, d_o, out, *, e
     return dq, dk, dv, dbias
 
 
+# ---- triangle multiplicative update: the contraction (include/tri_mul.h) ----
+
+def make_trimul_problem(B, N, C, *, incoming=False, abi_version=TRI_MUL_ABI_VERSION) -> TriMulProblem:
+    return TriMulProblem(abi_version, TRI_MUL_FLAG_INCOMING if incoming else 0, B, N, C)
+
+
+def _check_trimul(x):
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous() or x.dim() != 4 or x.shape[2] != x.shape[3]:
+        raise ValueError("triangle multiplication operands are contiguous bf16 CUDA tensors [B, C, N, N]")
+    return tuple(x.shape)
+
+
+def tri_mul_fwd(a, b, *, incoming=False, out=None):
+    """z = the outgoing (or incoming) contraction of a and b, all bf16 [B, C, N, N]."""
+    B, C, N, _ = _check_trimul(a)
+    for name, t in (("b", b),) + ((("out", out),) if out is not None else ()):
+        _check_tensor(name, t, a.shape, (torch.bfloat16,), a.device)
+    lib = load_library()
+    z = torch.empty_like(a) if out is None else out
+    st = lib.tri_mul_fwd(ctypes.byref(make_trimul_problem(B, N, C, incoming=incoming)), _ptr(a), _ptr(b),
+                         _ptr(z), _stream(a.device))
+    if st != 0:
+        raise TriAttnError(st, "tri_mul_fwd")
+    return z
+
+
+def tri_mul_bwd(a, b, dz, *, incoming=False, out=None):
+    """(da, db) of the contraction for the upstream gradient dz, all bf16 [B, C, N, N]."""
+    B, C, N, _ = _check_trimul(a)
+    for name, t in (("b", b), ("dz", dz)):
+        _check_tensor(name, t, a.shape, (torch.bfloat16,), a.device)
+    if out is None:
+        da, db = torch.empty_like(a), torch.empty_like(a)
+    else:
+        da, db = out
+        for name, t in (("da", da), ("db", db)):
+            _check_tensor(name, t, a.shape, (torch.bfloat16,), a.device)
+    lib = load_library()
+    st = lib.tri_mul_bwd(ctypes.byref(make_trimul_problem(B, N, C, incoming=incoming)), _ptr(a), _ptr(b),
+                         _ptr(dz), _ptr(da), _ptr(db), _stream(a.device))
+    if st != 0:
+        raise TriAttnError(st, "tri_mul_bwd")
+    return da, db
+
+
 class TriAttnFunction(torch.autograd.Function):
     """Autograd wrapper: the forward saves o, its residual and lse; the backward
     recomputes every probability tile once inside the HIP kernels."""
@@ -285,6 +345,7 @@ def tri_attn(q, k, v, bias, mask=None, ending=False, scale=None):
 
 
 __all__ = ["tri_attn", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_bwd_noalloc", "bwd_workspace_bytes",
+           "tri_mul_fwd", "tri_mul_bwd", "make_trimul_problem", "TriMulProblem",
            "load_library", "NOALLOC_SCRATCH_BYTES",
            "make_problem", "Problem", "TriAttnError", "TriAttnFunction", "LIB_PATH",
            "EXPORTED_SYMBOLS"]

@@ -9,6 +9,8 @@ from pathlib import Path
 HERE = Path(__file__).resolve().parent
 ROOT = HERE.parent
 SRC = HERE / "csrc" / "tri_attn.hip"
+# the triangle multiplicative update's contraction, built into the same library
+TRI_MUL_SRC = HERE / "csrc" / "tri_mul.hip"
 LIB = HERE / "libtri_attn.so"
 # the matrix-core rate probe bench.py reports next to the published peak
 PROBE_SRC = HERE / "csrc" / "mfma_probe.hip"
@@ -29,22 +31,22 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Wno-unused-command-line-argument"]
 
 
-def _compile(src: Path, lib: Path, verbose: bool) -> None:
+def _compile(srcs, lib: Path, verbose: bool) -> None:
     tmp = lib.with_suffix(".so.tmp")
-    cmd = [HIPCC, *FLAGS, "-I", str(ROOT / "include"), "-o", str(tmp), str(src)]
+    cmd = [HIPCC, *FLAGS, "-I", str(ROOT / "include"), "-o", str(tmp), *[str(s) for s in srcs]]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed building {src}")
+        raise RuntimeError(f"hipcc failed building {lib}")
     os.replace(tmp, lib)
 
 
 def build(verbose: bool = False) -> Path:
     """Compile the library and the matrix-core probe; returns the library's path."""
-    _compile(SRC, LIB, verbose)
-    _compile(PROBE_SRC, PROBE_LIB, verbose)
+    _compile([SRC, TRI_MUL_SRC], LIB, verbose)
+    _compile([PROBE_SRC], PROBE_LIB, verbose)
     return LIB
 
 
