@@ -136,14 +136,20 @@ def row_chunks(groups: int, N: int, cus: int = 256) -> int:
     return -(-N // per)
 
 
-def bias_dbias_bytes(B: int, N: int, H: int, dbias_bytes: int = 2) -> dict:
+def block_size(D: int) -> int:
+    """Queries per forward workgroup and keys per backward workgroup in the library's
+    launch plan: 64, or 32 at head dimension 64."""
+    return 32 if D == 64 else 64
+
+
+def bias_dbias_bytes(B: int, N: int, H: int, dbias_bytes: int = 2, D: int = 32) -> dict:
     """Pair-bias and bias-gradient HBM bytes of one step.  Every forward workgroup
-    (b, h, 64-query block, row chunk) and every backward workgroup (b, h, 64-key
-    block, row chunk) stages its bias block once; the backward main kernel writes
-    one fp32 dbias partial per row chunk, which the dbias reduction reads back
-    before writing dbias."""
+    (b, h, query block, row chunk) and every backward workgroup (b, h, key block, row
+    chunk) stages its bias block once; the backward main kernel writes one fp32
+    dbias partial per row chunk, which the dbias reduction reads back before writing
+    dbias."""
     nb = B * H * N * N
-    blocks = -(-N // 64)
+    blocks = -(-N // block_size(D))
     c_fwd = row_chunks(B * H * blocks, N)
     c_bwd = row_chunks(B * H * blocks, N)
     return {"bias_tensor_bytes": 2 * nb,
@@ -372,7 +378,7 @@ def run_workload(args, workload: str, ending: bool, with_extras: bool) -> dict:
     value = flops / (ms * 1e-3) / 1e12
     bwd_main_flops = flops * 10 / 14   # S, dP, dV, dK, dQ products of the backward
     achieved = bwd_main_flops / (main_ms * 1e-3) / 1e12
-    bd = bias_dbias_bytes(w.B, w.N, w.H)
+    bd = bias_dbias_bytes(w.B, w.N, w.H, D=w.D)
     red_ms = statistics.median(kern["reduce_dbias"])
     bd["reduce_dbias_ms"] = round(red_ms, 4)
     bd["reduce_dbias_GBps"] = round(bd["dbias_reduction_bytes"] / (red_ms * 1e-3) / 1e9, 1)

@@ -103,9 +103,11 @@ typedef struct {
     int64_t row_begin, row_end;
 } tri_attn_problem;
 
-/* Supported sizes of this build: D == 32 or D == 16, N a multiple of 32 with
- * 32 <= N <= 768, B >= 1, 1 <= H <= 64.  D == 16 runs the same kernels with the
- * tiles' channels 16..31 held at zero. */
+/* Supported sizes of this build: D == 16, 32 or 64, N a multiple of 32 with
+ * 32 <= N <= 768, B >= 1, 1 <= H <= 64.  D == 16 runs the D == 32 kernels with the
+ * tiles' channels 16..31 held at zero; D == 64 runs kernels with 64-channel tiles,
+ * 32-query forward blocks and 32-key backward blocks (its backward workspace holds
+ * N / 32 dQ partials instead of N / 64). */
 
 /*
  * Returns TRI_ATTN_ABI_VERSION of the loaded library (biocloudservice page,
@@ -151,8 +153,9 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem,
  * 0 if the problem is invalid or unsupported (biocloudservice page, "它优化了什么，
  * 而不是只“少存一点张量”": the backward never writes the full score gradient
  * out).  The workspace holds the per-query statistics (-lse/alpha and -D, fp32,
- * 2*B*N*H*N values), one bf16 dQ partial per 64-key block (ceil(N/64)*B*N*N*H*D
- * values) and one fp32 pair-bias-gradient partial per row chunk (C*B*H*N*N values,
+ * 2*B*N*H*N values), one bf16 dQ partial per key block of 64 keys (32 keys at
+ * D == 64: ceil(N/64)*B*N*N*H*D or N/32*B*N*N*H*D values) and one fp32
+ * pair-bias-gradient partial per row chunk (C*B*H*N*N values,
  * C = the number of row chunks the launch plan uses on this device), each
  * 256-byte aligned.  At N = 768, H = 4, D = 32 that is 1.87 GB against the 3.6 GB
  * of one bf16 score gradient (N^3*H values).  Host-only; no HIP call except the

@@ -57,6 +57,8 @@ WORKLOADS = {
                  "B=1 N=768 H=4 d=32, all keys valid (starting and ending node)"),
         Workload("crop768_h8d16", 6, 1, 768, 8, 16, 1.0, "none",
                  "B=1 N=768 H=8 d=16 (the same 128 pair channels as H=4 d=32), all keys valid"),
+        Workload("crop768_h2d64", 7, 1, 768, 2, 64, 1.0, "none",
+                 "B=1 N=768 H=2 d=64 (the same 128 pair channels as H=4 d=32), all keys valid"),
     ]
 }
 

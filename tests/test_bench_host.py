@@ -65,10 +65,11 @@ def test_bias_dbias_bytes_at_crop768():
 
 
 @pytest.mark.parametrize("B,N,H,D", [(1, 768, 4, 32), (1, 640, 4, 32), (1, 384, 4, 32), (2, 352, 3, 32),
-                                     (1, 768, 8, 16), (3, 128, 64, 32), (1, 96, 1, 16)])
+                                     (1, 768, 8, 16), (3, 128, 64, 32), (1, 96, 1, 16),
+                                     (1, 768, 2, 64), (2, 96, 3, 64), (1, 256, 33, 64)])
 def test_row_chunks_match_the_library_plan(B, N, H, D):
     """The library's backward workspace is the statistics, the dQ partials (one per
-    64-key block) and one fp32 dbias partial per row chunk, each 256-byte aligned:
+    key block: 64 keys, 32 at D = 64) and one fp32 dbias partial per row chunk, each 256-byte aligned:
     rebuilt from bench.row_chunks it must equal tri_attn_bwd_workspace_bytes."""
     import ctypes
     import triangle_attention_amd as ta
@@ -77,7 +78,7 @@ def test_row_chunks_match_the_library_plan(B, N, H, D):
 
     def a256(x):
         return (x + 255) // 256 * 256
-    T = -(-N // 64)
+    T = -(-N // bench.block_size(D))
     C = bench.row_chunks(B * H * T, N)
     want = a256(B * N * H * 2 * N * 4) + a256(T * B * N * N * H * D * 2) + a256(C * B * H * N * N * 4)
     assert got == want

@@ -175,10 +175,11 @@ def test_pad256_full(ta, ending):
     check_full(ta, si.make_workload("pad256"), ending=ending, tag="pad256")
 
 
-def chunk_rows(B, N, H):
+def chunk_rows(B, N, H, D=32):
     """First, second and last row of every row chunk of the launch plan (one round of
-    workgroups of 64 queries or keys; the same chunking in both passes)."""
-    C = bench.row_chunks(B * H * -(-N // 64), N)
+    workgroups of 64 queries or keys, 32 at D = 64; the same chunking in both
+    passes)."""
+    C = bench.row_chunks(B * H * -(-N // bench.block_size(D)), N)
     per = -(-N // C)
     rows = set()
     for c in range(C):
@@ -187,8 +188,8 @@ def chunk_rows(B, N, H):
     return rows
 
 
-def sample_rows(N, H=4, B=1):
-    rows = {0, 1, N // 2, N - 1, 37 % N, (N * 5) // 7} | chunk_rows(B, N, H)
+def sample_rows(N, H=4, B=1, D=32):
+    rows = {0, 1, N // 2, N - 1, 37 % N, (N * 5) // 7} | chunk_rows(B, N, H, D)
     return [(0, r) for r in sorted(rows)]
 
 
@@ -304,7 +305,8 @@ RERUN_FILLS = (0xFF, 0x00, 0x7F, 0xA5, 0x5A)
 
 @pytest.mark.parametrize("name,reps,ending", [("tiny64", 3, False), ("pad256", 3, False),
                                               ("crop640", 3, False), ("crop768_h8d16", 3, False),
-                                              ("crop768", 5, False), ("crop768", 5, True)])
+                                              ("crop768", 5, False), ("crop768", 5, True),
+                                              ("crop768_h2d64", 5, False), ("crop768_h2d64", 5, True)])
 def test_bitwise_determinism(ta, name, reps, ending):
     inp = si.make_workload(name)
     say(f"[determinism] {name} ending={ending} x{reps}")
@@ -423,6 +425,42 @@ def test_head_dim16_crop768_sampled(ta, ending):
                   sample_dbias(w.N, w.H), "crop768_h8d16")
 
 
+@pytest.mark.parametrize("B,N,H,mask_kind,ending", [
+    (1, 64, 2, "none", False),
+    (1, 64, 2, "random", True),
+    (1, 256, 2, "pad32", False),       # the workload sizes of pad256 at H = 2, d = 64
+    (1, 256, 2, "pad32", True),
+    (2, 96, 3, "random", False),       # three 32-key blocks, B > 1, an odd head count
+    (1, 160, 1, "pad32", True),
+])
+def test_head_dim64_full(ta, B, N, H, mask_kind, ending):
+    """Head dimension 64: 128-byte tile rows, four contraction slices, 32-query
+    forward blocks and 32-key backward blocks (whole-problem oracle)."""
+    inp = custom(B, N, H, 401 + N + H, mask_kind, D=64)
+    out, ref = check_full(ta, inp, ending=ending, tag=f"D64 B{B}N{N}H{H}{mask_kind}")
+    assert out["res"].shape[-1] == 64
+
+
+@pytest.mark.parametrize("ending", [False, True])
+def test_head_dim64_crop768_sampled(ta, ending):
+    """N = 768, H = 2, d = 64 (the 128 pair channels of the d = 32 workload) with a row
+    of every backward row chunk."""
+    w = si.WORKLOADS["crop768_h2d64"]
+    check_sampled(ta, si.make_workload("crop768_h2d64"), ending, sample_rows(w.N, w.H, D=64),
+                  sample_dbias(w.N, w.H), "crop768_h2d64")
+
+
+@pytest.mark.parametrize("B,N,H,mask_kind,ending", [
+    (1, 736, 3, "ragged512", False),  # 23 key blocks, ragged valid lengths, odd heads
+    (2, 352, 2, "random", True),
+])
+def test_head_dim64_large_sampled(ta, B, N, H, mask_kind, ending):
+    inp = custom(B, N, H, 503 + N + H, mask_kind, D=64)
+    rows = sorted(set((b, r) for b in range(B) for (_, r) in sample_rows(N, H, B, D=64)))
+    sel = sorted(set((b, h, j) for b in range(B) for (_, h, j) in sample_dbias(N, H)))
+    check_sampled(ta, inp, ending, rows, sel, f"D64 B{B}N{N}H{H}{mask_kind}")
+
+
 def test_fully_masked_rows_and_keys(ta):
     inp = custom(1, 64, 2, 11, "random")
     m = inp["mask"]
@@ -481,7 +519,7 @@ def test_custom_scale_and_fp32_dbias(ta):
     assert e32 <= e16
 
 
-@pytest.mark.parametrize("D,ending", [(32, False), (16, True)])
+@pytest.mark.parametrize("D,ending", [(32, False), (16, True), (64, True)])
 def test_autograd_wrapper(ta, D, ending):
     inp = custom(1, 64, 2, 17, "pad32", D=D)
     dev = torch.device("cuda:0")

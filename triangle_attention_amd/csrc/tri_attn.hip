@@ -47,7 +47,7 @@ static __device__ __align__(256) unsigned char scratch[TRI_ATTN_NOALLOC_SCRATCH_
 
 namespace {
 
-constexpr int HD = 32;  // head dimension handled by this build
+constexpr int HD = 32;  // channels of a 64-byte-row LDS tile (head dimensions 16 and 32)
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
@@ -131,6 +131,32 @@ __device__ __forceinline__ bf16x8 tr_operand_sw(const uint16_t *tile, int base_r
   return tr_read(p, p + 8 * HD);
 }
 
+// Tiles of TD = 32 or 64 channels.  For TD = 64 (128-byte rows) the 16-byte chunks
+// are permuted by row bits 1-3 as ((row >> 1) & 1) << 2 | ((row >> 2) & 3): the
+// row reads of 16 consecutive rows (one chunk each) then touch all 64 banks once,
+// and so do the transposing reads, whose 16-lane groups cover rows 4t..4t+3 over
+// four consecutive chunks (rows 4t and 4t + 2 map those chunks to disjoint halves).
+template <int TD>
+__device__ __forceinline__ int tile_off_w(int row, int col) {
+  if constexpr (TD == 32) {
+    return tile_off(row, col);
+  } else {
+    const int sw = (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+    return row * 64 + (((col >> 3) ^ sw) << 3) + (col & 7);
+  }
+}
+// tr_operand_sw for a tile_off_w<TD> tile, columns col0 .. col0 + 31
+template <int TD>
+__device__ __forceinline__ bf16x8 tr_operand_w(const uint16_t *tile, int base_row, int lane, int col0) {
+  if constexpr (TD == 32) {
+    return tr_operand_sw(tile, base_row, lane);
+  } else {
+    const int g = lane >> 4, w = lane & 15, m = w >> 2, s = w & 3;
+    const int row = base_row + 4 * (g >> 1) + m, col = col0 + 16 * (g & 1) + 4 * s;
+    return tr_read(tile + tile_off_w<64>(row, col), tile + tile_off_w<64>(row + 8, col));
+  }
+}
+
 // Workgroup index -> tile index such that consecutive tiles share an XCD
 // (workgroups are dealt to the 8 XCDs round-robin).
 __device__ __forceinline__ int xcd_remap(int L, int G) {
@@ -165,8 +191,25 @@ struct Frame {
 // tile's registers are staged to LDS as soon as they arrive and the next tile's
 // K, V and mask byte are fetched into them while the tile is computed; the key mask
 // is a compile-time variant, so an unmasked problem loads no mask at all.
-constexpr int FWD_WAVES = 12;
-constexpr int FWD_BJ = 64;
+// Head dimension 64: the K/V tiles have 128-byte rows (eight lanes per row), q.k
+// contracts over four 16-channel slices, o has two 32-channel halves, and a
+// workgroup takes 32 queries with 8 waves (two per SIMD), which keeps the LDS (bias
+// block and the waves' tiles) and each wave's registers within the same budgets.
+template <int DIN>
+struct FwdShape {
+  static constexpr int TD = DIN == 64 ? 64 : 32;    // channels of a K/V tile row
+  static constexpr int WAVES = DIN == 64 ? 8 : 12;  // waves per workgroup
+  static constexpr int BJ = DIN == 64 ? 32 : 64;    // queries per workgroup
+  static constexpr int NQ = BJ / 32;                // 32-query halves per workgroup
+  static constexpr int KP = TD / 8;                 // 16-byte parts of a K/V row
+  static constexpr int RPL = 64 / KP;               // K/V rows per wave-wide load
+  static constexpr int NL = 32 / RPL;               // loads per 32-key tile, each of K and V
+  static constexpr int NS = TD / 16;                // 16-channel slices of q.k
+  static constexpr int NC = TD / 32;                // 32-channel halves of o
+  static constexpr size_t lds_bytes(int bstride) {
+    return (size_t)BJ * bstride * 2 + (size_t)WAVES * 2 * 32 * TD * 2;
+  }
+};
 
 // a readable byte holding 1: the key mask of a problem without one
 __device__ const uint8_t kMaskAllValid = 1;
@@ -185,18 +228,21 @@ struct FwdArgs {
   float c1;     // alpha * log2(e)
 };
 
-// one key tile in flight: the lane's 16-byte chunks of K and V (rows lane/4 and
-// 16 + lane/4, part lane%4) and the mask byte of key (tile * 32 + lane % 32)
+// one key tile in flight: the lane's 16-byte chunks of K and V (rows lane / KP + RPL i,
+// part lane % KP) and the mask byte of key (tile * 32 + lane % 32)
+template <int NL>
 struct FwdTile {
-  u32x4 k0, k1, v0, v1;
+  u32x4 k[NL], v[NL];
   unsigned m;
 };
 
-// DIN: the head dimension of the caller's tensors (32, or 16: channels 16..31 are
+// DIN: the head dimension of the caller's tensors (64, 32, or 16: channels 16..31 are
 // then zero in every tile and never stored; the second contraction slice of q.k is
 // skipped)
 template <bool MASKED, bool RES32, int DIN>
-__global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(FwdShape<DIN>::WAVES * 64) void fwd_kernel(FwdArgs a) {
+  using S = FwdShape<DIN>;
+  constexpr int TD = S::TD, NQ = S::NQ, KP = S::KP, RPL = S::RPL, NL = S::NL, NS = S::NS, NC = S::NC;
   extern __shared__ float4 smem_f4[];
   _Float16 *bias_s = (_Float16 *)smem_f4;
   const int N = a.N;
@@ -215,17 +261,18 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
   const int chunk = t % a.n_chunks; t /= a.n_chunks;
   const int h = (t % (a.H / hw)) * hw + hp;
   const int b = t / (a.H / hw);
-  const int j0 = jb * FWD_BJ;
-  const bool two = j0 + 32 < N;  // second 32-query half present (N % 64 == 32: not in the last block)
-  uint16_t *kbuf = (uint16_t *)(bias_s + FWD_BJ * bstride) + wave * (2 * 32 * HD);
-  uint16_t *vbuf = kbuf + 32 * HD;
+  const int j0 = jb * S::BJ;
+  // second 32-query half present (64-query blocks; N % 64 == 32: not in the last block)
+  const bool two = NQ == 2 && j0 + 32 < N;
+  uint16_t *kbuf = (uint16_t *)(bias_s + S::BJ * bstride) + wave * (2 * 32 * TD);
+  uint16_t *vbuf = kbuf + 32 * TD;
 
   // pair bias of this query block: bias_s[j][k] = bias[b, h, j0 + j, k] in fp16
   {
     const uint16_t *src = a.bias + (((long long)b * a.H + h) * N + j0) * N;
     const int per_row = N / 8;
-    const int rows = two ? FWD_BJ : 32;
-    for (int idx = tid; idx < rows * per_row; idx += FWD_WAVES * 64) {
+    const int rows = two ? 64 : 32;
+    for (int idx = tid; idx < rows * per_row; idx += S::WAVES * 64) {
       const int row = idx / per_row, c8 = idx - row * per_row;
       const u32x4 w = ld16(src + (long long)row * N + c8 * 8);
       typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
@@ -244,28 +291,29 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
   __shared__ int s_next_row;
   const int r0 = a.row_begin + chunk * a.rows_per_chunk;
   const int r1 = min(a.row_end, r0 + a.rows_per_chunk);
-  if (tid == 0) s_next_row = r0 + FWD_WAVES;
+  if (tid == 0) s_next_row = r0 + S::WAVES;
   __syncthreads();
 
   const float c1 = a.c1;
   const int nkt = N / 32;
-  const int vkey = lane >> 2, vpart = lane & 3;  // the lane's K and V chunks within a tile
+  const int vkey = lane / KP, vpart = lane % KP;  // the lane's K and V chunks within a tile
   const long long mk = a.mask ? a.f.mK : 0;
   typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
   for (int r = r0 + wave; r < r1;) {
     const long long base = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * DIN;
-    bf16x8 qB[2][2];
+    bf16x8 qB[NQ][NS];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < NQ; ++s) {
       const uint16_t *qp = a.q + base + (long long)(j0 + (two ? 32 * s : 0) + jl) * a.f.sQ;
-      qB[s][0] = as_bf16x8(ld16(qp + 8 * hh));
-      qB[s][1] = DIN == 32 ? as_bf16x8(ld16(qp + 16 + 8 * hh)) : as_bf16x8((u32x4){0u, 0u, 0u, 0u});
+#pragma unroll
+      for (int x = 0; x < NS; ++x)
+        qB[s][x] = (DIN == 16 && x == 1) ? as_bf16x8((u32x4){0u, 0u, 0u, 0u}) : as_bf16x8(ld16(qp + 16 * x + 8 * hh));
     }
     const uint8_t *mrow = a.mask ? a.mask + (long long)b * a.f.mB + (long long)r * a.f.mR : &kMaskAllValid;
 
     // K and V tiles through buffer descriptors based at the tile (scalar registers):
     // the lane's byte offset is fixed for the row, so no per-tile vector address
-    // math.  A tile spans 32 * sQ * 2 < 2^27 bytes (N <= 768, H <= 64, D <= 32, in
+    // math.  A tile spans 32 * sQ * 2 < 2^29 bytes (N <= 768, H <= 64, D <= 64, in
     // either orientation), so every offset is far below 2^31.  With D = 16 the lanes
     // of channels 16..31 get the offset 2^31, past the tile: out-of-range buffer loads
     // return zeros.
@@ -273,32 +321,34 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
     const long long tstep = 32 * a.f.sQ;  // elements from one key tile to the next
     const int tile_bytes = (int)(tstep * 2);
     const int lane_off = (DIN == 16 && vpart >= 2) ? (int)0x80000000u : (int)(((long long)vkey * a.f.sQ + vpart * 8) * 2);
-    const int vhalf_b = (int)(16 * a.f.sQ * 2);
+    const int rstep_b = (int)(RPL * a.f.sQ * 2);  // bytes from one load's rows to the next's
     const uint8_t *ml = mrow + (long long)jl * mk;
     const long long mstep = 32 * mk;
     // every fetch is unconditional (a tile past the end refetches the last one, which
     // is then not processed): a load under a branch makes the compiler wait for all
     // outstanding memory operations where the paths merge
-    auto fetch = [&](int kt, FwdTile &T) {
+    auto fetch = [&](int kt, FwdTile<NL> &T) {
       kt = min(kt, nkt - 1);
       const __amdgpu_buffer_rsrc_t krs =
           __builtin_amdgcn_make_buffer_rsrc((void *)(krow + kt * tstep), (short)0, tile_bytes, kBufferWord3);
       const __amdgpu_buffer_rsrc_t vrs =
           __builtin_amdgcn_make_buffer_rsrc((void *)(vrow + kt * tstep), (short)0, tile_bytes, kBufferWord3);
-      T.k0 = __builtin_amdgcn_raw_buffer_load_b128(krs, lane_off, 0, 0);
-      T.k1 = __builtin_amdgcn_raw_buffer_load_b128(krs, lane_off, vhalf_b, 0);
-      T.v0 = __builtin_amdgcn_raw_buffer_load_b128(vrs, lane_off, 0, 0);
-      T.v1 = __builtin_amdgcn_raw_buffer_load_b128(vrs, lane_off, vhalf_b, 0);
+#pragma unroll
+      for (int i = 0; i < NL; ++i) T.k[i] = __builtin_amdgcn_raw_buffer_load_b128(krs, lane_off, i * rstep_b, 0);
+#pragma unroll
+      for (int i = 0; i < NL; ++i) T.v[i] = __builtin_amdgcn_raw_buffer_load_b128(vrs, lane_off, i * rstep_b, 0);
       T.m = MASKED ? (unsigned)ml[kt * mstep] : 1u;
     };
-    auto stage_k = [&](const FwdTile &T) {
-      *(u32x4 *)(kbuf + tile_off(vkey, vpart * 8)) = T.k0;
-      *(u32x4 *)(kbuf + tile_off(16 + vkey, vpart * 8)) = T.k1;
+    auto stage_k = [&](const FwdTile<NL> &T) {
+#pragma unroll
+      for (int i = 0; i < NL; ++i) *(u32x4 *)(kbuf + tile_off_w<TD>(vkey + RPL * i, vpart * 8)) = T.k[i];
     };
     // q.k of query half s against the staged key tile (masked keys at -inf)
     auto qk = [&](int s, unsigned valid) -> f32x16 {
-      f32x16 acc = mfma(*(const bf16x8 *)(kbuf + tile_off(jl, 8 * hh)), qB[s][0], (f32x16){});
-      if constexpr (DIN == 32) acc = mfma(*(const bf16x8 *)(kbuf + tile_off(jl, 16 + 8 * hh)), qB[s][1], acc);
+      f32x16 acc = mfma(*(const bf16x8 *)(kbuf + tile_off_w<TD>(jl, 8 * hh)), qB[s][0], (f32x16){});
+#pragma unroll
+      for (int x = 1; x < NS; ++x)
+        if (DIN != 16) acc = mfma(*(const bf16x8 *)(kbuf + tile_off_w<TD>(jl, 16 * x + 8 * hh)), qB[s][x], acc);
       if (__builtin_expect(valid != 0xffffffffu, 0)) {  // a partly masked tile
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -333,18 +383,23 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
     };
     // one tile of the output pass against the reference maxima m[s] (m[s] = -inf:
     // take this tile's maximum); T holds tile kt on entry and tile kt + 1 on return
-    auto tile = [&](int kt, FwdTile &T, float *m, f32x16 *oacc, float *lsum) {
+    auto tile = [&](int kt, FwdTile<NL> &T, float *m, f32x16 (*oacc)[NC], float *lsum) {
       const unsigned valid = MASKED ? (unsigned)__ballot(T.m != 0u) : 0xffffffffu;
       if (valid != 0u) {
         stage_k(T);
-        *(u32x4 *)(vbuf + tile_off(vkey, vpart * 8)) = T.v0;
-        *(u32x4 *)(vbuf + tile_off(16 + vkey, vpart * 8)) = T.v1;
+#pragma unroll
+        for (int i = 0; i < NL; ++i) *(u32x4 *)(vbuf + tile_off_w<TD>(vkey + RPL * i, vpart * 8)) = T.v[i];
       }
       fetch(kt + 1, T);
       if (valid == 0u) return;
-      const bf16x8 vA0 = tr_operand_sw(vbuf, 0, lane), vA1 = tr_operand_sw(vbuf, 16, lane);
+      bf16x8 vA[NC][2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
+      for (int c = 0; c < NC; ++c) {
+        vA[c][0] = tr_operand_w<TD>(vbuf, 0, lane, 32 * c);
+        vA[c][1] = tr_operand_w<TD>(vbuf, 16, lane, 32 * c);
+      }
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) {
         if (s == 1 && !two) break;
         const f32x16 acc = qk(s, valid);
         f16x4 bw[4];
@@ -361,33 +416,50 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
           ts += p[i];
         }
         lsum[s] += ts;
-        oacc[s] = mfma(vA0, pack8(p), oacc[s]);
-        oacc[s] = mfma(vA1, pack8(p + 8), oacc[s]);
+        const bf16x8 pB0 = pack8(p), pB1 = pack8(p + 8);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          oacc[s][c] = mfma(vA[c][0], pB0, oacc[s][c]);
+          oacc[s][c] = mfma(vA[c][1], pB1, oacc[s][c]);
+        }
       }
     };
     // the row's pass; lsum[s] = the sum of p over all keys (both lane halves)
-    auto pass = [&](float *m, f32x16 *oacc, float *lsum) {
-      oacc[0] = oacc[1] = (f32x16){};
-      lsum[0] = lsum[1] = 0.f;
-      FwdTile T;
+    auto pass = [&](float *m, f32x16 (*oacc)[NC], float *lsum) {
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) {
+        lsum[s] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) oacc[s][c] = (f32x16){};
+      }
+      FwdTile<NL> T;
       fetch(0, T);
       for (int kt = 0; kt < nkt; ++kt) tile(kt, T, m, oacc, lsum);
-      lsum[0] += __shfl_xor(lsum[0], 32);
-      lsum[1] += __shfl_xor(lsum[1], 32);
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) lsum[s] += __shfl_xor(lsum[s], 32);
     };
 
-    float m[2] = {-INFINITY, -INFINITY};  // reference maxima of t for the lane's two queries
-    f32x16 oacc[2];
-    float lsum[2];
-    pass(m, oacc, lsum);
-    bool bad = !isfinite(lsum[0]) || !isfinite(lsum[1]);
+    float m[NQ];  // reference maxima of t for the lane's queries
+    f32x16 oacc[NQ][NC];
+    float lsum[NQ];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) bad = bad || !isfinite(oacc[0][i]) || !isfinite(oacc[1][i]);
+    for (int s = 0; s < NQ; ++s) m[s] = -INFINITY;
+    pass(m, oacc, lsum);
+    bool bad = false;
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      bad = bad || !isfinite(lsum[s]);
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bad = bad || !isfinite(oacc[s][c][i]);
+    }
     if (__ballot(bad) != 0ull) {
       // a probability left the fp32 range: take each query's true maximum over the
       // row, then run the pass again against it
-      m[0] = m[1] = -INFINITY;
-      FwdTile T;
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) m[s] = -INFINITY;
+      FwdTile<NL> T;
       for (int kt = 0; kt < nkt; ++kt) {
         fetch(kt, T);
         const unsigned valid = MASKED ? (unsigned)__ballot(T.m != 0u) : 0xffffffffu;
@@ -402,41 +474,51 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
       pass(m, oacc, lsum);
     }
     // o and its rounding residual leave through the wave's K/V LDS tiles (free between
-    // rows, 4 KB): written there in the accumulator layout and read back by query, so
-    // that every query's segment of each (64 bytes of o, 128 bytes of an fp32 or 64 of a
-    // bf16 residual) is stored whole.  16-byte chunks are permuted by row bits so both
-    // LDS passes are free of bank conflicts.  An fp32 residual tile fills all 4 KB: it
-    // goes first, and o follows once its rows have been read back.
-    auto o_off = [](int row, int chunk) { return row * HD + ((chunk ^ ((row >> 2) & 3)) << 3); };
-    auto r32_off = [](int row, int c16) { return row * HD + ((c16 ^ ((row >> 1) & 7)) << 2); };
-    uint16_t *ot = kbuf;  // [32 queries][32 channels] bf16: o
-    uint16_t *rt = vbuf;  // [32 queries][32 channels] bf16: residual
-    float *r32t = (float *)kbuf;  // [32 queries][32 channels] fp32: residual (kbuf and vbuf)
+    // rows): written there in the accumulator layout and read back by query, so that
+    // every query's segment of each (2 D bytes of o, 4 D of an fp32 or 2 D of a bf16
+    // residual) is stored whole.  16-byte chunks are permuted by row bits so both LDS
+    // passes are free of bank conflicts.  An fp32 residual tile fills both K/V tiles:
+    // it goes first, and o follows once its rows have been read back.
+    auto o_off = [](int row, int chunk) {
+      if constexpr (TD == 32) return row * 32 + ((chunk ^ ((row >> 2) & 3)) << 3);
+      else return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3);
+    };
+    auto r32_off = [](int row, int c16) {
+      if constexpr (TD == 32) return row * 32 + ((c16 ^ ((row >> 1) & 7)) << 2);
+      else return row * 64 + ((c16 ^ (row & 15)) << 2);
+    };
+    uint16_t *ot = kbuf;  // [32 queries][TD channels] bf16: o
+    uint16_t *rt = vbuf;  // [32 queries][TD channels] bf16: residual
+    float *r32t = (float *)kbuf;  // [32 queries][TD channels] fp32: residual (kbuf and vbuf)
+    constexpr int LR = TD / 4;  // lanes per query row of the fp32 residual (16 bytes each)
+    constexpr int LO = TD / 8;  // lanes per query row of o
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < NQ; ++s) {
       if (s == 1 && !two) break;
       float inv = lsum[s] > 0.f ? 1.f / lsum[s] : 0.f;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        // no contraction here: fused into an fma, O - float(o) would be taken from the
-        // unrounded product and could exceed half a bf16 ulp of o
-#pragma clang fp contract(off)
-        float ov[4];
+      for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ov[i] = oacc[s][4 * g + i] * inv;
-        const unsigned p0 = pack_bf16(ov[0], ov[1]), p1 = pack_bf16(ov[2], ov[3]);
-        // channels 8g + 4hh .. 8g + 4hh + 3 of query jl; the residual O - float(o) is
-        // exact in fp32 (and rounded once more, to bf16, for a bf16 residual)
-        const f32x4 rv = {ov[0] - bf_lo(p0), ov[1] - bf_hi(p0), ov[2] - bf_lo(p1), ov[3] - bf_hi(p1)};
-        if (RES32) {
-          *(f32x4 *)(r32t + r32_off(jl, 2 * g + hh)) = rv;
-        } else {
-          *(u32x2 *)(ot + o_off(jl, g) + 4 * hh) = (u32x2){p0, p1};
-          *(u32x2 *)(rt + o_off(jl, g) + 4 * hh) = (u32x2){pack_bf16(rv[0], rv[1]), pack_bf16(rv[2], rv[3])};
+        for (int g = 0; g < 4; ++g) {
+          // no contraction here: fused into an fma, O - float(o) would be taken from the
+          // unrounded product and could exceed half a bf16 ulp of o
+#pragma clang fp contract(off)
+          float ov[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ov[i] = oacc[s][c][4 * g + i] * inv;
+          const unsigned p0 = pack_bf16(ov[0], ov[1]), p1 = pack_bf16(ov[2], ov[3]);
+          // channels 32c + 8g + 4hh .. + 3 of query jl; the residual O - float(o) is
+          // exact in fp32 (and rounded once more, to bf16, for a bf16 residual)
+          const f32x4 rv = {ov[0] - bf_lo(p0), ov[1] - bf_hi(p0), ov[2] - bf_lo(p1), ov[3] - bf_hi(p1)};
+          if (RES32) {
+            *(f32x4 *)(r32t + r32_off(jl, 8 * c + 2 * g + hh)) = rv;
+          } else {
+            *(u32x2 *)(ot + o_off(jl, 4 * c + g) + 4 * hh) = (u32x2){p0, p1};
+            *(u32x2 *)(rt + o_off(jl, 4 * c + g) + 4 * hh) = (u32x2){pack_bf16(rv[0], rv[1]), pack_bf16(rv[2], rv[3])};
+          }
         }
-      }
       if (RES32) {
-        // the residual rows (eight lanes per query's 128 bytes), then o into the freed
+        // the residual rows (LR lanes per query's 4 TD bytes), then o into the freed
         // tile, converted again rather than held.  The lane index passes through an
         // empty asm: otherwise the compiler hoists these stores' address arithmetic out
         // of the row loop and the tile loop spills.
@@ -444,26 +526,28 @@ __global__ __launch_bounds__(FWD_WAVES * 64) void fwd_kernel(FwdArgs a) {
           int ln = lane;
           __asm__ volatile("" : "+v"(ln));
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const int row = 8 * k + (ln >> 3), c16 = ln & 7;
+          for (int k = 0; k < LR / 2; ++k) {
+            const int row = (64 / LR) * k + ln / LR, c16 = ln % LR;
             const long long off = base + (long long)(j0 + 32 * s + row) * a.f.sQ + 4 * c16;
-            if (DIN == 32 || c16 < 4) *(f32x4 *)((float *)a.res + off) = *(const f32x4 *)(r32t + r32_off(row, c16));
+            if (DIN != 16 || c16 < 4) *(f32x4 *)((float *)a.res + off) = *(const f32x4 *)(r32t + r32_off(row, c16));
           }
         }
         __asm__ volatile("" : "+v"(inv));
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
 #pragma clang fp contract(off)
-          const f32x16 &ac = oacc[s];
-          *(u32x2 *)(ot + o_off(jl, g) + 4 * hh) =
-              (u32x2){pack_bf16(ac[4 * g] * inv, ac[4 * g + 1] * inv), pack_bf16(ac[4 * g + 2] * inv, ac[4 * g + 3] * inv)};
-        }
+            const f32x16 &ac = oacc[s][c];
+            *(u32x2 *)(ot + o_off(jl, 4 * c + g) + 4 * hh) =
+                (u32x2){pack_bf16(ac[4 * g] * inv, ac[4 * g + 1] * inv), pack_bf16(ac[4 * g + 2] * inv, ac[4 * g + 3] * inv)};
+          }
       }
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int row = (lane >> 2) + 16 * k, chunk = lane & 3;
+      for (int k = 0; k < LO / 2; ++k) {
+        const int row = lane / LO + (64 / LO) * k, chunk = lane % LO;
         const long long off = base + (long long)(j0 + 32 * s + row) * a.f.sQ + 8 * chunk;
-        if (DIN == 32 || chunk < 2) {
+        if (DIN != 16 || chunk < 2) {
           *(u32x4 *)(a.o + off) = *(const u32x4 *)(ot + o_off(row, chunk));
           if (!RES32 && a.res) *(u32x4 *)((uint16_t *)a.res + off) = *(const u32x4 *)(rt + o_off(row, chunk));
         }
@@ -501,17 +585,19 @@ struct PrepArgs {
 // One thread per (b, r, q, h), heads fastest so that a wave reads whole
 // 256-byte (position, all heads) segments.
 __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
-  // four lanes per (b, position, h): lane j takes channels 8j .. 8j + 7 (with D = 16
-  // lanes 2 and 3 hold none and add zero).  Groups run in the caller's memory order
+  // four lanes per (b, position, h), eight with D = 64: lane j takes channels 8j ..
+  // 8j + 7 (with D = 16 lanes 2 and 3 hold none and add zero).  Groups run in the
+  // caller's memory order
   // (b, first pair axis, second pair axis, h), so that the lanes of a wave read
   // contiguous runs of o, dO and the residual in both orientations; the attended
   // frame's row and query follow from the strides.
   // (only the attention rows of the range: along the first pair axis for the starting
   // node, the second for the ending node, so the order stays the memory order)
   const long long total = (long long)a.B * a.R * a.N * a.H;
-  const long long idx = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> 2;
-  const int j = threadIdx.x & 3;
-  if (idx >= total) return;  // whole groups of four leave together
+  const int lsh = a.D == 64 ? 3 : 2;  // log2 of the lanes per group
+  const long long idx = ((long long)blockIdx.x * blockDim.x + threadIdx.x) >> lsh;
+  const int j = threadIdx.x & ((1 << lsh) - 1);
+  if (idx >= total) return;  // whole groups leave together
   const bool starting = a.f.sR > a.f.sQ;  // rows along the first pair axis
   const int h = (int)(idx % a.H);
   long long t = idx / a.H;
@@ -551,9 +637,11 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
     acc = fmaf(bf_lo(gw[w]), o0, acc);
     acc = fmaf(bf_hi(gw[w]), o1, acc);
   }
-  // (l0 + l1) + (l2 + l3) on every lane of the group: a fixed order
+  // (l0 + l1) + (l2 + l3) on every lane of the group (then + the same over lanes 4-7
+  // with D = 64): a fixed order
   acc += __shfl_xor(acc, 1);
   acc += __shfl_xor(acc, 2);
+  if (lsh == 3) acc += __shfl_xor(acc, 4);
   const long long row = ((long long)b * a.N + r) * a.H + h;
   if (j == 0) a.stats[row * 2 * a.N + q] = -a.lse[row * a.N + q] * a.inv_alpha;
   if (j == 1) a.stats[row * 2 * a.N + a.N + q] = -acc;
@@ -994,6 +1082,316 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
   }
 }
 
+// Head dimension 64.  The same scheme over blocks of 32 keys: with 64 channels the
+// dK and dV partials of a 64-key block would not leave room for its dbias
+// accumulators, so a workgroup owns 32 keys (dbias: JT x 16 registers per lane; dK,
+// dV: two 32-channel halves each).  Per 32 x 32 (query, key) tile the score and dP
+// products contract over four 16-channel slices plus the per-query slice, dK and dV
+// take two products per channel half, and dQ^T = K^T dS^T leaves as two 32-channel
+// halves of the block's bf16 partial.  K/V, q and dO tiles have 128-byte rows
+// (tile_off_w<64>).  The row-end dK/dV exchange stages each wave's 32 x 64 fp32
+// partial in that wave's q/dO tiles.
+constexpr int BWD64_BK = 32;
+
+template <int JT, bool MASKED>
+__global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main64_kernel(BwdArgs a) {
+  constexpr int TD = 64, BK = BWD64_BK;
+  constexpr int NMAX = 32 * BWD_WAVES * JT;
+  constexpr int BSTR = NMAX + 4;  // fp16 row stride of the bias tile: conflict-free 8-byte reads
+  __shared__ __attribute__((aligned(16))) _Float16 s_bias[BK * BSTR];
+  // keys and values of the block for the current row and the next one
+  __shared__ __attribute__((aligned(16))) uint16_t s_kv[2][2 * BK * TD];
+  __shared__ uint8_t s_mask[2][BK];
+  __shared__ __attribute__((aligned(16))) uint16_t s_qd[BWD_WAVES * 2 * 32 * TD];
+  __shared__ __attribute__((aligned(16))) uint16_t s_ds[BWD_WAVES * BK * 32];
+
+  const int N = a.N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, ll = lane & 31;
+  uint16_t *wq = s_qd + wave * 2 * 32 * TD;
+  uint16_t *wdo = wq + 32 * TD;
+  uint16_t *wds = s_ds + wave * BK * 32;  // dS^T: [32 keys][32 queries], tile_off layout
+
+  int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int hw = a.H & 1 ? 1 : 2;
+  const int hp = t % hw; t /= hw;
+  const int kb = t % a.n_kblocks; t /= a.n_kblocks;
+  const int chunk = t % a.n_chunks; t /= a.n_chunks;
+  const int h = (t % (a.H / hw)) * hw + hp;
+  const int b = t / (a.H / hw);
+  const int k0 = kb * BK;  // N % 32 == 0: every block holds 32 keys
+  const int njt = N / 32;
+  const int r0 = a.row_begin + chunk * a.rows_per_chunk;
+  const int r1 = min(a.row_end, r0 + a.rows_per_chunk);
+  const float c1 = a.c1;
+
+  auto rowbase = [&](int r) -> long long {
+    return (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)h * TD;
+  };
+  auto stats_of = [&](int r) -> const float * {
+    return a.stats + (((long long)b * N + r) * a.H + h) * 2 * N;
+  };
+  // thread tid carries 16 bytes of the block's keys and values: key tid / 8, part tid % 8
+  auto load_kv = [&](int r, u32x4 &kw, u32x4 &vw) {
+    const long long off = rowbase(r) + (long long)(k0 + (tid >> 3)) * a.f.sQ + (tid & 7) * 8;
+    kw = ld16(a.k + off);
+    vw = ld16(a.v + off);
+  };
+  const uint8_t *mask_thr =
+      MASKED ? a.mask + (long long)b * a.f.mB + (long long)(k0 + (tid & 31)) * a.f.mK : nullptr;
+  auto load_mask = [&](int r, uint8_t &m) {
+    if constexpr (MASKED) m = mask_thr[(long long)r * a.f.mR];
+  };
+  auto store_kv = [&](u32x4 kw, u32x4 vw, uint8_t m, int buf) {
+    const int row = tid >> 3, part = tid & 7;
+    *(u32x4 *)(s_kv[buf] + tile_off_w<TD>(row, part * 8)) = kw;
+    *(u32x4 *)(s_kv[buf] + BK * TD + tile_off_w<TD>(row, part * 8)) = vw;
+    if (MASKED && wave == 0 && lane < BK) s_mask[buf][lane] = m;
+  };
+  // one query tile: the lane's q and dO rows (four 16-byte slices each, A operands as
+  // loaded) and the two per-query terms of the lane's query
+  u32x4 tq[4], td[4];
+  float tl = 0.f, tdl = 0.f;
+  auto stage_qtile = [&]() {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      *(u32x4 *)(wq + tile_off_w<TD>(ll, 16 * x + 8 * hh)) = tq[x];
+      *(u32x4 *)(wdo + tile_off_w<TD>(ll, 16 * x + 8 * hh)) = td[x];
+    }
+    __asm__ volatile("" ::"v"(tl), "v"(tdl));
+  };
+  auto load_qtile = [&](int r, int jt) {
+    const long long off = rowbase(r) + (long long)(jt * 32 + ll) * a.f.sQ + 8 * hh;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      tq[x] = ld16(a.q + off + 16 * x);
+      td[x] = ld16(a.d_o + off + 16 * x);
+    }
+    const float *sp = stats_of(r) + jt * 32 + ll;
+    tl = sp[0];
+    tdl = sp[N];
+  };
+
+  // transposed pair-bias tile: s_bias[kk][j] = bias[b, h, j, k0 + kk]
+  {
+    const uint16_t *src = a.bias + ((long long)b * a.H + h) * N * N;
+    for (int idx = tid; idx < N * 4; idx += BWD_WAVES * 64) {
+      const int j = idx >> 2, c8 = idx & 3;
+      const u32x4 w = ld16(src + (long long)j * N + k0 + c8 * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s_bias[(c8 * 8 + 2 * i) * BSTR + j] = bias_f16(bf_lo(w[i]));
+        s_bias[(c8 * 8 + 2 * i + 1) * BSTR + j] = bias_f16(bf_hi(w[i]));
+      }
+    }
+  }
+
+  // identity operands of the dbias accumulation and the ones of the per-query slice
+  bf16x8 ident[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    unsigned w[4];
+#pragma unroll
+    for (int e2 = 0; e2 < 4; ++e2) {
+      unsigned lo = 0, hi = 0;
+      const int e0 = 2 * e2, e1 = 2 * e2 + 1;
+      if (ll == 16 * s + 8 * (e0 >> 2) + 4 * hh + (e0 & 3)) lo = 0x3f80u;
+      if (ll == 16 * s + 8 * (e1 >> 2) + 4 * hh + (e1 & 3)) hi = 0x3f80u;
+      w[e2] = lo | (hi << 16);
+    }
+    ident[s] = as_bf16x8((u32x4){w[0], w[1], w[2], w[3]});
+  }
+  const bf16x8 ones3 = as_bf16x8(hh ? (u32x4){0u, 0u, 0u, 0u} : (u32x4){0x3f803f80u, 0x3f80u, 0u, 0u});
+
+  f32x16 dbias[JT];
+#pragma unroll
+  for (int jj = 0; jj < JT; ++jj) dbias[jj] = (f32x16){};
+
+  const long long E = (long long)a.B * N * N * a.H * TD;
+  uint16_t *dq_part = a.dq_part + (long long)kb * E;
+
+  u32x4 nk, nv;
+  uint8_t nm = 1;
+  const int rfirst = min(r0, N - 1);
+  load_kv(rfirst, nk, nv);
+  load_mask(rfirst, nm);
+  load_qtile(rfirst, min(wave, njt - 1));
+  store_kv(nk, nv, nm, 0);
+  stage_qtile();
+  lds_barrier();
+
+  for (int r = r0; r < r1; ++r) {
+    const int cur = (r - r0) & 1;
+    const uint16_t *s_k = s_kv[cur], *s_v = s_kv[cur] + BK * TD;
+    const bool has_next = r + 1 < r1;
+    const int rn = has_next ? r + 1 : r;
+    // exp2 argument offset of the lane's key k0 + ll: 0, or -inf if it is masked
+    const float moff = (MASKED && s_mask[cur][ll] == 0) ? -INFINITY : 0.f;
+    load_kv(rn, nk, nv);
+    load_mask(rn, nm);
+    const long long base = rowbase(r);
+
+    f32x16 dK[2], dV[2];  // 32-channel halves
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      dK[c] = (f32x16){};
+      dV[c] = (f32x16){};
+    }
+
+#pragma unroll
+    for (int jj = 0; jj < JT; ++jj) {
+      const int jt = wave + BWD_WAVES * jj;
+      if (jt >= njt) break;
+      const int j0 = jt * 32;
+      bf16x8 qA[4], dA[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        qA[x] = as_bf16x8(tq[x]);
+        dA[x] = as_bf16x8(td[x]);
+      }
+      const bf16x8 lA = split3_operand(tl, hh), dlA = split3_operand(tdl, hh);
+      if (jj > 0) stage_qtile();
+      // the block's keys and values as row operands, and the lane's bias values
+      bf16x8 kr[4], vr[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        kr[x] = *(const bf16x8 *)(s_k + tile_off_w<TD>(ll, 16 * x + 8 * hh));
+        vr[x] = *(const bf16x8 *)(s_v + tile_off_w<TD>(ll, 16 * x + 8 * hh));
+      }
+      f16x4 bw[4];
+      {
+        const _Float16 *brow = s_bias + ll * BSTR + j0 + 4 * hh;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) bw[g] = *(const f16x4 *)(brow + 8 * g);
+      }
+      f32x16 sv = mfma(lA, ones3, (f32x16){});  // -lse/alpha
+      f32x16 dp = mfma(dlA, ones3, (f32x16){});  // -D
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        sv = mfma(qA[x], kr[x], sv);  // q.k - lse/alpha
+        dp = mfma(dA[x], vr[x], dp);  // dP - D
+      }
+      {
+        const bool same_row = jt + BWD_WAVES < njt;
+        load_qtile(same_row ? r : rn, same_row ? jt + BWD_WAVES : wave);
+      }
+      if (jj == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        store_kv(nk, nv, nm, cur ^ 1);
+      }
+      // transposed q and dO operands of the dK and dV products: channel half c,
+      // query slice x
+      bf16x8 qB[2][2], dB[2][2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          qB[c][x] = tr_operand_w<TD>(wq, 16 * x, lane, 32 * c);
+          dB[c][x] = tr_operand_w<TD>(wdo, 16 * x, lane, 32 * c);
+        }
+      float p[16], ds[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        p[i] = __builtin_amdgcn_exp2f(fmaf((float)bw[i >> 2][i & 3], kLog2e, fmaf(sv[i], c1, moff)));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ds[i] = p[i] * dp[i];
+      const bf16x8 pA0 = pack8(p), pA1 = pack8(p + 8);
+      const bf16x8 sA0 = pack8(ds), sA1 = pack8(ds + 8);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        dV[c] = mfma(pA0, dB[c][0], dV[c]);
+        dV[c] = mfma(pA1, dB[c][1], dV[c]);
+        dK[c] = mfma(sA0, qB[c][0], dK[c]);
+        dK[c] = mfma(sA1, qB[c][1], dK[c]);
+      }
+      dbias[jj] = mfma(ident[0], sA0, dbias[jj]);
+      dbias[jj] = mfma(ident[1], sA1, dbias[jj]);
+      {
+        const u32x4 s0 = __builtin_bit_cast(u32x4, sA0), s1 = __builtin_bit_cast(u32x4, sA1);
+        *(u32x2 *)(wds + tile_off(ll, 4 * hh)) = (u32x2){s0[0], s0[1]};
+        *(u32x2 *)(wds + tile_off(ll, 8 + 4 * hh)) = (u32x2){s0[2], s0[3]};
+        *(u32x2 *)(wds + tile_off(ll, 16 + 4 * hh)) = (u32x2){s1[0], s1[1]};
+        *(u32x2 *)(wds + tile_off(ll, 24 + 4 * hh)) = (u32x2){s1[2], s1[3]};
+      }
+      // dQ^T over the block's 32 keys, per channel half, rounded to bf16 as this key
+      // block's partial (stored as in the 32-channel kernel, see there)
+      const bf16x8 dsB0 = tr_operand_sw(wds, 0, lane), dsB1 = tr_operand_sw(wds, 16, lane);
+      uint16_t *qout = dq_part + ((((long long)b * N + r) * a.H + h) * N + j0 + ll) * TD + 8 * hh;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        f32x16 dqT = mfma(tr_operand_w<TD>(s_k, 0, lane, 32 * c), dsB0, (f32x16){});
+        dqT = mfma(tr_operand_w<TD>(s_k, 16, lane, 32 * c), dsB1, dqT);
+        unsigned w[4][2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          w[g][0] = pack_bf16(dqT[4 * g], dqT[4 * g + 1]);
+          w[g][1] = pack_bf16(dqT[4 * g + 2], dqT[4 * g + 3]);
+        }
+#pragma unroll
+        for (int g = 0; g < 4; g += 2)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(w[g][e], w[g + 1][e], false, false);
+            w[g][e] = sw[0];
+            w[g + 1][e] = sw[1];
+          }
+        *(u32x4 *)(qout + 32 * c) = (u32x4){w[0][0], w[0][1], w[1][0], w[1][1]};
+        *(u32x4 *)(qout + 32 * c + 16) = (u32x4){w[2][0], w[2][1], w[3][0], w[3][1]};
+      }
+    }
+
+    if (wave >= njt) store_kv(nk, nv, nm, cur ^ 1);  // a wave without query tiles in this row
+
+    // fixed-order cross-wave reduction of dV then dK for this row: each wave's 32 x 64
+    // fp32 partial is staged in its own q/dO tiles
+    auto red_ptr = [&](int w, int kr) -> float * { return (float *)(s_qd + w * 2 * 32 * TD) + kr * TD; };
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      if (which) lds_barrier();  // every wave has read the dV partials
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const f32x16 &acc = which ? dK[c] : dV[c];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red_ptr(wave, 8 * (i >> 2) + 4 * hh + (i & 3))[32 * c + ll] = acc[i];
+      }
+      lds_barrier();
+      const float scale = which ? a.alpha : 1.f;
+      uint16_t *dst = which ? a.dk : a.dv;
+      {
+        // thread tid: channels 8 (tid % 8) .. + 7 of key row tid / 8
+        const int kr = tid >> 3, c = 8 * (tid & 7);
+        f32x4 s0 = *(const f32x4 *)(red_ptr(0, kr) + c);
+        f32x4 s1 = *(const f32x4 *)(red_ptr(0, kr) + c + 4);
+#pragma unroll
+        for (int w = 1; w < BWD_WAVES; ++w) {
+          s0 += *(const f32x4 *)(red_ptr(w, kr) + c);
+          s1 += *(const f32x4 *)(red_ptr(w, kr) + c + 4);
+        }
+        s0 *= scale;
+        s1 *= scale;
+        const long long off = base + (long long)(k0 + kr) * a.f.sQ + c;
+        *(u32x4 *)(dst + off) = (u32x4){pack_bf16(s0[0], s0[1]), pack_bf16(s0[2], s0[3]),
+                                         pack_bf16(s1[0], s1[1]), pack_bf16(s1[2], s1[3])};
+      }
+    }
+    lds_barrier();  // partials read; the next row's keys and values are visible
+    stage_qtile();  // the next row's first query tile
+  }
+
+  // dbias partial of this row chunk for the block's keys and every query
+  float *dbo = a.db_part + (((long long)chunk * a.B + b) * a.H + h) * N * N + k0;
+#pragma unroll
+  for (int jj = 0; jj < JT; ++jj) {
+    const int jt = wave + BWD_WAVES * jj;
+    if (jt >= njt) break;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int j = jt * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
+      dbo[(long long)j * N + ll] = dbias[jj][i];
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------
 // Backward: fixed-order reductions of the partials
 // ------------------------------------------------------------------------------------
@@ -1011,13 +1409,13 @@ struct ReduceArgs {
 // one thread per 8 channels: the bf16 partials of the key blocks summed in fp32 in
 // block order, times alpha, rounded to bf16 in the caller's frame
 __global__ __launch_bounds__(256) void reduce_dq_kernel(ReduceArgs a) {
-  // partials and output hold D channels (32 or 16)
+  // partials and output hold D channels (64, 32 or 16)
   const long long E = (long long)a.B * a.N * a.N * a.H * a.D;
   // thread -> 8 channels of output element (b, r, q, h, c), r in the row range, heads
   // inside positions, so that a wave writes whole multi-head position segments
   const long long e = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (e >= (long long)a.B * a.R * a.N * a.H * a.D) return;
-  const int dsh = a.D == 32 ? 5 : 4;  // D is 32 or 16
+  const int dsh = a.D == 64 ? 6 : a.D == 32 ? 5 : 4;  // log2(D)
   const int c = (int)(e & (a.D - 1));
   long long u = e >> dsh;
   const int h = (int)(u % a.H);
@@ -1088,8 +1486,10 @@ int device_cus() {
 // forward kernels (bit per variant, per device) whose dynamic LDS limit is raised
 std::atomic<unsigned> g_fwd_lds_set[kMaxDevices];
 // the forward's largest dynamic LDS: the fp16 bias block at the widest row stride
-// (N + 36 for N <= kMaxN) and the waves' K/V tiles
-constexpr size_t kFwdMaxLds = (size_t)FWD_BJ * (kMaxN + 36) * 2 + (size_t)FWD_WAVES * 2 * 32 * HD * 2;
+// (N + 36 for N <= kMaxN) and the waves' K/V tiles, over the head-dimension shapes
+constexpr size_t kFwdMaxLds = FwdShape<32>::lds_bytes(kMaxN + 36) > FwdShape<64>::lds_bytes(kMaxN + 36)
+                                  ? FwdShape<32>::lds_bytes(kMaxN + 36)
+                                  : FwdShape<64>::lds_bytes(kMaxN + 36);
 
 // Fixed device buffer of the allocation-free backward (tri_attn_bwd_noalloc): its
 // workspace (per-query statistics, dQ and dbias partials) lives here instead of in
@@ -1116,7 +1516,7 @@ tri_attn_status check_problem(const tri_attn_problem *p) {
   if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale)) return TRI_ATTN_ERROR_INVALID_VALUE;
   if (p->flags & ~(TRI_ATTN_FLAG_ENDING_NODE | TRI_ATTN_FLAG_DBIAS_FP32 | TRI_ATTN_FLAG_RESIDUAL_BF16))
     return TRI_ATTN_ERROR_NOT_SUPPORTED;
-  if ((p->D != HD && p->D != 16) || p->N % 32 != 0 || p->N > kMaxN || p->H > kMaxH) return TRI_ATTN_ERROR_NOT_SUPPORTED;
+  if ((p->D != 64 && p->D != 32 && p->D != 16) || p->N % 32 != 0 || p->N > kMaxN || p->H > kMaxH) return TRI_ATTN_ERROR_NOT_SUPPORTED;
   if (p->B * p->N * p->N * p->H * p->D > (int64_t)1 << 40) return TRI_ATTN_ERROR_NOT_SUPPORTED;
   // attention rows: [row_begin, row_end) with 0 <= row_begin < row_end <= N, or
   // 0, 0 for all rows
@@ -1173,7 +1573,8 @@ BwdPlan plan_bwd(const tri_attn_problem *p, int cus) {
   const int N = (int)p->N;
   const int njt = N / 32;
   pl.JT = (njt + BWD_WAVES - 1) / BWD_WAVES;
-  pl.T = (N + BWD_BK - 1) / BWD_BK;
+  const int bk = p->D == 64 ? BWD64_BK : BWD_BK;  // keys per block
+  pl.T = (N + bk - 1) / bk;
   // one workgroup per CU (its LDS and registers fill one); one wave of workgroups
   // over the call's R attention rows
   int i0, i1;
@@ -1196,8 +1597,9 @@ BwdPlan plan_bwd(const tri_attn_problem *p, int cus) {
 
 template <int JT>
 hipError_t launch_main(const BwdArgs &args, int D, int grid, size_t lds, hipStream_t stream) {
-  auto kern = D == 32 ? (args.mask ? bwd_main_kernel<JT, true, 32> : bwd_main_kernel<JT, false, 32>)
-                      : (args.mask ? bwd_main_kernel<JT, true, 16> : bwd_main_kernel<JT, false, 16>);
+  auto kern = D == 64   ? (args.mask ? bwd_main64_kernel<JT, true> : bwd_main64_kernel<JT, false>)
+              : D == 32 ? (args.mask ? bwd_main_kernel<JT, true, 32> : bwd_main_kernel<JT, false, 32>)
+                        : (args.mask ? bwd_main_kernel<JT, true, 16> : bwd_main_kernel<JT, false, 16>);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(BWD_WAVES * 64), lds, stream, args);
   return hipGetLastError();
 }
@@ -1285,7 +1687,9 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
   a.N = (int)p.N;
   a.H = (int)p.H;
   a.c1 = alpha_of(problem) * kLog2e;
-  a.n_jblocks = (a.N + FWD_BJ - 1) / FWD_BJ;
+  const int bj = p.D == 64 ? FwdShape<64>::BJ : FwdShape<32>::BJ;  // queries per workgroup
+  const int waves = p.D == 64 ? FwdShape<64>::WAVES : FwdShape<32>::WAVES;
+  a.n_jblocks = (a.N + bj - 1) / bj;
   // fp16 bias row stride with stride/2 = 2 (mod 32) 4-byte banks: the 8-byte reads of
   // 16 lanes (16 rows) are then conflict-free
   a.bstride = a.N + ((a.N & 63) ? 36 : 4);
@@ -1299,13 +1703,15 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
   if (chunks > R) chunks = R;
   a.rows_per_chunk = (R + chunks - 1) / chunks;
   a.n_chunks = (R + a.rows_per_chunk - 1) / a.rows_per_chunk;
-  const size_t lds = (size_t)FWD_BJ * a.bstride * 2 + (size_t)FWD_WAVES * 2 * 32 * HD * 2;
+  const size_t lds = p.D == 64 ? FwdShape<64>::lds_bytes(a.bstride) : FwdShape<32>::lds_bytes(a.bstride);
   const bool res32 = (p.flags & TRI_ATTN_FLAG_RESIDUAL_BF16) == 0;
-  void (*const kernels[8])(FwdArgs) = {fwd_kernel<false, false, 32>, fwd_kernel<false, true, 32>,
-                                        fwd_kernel<true, false, 32>,  fwd_kernel<true, true, 32>,
-                                        fwd_kernel<false, false, 16>, fwd_kernel<false, true, 16>,
-                                        fwd_kernel<true, false, 16>,  fwd_kernel<true, true, 16>};
-  const int variant = (p.D == 16 ? 4 : 0) | (mask ? 2 : 0) | (res32 ? 1 : 0);
+  void (*const kernels[12])(FwdArgs) = {fwd_kernel<false, false, 32>, fwd_kernel<false, true, 32>,
+                                         fwd_kernel<true, false, 32>,  fwd_kernel<true, true, 32>,
+                                         fwd_kernel<false, false, 16>, fwd_kernel<false, true, 16>,
+                                         fwd_kernel<true, false, 16>,  fwd_kernel<true, true, 16>,
+                                         fwd_kernel<false, false, 64>, fwd_kernel<false, true, 64>,
+                                         fwd_kernel<true, false, 64>,  fwd_kernel<true, true, 64>};
+  const int variant = (p.D == 16 ? 4 : p.D == 64 ? 8 : 0) | (mask ? 2 : 0) | (res32 ? 1 : 0);
   void (*kern)(FwdArgs) = kernels[variant];
   // the kernel's dynamic LDS limit, raised once per device and variant to the largest
   // size any accepted problem uses
@@ -1317,7 +1723,7 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
       return TRI_ATTN_ERROR_LAUNCH_FAILED;
     g_fwd_lds_set[dev].fetch_or(1u << variant, std::memory_order_acq_rel);
   }
-  hipLaunchKernelGGL(kern, dim3(groups * a.n_chunks), dim3(FWD_WAVES * 64), lds, stream, a);
+  hipLaunchKernelGGL(kern, dim3(groups * a.n_chunks), dim3(waves * 64), lds, stream, a);
   return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH_FAILED;
 }
 
@@ -1391,7 +1797,8 @@ static tri_attn_status bwd_run(const tri_attn_problem *problem, const void *q, c
   auto mark = [&](int i) { return !marks[i] || hipEventRecord(marks[i], stream) == hipSuccess; };
   if (!mark(0)) return TRI_ATTN_ERROR_LAUNCH_FAILED;
   const long long nrows = (long long)p.B * pa.R * p.N * p.H;
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((4 * nrows + 255) / 256)), dim3(256), 0, stream, pa);
+  const long long lanes = (p.D == 64 ? 8 : 4) * nrows;  // a lane group per (position, head)
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream, pa);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
 
   BwdArgs ba;
