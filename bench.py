@@ -28,9 +28,13 @@ The JSON line also carries
                  imply, the pair-bias and bias-gradient bytes of a step with the
                  measured rate of the dbias reduction, and whether the outputs of
                  the first and last timed steps are bitwise identical;
-  workloads    : the other reported crop sizes (384 and 640, and 768 in the ending
-                 node orientation), each timed over fewer steps: median time per
+  workloads    : the other reported crop sizes (384 and 640, 768 in the ending
+                 node orientation, and 768 at head dimensions 16 and 64 with the same
+                 128 pair channels), each timed over fewer steps: median time per
                  step, forward and backward, TFLOP/s and fraction of the MFMA peak;
+  tri_mul      : the triangle multiplicative update's contraction at the crop-768
+                 shape with 128 channels (tri_mul_fwd + tri_mul_bwd, outgoing and
+                 incoming edges): median times, TFLOP/s and fraction of the peak;
   accuracy     : the crop768 outputs of the last timed step against the FP64 oracle
                  run on the whole problem (forward max-abs and rel-RMSE, lse max-abs,
                  and the rel-RMSE of each gradient with the residual-compensated
@@ -368,6 +372,45 @@ def time_workload(args, workload: str, ending: bool, steps: int, warmup: int, ke
     return res
 
 
+def time_trimul(args, workload: str, incoming: bool, steps: int, warmup: int) -> dict:
+    """Time `steps` forward + backward calls of the triangle-multiplication contraction
+    (tri_mul_fwd, then tri_mul_bwd: three N^3 products per channel) after `warmup`."""
+    import seeded_inputs as si
+    import triangle_attention_amd as ta
+
+    w = si.TRIMUL_WORKLOADS[workload]
+    dev = torch.device("cuda:0")
+    log(f"workload {w.name} ({'incoming' if incoming else 'outgoing'} edges): {w.description}")
+    inp = si.make_trimul_workload(w.name)
+    a, b, g = (inp[n].to(dev) for n in ("a", "b", "g"))
+    z, da, db = torch.empty_like(a), torch.empty_like(a), torch.empty_like(a)
+    for _ in range(warmup):
+        ta.tri_mul_fwd(a, b, incoming=incoming, out=z)
+        ta.tri_mul_bwd(a, b, g, incoming=incoming, out=(da, db))
+    torch.cuda.synchronize()
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    first = None
+    for i in range(steps):
+        marks[i][0].record()
+        ta.tri_mul_fwd(a, b, incoming=incoming, out=z)
+        marks[i][1].record()
+        ta.tri_mul_bwd(a, b, g, incoming=incoming, out=(da, db))
+        marks[i][2].record()
+        if i == 0:
+            torch.cuda.synchronize()
+            first = [x.clone() for x in (z, da, db)]
+    torch.cuda.synchronize()
+    fwd = statistics.median(m[0].elapsed_time(m[1]) for m in marks)
+    bwd = statistics.median(m[1].elapsed_time(m[2]) for m in marks)
+    flops = si.trimul_flop_count(w.B, w.N, w.C)
+    v = flops / ((fwd + bwd) * 1e-3) / 1e12
+    return {"ms_per_step": round(fwd + bwd, 4), "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4),
+            "TFLOPs": round(v, 2), "mfma_peak_frac": round(v / MFMA_PEAK_BF16_TFLOPS, 4),
+            "flops_per_step": flops, "steps": steps,
+            "deterministic_first_vs_last_step": all(
+                torch.equal(x.view(torch.int16), y.view(torch.int16)) for x, y in zip(first, (z, da, db)))}
+
+
 def run_workload(args, workload: str, ending: bool, with_extras: bool) -> dict:
     """Time fwd+bwd steps of one workload and return its JSON line as a dict."""
     t = time_workload(args, workload, ending, args.steps, args.warmup, keep_outputs=with_extras)
@@ -417,9 +460,11 @@ def run_workload(args, workload: str, ending: bool, with_extras: bool) -> dict:
         return line
     out, unc, inp = t.pop("out"), t.pop("unc"), t["inp"]
     del t
-    # the other reported workloads: crop 384 and 640, and 768 in the ending orientation
+    # the other reported workloads: crop 384 and 640, 768 in the ending orientation, and
+    # 768 at head dimensions 16 and 64 (the same 128 pair channels)
     others = {}
-    for wl, end in (("crop384", False), ("crop640", False), ("crop768", True)):
+    for wl, end in (("crop384", False), ("crop640", False), ("crop768", True), ("crop768_h8d16", False),
+                    ("crop768_h2d64", False)):
         o = time_workload(args, wl, end, args.other_steps, min(args.warmup, 3),
                           keep_outputs=(wl == "crop640"))
         v = o["flops"] / (statistics.median(o["step_ms"]) * 1e-3) / 1e12
@@ -437,6 +482,10 @@ def run_workload(args, workload: str, ending: bool, with_extras: bool) -> dict:
         del o
         torch.cuda.empty_cache()
     line["workloads"] = others
+    # the triangle multiplicative update's contraction at the crop-768 shape, C = 128
+    line["tri_mul"] = {f"trimul_crop768_{d}": time_trimul(args, "trimul_crop768", d == "incoming",
+                                                          args.other_steps, 3)
+                       for d in ("outgoing", "incoming")}
     log("matrix-core probe")
     probe = mfma_probe_tflops()
     line["mfma_probe"] = {"TFLOPs": round(probe, 1),
@@ -491,6 +540,16 @@ def main():
         for wl, ending in (("crop384", False), ("crop640", False), ("crop768", False), ("crop768", True)):
             line = run_workload(args, wl, ending, False)
             print(json.dumps(line), flush=True)
+        return
+    if args.workload.startswith("trimul_"):
+        # the triangle-multiplication contraction alone (a profiling aid, not the metric)
+        d = "incoming" if args.ending else "outgoing"
+        r = time_trimul(args, args.workload, args.ending, args.steps, args.warmup)
+        print(json.dumps({"metric": "tri_mul_fwd_bwd_TFLOPs", "value": r["TFLOPs"], "unit": "TFLOP/s",
+                          "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "ms_per_step": r["ms_per_step"], "higher_is_better": True, "dtype": "bf16",
+                          "data": "synthetic", "config": {"workload": args.workload, "edges": d},
+                          "detail": r}), flush=True)
         return
     extras = not args.quick and args.workload == "crop768" and not args.ending
     line = run_workload(args, args.workload, args.ending, extras)
