@@ -22,7 +22,8 @@ import torch
 
 # tensor tags: each tensor of a workload draws from its own generator,
 # seeded with seed * 16 + tag
-_TAG = {"q": 0, "k": 1, "v": 2, "do": 3, "bias": 4, "length": 5, "tm_a": 6, "tm_b": 7, "tm_g": 8}
+_TAG = {"q": 0, "k": 1, "v": 2, "do": 3, "bias": 4, "length": 5, "tm_a": 6, "tm_b": 7, "tm_g": 8,
+        "md_z": 9, "md_ln": 10, "md_wqkvg": 11, "md_wb": 12, "md_wo": 13, "md_dy": 14}
 
 
 @dataclass(frozen=True)
@@ -176,3 +177,54 @@ def make_trimul_workload(name: str) -> dict:
 def trimul_flop_count(B: int, N: int, C: int) -> int:
     """Forward + backward flops of the contraction: three N^3 products per channel."""
     return 3 * 2 * B * C * N ** 3
+
+
+# Triangle-attention module around the core: the pair tensor z [B, N, N, C] (C = H * D
+# channels), its key mask, the LayerNorm scale and offset (fp32, [C]), the projection
+# weights w_qkvg [C, 4 C], w_bias [C, H] and w_out [C, C] (bf16, N(0, 1/C) entries, so
+# that every projection has unit variance) and the upstream gradient dy [B, N, N, C].
+@dataclass(frozen=True)
+class ModuleWorkload:
+    name: str
+    index: int
+    B: int
+    N: int
+    H: int
+    D: int
+    mask: str
+    description: str
+
+    @property
+    def seed(self) -> int:
+        return 3000 + self.index
+
+
+MODULE_WORKLOADS = {
+    w.name: w
+    for w in [
+        ModuleWorkload("module_tiny64", 1, 1, 64, 4, 32, "pad32", "B=1 N=64 H=4 d=32 (C=128), last 32 keys masked"),
+        ModuleWorkload("module_crop384", 2, 1, 384, 4, 32, "none", "B=1 N=384 H=4 d=32 (C=128)"),
+        ModuleWorkload("module_crop768", 3, 1, 768, 4, 32, "none", "B=1 N=768 H=4 d=32 (C=128)"),
+    ]
+}
+
+
+def make_module(B: int, N: int, H: int, D: int, seed: int, mask: str = "none") -> dict:
+    """Seeded inputs and parameters of one module problem (CPU tensors)."""
+    C = H * D
+    ln = torch.randn((2, C), generator=_gen(seed, "md_ln"), dtype=torch.float32) * 0.1
+    return {
+        "z": _randn_bf16((B, N, N, C), seed, "md_z"),
+        "mask": make_mask(B, N, mask, seed),
+        "ln_w": 1.0 + ln[0],
+        "ln_b": ln[1].clone(),
+        "w_qkvg": _randn_bf16((C, 4 * C), seed, "md_wqkvg", C ** -0.5),
+        "w_bias": _randn_bf16((C, H), seed, "md_wb", C ** -0.5),
+        "w_out": _randn_bf16((C, C), seed, "md_wo", C ** -0.5),
+        "dy": _randn_bf16((B, N, N, C), seed, "md_dy"),
+    }
+
+
+def make_module_workload(name: str) -> dict:
+    w = MODULE_WORKLOADS[name]
+    return make_module(w.B, w.N, w.H, w.D, w.seed, w.mask)
