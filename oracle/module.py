@@ -1,9 +1,9 @@
 """FP64 oracle of the triangle-attention module around the core — TEST INFRASTRUCTURE ONLY.
 
 Only the test suite, the smoke check and the benchmark may use it; the product path
-never does.  The pages name the module only as "AlphaFold3-style triangle attention"
-(biocloudservice page, opening paragraph) and describe nothing around the attention
-core, so this follows the plainest reading, the AlphaFold3 triangle-attention block
+never does.  The pages present the kernel only as triangle attention in the style of
+AlphaFold3 (biocloudservice page, opening paragraph) and describe nothing around the
+attention core, so this follows the plainest reading, the AlphaFold3 triangle-attention block
 around the starting node, on a pair tensor z [B, N, N, C] with C = H * D channels:
 
     zn        = LayerNorm(z) over the C channels (learned scale w and offset b, eps)

@@ -38,8 +38,12 @@ STATUS_NAMES = {
 
 EXPORTED_SYMBOLS = ("tri_attn_abi_version", "tri_attn_status_string", "tri_attn_fwd",
                     "tri_attn_bwd_workspace_bytes", "tri_attn_bwd", "tri_attn_bwd_timed",
-                    "tri_attn_bwd_noalloc", "tri_mul_abi_version", "tri_mul_fwd", "tri_mul_bwd")
+                    "tri_attn_bwd_noalloc", "tri_mul_abi_version", "tri_mul_fwd", "tri_mul_bwd",
+                    "tri_attn_module_abi_version", "tri_attn_module_fwd", "tri_attn_module_bwd_workspace_bytes",
+                    "tri_attn_module_bwd")
 TRI_MUL_ABI_VERSION = 1
+MODULE_ABI_VERSION = 1
+MODULE_CHANNELS = 128
 TRI_MUL_FLAG_INCOMING = 1
 NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024   # TRI_ATTN_NOALLOC_SCRATCH_BYTES
 
@@ -56,6 +60,29 @@ class TriMulProblem(ctypes.Structure):
     """Mirror of ``tri_mul_problem``."""
     _fields_ = [("abi_version", ctypes.c_int32), ("flags", ctypes.c_int32),
                 ("B", ctypes.c_int64), ("N", ctypes.c_int64), ("C", ctypes.c_int64)]
+
+
+class ModuleProblem(ctypes.Structure):
+    """Mirror of ``tri_attn_module_problem``."""
+    _fields_ = [("abi_version", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("B", ctypes.c_int64), ("N", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("D", ctypes.c_int64), ("ln_eps", ctypes.c_float)]
+
+
+class ModuleParams(ctypes.Structure):
+    """Mirror of ``tri_attn_module_params`` (device pointers)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("ln_w", "ln_b", "w_qkvg", "w_bias", "w_out")]
+
+
+class ModuleSaved(ctypes.Structure):
+    """Mirror of ``tri_attn_module_saved`` (device pointers)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("zn", "ln_stats", "q", "k", "v", "g", "bias", "o",
+                                                "o_residual", "lse")]
+
+
+class ModuleGrads(ctypes.Structure):
+    """Mirror of ``tri_attn_module_param_grads`` (device pointers)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("ln_w", "ln_b", "w_qkvg", "w_bias", "w_out")]
 
 
 class TriAttnError(RuntimeError):
@@ -100,7 +127,18 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.tri_mul_fwd.restype = i32
     lib.tri_mul_bwd.argtypes = [tp, vp, vp, vp, vp, vp, vp]
     lib.tri_mul_bwd.restype = i32
-    if lib.tri_attn_abi_version() != ABI_VERSION or lib.tri_mul_abi_version() != TRI_MUL_ABI_VERSION:
+    mp = ctypes.POINTER(ModuleProblem)
+    lib.tri_attn_module_abi_version.argtypes = []
+    lib.tri_attn_module_abi_version.restype = i32
+    lib.tri_attn_module_fwd.argtypes = [mp, vp, vp, ctypes.POINTER(ModuleParams), vp, ctypes.POINTER(ModuleSaved), vp]
+    lib.tri_attn_module_fwd.restype = i32
+    lib.tri_attn_module_bwd_workspace_bytes.argtypes = [mp]
+    lib.tri_attn_module_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.tri_attn_module_bwd.argtypes = [mp, vp, vp, ctypes.POINTER(ModuleParams), ctypes.POINTER(ModuleSaved), vp, vp,
+                                        ctypes.POINTER(ModuleGrads), vp, ctypes.c_size_t, vp]
+    lib.tri_attn_module_bwd.restype = i32
+    if (lib.tri_attn_abi_version() != ABI_VERSION or lib.tri_mul_abi_version() != TRI_MUL_ABI_VERSION
+            or lib.tri_attn_module_abi_version() != MODULE_ABI_VERSION):
         raise RuntimeError("libtri_attn.so ABI version mismatch")
     if path is None:
         _lib = lib
@@ -319,6 +357,87 @@ def tri_mul_bwd(a, b, dz, *, incoming=False, out=None):
     return da, db
 
 
+# ---- the triangle-attention module around the core (include/tri_module.h) ----
+
+def make_module_problem(B, N, H, D, *, ending=False, eps=0.0, abi_version=MODULE_ABI_VERSION) -> ModuleProblem:
+    return ModuleProblem(abi_version, FLAG_ENDING_NODE if ending else 0, B, N, H, D, float(eps))
+
+
+def _module_params(params, C, H, dev):
+    """params: dict ln_w, ln_b (fp32 [C]), w_qkvg (bf16 [C, 4C]), w_bias (bf16 [C, H]), w_out (bf16 [C, C])."""
+    shapes = {"ln_w": ((C,), torch.float32), "ln_b": ((C,), torch.float32), "w_qkvg": ((C, 4 * C), torch.bfloat16),
+              "w_bias": ((C, H), torch.bfloat16), "w_out": ((C, C), torch.bfloat16)}
+    for n, (shape, dt) in shapes.items():
+        _check_tensor(n, params[n], shape, (dt,), dev)
+    return ModuleParams(*(params[n].data_ptr() for n in ("ln_w", "ln_b", "w_qkvg", "w_bias", "w_out")))
+
+
+def _module_dims(z, H):
+    if z.dtype != torch.bfloat16 or not z.is_cuda or not z.is_contiguous() or z.dim() != 4 or z.shape[1] != z.shape[2]:
+        raise ValueError("z is a contiguous bf16 CUDA tensor [B, N, N, C]")
+    B, N, _, C = z.shape
+    if C % H:
+        raise ValueError("the channel count must be a multiple of H")
+    return B, N, C, C // H
+
+
+def tri_attn_module_fwd(z, mask, params, H, *, ending=False, eps=0.0):
+    """Forward of the triangle-attention block: returns (y, saved) where saved is the dict
+    of the activations tri_attn_module_bwd needs (all allocated here)."""
+    B, N, C, D = _module_dims(z, H)
+    dev = z.device
+    if mask is not None:
+        _check_tensor("mask", mask, (B, N, N), (torch.uint8,), dev)
+    p = _module_params(params, C, H, dev)
+    e = dict(dtype=torch.bfloat16, device=dev)
+    saved = {"zn": torch.empty_like(z), "ln_stats": torch.empty((B, N, N, 2), dtype=torch.float32, device=dev),
+             "q": torch.empty((B, N, N, H, D), **e), "k": torch.empty((B, N, N, H, D), **e),
+             "v": torch.empty((B, N, N, H, D), **e), "g": torch.empty_like(z),
+             "bias": torch.empty((B, H, N, N), **e), "o": torch.empty((B, N, N, H, D), **e),
+             "o_residual": torch.empty((B, N, N, H, D), dtype=torch.float32, device=dev),
+             "lse": torch.empty((B, N, H, N), dtype=torch.float32, device=dev)}
+    y = torch.empty_like(z)
+    sv = ModuleSaved(*(saved[n].data_ptr() for n, _ in ModuleSaved._fields_))
+    lib = load_library()
+    st = lib.tri_attn_module_fwd(ctypes.byref(make_module_problem(B, N, H, D, ending=ending, eps=eps)), _ptr(z),
+                                 _ptr(mask), ctypes.byref(p), _ptr(y), ctypes.byref(sv), _stream(dev))
+    if st != 0:
+        raise TriAttnError(st, "tri_attn_module_fwd")
+    return y, saved
+
+
+def module_bwd_workspace_bytes(B, N, H, D, *, ending=False) -> int:
+    return load_library().tri_attn_module_bwd_workspace_bytes(ctypes.byref(make_module_problem(B, N, H, D,
+                                                                                                ending=ending)))
+
+
+def tri_attn_module_bwd(z, mask, params, saved, dy, H, *, ending=False, eps=0.0, workspace=None):
+    """Backward of the block: returns (dz, grads) with grads the dict of fp32 parameter
+    gradients (ln_w, ln_b, w_qkvg, w_bias, w_out)."""
+    B, N, C, D = _module_dims(z, H)
+    dev = z.device
+    _check_tensor("dy", dy, z.shape, (torch.bfloat16,), dev)
+    if mask is not None:
+        _check_tensor("mask", mask, (B, N, N), (torch.uint8,), dev)
+    p = _module_params(params, C, H, dev)
+    sv = ModuleSaved(*(saved[n].data_ptr() for n, _ in ModuleSaved._fields_))
+    grads = {n: torch.empty(params[n].shape, dtype=torch.float32, device=dev)
+             for n in ("ln_w", "ln_b", "w_qkvg", "w_bias", "w_out")}
+    gr = ModuleGrads(*(grads[n].data_ptr() for n, _ in ModuleGrads._fields_))
+    dz = torch.empty_like(z)
+    prob = make_module_problem(B, N, H, D, ending=ending, eps=eps)
+    lib = load_library()
+    need = lib.tri_attn_module_bwd_workspace_bytes(ctypes.byref(prob))
+    if need == 0:
+        raise TriAttnError(2, "tri_attn_module_bwd")
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if workspace is None else workspace
+    st = lib.tri_attn_module_bwd(ctypes.byref(prob), _ptr(z), _ptr(mask), ctypes.byref(p), ctypes.byref(sv),
+                                 _ptr(dy), _ptr(dz), ctypes.byref(gr), _ptr(ws), ws.numel(), _stream(dev))
+    if st != 0:
+        raise TriAttnError(st, "tri_attn_module_bwd")
+    return dz, grads
+
+
 class TriAttnFunction(torch.autograd.Function):
     """Autograd wrapper: the forward saves o, its residual and lse; the backward
     recomputes every probability tile once inside the HIP kernels."""
@@ -346,6 +465,8 @@ def tri_attn(q, k, v, bias, mask=None, ending=False, scale=None):
 
 __all__ = ["tri_attn", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_bwd_noalloc", "bwd_workspace_bytes",
            "tri_mul_fwd", "tri_mul_bwd", "make_trimul_problem", "TriMulProblem",
+           "tri_attn_module_fwd", "tri_attn_module_bwd", "module_bwd_workspace_bytes", "make_module_problem",
+           "ModuleProblem", "ModuleParams", "ModuleSaved", "ModuleGrads",
            "load_library", "NOALLOC_SCRATCH_BYTES",
            "make_problem", "Problem", "TriAttnError", "TriAttnFunction", "LIB_PATH",
            "EXPORTED_SYMBOLS"]

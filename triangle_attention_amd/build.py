@@ -11,6 +11,8 @@ ROOT = HERE.parent
 SRC = HERE / "csrc" / "tri_attn.hip"
 # the triangle multiplicative update's contraction, built into the same library
 TRI_MUL_SRC = HERE / "csrc" / "tri_mul.hip"
+# the triangle-attention module around the core (LayerNorm, projections, gating)
+MODULE_SRC = HERE / "csrc" / "tri_module.hip"
 LIB = HERE / "libtri_attn.so"
 # the matrix-core rate probe bench.py reports next to the published peak
 PROBE_SRC = HERE / "csrc" / "mfma_probe.hip"
@@ -45,7 +47,7 @@ def _compile(srcs, lib: Path, verbose: bool) -> None:
 
 def build(verbose: bool = False) -> Path:
     """Compile the library and the matrix-core probe; returns the library's path."""
-    _compile([SRC, TRI_MUL_SRC], LIB, verbose)
+    _compile([SRC, TRI_MUL_SRC, MODULE_SRC], LIB, verbose)
     _compile([PROBE_SRC], PROBE_LIB, verbose)
     return LIB
 

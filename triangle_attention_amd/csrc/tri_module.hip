@@ -1,0 +1,775 @@
+// The triangle-attention module around the core, forward and backward, for MI355X
+// (gfx950, CDNA4).
+//
+// Operation (reading of the biocloudservice page's opening paragraph, which presents the
+// kernel as triangle attention in the style of AlphaFold3 and describes nothing around
+// the core): on a pair tensor
+// z [B, N, N, C], C = H * D = 128,
+//   zn = LayerNorm(z);  q, k, v = zn Wq, zn Wk, zn Wv;  bias[b,h,j,k] = (zn Wb)[b,j,k,h]
+//   g = sigmoid(zn Wg);  o = core(q, k, v, bias, mask);  y = (g * o) Wo
+// (no bias terms in the projections); the ending-node block is the same block on the
+// transposed pair tensor, i.e. the bias transposed (bias[b,h,j,k] = (zn Wb)[b,k,j,h])
+// and the core run with its ending-node flag.
+//
+// Every step but the core is per position, so the kernels work on tiles of 128
+// consecutive positions (rows of the [B N N, 128] matrices) times 128 x 128 weight
+// blocks, one v_mfma_f32_32x32x16_bf16 tile product per workgroup (4 waves, 2 x 2 of
+// 64 x 64), with the prologue or epilogue fused:
+//   mod_proj        LayerNorm in (statistics per position in fp32), zn into LDS; the
+//                   q, k, v, gate (sigmoid) or bias (transposed store) block out
+//   mod_gate_out    bf16(g * o) in, y out
+//   mod_out_bwd     dy Wo^T; out: dO = dgo * g and the gate's pre-activation gradient
+//                   dgo * o * g (1 - g)
+//   mod_in_bwd      dzn = [dq dk dv dg] Wqkvg^T + dbias Wb^T (five 128-deep steps);
+//                   the LayerNorm backward out, and per-tile partial sums of the
+//                   LayerNorm scale and offset gradients
+//   mod_wgrad       weight gradients zn^T [dq dk dv dg dbias] and bf16(g * o)^T dy:
+//                   contractions over all positions, split into fixed slices whose fp32
+//                   partials the reduction kernels sum in slice order
+// No floating-point atomics: every result is one fixed-order sum (bitwise reproducible,
+// as the core: Lambda post, "Как работает TurboPairFormer", third point).
+//
+// MFMA layouts (64 lanes, hh = lane / 32):
+//   A (32 x 16): lane supplies A[lane % 32][8 hh + e], e = 0..7
+//   B (16 x 32): lane supplies B[8 hh + e][lane % 32]
+//   C (32 x 32): lane holds C[8 (r / 4) + 4 hh + r % 4][lane % 32], r = 0..15
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+#include <string.h>
+
+#include "tri_attn.h"
+#include "tri_module.h"
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr int CH = 128;   // pair channels (H * D)
+constexpr int TP = 128;   // positions per tile
+constexpr int NT = 256;   // threads per workgroup (4 waves)
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Element (row, col) of a [128][128] bf16 LDS tile.  The 16-byte chunks of a row are
+// permuted by ((row & 3) << 2) | ((row >> 2) & 3): the 16-byte row reads of 16
+// consecutive rows (one chunk each) touch all 64 banks once, and so do the transposing
+// reads, whose 16-lane groups cover rows 4t .. 4t + 3 over two consecutive chunks (the
+// four rows map the chunk pair to four disjoint bank groups).
+__device__ __forceinline__ int toff(int row, int col) {
+  const int sw = ((row & 3) << 2) | ((row >> 2) & 3);
+  return row * 128 + (((col >> 3) ^ sw) << 3) + (col & 7);
+}
+// Row operand: lane gets tile[row0 + lane % 32][kk + 8 hh + e].
+__device__ __forceinline__ bf16x8 row_operand(const uint16_t *tile, int row0, int kk, int lane) {
+  return *(const bf16x8 *)(tile + toff(row0 + (lane & 31), kk + 8 * (lane >> 5)));
+}
+// Transposed operand: lane gets tile[kk + 8 hh + e][col0 + lane % 32].  ds_read_b64_tr_b16
+// works on 4 x 16 blocks: in each 16-lane group, lane 4 m + s addresses row m, columns
+// 4 s .. 4 s + 3, and lane c of the group receives column c of the four rows.
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t *tile, int kk, int col0, int lane) {
+  const int g = lane >> 4, w = lane & 15, m = w >> 2, s = w & 3;
+  const int row = kk + 8 * (lane >> 5) + m, col = col0 + 16 * (g & 1) + 4 * s;
+  i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + toff(row, col)));
+  i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + toff(row + 4, col)));
+  typedef __attribute__((ext_vector_type(8))) short i16x8;
+  return __builtin_bit_cast(bf16x8, (i16x8)__builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// How an operand sits in its LDS tile: ROW = [m or n][t] (contraction index
+// contiguous), TR = [t][m or n].
+enum Layout { ROW = 0, TR = 1 };
+
+// acc[i][j] += sum over t in [0, 16 * slices) of A(wm + 32 i + ., t) B(t, wn + 32 j + .)
+template <int AL, int BL>
+__device__ __forceinline__ void tile_product(const uint16_t *sA, const uint16_t *sB, int wm, int wn, int lane,
+                                             int slices, f32x16 (&acc)[2][2]) {
+  for (int s = 0; s < slices; ++s) {
+    const int kk = 16 * s;
+    bf16x8 a[2], b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      a[i] = AL == ROW ? row_operand(sA, wm + 32 * i, kk, lane) : tr_operand(sA, kk, wm + 32 * i, lane);
+      b[i] = BL == ROW ? row_operand(sB, wn + 32 * i, kk, lane) : tr_operand(sB, kk, wn + 32 * i, lane);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma(a[i], b[j], acc[i][j]);
+  }
+}
+
+__device__ __forceinline__ void zero(f32x16 (&acc)[2][2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16){};
+}
+
+// A [128][128] bf16 matrix block (rows row0.., 256-byte rows of a row-major matrix with
+// `ld` elements per row, columns col0 .. col0 + 127) into an LDS tile: thread t copies
+// 16-byte pieces t, t + 256, ...
+__device__ __forceinline__ void load_block(uint16_t *tile, const uint16_t *src, long long ld, int tid) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int p = tid + NT * i, row = p >> 4, c = (p & 15) * 8;
+    *(u32x4 *)(tile + toff(row, c)) = *(const u32x4 *)(src + (long long)row * ld + c);
+  }
+}
+
+// The accumulator tile as bf16 into an LDS tile (f applied to each value), then stored
+// as 128 rows of 256 bytes to dst (row stride 128 elements).
+template <typename F>
+__device__ __forceinline__ void store_tile_bf16(uint16_t *tile, uint16_t *dst, const f32x16 (&acc)[2][2], int wm,
+                                                int wn, int lane, int tid, F f) {
+  const int hh = lane >> 5, ll = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3), n = wn + 32 * j + ll;
+        tile[toff(m, n)] = (uint16_t)(pack_bf16(f(acc[i][j][r]), 0.f) & 0xffffu);
+      }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int p = tid + NT * i, row = p >> 4, c = (p & 15) * 8;
+    *(u32x4 *)(dst + (long long)row * CH + c) = *(const u32x4 *)(tile + toff(row, c));
+  }
+}
+
+// fp32 [128][128] LDS tile for epilogues that need whole position rows: element (row,
+// col) at row * 128 + (col ^ 4 * (row & 7)) (4-byte granules permuted in groups of
+// four so that the accumulator writes of the two lane halves use different banks).
+__device__ __forceinline__ int foff(int row, int col) { return row * 128 + (col ^ ((row & 7) << 2)); }
+
+template <typename F>
+__device__ __forceinline__ void stage_f32(float *t32, const f32x16 (&acc)[2][2], int wm, int wn, int lane, F f) {
+  const int hh = lane >> 5, ll = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3), n = wn + 32 * j + ll;
+        t32[foff(m, n)] = f(acc[i][j][r]);
+      }
+}
+// 8 consecutive columns c .. c + 7 (c a multiple of 8) of row `row` of a foff tile
+__device__ __forceinline__ void read8_f32(const float *t32, int row, int c, float *x) {
+  const f32x4 a = *(const f32x4 *)(t32 + foff(row, c)), b = *(const f32x4 *)(t32 + foff(row, c + 4));
+  x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+  x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+}
+
+__device__ __forceinline__ void unpack8(u32x4 w, float *x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf_lo(w[i]);
+    x[2 * i + 1] = bf_hi(w[i]);
+  }
+}
+__device__ __forceinline__ u32x4 pack8u(const float *x) {
+  return (u32x4){pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]), pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __builtin_amdgcn_exp2f(-x * kLog2e)); }
+
+// Workgroup index -> tile index such that consecutive tiles share an XCD.
+__device__ __forceinline__ int xcd_remap(int L, int G) {
+  const int per = G >> 3;
+  if (L < (per << 3)) return (L & 7) * per + (L >> 3);
+  return L;
+}
+
+struct ModArgs {
+  // forward
+  const uint16_t *z;
+  const float *ln_w, *ln_b;
+  const uint16_t *w_qkvg, *w_bias, *w_out;
+  uint16_t *zn;
+  float *stats;                // [P][2]: mean, rstd
+  uint16_t *q, *k, *v, *g, *bias, *o, *y;
+  // backward
+  const uint16_t *dy;
+  uint16_t *d_o, *dgp;         // dO for the core, the gate's pre-activation gradient
+  const uint16_t *dq, *dk, *dv;
+  const float *dbias;          // fp32 [B, H, N, N] (the core's frame)
+  uint16_t *dz;
+  float *ln_part;              // [tiles][2][128]: per-tile sums of dzn * xhat and dzn
+  float *w_part;               // [6][S][128][128]
+  int B, N, H, ending;
+  long long P;                 // positions B N N
+  int tiles, slices;
+  float eps;
+};
+
+// Position p (global) -> the bias element of head h it feeds: bias[b, h, j, k] for the
+// starting node (p = (b, j, k)), bias[b, h, k, j] for the ending node.
+__device__ __forceinline__ long long bias_index(const ModArgs &a, long long p, int h) {
+  const long long NN = (long long)a.N * a.N;
+  const long long b = p / NN, jk = p - b * NN;
+  const long long e = a.ending ? (jk % a.N) * a.N + jk / a.N : jk;
+  return (b * a.H + h) * NN + e;
+}
+
+// ------------------------------------------------------------------------------------
+// Forward
+// ------------------------------------------------------------------------------------
+// Workgroup = (tile of 128 positions, output block 0..4: q, k, v, gate, bias).  The
+// LayerNorm runs in every block's workgroup (the z tile is read five times, from L2
+// for all but the first: the five blocks of a tile run together on one XCD); block 0
+// also stores zn and the statistics for the backward.
+__global__ __launch_bounds__(NT, 2) void mod_proj_kernel(ModArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[TP * CH];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[CH * CH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int blk = t % 5, tile = t / 5;
+  const long long p0 = (long long)tile * TP;
+
+  // weights of the block: B[t = input channel][n = output column]
+  if (blk < 4) {
+    load_block(sB, a.w_qkvg + blk * CH, 4 * CH, tid);
+  } else {
+    for (int e = tid; e < CH * CH; e += NT) {
+      const int row = e >> 7, col = e & 127;
+      sB[toff(row, col)] = col < a.H ? a.w_bias[(long long)row * a.H + col] : (uint16_t)0;
+    }
+  }
+  // LayerNorm: thread -> position tid / 2, channels 64 (tid % 2) .. + 63
+  {
+    const int pr = tid >> 1, c0 = 64 * (tid & 1);
+    const uint16_t *src = a.z + (p0 + pr) * CH + c0;
+    float x[64];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) unpack8(*(const u32x4 *)(src + 8 * i), x + 8 * i);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) s += x[i];
+    s += __shfl_xor(s, 1);
+    const float mean = s * (1.f / CH);
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const float d = x[i] - mean;
+      v = fmaf(d, d, v);
+    }
+    v += __shfl_xor(v, 1);
+    const float rstd = 1.f / sqrtf(v * (1.f / CH) + a.eps);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] = fmaf((x[i] - mean) * rstd, a.ln_w[c0 + i], a.ln_b[c0 + i]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4 w = pack8u(x + 8 * i);
+      *(u32x4 *)(sA + toff(pr, c0 + 8 * i)) = w;
+      if (blk == 0) *(u32x4 *)(a.zn + (p0 + pr) * CH + c0 + 8 * i) = w;
+    }
+    if (blk == 0 && (tid & 1) == 0) *(f32x2 *)(a.stats + 2 * (p0 + pr)) = (f32x2){mean, rstd};
+  }
+  __syncthreads();
+
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  f32x16 acc[2][2];
+  zero(acc);
+  tile_product<ROW, TR>(sA, sB, wm, wn, lane, CH / 16, acc);
+  __syncthreads();  // sA is reused for the output
+
+  if (blk < 3) {
+    uint16_t *dst = (blk == 0 ? a.q : blk == 1 ? a.k : a.v) + p0 * CH;
+    store_tile_bf16(sA, dst, acc, wm, wn, lane, tid, [](float x) { return x; });
+  } else if (blk == 3) {
+    store_tile_bf16(sA, a.g + p0 * CH, acc, wm, wn, lane, tid, [](float x) { return sigmoidf_(x); });
+  } else {
+    // the bias: column n < H is head n
+    const int hh = lane >> 5, ll = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = wn + 32 * j + ll;
+        if (n >= a.H) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+          a.bias[bias_index(a, p0 + m, n)] = (uint16_t)(pack_bf16(acc[i][j][r], 0.f) & 0xffffu);
+        }
+      }
+  }
+}
+
+// y = bf16(g * o) Wo, one workgroup per tile of 128 positions.
+__global__ __launch_bounds__(NT, 2) void mod_gate_out_kernel(ModArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[TP * CH];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[CH * CH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long long p0 = (long long)xcd_remap(blockIdx.x, gridDim.x) * TP;
+  load_block(sB, a.w_out, CH, tid);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+    const long long off = (p0 + row) * CH + c;
+    float gv[8], ov[8];
+    unpack8(*(const u32x4 *)(a.g + off), gv);
+    unpack8(*(const u32x4 *)(a.o + off), ov);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gv[e] *= ov[e];
+    *(u32x4 *)(sA + toff(row, c)) = pack8u(gv);
+  }
+  __syncthreads();
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  f32x16 acc[2][2];
+  zero(acc);
+  tile_product<ROW, TR>(sA, sB, wm, wn, lane, CH / 16, acc);
+  __syncthreads();
+  store_tile_bf16(sA, a.y + p0 * CH, acc, wm, wn, lane, tid, [](float x) { return x; });
+}
+
+// ------------------------------------------------------------------------------------
+// Backward
+// ------------------------------------------------------------------------------------
+// dgo = dy Wo^T per tile; dO = dgo * g and dgp = dgo * o * g (1 - g), both bf16.
+__global__ __launch_bounds__(NT, 1) void mod_out_bwd_kernel(ModArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[TP * CH];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[CH * CH];
+  __shared__ __attribute__((aligned(16))) float s32[TP * CH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long long p0 = (long long)xcd_remap(blockIdx.x, gridDim.x) * TP;
+  load_block(sA, a.dy + p0 * CH, CH, tid);
+  load_block(sB, a.w_out, CH, tid);  // Wo [c_in][c_out]: B(t = c_out, n = c_in) as rows
+  __syncthreads();
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  f32x16 acc[2][2];
+  zero(acc);
+  tile_product<ROW, ROW>(sA, sB, wm, wn, lane, CH / 16, acc);
+  stage_f32(s32, acc, wm, wn, lane, [](float x) { return x; });
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+    const long long off = (p0 + row) * CH + c;
+    float d[8], gv[8], ov[8], dov[8], dgv[8];
+    read8_f32(s32, row, c, d);
+    unpack8(*(const u32x4 *)(a.g + off), gv);
+    unpack8(*(const u32x4 *)(a.o + off), ov);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      dov[e] = d[e] * gv[e];
+      dgv[e] = d[e] * ov[e] * gv[e] * (1.f - gv[e]);
+    }
+    *(u32x4 *)(a.d_o + off) = pack8u(dov);
+    *(u32x4 *)(a.dgp + off) = pack8u(dgv);
+  }
+}
+
+// dzn = [dq dk dv dgp] Wqkvg^T + dbias Wb^T per tile (five contraction blocks of 128,
+// the bias block only over its H columns), then the LayerNorm backward
+//   dxhat = dzn * w,  dz = rstd (dxhat - mean(dxhat) - xhat mean(dxhat xhat)),
+// and the tile's sums over its positions of dzn * xhat and of dzn (partials of the
+// LayerNorm scale and offset gradients), each in position order.
+__global__ __launch_bounds__(NT, 1) void mod_in_bwd_kernel(ModArgs a) {
+  // [0, 64 KB): the two operand tiles, then the fp32 tile of dzn * xhat;
+  // [64, 128 KB): the fp32 tile of dzn
+  __shared__ __attribute__((aligned(16))) float lds[2 * TP * CH];
+  uint16_t *sA = (uint16_t *)lds, *sB = sA + TP * CH;
+  float *s32 = lds + TP * CH, *sx = lds;
+  __shared__ float s_half[2][CH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const long long p0 = (long long)tile * TP;
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  f32x16 acc[2][2];
+  zero(acc);
+  for (int blk = 0; blk < 5; ++blk) {
+    if (blk) __syncthreads();  // the previous block's operands are consumed
+    if (blk < 4) {
+      const uint16_t *src = blk == 0 ? a.dq : blk == 1 ? a.dk : blk == 2 ? a.dv : a.dgp;
+      load_block(sA, src + p0 * CH, CH, tid);
+      load_block(sB, a.w_qkvg + blk * CH, 4 * CH, tid);  // B(t, n = c_in) = Wqkvg[c_in][128 blk + t]: rows
+    } else {
+      // A(position, t = head) = dbias at that position, rounded to bf16;
+      // B(t = head, n = c_in) = Wb[c_in][head]: rows
+      for (int e = tid; e < TP * CH; e += NT) {
+        const int row = e >> 7, col = e & 127;
+        sA[toff(row, col)] =
+            col < a.H ? (uint16_t)(pack_bf16(a.dbias[bias_index(a, p0 + row, col)], 0.f) & 0xffffu) : (uint16_t)0;
+        sB[toff(row, col)] = col < a.H ? a.w_bias[(long long)row * a.H + col] : (uint16_t)0;
+      }
+    }
+    __syncthreads();
+    tile_product<ROW, ROW>(sA, sB, wm, wn, lane, blk < 4 ? CH / 16 : (a.H + 15) / 16, acc);
+  }
+  stage_f32(s32, acc, wm, wn, lane, [](float x) { return x; });
+  __syncthreads();  // dzn staged; the operand tiles are free
+  // per position: thread -> position tid / 2, channels 64 (tid % 2) .. + 63
+  {
+    const int pr = tid >> 1, c0 = 64 * (tid & 1);
+    const f32x2 st = *(const f32x2 *)(a.stats + 2 * (p0 + pr));
+    const float mean = st[0], rstd = st[1];
+    float s1 = 0.f, s2 = 0.f;
+    float dx[64], xh[64];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float zv[8], d[8], dxh[8];
+      unpack8(*(const u32x4 *)(a.z + (p0 + pr) * CH + c0 + 8 * i), zv);
+      read8_f32(s32, pr, c0 + 8 * i, d);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = 8 * i + e;
+        xh[c] = (zv[e] - mean) * rstd;
+        dxh[e] = d[e] * xh[c];
+        dx[c] = d[e] * a.ln_w[c0 + c];
+        s1 += dx[c];
+        s2 = fmaf(dx[c], xh[c], s2);
+      }
+      *(f32x4 *)(sx + foff(pr, c0 + 8 * i)) = (f32x4){dxh[0], dxh[1], dxh[2], dxh[3]};
+      *(f32x4 *)(sx + foff(pr, c0 + 8 * i + 4)) = (f32x4){dxh[4], dxh[5], dxh[6], dxh[7]};
+    }
+    // the two halves of the position: (this half) + (other half) in the same order on
+    // both lanes
+    s1 += __shfl_xor(s1, 1);
+    s2 += __shfl_xor(s2, 1);
+    const float m1 = s1 * (1.f / CH), m2 = s2 * (1.f / CH);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = rstd * (dx[8 * i + e] - m1 - xh[8 * i + e] * m2);
+      *(u32x4 *)(a.dz + (p0 + pr) * CH + c0 + 8 * i) = pack8u(o);
+    }
+  }
+  __syncthreads();
+  // per channel: thread -> channel tid % 128, positions 64 (tid / 128) .. + 63 in order,
+  // then the lower half plus the upper half
+  {
+    const int c = tid & 127, hp = tid >> 7;
+    float sw = 0.f, sb = 0.f;
+    for (int r = 64 * hp; r < 64 * hp + 64; ++r) {
+      sw += sx[foff(r, c)];
+      sb += s32[foff(r, c)];
+    }
+    if (hp) {
+      s_half[0][c] = sw;
+      s_half[1][c] = sb;
+    }
+    __syncthreads();
+    if (!hp) {
+      float *dst = a.ln_part + (long long)tile * 2 * CH;
+      dst[c] = sw + s_half[0][c];
+      dst[CH + c] = sb + s_half[1][c];
+    }
+  }
+}
+
+// Weight gradients: workgroup = (output block, slice of tiles); out[m][n] = sum over
+// the slice's positions p of A[p][m] B[p][n] with
+//   blocks 0..3: A = zn, B = dq, dk, dv, dgp      (d Wqkvg, column block 0..3)
+//   block 4:     A = zn, B = dbias at p (bf16)    (d Wb, columns < H)
+//   block 5:     A = bf16(g * o), B = dy          (d Wo)
+// Both operands are read transposed from position-major tiles.  The fp32 partial of the
+// slice goes to w_part[block][slice].
+__global__ __launch_bounds__(NT, 2) void mod_wgrad_kernel(ModArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[TP * CH];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[TP * CH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int blk = t % 6, slice = t / 6;
+  const int t0 = (int)((long long)slice * a.tiles / a.slices), t1 = (int)((long long)(slice + 1) * a.tiles / a.slices);
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  f32x16 acc[2][2];
+  zero(acc);
+  for (int tile = t0; tile < t1; ++tile) {
+    const long long p0 = (long long)tile * TP;
+    if (tile > t0) __syncthreads();
+    if (blk < 5) {
+      load_block(sA, a.zn + p0 * CH, CH, tid);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+        const long long off = (p0 + row) * CH + c;
+        float gv[8], ov[8];
+        unpack8(*(const u32x4 *)(a.g + off), gv);
+        unpack8(*(const u32x4 *)(a.o + off), ov);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) gv[e] *= ov[e];
+        *(u32x4 *)(sA + toff(row, c)) = pack8u(gv);
+      }
+    }
+    if (blk < 4) {
+      const uint16_t *src = blk == 0 ? a.dq : blk == 1 ? a.dk : blk == 2 ? a.dv : a.dgp;
+      load_block(sB, src + p0 * CH, CH, tid);
+    } else if (blk == 5) {
+      load_block(sB, a.dy + p0 * CH, CH, tid);
+    } else {
+      for (int e = tid; e < TP * CH; e += NT) {
+        const int row = e >> 7, col = e & 127;
+        sB[toff(row, col)] =
+            col < a.H ? (uint16_t)(pack_bf16(a.dbias[bias_index(a, p0 + row, col)], 0.f) & 0xffffu) : (uint16_t)0;
+      }
+    }
+    __syncthreads();
+    tile_product<TR, TR>(sA, sB, wm, wn, lane, TP / 16, acc);
+  }
+  float *dst = a.w_part + ((long long)blk * a.slices + slice) * CH * CH;
+  const int hh = lane >> 5, ll = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3), n = wn + 32 * j + ll;
+        dst[m * CH + n] = acc[i][j][r];
+      }
+}
+
+struct ReduceArgs {
+  const float *w_part;
+  const float *ln_part;
+  float *dw_qkvg, *dw_bias, *dw_out, *d_ln_w, *d_ln_b;
+  int H, slices, tiles;
+};
+
+// One thread per weight-gradient element: the slices' partials summed in slice order.
+__global__ __launch_bounds__(256) void mod_reduce_w_kernel(ReduceArgs a) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= 6 * CH * CH) return;
+  const int blk = e / (CH * CH), mn = e - blk * CH * CH, m = mn >> 7, n = mn & 127;
+  if (blk == 4 && n >= a.H) return;
+  const float *src = a.w_part + (long long)blk * a.slices * CH * CH + mn;
+  float s = 0.f;
+  for (int sl = 0; sl < a.slices; ++sl) s += src[(long long)sl * CH * CH];
+  if (blk < 4) a.dw_qkvg[m * 4 * CH + blk * CH + n] = s;
+  else if (blk == 4) a.dw_bias[m * a.H + n] = s;
+  else a.dw_out[m * CH + n] = s;
+}
+
+// One workgroup (64 threads) per LayerNorm parameter gradient element: thread i sums the
+// tiles' partials of its contiguous share in tile order, then the 64 sums are combined
+// by a fixed butterfly.
+__global__ __launch_bounds__(64) void mod_reduce_ln_kernel(ReduceArgs a) {
+  const int e = blockIdx.x;  // 0..255: scale gradients, then offset gradients
+  const int i = threadIdx.x;
+  const int t0 = (int)((long long)i * a.tiles / 64), t1 = (int)((long long)(i + 1) * a.tiles / 64);
+  float s = 0.f;
+  for (int t = t0; t < t1; ++t) s += a.ln_part[(long long)t * 2 * CH + e];
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) s += __shfl_xor(s, d);
+  if (i == 0) (e < CH ? a.d_ln_w : a.d_ln_b)[e & 127] = s;
+}
+
+// ------------------------------------------------------------------------------------
+// Host side
+// ------------------------------------------------------------------------------------
+constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+bool aligned16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
+
+tri_attn_status check(const tri_attn_module_problem *p) {
+  if (!p) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (p->abi_version != TRI_ATTN_MODULE_ABI_VERSION) return TRI_ATTN_ERROR_ABI_MISMATCH;
+  if (p->B < 1 || p->N < 1 || p->H < 1 || p->D < 1) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!(p->ln_eps >= 0.f) || isinf(p->ln_eps)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (p->flags & ~TRI_ATTN_FLAG_ENDING_NODE) return TRI_ATTN_ERROR_NOT_SUPPORTED;
+  if (p->H * p->D != CH) return TRI_ATTN_ERROR_NOT_SUPPORTED;
+  return TRI_ATTN_SUCCESS;  // N, H and D are further checked by the core's validation
+}
+
+tri_attn_problem core_problem(const tri_attn_module_problem *p) {
+  tri_attn_problem c;
+  memset(&c, 0, sizeof c);
+  c.abi_version = TRI_ATTN_ABI_VERSION;
+  c.flags = (p->flags & TRI_ATTN_FLAG_ENDING_NODE) ? TRI_ATTN_FLAG_ENDING_NODE : 0;
+  c.B = p->B;
+  c.N = p->N;
+  c.H = p->H;
+  c.D = p->D;
+  c.softmax_scale = 0.f;
+  return c;
+}
+
+ModArgs base_args(const tri_attn_module_problem *p) {
+  ModArgs a;
+  memset(&a, 0, sizeof a);
+  a.B = (int)p->B;
+  a.N = (int)p->N;
+  a.H = (int)p->H;
+  a.ending = (p->flags & TRI_ATTN_FLAG_ENDING_NODE) ? 1 : 0;
+  a.P = p->B * p->N * p->N;
+  a.tiles = (int)(a.P / TP);
+  a.eps = p->ln_eps > 0.f ? p->ln_eps : 1e-5f;
+  return a;
+}
+
+int wgrad_slices(int tiles) { return tiles < 64 ? tiles : 64; }
+
+struct BwdLayout {
+  size_t off_do, off_dgp, off_dq, off_dk, off_dv, off_db, off_core, off_w, off_ln, total;
+  size_t core_bytes;
+  int slices;
+};
+
+BwdLayout bwd_layout(const tri_attn_module_problem *p, size_t core_bytes) {
+  BwdLayout l;
+  const size_t E = (size_t)p->B * p->N * p->N * CH * 2;  // one bf16 position tensor
+  const int tiles = (int)(p->B * p->N * p->N / TP);
+  l.slices = wgrad_slices(tiles);
+  l.core_bytes = core_bytes;
+  size_t o = 0;
+  l.off_do = o; o += align256(E);
+  l.off_dgp = o; o += align256(E);
+  l.off_dq = o; o += align256(E);
+  l.off_dk = o; o += align256(E);
+  l.off_dv = o; o += align256(E);
+  l.off_db = o; o += align256((size_t)p->B * p->H * p->N * p->N * 4);
+  l.off_core = o; o += align256(core_bytes);
+  l.off_w = o; o += align256((size_t)6 * l.slices * CH * CH * 4);
+  l.off_ln = o; o += align256((size_t)tiles * 2 * CH * 4);
+  l.total = o;
+  return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tri_attn_module_abi_version(void) { return TRI_ATTN_MODULE_ABI_VERSION; }
+
+tri_attn_status tri_attn_module_fwd(const tri_attn_module_problem *problem, const void *z, const uint8_t *mask,
+                                    const tri_attn_module_params *params, void *y,
+                                    const tri_attn_module_saved *saved, hipStream_t stream) {
+  tri_attn_status st = check(problem);
+  if (st != TRI_ATTN_SUCCESS) return st;
+  const tri_attn_problem cp = core_problem(problem);
+  // the core's own validation (sizes) before anything is enqueued
+  if (tri_attn_bwd_workspace_bytes(&cp) == 0) return TRI_ATTN_ERROR_NOT_SUPPORTED;
+  if (!params || !saved) return TRI_ATTN_ERROR_INVALID_VALUE;
+  const void *need[] = {z, y, params->ln_w, params->ln_b, params->w_qkvg, params->w_bias, params->w_out,
+                        saved->zn, saved->ln_stats, saved->q, saved->k, saved->v, saved->g, saved->bias,
+                        saved->o, saved->o_residual, saved->lse};
+  for (const void *x : need)
+    if (!aligned16(x)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  ModArgs a = base_args(problem);
+  a.z = (const uint16_t *)z;
+  a.ln_w = params->ln_w;
+  a.ln_b = params->ln_b;
+  a.w_qkvg = (const uint16_t *)params->w_qkvg;
+  a.w_bias = (const uint16_t *)params->w_bias;
+  a.w_out = (const uint16_t *)params->w_out;
+  a.zn = (uint16_t *)saved->zn;
+  a.stats = saved->ln_stats;
+  a.q = (uint16_t *)saved->q;
+  a.k = (uint16_t *)saved->k;
+  a.v = (uint16_t *)saved->v;
+  a.g = (uint16_t *)saved->g;
+  a.bias = (uint16_t *)saved->bias;
+  a.o = (uint16_t *)saved->o;
+  a.y = (uint16_t *)y;
+  hipLaunchKernelGGL(mod_proj_kernel, dim3((unsigned)(a.tiles * 5)), dim3(NT), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  st = tri_attn_fwd(&cp, saved->q, saved->k, saved->v, saved->bias, mask, saved->o, saved->o_residual, saved->lse,
+                    stream);
+  if (st != TRI_ATTN_SUCCESS) return st;
+  hipLaunchKernelGGL(mod_gate_out_kernel, dim3((unsigned)a.tiles), dim3(NT), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH_FAILED;
+}
+
+size_t tri_attn_module_bwd_workspace_bytes(const tri_attn_module_problem *problem) {
+  if (check(problem) != TRI_ATTN_SUCCESS) return 0;
+  const tri_attn_problem cp = core_problem(problem);
+  const size_t core = tri_attn_bwd_workspace_bytes(&cp);
+  if (core == 0) return 0;
+  return bwd_layout(problem, core).total;
+}
+
+tri_attn_status tri_attn_module_bwd(const tri_attn_module_problem *problem, const void *z, const uint8_t *mask,
+                                    const tri_attn_module_params *params, const tri_attn_module_saved *saved,
+                                    const void *dy, void *dz, const tri_attn_module_param_grads *grads,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  tri_attn_status st = check(problem);
+  if (st != TRI_ATTN_SUCCESS) return st;
+  const tri_attn_problem cp = core_problem(problem);
+  const size_t core = tri_attn_bwd_workspace_bytes(&cp);
+  if (core == 0) return TRI_ATTN_ERROR_NOT_SUPPORTED;
+  if (!params || !saved || !grads) return TRI_ATTN_ERROR_INVALID_VALUE;
+  const void *need[] = {z, dy, dz, params->ln_w, params->ln_b, params->w_qkvg, params->w_bias, params->w_out,
+                        saved->zn, saved->ln_stats, saved->q, saved->k, saved->v, saved->g, saved->bias, saved->o,
+                        saved->o_residual, saved->lse, grads->ln_w, grads->ln_b, grads->w_qkvg, grads->w_bias,
+                        grads->w_out};
+  for (const void *x : need)
+    if (!aligned16(x)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!workspace || ((uintptr_t)workspace & 255u)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  const BwdLayout l = bwd_layout(problem, core);
+  if (workspace_bytes < l.total) return TRI_ATTN_ERROR_INSUFFICIENT_WORKSPACE;
+  char *ws = (char *)workspace;
+  ModArgs a = base_args(problem);
+  a.z = (const uint16_t *)z;
+  a.ln_w = params->ln_w;
+  a.ln_b = params->ln_b;
+  a.w_qkvg = (const uint16_t *)params->w_qkvg;
+  a.w_bias = (const uint16_t *)params->w_bias;
+  a.w_out = (const uint16_t *)params->w_out;
+  a.zn = (uint16_t *)saved->zn;
+  a.stats = saved->ln_stats;
+  a.g = (uint16_t *)saved->g;
+  a.o = (uint16_t *)saved->o;
+  a.dy = (const uint16_t *)dy;
+  a.d_o = (uint16_t *)(ws + l.off_do);
+  a.dgp = (uint16_t *)(ws + l.off_dgp);
+  a.dq = (const uint16_t *)(ws + l.off_dq);
+  a.dk = (const uint16_t *)(ws + l.off_dk);
+  a.dv = (const uint16_t *)(ws + l.off_dv);
+  a.dbias = (const float *)(ws + l.off_db);
+  a.dz = (uint16_t *)dz;
+  a.w_part = (float *)(ws + l.off_w);
+  a.ln_part = (float *)(ws + l.off_ln);
+  a.slices = l.slices;
+
+  hipLaunchKernelGGL(mod_out_bwd_kernel, dim3((unsigned)a.tiles), dim3(NT), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  tri_attn_problem cpb = cp;
+  cpb.flags |= TRI_ATTN_FLAG_DBIAS_FP32;
+  st = tri_attn_bwd(&cpb, saved->q, saved->k, saved->v, saved->bias, mask, saved->o, saved->o_residual, saved->lse,
+                    a.d_o, ws + l.off_dq, ws + l.off_dk, ws + l.off_dv, ws + l.off_db, ws + l.off_core, l.core_bytes,
+                    stream);
+  if (st != TRI_ATTN_SUCCESS) return st;
+  hipLaunchKernelGGL(mod_in_bwd_kernel, dim3((unsigned)a.tiles), dim3(NT), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  hipLaunchKernelGGL(mod_wgrad_kernel, dim3((unsigned)(6 * a.slices)), dim3(NT), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  ReduceArgs r;
+  r.w_part = a.w_part;
+  r.ln_part = a.ln_part;
+  r.dw_qkvg = grads->w_qkvg;
+  r.dw_bias = grads->w_bias;
+  r.dw_out = grads->w_out;
+  r.d_ln_w = grads->ln_w;
+  r.d_ln_b = grads->ln_b;
+  r.H = a.H;
+  r.slices = a.slices;
+  r.tiles = a.tiles;
+  hipLaunchKernelGGL(mod_reduce_w_kernel, dim3((6 * CH * CH + 255) / 256), dim3(256), 0, stream, r);
+  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  hipLaunchKernelGGL(mod_reduce_ln_kernel, dim3(2 * CH), dim3(64), 0, stream, r);
+  return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH_FAILED;
+}
+
+}  // extern "C"
