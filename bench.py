@@ -32,6 +32,10 @@ The JSON line also carries
                  node orientation, and 768 at head dimensions 16 and 64 with the same
                  128 pair channels), each timed over fewer steps: median time per
                  step, forward and backward, TFLOP/s and fraction of the MFMA peak;
+  module       : the triangle-attention module around the core (LayerNorm, the q, k, v,
+                 bias and gate projections, the core, the gated output projection, and
+                 the backward to dz and the parameter gradients) at crop 768: median
+                 forward and backward times;
   tri_mul      : the triangle multiplicative update's contraction at the crop-768
                  shape with 128 channels (tri_mul_fwd + tri_mul_bwd, outgoing and
                  incoming edges): median times, TFLOP/s and fraction of the peak;
@@ -411,6 +415,62 @@ def time_trimul(args, workload: str, incoming: bool, steps: int, warmup: int) ->
                 torch.equal(x.view(torch.int16), y.view(torch.int16)) for x, y in zip(first, (z, da, db)))}
 
 
+def module_bytes(B: int, N: int, H: int) -> dict:
+    """Algorithmic HBM bytes of one module step outside the core: each bf16 position
+    tensor ([B, N, N, 128], E bytes) read or written once per kernel that needs it.
+    Forward: projections read z and write zn, q, k, v, g (+ statistics and the bias);
+    the gated output reads g, o and writes y.  Backward: dy, g, o in and dO, dg out;
+    dq, dk, dv, dg, z in and dz out (+ dbias, statistics); the weight gradients read
+    zn, dq, dk, dv, dg, g, o, dy (+ dbias)."""
+    P = B * N * N
+    E = P * 128 * 2
+    nb = B * H * N * N
+    fwd = 6 * E + 8 * P + 2 * nb + 3 * E
+    bwd = 5 * E + 6 * E + 4 * nb + 8 * P + 8 * E + 4 * nb
+    return {"forward": fwd, "backward": bwd, "total": fwd + bwd}
+
+
+def time_module(args, workload: str, steps: int, warmup: int) -> dict:
+    """Time `steps` forward + backward calls of the triangle-attention module (the core
+    included) after `warmup`; events on the launch stream."""
+    import seeded_inputs as si
+    import triangle_attention_amd as ta
+
+    w = si.MODULE_WORKLOADS[workload]
+    dev = torch.device("cuda:0")
+    log(f"workload {w.name}: {w.description}")
+    inp = {n: t.to(dev) for n, t in si.make_module_workload(w.name).items()}
+    mask = inp["mask"] if w.mask != "none" else None
+    params = {n: inp[n] for n in ("ln_w", "ln_b", "w_qkvg", "w_bias", "w_out")}
+    ws = torch.empty(ta.module_bwd_workspace_bytes(w.B, w.N, w.H, w.D), dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        y, saved = ta.tri_attn_module_fwd(inp["z"], mask, params, w.H)
+        ta.tri_attn_module_bwd(inp["z"], mask, params, saved, inp["dy"], w.H, workspace=ws)
+    torch.cuda.synchronize()
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    outs = []
+    for i in range(steps):
+        marks[i][0].record()
+        y, saved = ta.tri_attn_module_fwd(inp["z"], mask, params, w.H)
+        marks[i][1].record()
+        dz, grads = ta.tri_attn_module_bwd(inp["z"], mask, params, saved, inp["dy"], w.H, workspace=ws)
+        marks[i][2].record()
+        if i == 0 or i == steps - 1:
+            outs.append([y, dz] + [grads[n] for n in sorted(grads)])
+    torch.cuda.synchronize()
+    fwd = statistics.median(m[0].elapsed_time(m[1]) for m in marks)
+    bwd = statistics.median(m[1].elapsed_time(m[2]) for m in marks)
+    flops = si.flop_count(w.B, w.N, w.H, w.D, inp["mask"].cpu() if mask is not None else None)
+    nb = module_bytes(w.B, w.N, w.H)
+    same = all(torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32))
+               for x, y in zip(outs[0], outs[-1]))
+    return {"ms_per_step": round(fwd + bwd, 4), "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4),
+            "core_TFLOPs_equivalent": round(flops / ((fwd + bwd) * 1e-3) / 1e12, 2),
+            "module_bytes_outside_core": nb["total"], "steps": steps,
+            "deterministic_first_vs_last_step": same}
+
+
 def run_workload(args, workload: str, ending: bool, with_extras: bool) -> dict:
     """Time fwd+bwd steps of one workload and return its JSON line as a dict."""
     t = time_workload(args, workload, ending, args.steps, args.warmup, keep_outputs=with_extras)
@@ -486,6 +546,9 @@ def run_workload(args, workload: str, ending: bool, with_extras: bool) -> dict:
     line["tri_mul"] = {f"trimul_crop768_{d}": time_trimul(args, "trimul_crop768", d == "incoming",
                                                           args.other_steps, 3)
                        for d in ("outgoing", "incoming")}
+    # the module around the core (LayerNorm, projections, gating) at the crop-768 shape
+    line["module"] = {"module_crop768": time_module(args, "module_crop768", args.other_steps, 3)}
+    torch.cuda.empty_cache()
     log("matrix-core probe")
     probe = mfma_probe_tflops()
     line["mfma_probe"] = {"TFLOPs": round(probe, 1),
@@ -540,6 +603,14 @@ def main():
         for wl, ending in (("crop384", False), ("crop640", False), ("crop768", False), ("crop768", True)):
             line = run_workload(args, wl, ending, False)
             print(json.dumps(line), flush=True)
+        return
+    if args.workload.startswith("module_"):
+        # the whole module (LayerNorm, projections, gating, core) alone: a profiling aid
+        r = time_module(args, args.workload, args.steps, args.warmup)
+        print(json.dumps({"metric": "tri_attn_module_fwd_bwd_ms", "value": r["ms_per_step"], "unit": "ms",
+                          "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "ms_per_step": r["ms_per_step"], "higher_is_better": False, "dtype": "bf16",
+                          "data": "synthetic", "config": {"workload": args.workload}, "detail": r}), flush=True)
         return
     if args.workload.startswith("trimul_"):
         # the triangle-multiplication contraction alone (a profiling aid, not the metric)

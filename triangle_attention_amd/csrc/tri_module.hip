@@ -222,14 +222,32 @@ struct ModArgs {
   float eps;
 };
 
-// Position p (global) -> the bias element of head h it feeds: bias[b, h, j, k] for the
-// starting node (p = (b, j, k)), bias[b, h, k, j] for the ending node.
-__device__ __forceinline__ long long bias_index(const ModArgs &a, long long p, int h) {
-  const long long NN = (long long)a.N * a.N;
-  const long long b = p / NN, jk = p - b * NN;
-  const long long e = a.ending ? (jk % a.N) * a.N + jk / a.N : jk;
-  return (b * a.H + h) * NN + e;
-}
+// The bias elements of one tile of 128 positions p0 + row: every position of a tile
+// lies in one batch b (N^2 is a multiple of 1024), so the tile's pair-bias offsets are
+//   bias[b, h, j, k] = base + h N^2 + (j N + k)    (starting node, position (b, j, k))
+//   bias[b, h, k, j] = base + h N^2 + (k N + j)    (ending node)
+// with base = b H N^2 and 32-bit position offsets within the batch.
+struct BiasTile {
+  long long base, nn;
+  int jk0, n, ending;
+  __device__ BiasTile(const ModArgs &a, long long p0) {
+    nn = (long long)a.N * a.N;
+    const long long b = p0 / nn;
+    base = b * a.H * nn;
+    jk0 = (int)(p0 - b * nn);
+    n = a.N;
+    ending = a.ending;
+  }
+  __device__ long long at(int row, int h) const {
+    const int jk = jk0 + row;
+    int e = jk;
+    if (ending) {
+      const int j = jk / n;
+      e = (jk - j * n) * n + j;
+    }
+    return base + h * nn + e;
+  }
+};
 
 // ------------------------------------------------------------------------------------
 // Forward
@@ -301,6 +319,7 @@ __global__ __launch_bounds__(NT, 2) void mod_proj_kernel(ModArgs a) {
   } else {
     // the bias: column n < H is head n
     const int hh = lane >> 5, ll = lane & 31;
+    const BiasTile bt(a, p0);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -310,7 +329,7 @@ __global__ __launch_bounds__(NT, 2) void mod_proj_kernel(ModArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
-          a.bias[bias_index(a, p0 + m, n)] = (uint16_t)(pack_bf16(acc[i][j][r], 0.f) & 0xffffu);
+          a.bias[bt.at(m, n)] = (uint16_t)(pack_bf16(acc[i][j][r], 0.f) & 0xffffu);
         }
       }
   }
@@ -406,12 +425,20 @@ __global__ __launch_bounds__(NT, 1) void mod_in_bwd_kernel(ModArgs a) {
       load_block(sB, a.w_qkvg + blk * CH, 4 * CH, tid);  // B(t, n = c_in) = Wqkvg[c_in][128 blk + t]: rows
     } else {
       // A(position, t = head) = dbias at that position, rounded to bf16;
-      // B(t = head, n = c_in) = Wb[c_in][head]: rows
-      for (int e = tid; e < TP * CH; e += NT) {
-        const int row = e >> 7, col = e & 127;
-        sA[toff(row, col)] =
-            col < a.H ? (uint16_t)(pack_bf16(a.dbias[bias_index(a, p0 + row, col)], 0.f) & 0xffffu) : (uint16_t)0;
-        sB[toff(row, col)] = col < a.H ? a.w_bias[(long long)row * a.H + col] : (uint16_t)0;
+      // B(t = head, n = c_in) = Wb[c_in][head]: rows; zeros beyond the H heads
+      const u32x4 z4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+        *(u32x4 *)(sA + toff(row, c)) = z4;
+        *(u32x4 *)(sB + toff(row, c)) = z4;
+      }
+      __syncthreads();
+      const BiasTile bt(a, p0);
+      for (int e = tid; e < TP * a.H; e += NT) {
+        const int row = e / a.H, h = e - row * a.H;
+        sA[toff(row, h)] = (uint16_t)(pack_bf16(a.dbias[bt.at(row, h)], 0.f) & 0xffffu);
+        sB[toff(row, h)] = a.w_bias[e];  // row = input channel: Wb[c_in][h] is element c_in H + h
       }
     }
     __syncthreads();
@@ -496,6 +523,14 @@ __global__ __launch_bounds__(NT, 2) void mod_wgrad_kernel(ModArgs a) {
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   f32x16 acc[2][2];
   zero(acc);
+  if (blk == 4) {  // the bias block's B tile: zeros beyond the H head columns
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+      *(u32x4 *)(sB + toff(row, c)) = z4;
+    }
+  }
   for (int tile = t0; tile < t1; ++tile) {
     const long long p0 = (long long)tile * TP;
     if (tile > t0) __syncthreads();
@@ -520,10 +555,11 @@ __global__ __launch_bounds__(NT, 2) void mod_wgrad_kernel(ModArgs a) {
     } else if (blk == 5) {
       load_block(sB, a.dy + p0 * CH, CH, tid);
     } else {
-      for (int e = tid; e < TP * CH; e += NT) {
-        const int row = e >> 7, col = e & 127;
-        sB[toff(row, col)] =
-            col < a.H ? (uint16_t)(pack_bf16(a.dbias[bias_index(a, p0 + row, col)], 0.f) & 0xffffu) : (uint16_t)0;
+      // the H head columns of the tile (the others were zeroed before the loop)
+      const BiasTile bt(a, p0);
+      for (int e = tid; e < TP * a.H; e += NT) {
+        const int row = e / a.H, h = e - row * a.H;
+        sB[toff(row, h)] = (uint16_t)(pack_bf16(a.dbias[bt.at(row, h)], 0.f) & 0xffffu);
       }
     }
     __syncthreads();
