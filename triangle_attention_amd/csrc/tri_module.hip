@@ -15,8 +15,8 @@
 // consecutive positions (rows of the [B N N, 128] matrices) times 128 x 128 weight
 // blocks, one v_mfma_f32_32x32x16_bf16 tile product per workgroup (4 waves, 2 x 2 of
 // 64 x 64), with the prologue or epilogue fused:
-//   mod_proj        LayerNorm in (statistics per position in fp32), zn into LDS; the
-//                   q, k, v, gate (sigmoid) or bias (transposed store) block out
+//   mod_proj        LayerNorm in (statistics per position in fp32), zn into LDS; then
+//                   the q, k, v, gate (sigmoid) and bias (transposed store) blocks out
 //   mod_gate_out    bf16(g * o) in, y out
 //   mod_out_bwd     dy Wo^T; out: dO = dgo * g and the gate's pre-activation gradient
 //                   dgo * o * g (1 - g)
@@ -252,27 +252,34 @@ struct BiasTile {
 // ------------------------------------------------------------------------------------
 // Forward
 // ------------------------------------------------------------------------------------
-// Workgroup = (tile of 128 positions, output block 0..4: q, k, v, gate, bias).  The
-// LayerNorm runs in every block's workgroup (the z tile is read five times, from L2
-// for all but the first: the five blocks of a tile run together on one XCD); block 0
-// also stores zn and the statistics for the backward.
+// Workgroup = one tile of 128 positions: the LayerNorm once (zn into LDS, and with the
+// statistics to HBM for the backward), then the five output blocks in turn (q, k, v,
+// the gate, the bias), each a 128 x 128 weight block times the zn tile.  The next
+// block's weights are loaded into registers while the current block's products run;
+// each block's output leaves through the weight tile's LDS space once the products
+// are done.
 __global__ __launch_bounds__(NT, 2) void mod_proj_kernel(ModArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[TP * CH];
   __shared__ __attribute__((aligned(16))) uint16_t sB[CH * CH];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int blk = t % 5, tile = t / 5;
-  const long long p0 = (long long)tile * TP;
+  const long long p0 = (long long)xcd_remap(blockIdx.x, gridDim.x) * TP;
 
-  // weights of the block: B[t = input channel][n = output column]
-  if (blk < 4) {
-    load_block(sB, a.w_qkvg + blk * CH, 4 * CH, tid);
-  } else {
-    for (int e = tid; e < CH * CH; e += NT) {
-      const int row = e >> 7, col = e & 127;
-      sB[toff(row, col)] = col < a.H ? a.w_bias[(long long)row * a.H + col] : (uint16_t)0;
+  // weights of block blk (< 4) as 16-byte pieces: B[t = input channel][n = output column]
+  u32x4 wr[8];
+  auto fetch_w = [&](int blk) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+      wr[i] = *(const u32x4 *)(a.w_qkvg + (long long)row * 4 * CH + blk * CH + c);
     }
-  }
+  };
+  auto stage_w = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+      *(u32x4 *)(sB + toff(row, c)) = wr[i];
+    }
+  };
   // LayerNorm: thread -> position tid / 2, channels 64 (tid % 2) .. + 63
   {
     const int pr = tid >> 1, c0 = 64 * (tid & 1);
@@ -294,44 +301,74 @@ __global__ __launch_bounds__(NT, 2) void mod_proj_kernel(ModArgs a) {
     v += __shfl_xor(v, 1);
     const float rstd = 1.f / sqrtf(v * (1.f / CH) + a.eps);
 #pragma unroll
-    for (int i = 0; i < 64; ++i) x[i] = fmaf((x[i] - mean) * rstd, a.ln_w[c0 + i], a.ln_b[c0 + i]);
-#pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const u32x4 w = pack8u(x + 8 * i);
+      float y8[8];
+      const f32x4 w0 = *(const f32x4 *)(a.ln_w + c0 + 8 * i), w1 = *(const f32x4 *)(a.ln_w + c0 + 8 * i + 4);
+      const f32x4 b0 = *(const f32x4 *)(a.ln_b + c0 + 8 * i), b1 = *(const f32x4 *)(a.ln_b + c0 + 8 * i + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y8[e] = fmaf((x[8 * i + e] - mean) * rstd, w0[e], b0[e]);
+        y8[4 + e] = fmaf((x[8 * i + 4 + e] - mean) * rstd, w1[e], b1[e]);
+      }
+      const u32x4 w = pack8u(y8);
       *(u32x4 *)(sA + toff(pr, c0 + 8 * i)) = w;
-      if (blk == 0) *(u32x4 *)(a.zn + (p0 + pr) * CH + c0 + 8 * i) = w;
+      *(u32x4 *)(a.zn + (p0 + pr) * CH + c0 + 8 * i) = w;
     }
-    if (blk == 0 && (tid & 1) == 0) *(f32x2 *)(a.stats + 2 * (p0 + pr)) = (f32x2){mean, rstd};
+    if ((tid & 1) == 0) *(f32x2 *)(a.stats + 2 * (p0 + pr)) = (f32x2){mean, rstd};
   }
+  fetch_w(0);
+  stage_w();
   __syncthreads();
 
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  f32x16 acc[2][2];
-  zero(acc);
-  tile_product<ROW, TR>(sA, sB, wm, wn, lane, CH / 16, acc);
-  __syncthreads();  // sA is reused for the output
-
-  if (blk < 3) {
-    uint16_t *dst = (blk == 0 ? a.q : blk == 1 ? a.k : a.v) + p0 * CH;
-    store_tile_bf16(sA, dst, acc, wm, wn, lane, tid, [](float x) { return x; });
-  } else if (blk == 3) {
-    store_tile_bf16(sA, a.g + p0 * CH, acc, wm, wn, lane, tid, [](float x) { return sigmoidf_(x); });
-  } else {
-    // the bias: column n < H is head n
-    const int hh = lane >> 5, ll = lane & 31;
-    const BiasTile bt(a, p0);
+#pragma unroll 1
+  for (int blk = 0; blk < 5; ++blk) {
+    if (blk + 1 < 4) fetch_w(blk + 1);  // in flight during the products
+    f32x16 acc[2][2];
+    zero(acc);
+    tile_product<ROW, TR>(sA, sB, wm, wn, lane, CH / 16, acc);
+    __syncthreads();  // every wave is done with the weight tile
+    if (blk < 3) {
+      uint16_t *dst = (blk == 0 ? a.q : blk == 1 ? a.k : a.v) + p0 * CH;
+      store_tile_bf16(sB, dst, acc, wm, wn, lane, tid, [](float x) { return x; });
+    } else if (blk == 3) {
+      store_tile_bf16(sB, a.g + p0 * CH, acc, wm, wn, lane, tid, [](float x) { return sigmoidf_(x); });
+    } else {
+      // the bias: column n < H is head n
+      const int hh = lane >> 5, ll = lane & 31;
+      const BiasTile bt(a, p0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = wn + 32 * j + ll;
-        if (n >= a.H) continue;
+        for (int j = 0; j < 2; ++j) {
+          const int n = wn + 32 * j + ll;
+          if (n >= a.H) continue;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
-          a.bias[bt.at(m, n)] = (uint16_t)(pack_bf16(acc[i][j][r], 0.f) & 0xffffu);
+          for (int r = 0; r < 16; ++r) {
+            const int m = wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+            a.bias[bt.at(m, n)] = (uint16_t)(pack_bf16(acc[i][j][r], 0.f) & 0xffffu);
+          }
         }
+      break;
+    }
+    __syncthreads();  // the staged output is read back
+    if (blk + 1 < 4) {
+      stage_w();
+    } else {
+      // the bias block's weights: Wb[c_in][h] in the H head columns, zeros elsewhere
+      const u32x4 z4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+        *(u32x4 *)(sB + toff(row, c)) = z4;
       }
+      __syncthreads();
+      for (int e = tid; e < CH * a.H; e += NT) {
+        const int row = e / a.H, h = e - row * a.H;
+        sB[toff(row, h)] = a.w_bias[e];
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -366,10 +403,11 @@ __global__ __launch_bounds__(NT, 2) void mod_gate_out_kernel(ModArgs a) {
 // Backward
 // ------------------------------------------------------------------------------------
 // dgo = dy Wo^T per tile; dO = dgo * g and dgp = dgo * o * g (1 - g), both bf16.
-__global__ __launch_bounds__(NT, 1) void mod_out_bwd_kernel(ModArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[TP * CH];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[CH * CH];
-  __shared__ __attribute__((aligned(16))) float s32[TP * CH];
+__global__ __launch_bounds__(NT, 2) void mod_out_bwd_kernel(ModArgs a) {
+  // the operand tiles, then (after the products) the fp32 tile of dgo in the same space
+  __shared__ __attribute__((aligned(16))) float lds[TP * CH];
+  uint16_t *sA = (uint16_t *)lds, *sB = sA + TP * CH;
+  float *s32 = lds;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long long p0 = (long long)xcd_remap(blockIdx.x, gridDim.x) * TP;
   load_block(sA, a.dy + p0 * CH, CH, tid);
@@ -379,6 +417,7 @@ __global__ __launch_bounds__(NT, 1) void mod_out_bwd_kernel(ModArgs a) {
   f32x16 acc[2][2];
   zero(acc);
   tile_product<ROW, ROW>(sA, sB, wm, wn, lane, CH / 16, acc);
+  __syncthreads();  // the operand tiles are consumed
   stage_f32(s32, acc, wm, wn, lane, [](float x) { return x; });
   __syncthreads();
 #pragma unroll
@@ -417,12 +456,31 @@ __global__ __launch_bounds__(NT, 1) void mod_in_bwd_kernel(ModArgs a) {
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   f32x16 acc[2][2];
   zero(acc);
+  // block blk < 4 as 16-byte pieces: A = dq, dk, dv, dgp at the tile's positions, B(t,
+  // n = c_in) = Wqkvg[c_in][128 blk + t] (rows); the next block's are loaded while the
+  // current block's products run
+  u32x4 ra[8], rb[8];
+  auto fetch = [&](int blk) {
+    const uint16_t *src = (blk == 0 ? a.dq : blk == 1 ? a.dk : blk == 2 ? a.dv : a.dgp) + p0 * CH;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+      ra[i] = *(const u32x4 *)(src + (long long)row * CH + c);
+      rb[i] = *(const u32x4 *)(a.w_qkvg + (long long)row * 4 * CH + blk * CH + c);
+    }
+  };
+  fetch(0);
+#pragma unroll 1
   for (int blk = 0; blk < 5; ++blk) {
     if (blk) __syncthreads();  // the previous block's operands are consumed
     if (blk < 4) {
-      const uint16_t *src = blk == 0 ? a.dq : blk == 1 ? a.dk : blk == 2 ? a.dv : a.dgp;
-      load_block(sA, src + p0 * CH, CH, tid);
-      load_block(sB, a.w_qkvg + blk * CH, 4 * CH, tid);  // B(t, n = c_in) = Wqkvg[c_in][128 blk + t]: rows
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+        *(u32x4 *)(sA + toff(row, c)) = ra[i];
+        *(u32x4 *)(sB + toff(row, c)) = rb[i];
+      }
+      if (blk + 1 < 4) fetch(blk + 1);
     } else {
       // A(position, t = head) = dbias at that position, rounded to bf16;
       // B(t = head, n = c_in) = Wb[c_in][head]: rows; zeros beyond the H heads
@@ -489,6 +547,7 @@ __global__ __launch_bounds__(NT, 1) void mod_in_bwd_kernel(ModArgs a) {
   {
     const int c = tid & 127, hp = tid >> 7;
     float sw = 0.f, sb = 0.f;
+#pragma unroll 16
     for (int r = 64 * hp; r < 64 * hp + 64; ++r) {
       sw += sx[foff(r, c)];
       sb += s32[foff(r, c)];
@@ -521,6 +580,8 @@ __global__ __launch_bounds__(NT, 2) void mod_wgrad_kernel(ModArgs a) {
   const int blk = t % 6, slice = t / 6;
   const int t0 = (int)((long long)slice * a.tiles / a.slices), t1 = (int)((long long)(slice + 1) * a.tiles / a.slices);
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const uint16_t *asrc = blk < 5 ? a.zn : a.g;
+  const uint16_t *bsrc = blk == 0 ? a.dq : blk == 1 ? a.dk : blk == 2 ? a.dv : blk == 3 ? a.dgp : a.dy;
   f32x16 acc[2][2];
   zero(acc);
   if (blk == 4) {  // the bias block's B tile: zeros beyond the H head columns
@@ -531,30 +592,41 @@ __global__ __launch_bounds__(NT, 2) void mod_wgrad_kernel(ModArgs a) {
       *(u32x4 *)(sB + toff(row, c)) = z4;
     }
   }
+  // one tile's operands as 16-byte pieces (A: zn, or g and o for block 5; B: the
+  // gradient tile, except for the bias block), loaded a tile ahead
+  u32x4 ra[8], ro[8], rb[8];
+  auto fetch = [&](int tile) {
+    const long long p0 = (long long)tile * TP;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+      const long long off = (p0 + row) * CH + c;
+      ra[i] = *(const u32x4 *)(asrc + off);
+      if (blk == 5) ro[i] = *(const u32x4 *)(a.o + off);
+      if (blk != 4) rb[i] = *(const u32x4 *)(bsrc + off);
+    }
+  };
+  fetch(t0);
+#pragma unroll 1
   for (int tile = t0; tile < t1; ++tile) {
     const long long p0 = (long long)tile * TP;
-    if (tile > t0) __syncthreads();
-    if (blk < 5) {
-      load_block(sA, a.zn + p0 * CH, CH, tid);
-    } else {
+    if (tile > t0) __syncthreads();  // the previous tile's operands are consumed
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
-        const long long off = (p0 + row) * CH + c;
+    for (int i = 0; i < 8; ++i) {
+      const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+      u32x4 w = ra[i];
+      if (blk == 5) {
         float gv[8], ov[8];
-        unpack8(*(const u32x4 *)(a.g + off), gv);
-        unpack8(*(const u32x4 *)(a.o + off), ov);
+        unpack8(ra[i], gv);
+        unpack8(ro[i], ov);
 #pragma unroll
         for (int e = 0; e < 8; ++e) gv[e] *= ov[e];
-        *(u32x4 *)(sA + toff(row, c)) = pack8u(gv);
+        w = pack8u(gv);
       }
+      *(u32x4 *)(sA + toff(row, c)) = w;
+      if (blk != 4) *(u32x4 *)(sB + toff(row, c)) = rb[i];
     }
-    if (blk < 4) {
-      const uint16_t *src = blk == 0 ? a.dq : blk == 1 ? a.dk : blk == 2 ? a.dv : a.dgp;
-      load_block(sB, src + p0 * CH, CH, tid);
-    } else if (blk == 5) {
-      load_block(sB, a.dy + p0 * CH, CH, tid);
-    } else {
+    if (blk == 4) {
       // the H head columns of the tile (the others were zeroed before the loop)
       const BiasTile bt(a, p0);
       for (int e = tid; e < TP * a.H; e += NT) {
@@ -562,6 +634,7 @@ __global__ __launch_bounds__(NT, 2) void mod_wgrad_kernel(ModArgs a) {
         sB[toff(row, h)] = (uint16_t)(pack_bf16(a.dbias[bt.at(row, h)], 0.f) & 0xffffu);
       }
     }
+    if (tile + 1 < t1) fetch(tile + 1);  // in flight during the products
     __syncthreads();
     tile_product<TR, TR>(sA, sB, wm, wn, lane, TP / 16, acc);
   }
@@ -719,7 +792,7 @@ tri_attn_status tri_attn_module_fwd(const tri_attn_module_problem *problem, cons
   a.bias = (uint16_t *)saved->bias;
   a.o = (uint16_t *)saved->o;
   a.y = (uint16_t *)y;
-  hipLaunchKernelGGL(mod_proj_kernel, dim3((unsigned)(a.tiles * 5)), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL(mod_proj_kernel, dim3((unsigned)a.tiles), dim3(NT), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
   st = tri_attn_fwd(&cp, saved->q, saved->k, saved->v, saved->bias, mask, saved->o, saved->o_residual, saved->lse,
                     stream);
