@@ -20,7 +20,10 @@
 // fp32 accumulation over the whole contraction in registers (one fixed order: results
 // are bitwise reproducible), bf16 round-to-nearest-even output.  K steps of 32: the
 // next step's operand tiles are loaded into registers while the current one's are
-// multiplied out of LDS (two LDS buffers, one barrier per step).  Workgroups of one
+// multiplied out of LDS (two LDS buffers, one barrier per step); the output tile leaves
+// through LDS as 16-byte row pieces.  Loading two steps ahead (a second register set)
+// measured 35 % slower: its registers cut the workgroups resident per CU from four to
+// three, and that concurrency hides more of the load latency than the deeper prefetch.  Workgroups of one
 // (batch, channel) follow each other on one XCD (the channel's operands, 2 x 1.2 MB at
 // N = 768, stay in that XCD's L2).
 //
@@ -151,8 +154,9 @@ struct TileIO {
 //   RT = false: R stored [n][t];  RT = true: R stored [t][n]
 template <bool LT, bool RT>
 __global__ __launch_bounds__(WAVES * 64, 2) void tri_mul_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sL[2][TM * TK];
-  __shared__ __attribute__((aligned(16))) uint16_t sR[2][TN * TK];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (TM + TN) * TK];
+  uint16_t (*sL)[TM * TK] = (uint16_t (*)[TM * TK])smem;
+  uint16_t (*sR)[TN * TK] = (uint16_t (*)[TN * TK])(smem + 2 * TM * TK);
   const int N = a.N;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, ll = lane & 31;
@@ -205,22 +209,27 @@ __global__ __launch_bounds__(WAVES * 64, 2) void tri_mul_gemm(GemmArgs a) {
     __syncthreads();
   }
 
-  // bf16 output: lane holds rows 8 (r / 4) + 4 hh + r % 4 of column ll of each product
-  uint16_t *out = a.out + mat;
+  // bf16 output through LDS: lane holds rows 8 (r / 4) + 4 hh + r % 4 of column ll of
+  // each product; the staged [128][128] tile leaves as 16-byte row pieces
+  uint16_t *so = smem;  // [TM][TN], 16-byte chunks permuted per row like the step tiles
+  auto ooff = [](int row, int col) { return row * TN + (((col >> 3) ^ (row & 15)) << 3) + (col & 7); };
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + wn + 32 * j + ll;
-      if (n >= N) continue;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const int m = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const unsigned pk = pack_bf16(acc[i][j][r], acc[i][j][r + 1]);
-        if (m < N) out[(long long)m * N + n] = (uint16_t)(pk & 0xffffu);
-        if (m + 1 < N) out[(long long)(m + 1) * N + n] = (uint16_t)(pk >> 16);
+      for (int r = 0; r < 16; ++r) {
+        const int m = wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3), n = wn + 32 * j + ll;
+        so[ooff(m, n)] = (uint16_t)(pack_bf16(acc[i][j][r], 0.f) & 0xffffu);
       }
-    }
+  __syncthreads();
+  uint16_t *out = a.out + mat;
+#pragma unroll
+  for (int i = 0; i < (TM * TN / 8) / (WAVES * 64); ++i) {
+    const int pc = tid + WAVES * 64 * i, row = pc / (TN / 8), c = (pc % (TN / 8)) * 8;
+    const int m = m0 + row, n = n0 + c;
+    if (m < N && n < N) *(u32x4 *)(out + (long long)m * N + n) = *(const u32x4 *)(so + ooff(row, c));
+  }
 }
 
 // ------------------------------------------------------------------------------------
