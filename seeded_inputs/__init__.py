@@ -23,7 +23,8 @@ import torch
 # tensor tags: each tensor of a workload draws from its own generator,
 # seeded with seed * 16 + tag
 _TAG = {"q": 0, "k": 1, "v": 2, "do": 3, "bias": 4, "length": 5, "tm_a": 6, "tm_b": 7, "tm_g": 8,
-        "md_z": 9, "md_ln": 10, "md_wqkvg": 11, "md_wb": 12, "md_wo": 13, "md_dy": 14}
+        "md_z": 9, "md_ln": 10, "md_wqkvg": 11, "md_wb": 12, "md_wo": 13, "md_dy": 14,
+        "tb_z": 15, "tb_ln": 16, "tb_win": 17, "tb_wout": 18, "tb_dy": 19, "tb_mask": 20}
 
 
 @dataclass(frozen=True)
@@ -228,3 +229,55 @@ def make_module(B: int, N: int, H: int, D: int, seed: int, mask: str = "none") -
 def make_module_workload(name: str) -> dict:
     w = MODULE_WORKLOADS[name]
     return make_module(w.B, w.N, w.H, w.D, w.seed, w.mask)
+
+
+# Triangle multiplicative update block: the pair tensor z [B, N, N, C], a pair mask
+# [B, N, N] (uint8, 1 = kept), the two LayerNorms' scales and offsets (fp32 [C]), the
+# input projections w_in [C, 5 C] (a gate, a, b gate, b, output gate) and the output
+# projection w_out [C, C] (bf16, N(0, 1/C) entries) and the upstream gradient dy.
+@dataclass(frozen=True)
+class TriMulModuleWorkload:
+    name: str
+    index: int
+    B: int
+    N: int
+    C: int
+    mask: str
+    description: str
+
+    @property
+    def seed(self) -> int:
+        return 4000 + self.index
+
+
+TRIMUL_MODULE_WORKLOADS = {
+    w.name: w
+    for w in [
+        TriMulModuleWorkload("trimul_block_tiny64", 1, 1, 64, 128, "pad32",
+                             "B=1 N=64 C=128, the last 32 positions of every row masked"),
+        TriMulModuleWorkload("trimul_block_crop768", 2, 1, 768, 128, "none", "B=1 N=768 C=128"),
+    ]
+}
+
+
+def make_trimul_module(B: int, N: int, C: int, seed: int, mask: str = "none") -> dict:
+    """Seeded inputs and parameters of one triangle-multiplication block (CPU tensors)."""
+    ln = torch.randn((4, C), generator=_gen(seed, "tb_ln"), dtype=torch.float32) * 0.1
+    if mask == "random":
+        m = (torch.rand((B, N, N), generator=_gen(seed, "tb_mask")) < 0.8).to(torch.uint8)
+    else:
+        m = make_mask(B, N, mask, seed)
+    return {
+        "z": _randn_bf16((B, N, N, C), seed, "tb_z"),
+        "mask": m,
+        "ln_in_w": 1.0 + ln[0], "ln_in_b": ln[1].clone(),
+        "ln_out_w": 1.0 + ln[2], "ln_out_b": ln[3].clone(),
+        "w_in": _randn_bf16((C, 5 * C), seed, "tb_win", C ** -0.5),
+        "w_out": _randn_bf16((C, C), seed, "tb_wout", C ** -0.5),
+        "dy": _randn_bf16((B, N, N, C), seed, "tb_dy"),
+    }
+
+
+def make_trimul_module_workload(name: str) -> dict:
+    w = TRIMUL_MODULE_WORKLOADS[name]
+    return make_trimul_module(w.B, w.N, w.C, w.seed, w.mask)
