@@ -38,7 +38,9 @@ The JSON line also carries
                  forward and backward times;
   tri_mul      : the triangle multiplicative update's contraction at the crop-768
                  shape with 128 channels (tri_mul_fwd + tri_mul_bwd, outgoing and
-                 incoming edges): median times, TFLOP/s and fraction of the peak;
+                 incoming edges): median times, TFLOP/s and fraction of the peak; and
+                 the whole block around it (LayerNorms, gated projections, output
+                 gate) at the same shape;
   accuracy     : the crop768 outputs of the last timed step against the FP64 oracle
                  run on the whole problem (forward max-abs and rel-RMSE, lse max-abs,
                  and the rel-RMSE of each gradient with the residual-compensated
@@ -471,6 +473,46 @@ def time_module(args, workload: str, steps: int, warmup: int) -> dict:
             "deterministic_first_vs_last_step": same}
 
 
+def time_trimul_module(args, workload: str, incoming: bool, steps: int, warmup: int) -> dict:
+    """Time `steps` forward + backward calls of the triangle multiplicative update block
+    (LayerNorms, gated projections, the contraction) after `warmup`."""
+    import seeded_inputs as si
+    import triangle_attention_amd as ta
+
+    w = si.TRIMUL_MODULE_WORKLOADS[workload]
+    dev = torch.device("cuda:0")
+    log(f"workload {w.name} ({'incoming' if incoming else 'outgoing'} edges): {w.description}")
+    inp = {n: t.to(dev) for n, t in si.make_trimul_module_workload(w.name).items()}
+    mask = inp["mask"] if w.mask != "none" else None
+    params = {n: inp[n] for n in ("ln_in_w", "ln_in_b", "w_in", "ln_out_w", "ln_out_b", "w_out")}
+    ws = torch.empty(ta.trimul_module_bwd_workspace_bytes(w.B, w.N, w.C, incoming=incoming), dtype=torch.uint8,
+                     device=dev)
+    for _ in range(warmup):
+        y, saved = ta.tri_mul_module_fwd(inp["z"], mask, params, incoming=incoming)
+        ta.tri_mul_module_bwd(inp["z"], mask, params, saved, inp["dy"], incoming=incoming, workspace=ws)
+    torch.cuda.synchronize()
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    outs = []
+    for i in range(steps):
+        marks[i][0].record()
+        y, saved = ta.tri_mul_module_fwd(inp["z"], mask, params, incoming=incoming)
+        marks[i][1].record()
+        dz, grads = ta.tri_mul_module_bwd(inp["z"], mask, params, saved, inp["dy"], incoming=incoming, workspace=ws)
+        marks[i][2].record()
+        if i == 0 or i == steps - 1:
+            outs.append([y, dz] + [grads[n] for n in sorted(grads)])
+    torch.cuda.synchronize()
+    fwd = statistics.median(m[0].elapsed_time(m[1]) for m in marks)
+    bwd = statistics.median(m[1].elapsed_time(m[2]) for m in marks)
+    same = all(torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32))
+               for x, y in zip(outs[0], outs[-1]))
+    flops = si.trimul_flop_count(w.B, w.N, w.C)
+    return {"ms_per_step": round(fwd + bwd, 4), "fwd_ms": round(fwd, 4), "bwd_ms": round(bwd, 4),
+            "contraction_TFLOPs_equivalent": round(flops / ((fwd + bwd) * 1e-3) / 1e12, 2), "steps": steps,
+            "deterministic_first_vs_last_step": same}
+
+
 def run_workload(args, workload: str, ending: bool, with_extras: bool) -> dict:
     """Time fwd+bwd steps of one workload and return its JSON line as a dict."""
     t = time_workload(args, workload, ending, args.steps, args.warmup, keep_outputs=with_extras)
@@ -549,6 +591,9 @@ def run_workload(args, workload: str, ending: bool, with_extras: bool) -> dict:
     # the module around the core (LayerNorm, projections, gating) at the crop-768 shape
     line["module"] = {"module_crop768": time_module(args, "module_crop768", args.other_steps, 3)}
     torch.cuda.empty_cache()
+    line["tri_mul"]["trimul_block_crop768_outgoing"] = time_trimul_module(args, "trimul_block_crop768", False,
+                                                                          args.other_steps, 3)
+    torch.cuda.empty_cache()
     log("matrix-core probe")
     probe = mfma_probe_tflops()
     line["mfma_probe"] = {"TFLOPs": round(probe, 1),
@@ -611,6 +656,16 @@ def main():
                           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                           "ms_per_step": r["ms_per_step"], "higher_is_better": False, "dtype": "bf16",
                           "data": "synthetic", "config": {"workload": args.workload}, "detail": r}), flush=True)
+        return
+    if args.workload.startswith("trimul_block_"):
+        # the whole triangle multiplicative update block alone: a profiling aid
+        r = time_trimul_module(args, args.workload, args.ending, args.steps, args.warmup)
+        print(json.dumps({"metric": "tri_mul_module_fwd_bwd_ms", "value": r["ms_per_step"], "unit": "ms",
+                          "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                          "ms_per_step": r["ms_per_step"], "higher_is_better": False, "dtype": "bf16",
+                          "data": "synthetic",
+                          "config": {"workload": args.workload, "edges": "incoming" if args.ending else "outgoing"},
+                          "detail": r}), flush=True)
         return
     if args.workload.startswith("trimul_"):
         # the triangle-multiplication contraction alone (a profiling aid, not the metric)

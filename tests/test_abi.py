@@ -15,7 +15,8 @@ import triangle_attention_amd as ta
 
 ROOT = Path(__file__).resolve().parents[1]
 HEADER = ROOT / "include" / "tri_attn.h"
-HEADERS = (HEADER, ROOT / "include" / "tri_mul.h", ROOT / "include" / "tri_module.h")
+HEADERS = (HEADER, ROOT / "include" / "tri_mul.h", ROOT / "include" / "tri_module.h",
+           ROOT / "include" / "tri_mul_module.h")
 
 OK, INVALID, UNSUPPORTED, WORKSPACE, LAUNCH, ABI = 0, 1, 2, 3, 4, 5
 ADDR = 1 << 40  # fake, 256-byte-aligned device address

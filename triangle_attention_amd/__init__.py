@@ -40,8 +40,10 @@ EXPORTED_SYMBOLS = ("tri_attn_abi_version", "tri_attn_status_string", "tri_attn_
                     "tri_attn_bwd_workspace_bytes", "tri_attn_bwd", "tri_attn_bwd_timed",
                     "tri_attn_bwd_noalloc", "tri_mul_abi_version", "tri_mul_fwd", "tri_mul_bwd",
                     "tri_attn_module_abi_version", "tri_attn_module_fwd", "tri_attn_module_bwd_workspace_bytes",
-                    "tri_attn_module_bwd")
+                    "tri_attn_module_bwd", "tri_mul_module_abi_version", "tri_mul_module_fwd",
+                    "tri_mul_module_bwd_workspace_bytes", "tri_mul_module_bwd")
 TRI_MUL_ABI_VERSION = 1
+TRI_MUL_MODULE_ABI_VERSION = 1
 MODULE_ABI_VERSION = 1
 MODULE_CHANNELS = 128
 TRI_MUL_FLAG_INCOMING = 1
@@ -83,6 +85,26 @@ class ModuleSaved(ctypes.Structure):
 class ModuleGrads(ctypes.Structure):
     """Mirror of ``tri_attn_module_param_grads`` (device pointers)."""
     _fields_ = [(n, ctypes.c_void_p) for n in ("ln_w", "ln_b", "w_qkvg", "w_bias", "w_out")]
+
+
+class TriMulModuleProblem(ctypes.Structure):
+    """Mirror of ``tri_mul_module_problem``."""
+    _fields_ = [("abi_version", ctypes.c_int32), ("flags", ctypes.c_int32),
+                ("B", ctypes.c_int64), ("N", ctypes.c_int64), ("C", ctypes.c_int64), ("ln_eps", ctypes.c_float)]
+
+
+TRI_MUL_MODULE_PARAMS = ("ln_in_w", "ln_in_b", "w_in", "ln_out_w", "ln_out_b", "w_out")
+TRI_MUL_MODULE_SAVED = ("zn", "ln_in_stats", "a", "b", "g", "x", "xn", "ln_out_stats")
+
+
+class TriMulModuleParams(ctypes.Structure):
+    """Mirror of ``tri_mul_module_params`` and ``tri_mul_module_param_grads`` (device pointers)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in TRI_MUL_MODULE_PARAMS]
+
+
+class TriMulModuleSaved(ctypes.Structure):
+    """Mirror of ``tri_mul_module_saved`` (device pointers)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in TRI_MUL_MODULE_SAVED]
 
 
 class TriAttnError(RuntimeError):
@@ -137,8 +159,21 @@ def load_library(path: Path | str | None = None) -> ctypes.CDLL:
     lib.tri_attn_module_bwd.argtypes = [mp, vp, vp, ctypes.POINTER(ModuleParams), ctypes.POINTER(ModuleSaved), vp, vp,
                                         ctypes.POINTER(ModuleGrads), vp, ctypes.c_size_t, vp]
     lib.tri_attn_module_bwd.restype = i32
+    tp2 = ctypes.POINTER(TriMulModuleProblem)
+    lib.tri_mul_module_abi_version.argtypes = []
+    lib.tri_mul_module_abi_version.restype = i32
+    lib.tri_mul_module_fwd.argtypes = [tp2, vp, vp, ctypes.POINTER(TriMulModuleParams), vp,
+                                       ctypes.POINTER(TriMulModuleSaved), vp]
+    lib.tri_mul_module_fwd.restype = i32
+    lib.tri_mul_module_bwd_workspace_bytes.argtypes = [tp2]
+    lib.tri_mul_module_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.tri_mul_module_bwd.argtypes = [tp2, vp, vp, ctypes.POINTER(TriMulModuleParams),
+                                       ctypes.POINTER(TriMulModuleSaved), vp, vp,
+                                       ctypes.POINTER(TriMulModuleParams), vp, ctypes.c_size_t, vp]
+    lib.tri_mul_module_bwd.restype = i32
     if (lib.tri_attn_abi_version() != ABI_VERSION or lib.tri_mul_abi_version() != TRI_MUL_ABI_VERSION
-            or lib.tri_attn_module_abi_version() != MODULE_ABI_VERSION):
+            or lib.tri_attn_module_abi_version() != MODULE_ABI_VERSION
+            or lib.tri_mul_module_abi_version() != TRI_MUL_MODULE_ABI_VERSION):
         raise RuntimeError("libtri_attn.so ABI version mismatch")
     if path is None:
         _lib = lib
@@ -438,6 +473,74 @@ def tri_attn_module_bwd(z, mask, params, saved, dy, H, *, ending=False, eps=0.0,
     return dz, grads
 
 
+# ---- the triangle multiplicative update block (include/tri_mul_module.h) ----
+
+def make_trimul_module_problem(B, N, C, *, incoming=False, eps=0.0,
+                               abi_version=TRI_MUL_MODULE_ABI_VERSION) -> TriMulModuleProblem:
+    return TriMulModuleProblem(abi_version, TRI_MUL_FLAG_INCOMING if incoming else 0, B, N, C, float(eps))
+
+
+def _trimul_module_params(params, C, dev):
+    shapes = {"ln_in_w": ((C,), torch.float32), "ln_in_b": ((C,), torch.float32),
+              "w_in": ((C, 5 * C), torch.bfloat16), "ln_out_w": ((C,), torch.float32),
+              "ln_out_b": ((C,), torch.float32), "w_out": ((C, C), torch.bfloat16)}
+    for n, (shape, dt) in shapes.items():
+        _check_tensor(n, params[n], shape, (dt,), dev)
+    return TriMulModuleParams(*(params[n].data_ptr() for n in TRI_MUL_MODULE_PARAMS))
+
+
+def tri_mul_module_fwd(z, mask, params, *, incoming=False, eps=0.0):
+    """Forward of the triangle multiplicative update block: returns (y, saved)."""
+    B, N, C, _ = _module_dims(z, 1)
+    dev = z.device
+    if mask is not None:
+        _check_tensor("mask", mask, (B, N, N), (torch.uint8,), dev)
+    p = _trimul_module_params(params, C, dev)
+    cm = dict(dtype=torch.bfloat16, device=dev)
+    saved = {"zn": torch.empty_like(z), "ln_in_stats": torch.empty((B, N, N, 2), dtype=torch.float32, device=dev),
+             "a": torch.empty((B, C, N, N), **cm), "b": torch.empty((B, C, N, N), **cm), "g": torch.empty_like(z),
+             "x": torch.empty((B, C, N, N), **cm), "xn": torch.empty_like(z),
+             "ln_out_stats": torch.empty((B, N, N, 2), dtype=torch.float32, device=dev)}
+    y = torch.empty_like(z)
+    sv = TriMulModuleSaved(*(saved[n].data_ptr() for n in TRI_MUL_MODULE_SAVED))
+    lib = load_library()
+    st = lib.tri_mul_module_fwd(ctypes.byref(make_trimul_module_problem(B, N, C, incoming=incoming, eps=eps)),
+                                _ptr(z), _ptr(mask), ctypes.byref(p), _ptr(y), ctypes.byref(sv), _stream(dev))
+    if st != 0:
+        raise TriAttnError(st, "tri_mul_module_fwd")
+    return y, saved
+
+
+def trimul_module_bwd_workspace_bytes(B, N, C, *, incoming=False) -> int:
+    return load_library().tri_mul_module_bwd_workspace_bytes(
+        ctypes.byref(make_trimul_module_problem(B, N, C, incoming=incoming)))
+
+
+def tri_mul_module_bwd(z, mask, params, saved, dy, *, incoming=False, eps=0.0, workspace=None):
+    """Backward of the block: returns (dz, grads), grads the fp32 parameter gradients."""
+    B, N, C, _ = _module_dims(z, 1)
+    dev = z.device
+    _check_tensor("dy", dy, z.shape, (torch.bfloat16,), dev)
+    if mask is not None:
+        _check_tensor("mask", mask, (B, N, N), (torch.uint8,), dev)
+    p = _trimul_module_params(params, C, dev)
+    sv = TriMulModuleSaved(*(saved[n].data_ptr() for n in TRI_MUL_MODULE_SAVED))
+    grads = {n: torch.empty(params[n].shape, dtype=torch.float32, device=dev) for n in TRI_MUL_MODULE_PARAMS}
+    gr = TriMulModuleParams(*(grads[n].data_ptr() for n in TRI_MUL_MODULE_PARAMS))
+    dz = torch.empty_like(z)
+    prob = make_trimul_module_problem(B, N, C, incoming=incoming, eps=eps)
+    lib = load_library()
+    need = lib.tri_mul_module_bwd_workspace_bytes(ctypes.byref(prob))
+    if need == 0:
+        raise TriAttnError(2, "tri_mul_module_bwd")
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if workspace is None else workspace
+    st = lib.tri_mul_module_bwd(ctypes.byref(prob), _ptr(z), _ptr(mask), ctypes.byref(p), ctypes.byref(sv),
+                                _ptr(dy), _ptr(dz), ctypes.byref(gr), _ptr(ws), ws.numel(), _stream(dev))
+    if st != 0:
+        raise TriAttnError(st, "tri_mul_module_bwd")
+    return dz, grads
+
+
 class TriAttnFunction(torch.autograd.Function):
     """Autograd wrapper: the forward saves o, its residual and lse; the backward
     recomputes every probability tile once inside the HIP kernels."""
@@ -467,6 +570,8 @@ __all__ = ["tri_attn", "tri_attn_fwd", "tri_attn_bwd", "tri_attn_bwd_noalloc", "
            "tri_mul_fwd", "tri_mul_bwd", "make_trimul_problem", "TriMulProblem",
            "tri_attn_module_fwd", "tri_attn_module_bwd", "module_bwd_workspace_bytes", "make_module_problem",
            "ModuleProblem", "ModuleParams", "ModuleSaved", "ModuleGrads",
+           "tri_mul_module_fwd", "tri_mul_module_bwd", "trimul_module_bwd_workspace_bytes",
+           "make_trimul_module_problem", "TriMulModuleProblem",
            "load_library", "NOALLOC_SCRATCH_BYTES",
            "make_problem", "Problem", "TriAttnError", "TriAttnFunction", "LIB_PATH",
            "EXPORTED_SYMBOLS"]

@@ -40,6 +40,8 @@
 
 #include "tri_attn.h"
 #include "tri_module.h"
+#include "tri_mul.h"
+#include "tri_mul_module.h"
 
 namespace {
 
@@ -687,6 +689,515 @@ __global__ __launch_bounds__(64) void mod_reduce_ln_kernel(ReduceArgs a) {
 }
 
 // ------------------------------------------------------------------------------------
+// Triangle multiplicative update block around the contraction (tri_mul_module.h)
+// ------------------------------------------------------------------------------------
+// zn = LayerNorm_in(z); a = sigmoid(zn Wag) (zn Wap) m; b = sigmoid(zn Wbg) (zn Wbp) m;
+// g = sigmoid(zn Wg); x = the contraction of a and b (tri_mul_fwd); y = g (LayerNorm_out(x)
+// Wo).  a, b, x and their gradients are channel-major [B, C, N, N] (the contraction's
+// layout): the 128 positions of a tile are 128 contiguous elements of every channel, so
+// such a tile moves as 16-byte rows of a [channel][position] LDS tile, which is also a
+// transposed-layout MFMA operand.  A weight block in LDS, [input channel][output
+// column], is read transposed by the forward products and as rows by the backward ones.
+struct TmbArgs {
+  const uint16_t *z;
+  const uint8_t *mask;
+  const float *ln_in_w, *ln_in_b, *ln_out_w, *ln_out_b;
+  const uint16_t *w_in, *w_out;   // [C][5 C], [C][C]
+  uint16_t *zn;
+  float *stats_in, *stats_out;    // [P][2]
+  uint16_t *a, *b;                // channel-major
+  uint16_t *g;                    // [P][C]
+  const uint16_t *x;              // channel-major
+  uint16_t *xn, *y;               // [P][C]
+  const uint16_t *dy;
+  uint16_t *dyp, *dgp;            // [P][C]: dL/d(xn Wo), the output gate's pre-activation gradient
+  uint16_t *dx;                   // channel-major
+  const uint16_t *da, *db;        // channel-major
+  uint16_t *dag, *dap, *dbg, *dbp;  // channel-major: gradients of the four a / b projections
+  uint16_t *dz;
+  float *ln_in_part, *ln_out_part, *w_part;
+  int B, N;
+  long long P, NN;
+  int tiles, slices;
+  float eps;
+};
+
+// the tile's offset in a channel-major tensor: element (channel c, tile position r) is at
+// cm + c N^2 + r
+__device__ __forceinline__ long long cm_tile(const TmbArgs &a, long long p0) {
+  const long long b = p0 / a.NN;
+  return b * CH * a.NN + (p0 - b * a.NN);
+}
+// the [128 channel][128 position] block of a channel-major tensor into an LDS tile, and back
+__device__ __forceinline__ void load_cm(uint16_t *tile, const uint16_t *src, long long nn, int tid) {
+  load_block(tile, src, nn, tid);
+}
+__device__ __forceinline__ void store_rows(const uint16_t *tile, uint16_t *dst, long long ld, int tid) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int p = tid + NT * i, row = p >> 4, c = (p & 15) * 8;
+    *(u32x4 *)(dst + (long long)row * ld + c) = *(const u32x4 *)(tile + toff(row, c));
+  }
+}
+__device__ __forceinline__ uint16_t bf16_of(float x) { return (uint16_t)(pack_bf16(x, 0.f) & 0xffffu); }
+
+// LayerNorm of the tile's positions from a position-major bf16 source: thread -> position
+// tid / 2, channels 64 (tid % 2) .. + 63; the normalised row goes to tile (row layout)
+// and to `out` (bf16), the statistics to `stats`
+__device__ __forceinline__ void layer_norm_tile(const uint16_t *src, const float *w, const float *bb, float eps,
+                                                uint16_t *tile, uint16_t *out, float *stats, int tid) {
+  const int pr = tid >> 1, c0 = 64 * (tid & 1);
+  float x[64];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) unpack8(*(const u32x4 *)(src + pr * CH + c0 + 8 * i), x + 8 * i);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) s += x[i];
+  s += __shfl_xor(s, 1);
+  const float mean = s * (1.f / CH);
+  float v = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    const float d = x[i] - mean;
+    v = fmaf(d, d, v);
+  }
+  v += __shfl_xor(v, 1);
+  const float rstd = 1.f / sqrtf(v * (1.f / CH) + eps);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float y8[8];
+    const f32x4 w0 = *(const f32x4 *)(w + c0 + 8 * i), w1 = *(const f32x4 *)(w + c0 + 8 * i + 4);
+    const f32x4 b0 = *(const f32x4 *)(bb + c0 + 8 * i), b1 = *(const f32x4 *)(bb + c0 + 8 * i + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y8[e] = fmaf((x[8 * i + e] - mean) * rstd, w0[e], b0[e]);
+      y8[4 + e] = fmaf((x[8 * i + 4 + e] - mean) * rstd, w1[e], b1[e]);
+    }
+    const u32x4 q = pack8u(y8);
+    *(u32x4 *)(tile + toff(pr, c0 + 8 * i)) = q;
+    *(u32x4 *)(out + pr * CH + c0 + 8 * i) = q;
+  }
+  if ((tid & 1) == 0) *(f32x2 *)(stats + 2 * pr) = (f32x2){mean, rstd};
+}
+
+// Forward, part 1: LayerNorm_in, then the blocks ag, ap (-> a), bg, bp (-> b) and g.
+// One workgroup per CU: the gate and projection accumulators of a pair are live at once.
+__global__ __launch_bounds__(NT, 1) void tmb_proj_kernel(TmbArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[TP * CH];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[CH * CH];
+  __shared__ float s_m[TP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long long p0 = (long long)xcd_remap(blockIdx.x, gridDim.x) * TP;
+  const long long cm = cm_tile(a, p0);
+  u32x4 wr[8];
+  auto fetch_w = [&](int blk) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+      wr[i] = *(const u32x4 *)(a.w_in + (long long)row * 5 * CH + blk * CH + c);
+    }
+  };
+  auto stage_w = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+      *(u32x4 *)(sB + toff(row, c)) = wr[i];
+    }
+  };
+  if (tid < TP) s_m[tid] = a.mask ? (a.mask[p0 + tid] ? 1.f : 0.f) : 1.f;
+  layer_norm_tile(a.z + p0 * CH, a.ln_in_w, a.ln_in_b, a.eps, sA, a.zn + p0 * CH, a.stats_in + 2 * p0, tid);
+  fetch_w(0);
+  stage_w();
+  fetch_w(1);
+  __syncthreads();
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64, hh = lane >> 5, ll = lane & 31;
+  f32x16 acc0[2][2], acc1[2][2];
+#pragma unroll 1
+  for (int pr = 0; pr < 2; ++pr) {
+    zero(acc0);
+    tile_product<ROW, TR>(sA, sB, wm, wn, lane, CH / 16, acc0);  // gate pre-activation
+    __syncthreads();
+    stage_w();
+    fetch_w(2 * pr + 2);
+    __syncthreads();
+    zero(acc1);
+    tile_product<ROW, TR>(sA, sB, wm, wn, lane, CH / 16, acc1);  // projection
+    __syncthreads();
+    // sigmoid(gate) * projection * mask, transposed into [channel][position]
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3), n = wn + 32 * j + ll;
+          sB[toff(n, m)] = bf16_of(sigmoidf_(acc0[i][j][r]) * acc1[i][j][r] * s_m[m]);
+        }
+    __syncthreads();
+    store_rows(sB, (pr ? a.b : a.a) + cm, a.NN, tid);
+    __syncthreads();
+    stage_w();
+    if (2 * pr + 3 < 5) fetch_w(2 * pr + 3);
+    __syncthreads();
+  }
+  zero(acc0);
+  tile_product<ROW, TR>(sA, sB, wm, wn, lane, CH / 16, acc0);
+  __syncthreads();
+  store_tile_bf16(sB, a.g + p0 * CH, acc0, wm, wn, lane, tid, [](float x) { return sigmoidf_(x); });
+}
+
+// Forward, part 2: LayerNorm_out of the contraction's x (read channel-major), then
+// y = g * (xn Wo).
+__global__ __launch_bounds__(NT, 2) void tmb_out_kernel(TmbArgs a) {
+  __shared__ __attribute__((aligned(16))) float lds[TP * CH];  // sA | sB, then the fp32 tile
+  uint16_t *sA = (uint16_t *)lds, *sB = sA + TP * CH;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long long p0 = (long long)xcd_remap(blockIdx.x, gridDim.x) * TP;
+  load_cm(sB, a.x + cm_tile(a, p0), a.NN, tid);  // [channel][position]
+  __syncthreads();
+  {
+    const int pr = tid >> 1, c0 = 64 * (tid & 1);
+    float x[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) x[i] = bf_lo(sB[toff(c0 + i, pr)]);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) s += x[i];
+    s += __shfl_xor(s, 1);
+    const float mean = s * (1.f / CH);
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const float d = x[i] - mean;
+      v = fmaf(d, d, v);
+    }
+    v += __shfl_xor(v, 1);
+    const float rstd = 1.f / sqrtf(v * (1.f / CH) + a.eps);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float y8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y8[e] = fmaf((x[8 * i + e] - mean) * rstd, a.ln_out_w[c0 + 8 * i + e], a.ln_out_b[c0 + 8 * i + e]);
+      const u32x4 q = pack8u(y8);
+      *(u32x4 *)(sA + toff(pr, c0 + 8 * i)) = q;
+      *(u32x4 *)(a.xn + (p0 + pr) * CH + c0 + 8 * i) = q;
+    }
+    if ((tid & 1) == 0) *(f32x2 *)(a.stats_out + 2 * (p0 + pr)) = (f32x2){mean, rstd};
+  }
+  __syncthreads();
+  load_block(sB, a.w_out, CH, tid);
+  __syncthreads();
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  f32x16 acc[2][2];
+  zero(acc);
+  tile_product<ROW, TR>(sA, sB, wm, wn, lane, CH / 16, acc);
+  __syncthreads();
+  stage_f32(lds, acc, wm, wn, lane, [](float x) { return x; });
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+    const long long off = (p0 + row) * CH + c;
+    float yp[8], gv[8];
+    read8_f32(lds, row, c, yp);
+    unpack8(*(const u32x4 *)(a.g + off), gv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) yp[e] *= gv[e];
+    *(u32x4 *)(a.y + off) = pack8u(yp);
+  }
+}
+
+// Column sums over the tile's 128 positions of an fp32 foff tile, in position order
+// (thread -> channel tid % 128, half tid / 128, then lower + upper half): channel c's
+// sum to dst[c].  Ends with the workgroup synchronised.
+__device__ __forceinline__ void column_sums(const float *t32, float (*s_half)[CH], int slot, float *dst, int tid) {
+  const int c = tid & 127, hp = tid >> 7;
+  float sum = 0.f;
+#pragma unroll 16
+  for (int r = 64 * hp; r < 64 * hp + 64; ++r) sum += t32[foff(r, c)];
+  if (hp) s_half[slot][c] = sum;
+  __syncthreads();
+  if (!hp) dst[c] = sum + s_half[slot][c];
+  __syncthreads();
+}
+
+// Backward, part 1: the output gate and projection and LayerNorm_out's backward:
+//   yp = xn Wo (recomputed), dyp = dy g, dgp = dy yp g (1 - g), dxn = dyp Wo^T,
+//   dx = LayerNorm_out backward of dxn (channel-major), and the tile's column sums of
+//   dxn xhat and dxn.
+__global__ __launch_bounds__(NT, 1) void tmb_out_bwd_kernel(TmbArgs a) {
+  __shared__ __attribute__((aligned(16))) float lds[TP * CH];  // sA | sB, or an fp32 tile
+  __shared__ __attribute__((aligned(16))) uint16_t sD[TP * CH];  // dyp [position][channel], then dx^T
+  __shared__ __attribute__((aligned(16))) uint16_t sX[TP * CH];  // x [channel][position]
+  __shared__ float s_half[2][CH];
+  uint16_t *sA = (uint16_t *)lds, *sB = sA + TP * CH;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const long long p0 = (long long)tile * TP;
+  const long long cm = cm_tile(a, p0);
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  load_block(sA, a.xn + p0 * CH, CH, tid);
+  load_block(sB, a.w_out, CH, tid);
+  load_cm(sX, a.x + cm, a.NN, tid);
+  __syncthreads();
+  f32x16 acc[2][2];
+  zero(acc);
+  tile_product<ROW, TR>(sA, sB, wm, wn, lane, CH / 16, acc);  // yp
+  __syncthreads();
+  stage_f32(lds, acc, wm, wn, lane, [](float x) { return x; });
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+    const long long off = (p0 + row) * CH + c;
+    float yp[8], gv[8], d[8], dyp[8], dgp[8];
+    read8_f32(lds, row, c, yp);
+    unpack8(*(const u32x4 *)(a.g + off), gv);
+    unpack8(*(const u32x4 *)(a.dy + off), d);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      dyp[e] = d[e] * gv[e];
+      dgp[e] = d[e] * yp[e] * gv[e] * (1.f - gv[e]);
+    }
+    const u32x4 q = pack8u(dyp);
+    *(u32x4 *)(sD + toff(row, c)) = q;
+    *(u32x4 *)(a.dyp + off) = q;
+    *(u32x4 *)(a.dgp + off) = pack8u(dgp);
+  }
+  __syncthreads();
+  load_block(sB, a.w_out, CH, tid);  // read as rows: B(t = c_out, n = c_in) = Wo[c_in][c_out]
+  __syncthreads();
+  zero(acc);
+  tile_product<ROW, ROW>(sD, sB, wm, wn, lane, CH / 16, acc);  // dxn
+  __syncthreads();
+  stage_f32(lds, acc, wm, wn, lane, [](float x) { return x; });
+  __syncthreads();
+  float *part = a.ln_out_part + (long long)tile * 2 * CH;
+  column_sums(lds, s_half, 1, part + CH, tid);  // sum of dxn: the offset gradient's partial
+  {
+    const int pr = tid >> 1, c0 = 64 * (tid & 1);
+    const f32x2 st = *(const f32x2 *)(a.stats_out + 2 * (p0 + pr));
+    const float mean = st[0], rstd = st[1];
+    float s1 = 0.f, s2 = 0.f;
+    float dx[64], xh[64];
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const int c = c0 + i;
+      const float d = lds[foff(pr, c)];
+      xh[i] = (bf_lo(sX[toff(c, pr)]) - mean) * rstd;
+      dx[i] = d * a.ln_out_w[c];
+      s1 += dx[i];
+      s2 = fmaf(dx[i], xh[i], s2);
+      lds[foff(pr, c)] = d * xh[i];  // dxn * xhat, in place, for the scale gradient
+    }
+    s1 += __shfl_xor(s1, 1);
+    s2 += __shfl_xor(s2, 1);
+    const float m1 = s1 * (1.f / CH), m2 = s2 * (1.f / CH);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) sD[toff(c0 + i, pr)] = bf16_of(rstd * (dx[i] - m1 - xh[i] * m2));
+  }
+  __syncthreads();
+  column_sums(lds, s_half, 0, part, tid);  // sum of dxn * xhat
+  store_rows(sD, a.dx + cm, a.NN, tid);
+}
+
+// Backward, part 2: the gated projections' gradients from da and db (channel-major),
+//   d(ap) = da sigmoid(ag) m,  d(ag) = da ap m sigmoid(ag) (1 - sigmoid(ag))   (b likewise)
+// with ag, ap, bg, bp recomputed from zn; stored channel-major.
+__global__ __launch_bounds__(NT, 1) void tmb_grad_proj_kernel(TmbArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[TP * CH];  // zn
+  __shared__ __attribute__((aligned(16))) uint16_t sB[CH * CH];  // weights, then d(proj)
+  __shared__ __attribute__((aligned(16))) uint16_t sT[CH * TP];  // da, then d(gate)
+  __shared__ float s_m[TP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long long p0 = (long long)xcd_remap(blockIdx.x, gridDim.x) * TP;
+  const long long cm = cm_tile(a, p0);
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64, hh = lane >> 5, ll = lane & 31;
+  if (tid < TP) s_m[tid] = a.mask ? (a.mask[p0 + tid] ? 1.f : 0.f) : 1.f;
+  load_block(sA, a.zn + p0 * CH, CH, tid);
+  f32x16 acc_g[2][2], acc_p[2][2];
+#pragma unroll 1
+  for (int pr = 0; pr < 2; ++pr) {
+    if (pr) __syncthreads();
+    load_block(sB, a.w_in + 2 * pr * CH, 5 * CH, tid);  // the gate block
+    __syncthreads();
+    zero(acc_g);
+    tile_product<ROW, TR>(sA, sB, wm, wn, lane, CH / 16, acc_g);
+    __syncthreads();
+    load_block(sB, a.w_in + (2 * pr + 1) * CH, 5 * CH, tid);  // the projection block
+    load_cm(sT, (pr ? a.db : a.da) + cm, a.NN, tid);
+    __syncthreads();
+    zero(acc_p);
+    tile_product<ROW, TR>(sA, sB, wm, wn, lane, CH / 16, acc_p);
+    __syncthreads();  // sB is free for d(proj)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3), n = wn + 32 * j + ll;
+          const float d = bf_lo(sT[toff(n, m)]) * s_m[m];
+          const float sg = sigmoidf_(acc_g[i][j][r]);
+          sT[toff(n, m)] = bf16_of(d * acc_p[i][j][r] * sg * (1.f - sg));
+          sB[toff(n, m)] = bf16_of(d * sg);
+        }
+    __syncthreads();
+    store_rows(sT, (pr ? a.dbg : a.dag) + cm, a.NN, tid);
+    store_rows(sB, (pr ? a.dbp : a.dap) + cm, a.NN, tid);
+  }
+}
+
+// Backward, part 3: dzn = [d(ag) d(ap) d(bg) d(bp) dgp] Win^T (five 128-deep blocks), the
+// LayerNorm_in backward to dz and the tile's column sums of dzn xhat and dzn.
+__global__ __launch_bounds__(NT, 1) void tmb_in_bwd_kernel(TmbArgs a) {
+  // [sA | sB] operands, then the dzn * xhat fp32 tile; the dzn fp32 tile
+  __shared__ __attribute__((aligned(16))) float lds0[TP * CH];
+  __shared__ __attribute__((aligned(16))) float lds1[TP * CH];
+  __shared__ float s_half[2][CH];
+  uint16_t *sA = (uint16_t *)lds0, *sB = sA + TP * CH;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tile = xcd_remap(blockIdx.x, gridDim.x);
+  const long long p0 = (long long)tile * TP;
+  const long long cm = cm_tile(a, p0);
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  f32x16 dzn[2][2];
+  zero(dzn);
+#pragma unroll 1
+  for (int blk = 0; blk < 5; ++blk) {
+    if (blk) __syncthreads();
+    load_block(sB, a.w_in + blk * CH, 5 * CH, tid);  // read as rows: B(t = out, n = c_in)
+    if (blk < 4) {
+      const uint16_t *src = blk == 0 ? a.dag : blk == 1 ? a.dap : blk == 2 ? a.dbg : a.dbp;
+      load_cm(sA, src + cm, a.NN, tid);  // [channel][position]
+      __syncthreads();
+      tile_product<TR, ROW>(sA, sB, wm, wn, lane, CH / 16, dzn);
+    } else {
+      load_block(sA, a.dgp + p0 * CH, CH, tid);  // [position][channel]
+      __syncthreads();
+      tile_product<ROW, ROW>(sA, sB, wm, wn, lane, CH / 16, dzn);
+    }
+  }
+  float *t_dzn = lds1, *t_dx = lds0;
+  stage_f32(t_dzn, dzn, wm, wn, lane, [](float x) { return x; });
+  __syncthreads();  // dzn staged, the operand tiles consumed
+  float *part = a.ln_in_part + (long long)tile * 2 * CH;
+  {
+    const int pr = tid >> 1, c0 = 64 * (tid & 1);
+    const f32x2 st = *(const f32x2 *)(a.stats_in + 2 * (p0 + pr));
+    const float mean = st[0], rstd = st[1];
+    float s1 = 0.f, s2 = 0.f;
+    float dx[64], xh[64];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float zv[8], d[8], dxh[8];
+      unpack8(*(const u32x4 *)(a.z + (p0 + pr) * CH + c0 + 8 * i), zv);
+      read8_f32(t_dzn, pr, c0 + 8 * i, d);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = 8 * i + e;
+        xh[c] = (zv[e] - mean) * rstd;
+        dxh[e] = d[e] * xh[c];
+        dx[c] = d[e] * a.ln_in_w[c0 + c];
+        s1 += dx[c];
+        s2 = fmaf(dx[c], xh[c], s2);
+      }
+      *(f32x4 *)(t_dx + foff(pr, c0 + 8 * i)) = (f32x4){dxh[0], dxh[1], dxh[2], dxh[3]};
+      *(f32x4 *)(t_dx + foff(pr, c0 + 8 * i + 4)) = (f32x4){dxh[4], dxh[5], dxh[6], dxh[7]};
+    }
+    s1 += __shfl_xor(s1, 1);
+    s2 += __shfl_xor(s2, 1);
+    const float m1 = s1 * (1.f / CH), m2 = s2 * (1.f / CH);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = rstd * (dx[8 * i + e] - m1 - xh[8 * i + e] * m2);
+      *(u32x4 *)(a.dz + (p0 + pr) * CH + c0 + 8 * i) = pack8u(o);
+    }
+  }
+  __syncthreads();
+  column_sums(t_dx, s_half, 0, part, tid);
+  column_sums(t_dzn, s_half, 1, part + CH, tid);
+}
+
+// Weight gradients of the block: workgroup = (output block, slice of tiles),
+//   blocks 0..3: zn^T d(ag), d(ap), d(bg), d(bp)   (CMB: the gradients channel-major)
+//   block 4:     zn^T dgp
+//   block 5:     xn^T dyp                           (d Wo)
+// launched once with CMB for blocks 0..3 and once without for blocks 4 and 5.
+template <bool CMB>
+__global__ __launch_bounds__(NT, 2) void tmb_wgrad_kernel(TmbArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[TP * CH];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[TP * CH];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int nb = CMB ? 4 : 2;
+  const int blk = t % nb + (CMB ? 0 : 4), slice = t / nb;
+  const int t0 = (int)((long long)slice * a.tiles / a.slices), t1 = (int)((long long)(slice + 1) * a.tiles / a.slices);
+  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const uint16_t *asrc = blk < 5 ? a.zn : a.xn;
+  const uint16_t *bsrc = blk == 0 ? a.dag : blk == 1 ? a.dap : blk == 2 ? a.dbg : blk == 3 ? a.dbp
+                       : blk == 4 ? a.dgp : a.dyp;
+  f32x16 acc[2][2];
+  zero(acc);
+#pragma unroll 1
+  for (int tile = t0; tile < t1; ++tile) {
+    const long long p0 = (long long)tile * TP;
+    if (tile > t0) __syncthreads();
+    load_block(sA, asrc + p0 * CH, CH, tid);
+    if (CMB) load_cm(sB, bsrc + cm_tile(a, p0), a.NN, tid);  // [channel n][position t]
+    else load_block(sB, bsrc + p0 * CH, CH, tid);            // [position t][channel n]
+    __syncthreads();
+    tile_product<TR, CMB ? ROW : TR>(sA, sB, wm, wn, lane, TP / 16, acc);
+  }
+  float *dst = a.w_part + ((long long)blk * a.slices + slice) * CH * CH;
+  const int hh = lane >> 5, ll = lane & 31;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3), n = wn + 32 * j + ll;
+        dst[m * CH + n] = acc[i][j][r];
+      }
+}
+
+struct TmbReduceArgs {
+  const float *w_part, *ln_in_part, *ln_out_part;
+  float *dw_in, *dw_out, *d_ln_in_w, *d_ln_in_b, *d_ln_out_w, *d_ln_out_b;
+  int slices, tiles;
+};
+
+__global__ __launch_bounds__(256) void tmb_reduce_w_kernel(TmbReduceArgs a) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= 6 * CH * CH) return;
+  const int blk = e / (CH * CH), mn = e - blk * CH * CH, m = mn >> 7, n = mn & 127;
+  const float *src = a.w_part + (long long)blk * a.slices * CH * CH + mn;
+  float s = 0.f;
+  for (int sl = 0; sl < a.slices; ++sl) s += src[(long long)sl * CH * CH];
+  if (blk < 5) a.dw_in[m * 5 * CH + blk * CH + n] = s;
+  else a.dw_out[m * CH + n] = s;
+}
+
+// 512 outputs: the input LayerNorm's scale and offset gradients, then the output one's
+__global__ __launch_bounds__(64) void tmb_reduce_ln_kernel(TmbReduceArgs a) {
+  const int e = blockIdx.x, which = e >> 8, k = e & 255;
+  const float *part = which ? a.ln_out_part : a.ln_in_part;
+  const int i = threadIdx.x;
+  const int t0 = (int)((long long)i * a.tiles / 64), t1 = (int)((long long)(i + 1) * a.tiles / 64);
+  float s = 0.f;
+  for (int t = t0; t < t1; ++t) s += part[(long long)t * 2 * CH + k];
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) s += __shfl_xor(s, d);
+  if (i == 0) {
+    float *dst = which ? (k < CH ? a.d_ln_out_w : a.d_ln_out_b) : (k < CH ? a.d_ln_in_w : a.d_ln_in_b);
+    dst[k & 127] = s;
+  }
+}
+
+// ------------------------------------------------------------------------------------
 // Host side
 // ------------------------------------------------------------------------------------
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -756,9 +1267,174 @@ BwdLayout bwd_layout(const tri_attn_module_problem *p, size_t core_bytes) {
   return l;
 }
 
+tri_attn_status tmb_check(const tri_mul_module_problem *p) {
+  if (!p) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (p->abi_version != TRI_MUL_MODULE_ABI_VERSION) return TRI_ATTN_ERROR_ABI_MISMATCH;
+  if (p->B < 1 || p->N < 1 || p->C < 1) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!(p->ln_eps >= 0.f) || isinf(p->ln_eps)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (p->flags & ~TRI_MUL_FLAG_INCOMING) return TRI_ATTN_ERROR_NOT_SUPPORTED;
+  if (p->C != CH || p->N % 32 != 0 || p->N > 1024 || p->B * p->C > 65536) return TRI_ATTN_ERROR_NOT_SUPPORTED;
+  return TRI_ATTN_SUCCESS;
+}
+
+tri_mul_problem tmb_contraction(const tri_mul_module_problem *p) {
+  tri_mul_problem m;
+  memset(&m, 0, sizeof m);
+  m.abi_version = TRI_MUL_ABI_VERSION;
+  m.flags = p->flags & TRI_MUL_FLAG_INCOMING;
+  m.B = p->B;
+  m.N = p->N;
+  m.C = p->C;
+  return m;
+}
+
+TmbArgs tmb_args(const tri_mul_module_problem *p, const void *z, const uint8_t *mask,
+                 const tri_mul_module_params *pr, const tri_mul_module_saved *sv) {
+  TmbArgs a;
+  memset(&a, 0, sizeof a);
+  a.z = (const uint16_t *)z;
+  a.mask = mask;
+  a.ln_in_w = pr->ln_in_w;
+  a.ln_in_b = pr->ln_in_b;
+  a.ln_out_w = pr->ln_out_w;
+  a.ln_out_b = pr->ln_out_b;
+  a.w_in = (const uint16_t *)pr->w_in;
+  a.w_out = (const uint16_t *)pr->w_out;
+  a.zn = (uint16_t *)sv->zn;
+  a.stats_in = sv->ln_in_stats;
+  a.stats_out = sv->ln_out_stats;
+  a.a = (uint16_t *)sv->a;
+  a.b = (uint16_t *)sv->b;
+  a.g = (uint16_t *)sv->g;
+  a.x = (const uint16_t *)sv->x;
+  a.xn = (uint16_t *)sv->xn;
+  a.B = (int)p->B;
+  a.N = (int)p->N;
+  a.NN = p->N * p->N;
+  a.P = p->B * a.NN;
+  a.tiles = (int)(a.P / TP);
+  a.slices = wgrad_slices(a.tiles);
+  a.eps = p->ln_eps > 0.f ? p->ln_eps : 1e-5f;
+  return a;
+}
+
+struct TmbLayout {
+  size_t off_dyp, off_dgp, off_dx, off_da, off_db, off_dag, off_dap, off_dbg, off_dbp, off_w, off_lni, off_lno, total;
+};
+
+TmbLayout tmb_layout(const tri_mul_module_problem *p) {
+  TmbLayout l;
+  const size_t E = (size_t)p->B * p->N * p->N * CH * 2;
+  const int tiles = (int)(p->B * p->N * p->N / TP);
+  size_t o = 0;
+  size_t *bf[] = {&l.off_dyp, &l.off_dgp, &l.off_dx, &l.off_da, &l.off_db, &l.off_dag, &l.off_dap, &l.off_dbg,
+                  &l.off_dbp};
+  for (size_t *x : bf) {
+    *x = o;
+    o += align256(E);
+  }
+  l.off_w = o; o += align256((size_t)6 * wgrad_slices(tiles) * CH * CH * 4);
+  l.off_lni = o; o += align256((size_t)tiles * 2 * CH * 4);
+  l.off_lno = o; o += align256((size_t)tiles * 2 * CH * 4);
+  l.total = o;
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
+
+int tri_mul_module_abi_version(void) { return TRI_MUL_MODULE_ABI_VERSION; }
+
+tri_attn_status tri_mul_module_fwd(const tri_mul_module_problem *problem, const void *z, const uint8_t *mask,
+                                   const tri_mul_module_params *params, void *y, const tri_mul_module_saved *saved,
+                                   hipStream_t stream) {
+  tri_attn_status st = tmb_check(problem);
+  if (st != TRI_ATTN_SUCCESS) return st;
+  if (!params || !saved) return TRI_ATTN_ERROR_INVALID_VALUE;
+  const void *need[] = {z, y, params->ln_in_w, params->ln_in_b, params->w_in, params->ln_out_w, params->ln_out_b,
+                        params->w_out, saved->zn, saved->ln_in_stats, saved->a, saved->b, saved->g, saved->x,
+                        saved->xn, saved->ln_out_stats};
+  for (const void *x : need)
+    if (!aligned16(x)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  TmbArgs a = tmb_args(problem, z, mask, params, saved);
+  a.y = (uint16_t *)y;
+  hipLaunchKernelGGL(tmb_proj_kernel, dim3((unsigned)a.tiles), dim3(NT), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  const tri_mul_problem mp = tmb_contraction(problem);
+  st = tri_mul_fwd(&mp, saved->a, saved->b, saved->x, stream);
+  if (st != TRI_ATTN_SUCCESS) return st;
+  hipLaunchKernelGGL(tmb_out_kernel, dim3((unsigned)a.tiles), dim3(NT), 0, stream, a);
+  return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH_FAILED;
+}
+
+size_t tri_mul_module_bwd_workspace_bytes(const tri_mul_module_problem *problem) {
+  if (tmb_check(problem) != TRI_ATTN_SUCCESS) return 0;
+  return tmb_layout(problem).total;
+}
+
+tri_attn_status tri_mul_module_bwd(const tri_mul_module_problem *problem, const void *z, const uint8_t *mask,
+                                   const tri_mul_module_params *params, const tri_mul_module_saved *saved,
+                                   const void *dy, void *dz, const tri_mul_module_param_grads *grads,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  tri_attn_status st = tmb_check(problem);
+  if (st != TRI_ATTN_SUCCESS) return st;
+  if (!params || !saved || !grads) return TRI_ATTN_ERROR_INVALID_VALUE;
+  const void *need[] = {z, dy, dz, params->ln_in_w, params->ln_in_b, params->w_in, params->ln_out_w,
+                        params->ln_out_b, params->w_out, saved->zn, saved->ln_in_stats, saved->a, saved->b, saved->g,
+                        saved->x, saved->xn, saved->ln_out_stats, grads->ln_in_w, grads->ln_in_b, grads->w_in,
+                        grads->ln_out_w, grads->ln_out_b, grads->w_out};
+  for (const void *x : need)
+    if (!aligned16(x)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  if (!workspace || ((uintptr_t)workspace & 255u)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  const TmbLayout l = tmb_layout(problem);
+  if (workspace_bytes < l.total) return TRI_ATTN_ERROR_INSUFFICIENT_WORKSPACE;
+  char *ws = (char *)workspace;
+  TmbArgs a = tmb_args(problem, z, mask, params, saved);
+  a.dy = (const uint16_t *)dy;
+  a.dyp = (uint16_t *)(ws + l.off_dyp);
+  a.dgp = (uint16_t *)(ws + l.off_dgp);
+  a.dx = (uint16_t *)(ws + l.off_dx);
+  a.da = (const uint16_t *)(ws + l.off_da);
+  a.db = (const uint16_t *)(ws + l.off_db);
+  a.dag = (uint16_t *)(ws + l.off_dag);
+  a.dap = (uint16_t *)(ws + l.off_dap);
+  a.dbg = (uint16_t *)(ws + l.off_dbg);
+  a.dbp = (uint16_t *)(ws + l.off_dbp);
+  a.dz = (uint16_t *)dz;
+  a.w_part = (float *)(ws + l.off_w);
+  a.ln_in_part = (float *)(ws + l.off_lni);
+  a.ln_out_part = (float *)(ws + l.off_lno);
+  hipLaunchKernelGGL(tmb_out_bwd_kernel, dim3((unsigned)a.tiles), dim3(NT), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  const tri_mul_problem mp = tmb_contraction(problem);
+  st = tri_mul_bwd(&mp, saved->a, saved->b, a.dx, ws + l.off_da, ws + l.off_db, stream);
+  if (st != TRI_ATTN_SUCCESS) return st;
+  hipLaunchKernelGGL(tmb_grad_proj_kernel, dim3((unsigned)a.tiles), dim3(NT), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  hipLaunchKernelGGL(tmb_in_bwd_kernel, dim3((unsigned)a.tiles), dim3(NT), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  hipLaunchKernelGGL(tmb_wgrad_kernel<true>, dim3((unsigned)(4 * a.slices)), dim3(NT), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  hipLaunchKernelGGL(tmb_wgrad_kernel<false>, dim3((unsigned)(2 * a.slices)), dim3(NT), 0, stream, a);
+  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  TmbReduceArgs r;
+  r.w_part = a.w_part;
+  r.ln_in_part = a.ln_in_part;
+  r.ln_out_part = a.ln_out_part;
+  r.dw_in = grads->w_in;
+  r.dw_out = grads->w_out;
+  r.d_ln_in_w = grads->ln_in_w;
+  r.d_ln_in_b = grads->ln_in_b;
+  r.d_ln_out_w = grads->ln_out_w;
+  r.d_ln_out_b = grads->ln_out_b;
+  r.slices = a.slices;
+  r.tiles = a.tiles;
+  hipLaunchKernelGGL(tmb_reduce_w_kernel, dim3((6 * CH * CH + 255) / 256), dim3(256), 0, stream, r);
+  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  hipLaunchKernelGGL(tmb_reduce_ln_kernel, dim3(4 * CH), dim3(64), 0, stream, r);
+  return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH_FAILED;
+}
 
 int tri_attn_module_abi_version(void) { return TRI_ATTN_MODULE_ABI_VERSION; }
 
