@@ -41,8 +41,10 @@
  * TurboPairFormer", third point); the weight gradients are sums over all B N N
  * positions, taken as fixed slices whose fp32 partials are added in slice order.
  *
- * Conventions as in tri_attn.h: caller-owned device pointers, 16-byte aligned, outputs
- * not overlapping inputs (not checked here beyond alignment); work enqueued on
+ * Conventions as in tri_attn.h: caller-owned device pointers, 16-byte aligned; every
+ * output (the saved activations of the forward, the gradients and the workspace of the
+ * backward) must not overlap any input or other output (checked: TRI_ATTN_ERROR_INVALID_
+ * VALUE before anything is enqueued); work enqueued on
  * `stream`, no synchronisation; host-side validation before anything is enqueued.
  * Supported: H * D == 128 with the core's supported H and D, the core's N (a multiple
  * of 32 up to 768), any B; other sizes return TRI_ATTN_ERROR_NOT_SUPPORTED.

@@ -32,8 +32,10 @@
  * contraction are round-to-nearest-even bf16.  Every sum runs in a fixed order
  * (bitwise reproducible; Lambda post, "Как работает TurboPairFormer", third point).
  *
- * Conventions as in tri_attn.h: caller-owned device pointers, 16-byte aligned, outputs
- * not overlapping inputs (not checked beyond alignment); work enqueued on `stream`;
+ * Conventions as in tri_attn.h: caller-owned device pointers, 16-byte aligned; every
+ * output (the saved activations of the forward, the gradients and the workspace of the
+ * backward) must not overlap any input or other output (checked: TRI_ATTN_ERROR_INVALID_
+ * VALUE before anything is enqueued); work enqueued on `stream`;
  * host-side validation before anything is enqueued.  Supported: C == 128, N a multiple
  * of 32 up to 1024, B * C <= 65536; otherwise TRI_ATTN_ERROR_NOT_SUPPORTED.
  */

@@ -415,3 +415,84 @@ def test_tri_mul_rejects_null_misaligned_and_aliased_pointers(lib):
     p = fake_ptrs(5)
     p[3] = p[2]   # da == dz
     assert call_mul_bwd(lib, prob, p) == INVALID
+
+
+# ---- the modules around the cores (include/tri_module.h, include/tri_mul_module.h) ----
+
+def module_structs(n_params, n_saved, start=1):
+    """Distinct fake device addresses, 4 GiB apart, for the pointer structs."""
+    addr = [ADDR + (start + i) * (1 << 32) for i in range(n_params + n_saved)]
+    return addr[:n_params], addr[n_params:]
+
+
+def call_attn_module_fwd(lib, prob, z=ADDR, y=ADDR + 7 * (1 << 36), params=None, saved=None):
+    pp, sv = module_structs(5, 10)
+    p = ta.ModuleParams(*(params or pp))
+    s = ta.ModuleSaved(*(saved or sv))
+    return lib.tri_attn_module_fwd(ctypes.byref(prob) if prob is not None else None, ctypes.c_void_p(z), None,
+                                   ctypes.byref(p), ctypes.c_void_p(y), ctypes.byref(s), None)
+
+
+@pytest.mark.parametrize("field,value,expect", [("abi_version", ta.MODULE_ABI_VERSION + 1, ABI), ("B", 0, INVALID),
+                                                ("H", 3, UNSUPPORTED), ("D", 64, UNSUPPORTED), ("N", 48, UNSUPPORTED),
+                                                ("flags", 4, UNSUPPORTED), ("ln_eps", -1.0, INVALID)])
+def test_attn_module_problem_validation(lib, field, value, expect):
+    prob = ta.make_module_problem(1, 64, 4, 32)
+    setattr(prob, field, value)
+    assert call_attn_module_fwd(lib, prob) == expect
+    assert lib.tri_attn_module_bwd_workspace_bytes(ctypes.byref(prob)) == 0
+
+
+def test_attn_module_rejects_null_misaligned_and_aliased_pointers(lib):
+    prob = ta.make_module_problem(1, 64, 4, 32)
+    assert call_attn_module_fwd(lib, None) == INVALID
+    pp, sv = module_structs(5, 10)
+    bad = list(pp)
+    bad[2] += 2  # a misaligned weight matrix
+    assert call_attn_module_fwd(lib, prob, params=bad) == INVALID
+    bad = list(sv)
+    bad[3] = None  # no k
+    assert call_attn_module_fwd(lib, prob, saved=bad) == INVALID
+    assert call_attn_module_fwd(lib, prob, y=ADDR) == INVALID  # y over z
+    bad = list(sv)
+    bad[7] = sv[6]  # o over g
+    assert call_attn_module_fwd(lib, prob, saved=bad) == INVALID
+
+
+def test_attn_module_workspace_holds_the_core_workspace(lib):
+    for N in (64, 256):
+        core = lib.tri_attn_bwd_workspace_bytes(ctypes.byref(ta.make_problem(1, N, 4, 32)))
+        mod = lib.tri_attn_module_bwd_workspace_bytes(ctypes.byref(ta.make_module_problem(1, N, 4, 32)))
+        assert mod > core + 5 * N * N * 128 * 2   # + dO, the gate gradient, dq, dk, dv
+
+
+def call_trimul_module_fwd(lib, prob, z=ADDR, y=ADDR + 7 * (1 << 36), params=None, saved=None):
+    pp, sv = module_structs(6, 8)
+    p = ta.TriMulModuleParams(*(params or pp))
+    s = ta.TriMulModuleSaved(*(saved or sv))
+    return lib.tri_mul_module_fwd(ctypes.byref(prob) if prob is not None else None, ctypes.c_void_p(z), None,
+                                  ctypes.byref(p), ctypes.c_void_p(y), ctypes.byref(s), None)
+
+
+@pytest.mark.parametrize("field,value,expect", [("abi_version", ta.TRI_MUL_MODULE_ABI_VERSION + 1, ABI),
+                                                ("B", 0, INVALID), ("C", 64, UNSUPPORTED), ("N", 48, UNSUPPORTED),
+                                                ("N", 1056, UNSUPPORTED), ("flags", 2, UNSUPPORTED),
+                                                ("ln_eps", float("inf"), INVALID)])
+def test_trimul_module_problem_validation(lib, field, value, expect):
+    prob = ta.make_trimul_module_problem(1, 64, 128)
+    setattr(prob, field, value)
+    assert call_trimul_module_fwd(lib, prob) == expect
+    assert lib.tri_mul_module_bwd_workspace_bytes(ctypes.byref(prob)) == 0
+
+
+def test_trimul_module_rejects_null_misaligned_and_aliased_pointers(lib):
+    prob = ta.make_trimul_module_problem(1, 64, 128)
+    assert call_trimul_module_fwd(lib, None) == INVALID
+    pp, sv = module_structs(6, 8)
+    bad = list(pp)
+    bad[0] += 4
+    assert call_trimul_module_fwd(lib, prob, params=bad) == INVALID
+    assert call_trimul_module_fwd(lib, prob, y=sv[5]) == INVALID  # y over the saved x
+    bad = list(sv)
+    bad[3] = sv[2]  # b over a
+    assert call_trimul_module_fwd(lib, prob, saved=bad) == INVALID

@@ -1203,6 +1203,24 @@ __global__ __launch_bounds__(64) void tmb_reduce_ln_kernel(TmbReduceArgs a) {
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool aligned16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
 
+// Byte ranges of the tensors of a call: every output must be disjoint from every input
+// and from every other output.
+struct Span {
+  uintptr_t lo, hi;
+};
+Span span(const void *p, size_t bytes) { return {(uintptr_t)p, (uintptr_t)p + (p ? bytes : 0)}; }
+bool overlap(Span x, Span y) { return x.lo < y.hi && y.lo < x.hi; }
+template <size_t NO, size_t NI>
+bool outputs_disjoint(const Span (&outs)[NO], const Span (&ins)[NI]) {
+  for (size_t i = 0; i < NO; ++i) {
+    for (size_t j = 0; j < NI; ++j)
+      if (overlap(outs[i], ins[j])) return false;
+    for (size_t k = 0; k < NO; ++k)
+      if (k != i && overlap(outs[i], outs[k])) return false;
+  }
+  return true;
+}
+
 tri_attn_status check(const tri_attn_module_problem *p) {
   if (!p) return TRI_ATTN_ERROR_INVALID_VALUE;
   if (p->abi_version != TRI_ATTN_MODULE_ABI_VERSION) return TRI_ATTN_ERROR_ABI_MISMATCH;
@@ -1357,6 +1375,17 @@ tri_attn_status tri_mul_module_fwd(const tri_mul_module_problem *problem, const 
                         saved->xn, saved->ln_out_stats};
   for (const void *x : need)
     if (!aligned16(x)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  {
+    const size_t P = (size_t)problem->B * problem->N * problem->N, E = P * CH * 2;
+    const Span ins[] = {span(z, E), span(mask, mask ? P : 0), span(params->ln_in_w, CH * 4),
+                        span(params->ln_in_b, CH * 4), span(params->w_in, CH * 5 * CH * 2),
+                        span(params->ln_out_w, CH * 4), span(params->ln_out_b, CH * 4),
+                        span(params->w_out, CH * CH * 2)};
+    const Span outs[] = {span(y, E), span(saved->zn, E), span(saved->ln_in_stats, P * 8), span(saved->a, E),
+                         span(saved->b, E), span(saved->g, E), span(saved->x, E), span(saved->xn, E),
+                         span(saved->ln_out_stats, P * 8)};
+    if (!outputs_disjoint(outs, ins)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  }
   TmbArgs a = tmb_args(problem, z, mask, params, saved);
   a.y = (uint16_t *)y;
   hipLaunchKernelGGL(tmb_proj_kernel, dim3((unsigned)a.tiles), dim3(NT), 0, stream, a);
@@ -1389,6 +1418,19 @@ tri_attn_status tri_mul_module_bwd(const tri_mul_module_problem *problem, const 
   if (!workspace || ((uintptr_t)workspace & 255u)) return TRI_ATTN_ERROR_INVALID_VALUE;
   const TmbLayout l = tmb_layout(problem);
   if (workspace_bytes < l.total) return TRI_ATTN_ERROR_INSUFFICIENT_WORKSPACE;
+  {
+    const size_t P = (size_t)problem->B * problem->N * problem->N, E = P * CH * 2;
+    const Span ins[] = {span(z, E), span(mask, mask ? P : 0), span(dy, E), span(params->ln_in_w, CH * 4),
+                        span(params->ln_in_b, CH * 4), span(params->w_in, CH * 5 * CH * 2),
+                        span(params->ln_out_w, CH * 4), span(params->ln_out_b, CH * 4),
+                        span(params->w_out, CH * CH * 2), span(saved->zn, E), span(saved->ln_in_stats, P * 8),
+                        span(saved->a, E), span(saved->b, E), span(saved->g, E), span(saved->x, E),
+                        span(saved->xn, E), span(saved->ln_out_stats, P * 8)};
+    const Span outs[] = {span(dz, E), span(grads->ln_in_w, CH * 4), span(grads->ln_in_b, CH * 4),
+                         span(grads->w_in, CH * 5 * CH * 4), span(grads->ln_out_w, CH * 4),
+                         span(grads->ln_out_b, CH * 4), span(grads->w_out, CH * CH * 4), span(workspace, l.total)};
+    if (!outputs_disjoint(outs, ins)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  }
   char *ws = (char *)workspace;
   TmbArgs a = tmb_args(problem, z, mask, params, saved);
   a.dy = (const uint16_t *)dy;
@@ -1452,6 +1494,16 @@ tri_attn_status tri_attn_module_fwd(const tri_attn_module_problem *problem, cons
                         saved->o, saved->o_residual, saved->lse};
   for (const void *x : need)
     if (!aligned16(x)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  const size_t P = (size_t)problem->B * problem->N * problem->N, E = P * CH * 2;
+  const size_t nb = (size_t)problem->B * problem->H * problem->N * problem->N;
+  const Span ins[] = {span(z, E), span(mask, mask ? P : 0), span(params->ln_w, CH * 4), span(params->ln_b, CH * 4),
+                      span(params->w_qkvg, CH * 4 * CH * 2), span(params->w_bias, CH * problem->H * 2),
+                      span(params->w_out, CH * CH * 2)};
+  const Span outs[] = {span(y, E), span(saved->zn, E), span(saved->ln_stats, P * 8), span(saved->q, E),
+                       span(saved->k, E), span(saved->v, E), span(saved->g, E), span(saved->bias, nb * 2),
+                       span(saved->o, E), span(saved->o_residual, 2 * E),
+                       span(saved->lse, (size_t)problem->B * problem->N * problem->H * problem->N * 4)};
+  if (!outputs_disjoint(outs, ins)) return TRI_ATTN_ERROR_INVALID_VALUE;
   ModArgs a = base_args(problem);
   a.z = (const uint16_t *)z;
   a.ln_w = params->ln_w;
@@ -1504,6 +1556,20 @@ tri_attn_status tri_attn_module_bwd(const tri_attn_module_problem *problem, cons
   if (!workspace || ((uintptr_t)workspace & 255u)) return TRI_ATTN_ERROR_INVALID_VALUE;
   const BwdLayout l = bwd_layout(problem, core);
   if (workspace_bytes < l.total) return TRI_ATTN_ERROR_INSUFFICIENT_WORKSPACE;
+  {
+    const size_t P = (size_t)problem->B * problem->N * problem->N, E = P * CH * 2;
+    const size_t nb = (size_t)problem->B * problem->H * problem->N * problem->N, H = problem->H;
+    const Span ins[] = {span(z, E), span(mask, mask ? P : 0), span(dy, E), span(params->ln_w, CH * 4),
+                        span(params->ln_b, CH * 4), span(params->w_qkvg, CH * 4 * CH * 2),
+                        span(params->w_bias, CH * H * 2), span(params->w_out, CH * CH * 2), span(saved->zn, E),
+                        span(saved->ln_stats, P * 8), span(saved->q, E), span(saved->k, E), span(saved->v, E),
+                        span(saved->g, E), span(saved->bias, nb * 2), span(saved->o, E),
+                        span(saved->o_residual, 2 * E), span(saved->lse, (size_t)problem->B * problem->N * H * problem->N * 4)};
+    const Span outs[] = {span(dz, E), span(grads->ln_w, CH * 4), span(grads->ln_b, CH * 4),
+                         span(grads->w_qkvg, CH * 4 * CH * 4), span(grads->w_bias, CH * H * 4),
+                         span(grads->w_out, CH * CH * 4), span(workspace, l.total)};
+    if (!outputs_disjoint(outs, ins)) return TRI_ATTN_ERROR_INVALID_VALUE;
+  }
   char *ws = (char *)workspace;
   ModArgs a = base_args(problem);
   a.z = (const uint16_t *)z;
