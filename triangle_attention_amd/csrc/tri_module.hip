@@ -35,6 +35,7 @@
 //   C (32 x 32): lane holds C[8 (r / 4) + 4 hh + r % 4][lane % 32], r = 0..15
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 #include <math.h>
 #include <string.h>
 
@@ -97,51 +98,74 @@ __device__ __forceinline__ bf16x8 tr_operand(const uint16_t *tile, int kk, int c
 // contiguous), TR = [t][m or n].
 enum Layout { ROW = 0, TR = 1 };
 
-// acc[i][j] += sum over t in [0, 16 * slices) of A(wm + 32 i + ., t) B(t, wn + 32 j + .)
-template <int AL, int BL>
+// acc[i][j] += sum over t in [0, 16 * slices) of A(wm + 32 i + ., t) B(t, wn + 32 j + .).
+// MI = 2: a wave owns 64 x 64 of the 128 x 128 tile (4 waves); MI = 1: 32 x 64 (8 waves).
+template <int AL, int BL, int MI = 2>
 __device__ __forceinline__ void tile_product(const uint16_t *sA, const uint16_t *sB, int wm, int wn, int lane,
-                                             int slices, f32x16 (&acc)[2][2]) {
+                                             int slices, f32x16 (&acc)[MI][2]) {
   for (int s = 0; s < slices; ++s) {
     const int kk = 16 * s;
-    bf16x8 a[2], b[2];
+    bf16x8 a[MI], b[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < MI; ++i)
       a[i] = AL == ROW ? row_operand(sA, wm + 32 * i, kk, lane) : tr_operand(sA, kk, wm + 32 * i, lane);
-      b[i] = BL == ROW ? row_operand(sB, wn + 32 * i, kk, lane) : tr_operand(sB, kk, wn + 32 * i, lane);
-    }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j)
+      b[j] = BL == ROW ? row_operand(sB, wn + 32 * j, kk, lane) : tr_operand(sB, kk, wn + 32 * j, lane);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[i][j] = mfma(a[i], b[j], acc[i][j]);
   }
 }
 
-__device__ __forceinline__ void zero(f32x16 (&acc)[2][2]) {
+template <int MI = 2>
+__device__ __forceinline__ void zero(f32x16 (&acc)[MI][2]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = (f32x16){};
 }
 
 // A [128][128] bf16 matrix block (rows row0.., 256-byte rows of a row-major matrix with
-// `ld` elements per row, columns col0 .. col0 + 127) into an LDS tile: thread t copies
-// 16-byte pieces t, t + 256, ...
+// `ld` elements per row, columns col0 .. col0 + 127) into an LDS tile: thread t of T
+// copies 16-byte pieces t, t + T, ...
+template <int T = NT>
 __device__ __forceinline__ void load_block(uint16_t *tile, const uint16_t *src, long long ld, int tid) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int p = tid + NT * i, row = p >> 4, c = (p & 15) * 8;
+  for (int i = 0; i < 2048 / T; ++i) {
+    const int p = tid + T * i, row = p >> 4, c = (p & 15) * 8;
     *(u32x4 *)(tile + toff(row, c)) = *(const u32x4 *)(src + (long long)row * ld + c);
   }
 }
 
+// load_block in two halves, so that the loads can be in flight while the workgroup
+// computes: fetch_block issues them into registers, put_block writes those to the tile.
+template <int T>
+__device__ __forceinline__ void fetch_block(u32x4 (&r)[2048 / T], const uint16_t *src, long long ld, int tid) {
+#pragma unroll
+  for (int i = 0; i < 2048 / T; ++i) {
+    const int p = tid + T * i, row = p >> 4, c = (p & 15) * 8;
+    r[i] = *(const u32x4 *)(src + (long long)row * ld + c);
+  }
+}
+template <int T>
+__device__ __forceinline__ void put_block(uint16_t *tile, const u32x4 (&r)[2048 / T], int tid) {
+#pragma unroll
+  for (int i = 0; i < 2048 / T; ++i) {
+    const int p = tid + T * i, row = p >> 4, c = (p & 15) * 8;
+    *(u32x4 *)(tile + toff(row, c)) = r[i];
+  }
+}
+
 // The accumulator tile as bf16 into an LDS tile (f applied to each value), then stored
-// as 128 rows of 256 bytes to dst (row stride 128 elements).
-template <typename F>
-__device__ __forceinline__ void store_tile_bf16(uint16_t *tile, uint16_t *dst, const f32x16 (&acc)[2][2], int wm,
+// as 128 rows of 256 bytes to dst (row stride 128 elements) by the workgroup's T threads.
+template <int MI = 2, int T = NT, typename F>
+__device__ __forceinline__ void store_tile_bf16(uint16_t *tile, uint16_t *dst, const f32x16 (&acc)[MI][2], int wm,
                                                 int wn, int lane, int tid, F f) {
   const int hh = lane >> 5, ll = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -151,8 +175,8 @@ __device__ __forceinline__ void store_tile_bf16(uint16_t *tile, uint16_t *dst, c
       }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int p = tid + NT * i, row = p >> 4, c = (p & 15) * 8;
+  for (int i = 0; i < 2048 / T; ++i) {
+    const int p = tid + T * i, row = p >> 4, c = (p & 15) * 8;
     *(u32x4 *)(dst + (long long)row * CH + c) = *(const u32x4 *)(tile + toff(row, c));
   }
 }
@@ -162,11 +186,11 @@ __device__ __forceinline__ void store_tile_bf16(uint16_t *tile, uint16_t *dst, c
 // four so that the accumulator writes of the two lane halves use different banks).
 __device__ __forceinline__ int foff(int row, int col) { return row * 128 + (col ^ ((row & 7) << 2)); }
 
-template <typename F>
-__device__ __forceinline__ void stage_f32(float *t32, const f32x16 (&acc)[2][2], int wm, int wn, int lane, F f) {
+template <int MI = 2, typename F>
+__device__ __forceinline__ void stage_f32(float *t32, const f32x16 (&acc)[MI][2], int wm, int wn, int lane, F f) {
   const int hh = lane >> 5, ll = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -567,55 +591,52 @@ __global__ __launch_bounds__(NT, 1) void mod_in_bwd_kernel(ModArgs a) {
   }
 }
 
-// Weight gradients: workgroup = (output block, slice of tiles); out[m][n] = sum over
-// the slice's positions p of A[p][m] B[p][n] with
+// Weight gradients: workgroup = (slice of tiles, output block), 8 waves each owning
+// 32 x 64 of the 128 x 128 block; out[m][n] = sum over the slice's positions p of
+// A[p][m] B[p][n] with
 //   blocks 0..3: A = zn, B = dq, dk, dv, dgp      (d Wqkvg, column block 0..3)
 //   block 4:     A = zn, B = dbias at p (bf16)    (d Wb, columns < H)
 //   block 5:     A = bf16(g * o), B = dy          (d Wo)
-// Both operands are read transposed from position-major tiles.  The fp32 partial of the
-// slice goes to w_part[block][slice].
-__global__ __launch_bounds__(NT, 2) void mod_wgrad_kernel(ModArgs a) {
+// Both operands are read transposed from position-major tiles, fetched into registers a
+// tile ahead.  The six blocks of a slice are neighbouring workgroups on one XCD.  The
+// fp32 partial of the slice goes to w_part[block][slice].
+constexpr int NT8M = 512;
+__global__ __launch_bounds__(NT8M, 4) void mod_wgrad_kernel(ModArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[TP * CH];
   __shared__ __attribute__((aligned(16))) uint16_t sB[TP * CH];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int blk = t % 6, slice = t / 6;
   const int t0 = (int)((long long)slice * a.tiles / a.slices), t1 = (int)((long long)(slice + 1) * a.tiles / a.slices);
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 64;
   const uint16_t *asrc = blk < 5 ? a.zn : a.g;
-  const uint16_t *bsrc = blk == 0 ? a.dq : blk == 1 ? a.dk : blk == 2 ? a.dv : blk == 3 ? a.dgp : a.dy;
-  f32x16 acc[2][2];
-  zero(acc);
+  // the bias block fetches dq as a stand-in B (never used: its B tile is gathered)
+  const uint16_t *bsrc = blk == 0 || blk == 4 ? a.dq : blk == 1 ? a.dk : blk == 2 ? a.dv : blk == 3 ? a.dgp : a.dy;
   if (blk == 4) {  // the bias block's B tile: zeros beyond the H head columns
     const u32x4 z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+    for (int i = 0; i < 4; ++i) {
+      const int pc = tid + NT8M * i, row = pc >> 4, c = (pc & 15) * 8;
       *(u32x4 *)(sB + toff(row, c)) = z4;
     }
   }
-  // one tile's operands as 16-byte pieces (A: zn, or g and o for block 5; B: the
-  // gradient tile, except for the bias block), loaded a tile ahead
-  u32x4 ra[8], ro[8], rb[8];
+  u32x4 ra[4], ro[4], rb[4];
   auto fetch = [&](int tile) {
     const long long p0 = (long long)tile * TP;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
-      const long long off = (p0 + row) * CH + c;
-      ra[i] = *(const u32x4 *)(asrc + off);
-      if (blk == 5) ro[i] = *(const u32x4 *)(a.o + off);
-      if (blk != 4) rb[i] = *(const u32x4 *)(bsrc + off);
-    }
+    fetch_block<NT8M>(ra, asrc + p0 * CH, CH, tid);
+    fetch_block<NT8M>(rb, bsrc + p0 * CH, CH, tid);
+    if (blk == 5) fetch_block<NT8M>(ro, a.o + p0 * CH, CH, tid);
   };
+  f32x16 acc[1][2];
+  zero<1>(acc);
   fetch(t0);
 #pragma unroll 1
   for (int tile = t0; tile < t1; ++tile) {
     const long long p0 = (long long)tile * TP;
     if (tile > t0) __syncthreads();  // the previous tile's operands are consumed
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
+    for (int i = 0; i < 4; ++i) {
+      const int pc = tid + NT8M * i, row = pc >> 4, c = (pc & 15) * 8;
       u32x4 w = ra[i];
       if (blk == 5) {
         float gv[8], ov[8];
@@ -631,26 +652,24 @@ __global__ __launch_bounds__(NT, 2) void mod_wgrad_kernel(ModArgs a) {
     if (blk == 4) {
       // the H head columns of the tile (the others were zeroed before the loop)
       const BiasTile bt(a, p0);
-      for (int e = tid; e < TP * a.H; e += NT) {
+      for (int e = tid; e < TP * a.H; e += NT8M) {
         const int row = e / a.H, h = e - row * a.H;
         sB[toff(row, h)] = (uint16_t)(pack_bf16(a.dbias[bt.at(row, h)], 0.f) & 0xffffu);
       }
     }
-    if (tile + 1 < t1) fetch(tile + 1);  // in flight during the products
     __syncthreads();
-    tile_product<TR, TR>(sA, sB, wm, wn, lane, TP / 16, acc);
+    fetch(min(tile + 1, t1 - 1));  // in flight during the products (the last tile again at the end)
+    tile_product<TR, TR, 1>(sA, sB, wm, wn, lane, TP / 16, acc);
   }
   float *dst = a.w_part + ((long long)blk * a.slices + slice) * CH * CH;
   const int hh = lane >> 5, ll = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3), n = wn + 32 * j + ll;
-        dst[m * CH + n] = acc[i][j][r];
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int m = wm + 8 * (r >> 2) + 4 * hh + (r & 3), n = wn + 32 * j + ll;
+      dst[m * CH + n] = acc[0][j][r];
+    }
 }
 
 struct ReduceArgs {
@@ -668,25 +687,54 @@ __global__ __launch_bounds__(256) void mod_reduce_w_kernel(ReduceArgs a) {
   if (blk == 4 && n >= a.H) return;
   const float *src = a.w_part + (long long)blk * a.slices * CH * CH + mn;
   float s = 0.f;
+#pragma unroll 8
   for (int sl = 0; sl < a.slices; ++sl) s += src[(long long)sl * CH * CH];
   if (blk < 4) a.dw_qkvg[m * 4 * CH + blk * CH + n] = s;
   else if (blk == 4) a.dw_bias[m * a.H + n] = s;
   else a.dw_out[m * CH + n] = s;
 }
 
-// One workgroup (64 threads) per LayerNorm parameter gradient element: thread i sums the
-// tiles' partials of its contiguous share in tile order, then the 64 sums are combined
-// by a fixed butterfly.
-__global__ __launch_bounds__(64) void mod_reduce_ln_kernel(ReduceArgs a) {
-  const int e = blockIdx.x;  // 0..255: scale gradients, then offset gradients
-  const int i = threadIdx.x;
-  const int t0 = (int)((long long)i * a.tiles / 64), t1 = (int)((long long)(i + 1) * a.tiles / 64);
+// LayerNorm parameter gradients from the per-tile partials part[tile][256] (scale
+// gradient in elements 0..127, offset gradient in 128..255) of one or two LayerNorms, in
+// two fixed-order stages.  Stage 1, workgroup (group g, LayerNorm l), thread k: the sum
+// over the tiles of group g (G contiguous groups) in tile order, to scratch[l][g][k].
+__global__ __launch_bounds__(256) void ln_reduce1_kernel(const float *part0, const float *part1, float *scratch,
+                                                          int tiles, int groups) {
+  const int g = blockIdx.x, l = blockIdx.y, k = threadIdx.x;
+  const float *part = l ? part1 : part0;
+  const int t0 = (int)((long long)g * tiles / groups), t1 = (int)((long long)(g + 1) * tiles / groups);
   float s = 0.f;
-  for (int t = t0; t < t1; ++t) s += a.ln_part[(long long)t * 2 * CH + e];
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) s += __shfl_xor(s, d);
-  if (i == 0) (e < CH ? a.d_ln_w : a.d_ln_b)[e & 127] = s;
+#pragma unroll 8
+  for (int t = t0; t < t1; ++t) s += part[(long long)t * 2 * CH + k];
+  scratch[((long long)l * groups + g) * 2 * CH + k] = s;
 }
+
+// Stage 2, workgroup = 64 of the 256 L outputs, thread (element kk = tid % 64, quarter
+// q = tid / 64 of the groups): the quarter's groups in order, then the four quarters in
+// order; element k of LayerNorm l to (k < 128 ? w_l : b_l)[k % 128].
+__global__ __launch_bounds__(256) void ln_reduce2_kernel(const float *scratch, int groups, float *w0, float *b0,
+                                                          float *w1, float *b1) {
+  __shared__ float sq[4][64];
+  const int kk = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int e = 64 * blockIdx.x + kk, l = e >> 8, k = e & 255;
+  const float *src = scratch + (long long)l * groups * 2 * CH + k;
+  const int g0 = q * groups / 4, g1 = (q + 1) * groups / 4;
+  float s = 0.f;
+#pragma unroll 8
+  for (int g = g0; g < g1; ++g) s += src[(long long)g * 2 * CH];
+  sq[q][kk] = s;
+  __syncthreads();
+  if (q == 0) {
+    const float v = ((sq[0][kk] + sq[1][kk]) + sq[2][kk]) + sq[3][kk];
+    float *dst = l ? (k < CH ? w1 : b1) : (k < CH ? w0 : b0);
+    dst[k & 127] = v;
+  }
+}
+
+// Groups of the first stage (a fixed number: results do not depend on the device); its
+// scratch, kLnGroups x 256 floats per LayerNorm, is the weight gradients' slice
+// partials, already reduced when the stage runs.
+constexpr int kLnGroups = 64;
 
 // ------------------------------------------------------------------------------------
 // Triangle multiplicative update block around the contraction (tri_mul_module.h)
@@ -729,13 +777,15 @@ __device__ __forceinline__ long long cm_tile(const TmbArgs &a, long long p0) {
   return b * CH * a.NN + (p0 - b * a.NN);
 }
 // the [128 channel][128 position] block of a channel-major tensor into an LDS tile, and back
+template <int T = NT>
 __device__ __forceinline__ void load_cm(uint16_t *tile, const uint16_t *src, long long nn, int tid) {
-  load_block(tile, src, nn, tid);
+  load_block<T>(tile, src, nn, tid);
 }
+template <int T = NT>
 __device__ __forceinline__ void store_rows(const uint16_t *tile, uint16_t *dst, long long ld, int tid) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int p = tid + NT * i, row = p >> 4, c = (p & 15) * 8;
+  for (int i = 0; i < 2048 / T; ++i) {
+    const int p = tid + T * i, row = p >> 4, c = (p & 15) * 8;
     *(u32x4 *)(dst + (long long)row * ld + c) = *(const u32x4 *)(tile + toff(row, c));
   }
 }
@@ -907,17 +957,19 @@ __global__ __launch_bounds__(NT, 2) void tmb_out_kernel(TmbArgs a) {
   }
 }
 
-// Column sums over the tile's 128 positions of an fp32 foff tile, in position order
-// (thread -> channel tid % 128, half tid / 128, then lower + upper half): channel c's
-// sum to dst[c].  Ends with the workgroup synchronised.
-__device__ __forceinline__ void column_sums(const float *t32, float (*s_half)[CH], int slot, float *dst, int tid) {
-  const int c = tid & 127, hp = tid >> 7;
+constexpr int NT8 = 512;  // threads of the 8-wave kernels (two waves per SIMD)
+
+// Column sums over the tile's 128 positions of an fp32 foff tile by 512 threads (thread
+// -> channel tid % 128, quarter tid / 128 of the positions in order, then the quarters
+// in order): channel c's sum to dst[c].  Ends with the workgroup synchronised.
+__device__ __forceinline__ void column_sums8(const float *t32, float (*s_part)[CH], float *dst, int tid) {
+  const int c = tid & 127, q = tid >> 7;
   float sum = 0.f;
 #pragma unroll 16
-  for (int r = 64 * hp; r < 64 * hp + 64; ++r) sum += t32[foff(r, c)];
-  if (hp) s_half[slot][c] = sum;
+  for (int r = 32 * q; r < 32 * q + 32; ++r) sum += t32[foff(r, c)];
+  s_part[q][c] = sum;
   __syncthreads();
-  if (!hp) dst[c] = sum + s_half[slot][c];
+  if (q == 0) dst[c] = ((s_part[0][c] + s_part[1][c]) + s_part[2][c]) + s_part[3][c];
   __syncthreads();
 }
 
@@ -925,86 +977,94 @@ __device__ __forceinline__ void column_sums(const float *t32, float (*s_half)[CH
 //   yp = xn Wo (recomputed), dyp = dy g, dgp = dy yp g (1 - g), dxn = dyp Wo^T,
 //   dx = LayerNorm_out backward of dxn (channel-major), and the tile's column sums of
 //   dxn xhat and dxn.
-__global__ __launch_bounds__(NT, 1) void tmb_out_bwd_kernel(TmbArgs a) {
-  __shared__ __attribute__((aligned(16))) float lds[TP * CH];  // sA | sB, or an fp32 tile
-  __shared__ __attribute__((aligned(16))) uint16_t sD[TP * CH];  // dyp [position][channel], then dx^T
-  __shared__ __attribute__((aligned(16))) uint16_t sX[TP * CH];  // x [channel][position]
-  __shared__ float s_half[2][CH];
-  uint16_t *sA = (uint16_t *)lds, *sB = sA + TP * CH;
+// 8 waves (two per SIMD), each owning 32 x 64 of the products.  Every input of the tile
+// (xn, Wo, g, dy and x) is fetched at the start; one Wo tile serves both products
+// (transposed reads for yp, row reads for dxn), and the gate's element-wise step runs
+// in the accumulator layout against g and dy tiles in LDS, overwriting them in place
+// with dgp and dyp.
+__global__ __launch_bounds__(NT8, 1) void tmb_out_bwd_kernel(TmbArgs a) {
+  __shared__ __attribute__((aligned(16))) float lds[TP * CH];  // xn | g (then dgp), or an fp32 tile
+  __shared__ __attribute__((aligned(16))) uint16_t sB[CH * CH];  // Wo
+  __shared__ __attribute__((aligned(16))) uint16_t sR[TP * CH];  // dy (then dyp), then x^T (then dx^T)
+  __shared__ float s_part[4][CH];
+  uint16_t *sA = (uint16_t *)lds, *sG = sA + TP * CH;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, ll = lane & 31;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const long long p0 = (long long)tile * TP;
   const long long cm = cm_tile(a, p0);
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  load_block(sA, a.xn + p0 * CH, CH, tid);
-  load_block(sB, a.w_out, CH, tid);
-  load_cm(sX, a.x + cm, a.NN, tid);
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 64;
+  u32x4 rxn[4], rw[4], rg[4], rdy[4], rx[4];
+  fetch_block<NT8>(rxn, a.xn + p0 * CH, CH, tid);
+  fetch_block<NT8>(rw, a.w_out, CH, tid);
+  fetch_block<NT8>(rg, a.g + p0 * CH, CH, tid);
+  fetch_block<NT8>(rdy, a.dy + p0 * CH, CH, tid);
+  fetch_block<NT8>(rx, a.x + cm, a.NN, tid);
+  put_block<NT8>(sA, rxn, tid);
+  put_block<NT8>(sB, rw, tid);
+  put_block<NT8>(sG, rg, tid);
+  put_block<NT8>(sR, rdy, tid);
   __syncthreads();
-  f32x16 acc[2][2];
-  zero(acc);
-  tile_product<ROW, TR>(sA, sB, wm, wn, lane, CH / 16, acc);  // yp
-  __syncthreads();
-  stage_f32(lds, acc, wm, wn, lane, [](float x) { return x; });
-  __syncthreads();
+  f32x16 acc[1][2];
+  zero<1>(acc);
+  tile_product<ROW, TR, 1>(sA, sB, wm, wn, lane, CH / 16, acc);  // yp
+  // element (m, n) of g and dy is read and overwritten by the lane that holds yp there
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
-    const long long off = (p0 + row) * CH + c;
-    float yp[8], gv[8], d[8], dyp[8], dgp[8];
-    read8_f32(lds, row, c, yp);
-    unpack8(*(const u32x4 *)(a.g + off), gv);
-    unpack8(*(const u32x4 *)(a.dy + off), d);
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      dyp[e] = d[e] * gv[e];
-      dgp[e] = d[e] * yp[e] * gv[e] * (1.f - gv[e]);
+    for (int r = 0; r < 16; ++r) {
+      const int m = wm + 8 * (r >> 2) + 4 * hh + (r & 3), n = wn + 32 * j + ll;
+      const float gv = bf_lo(sG[toff(m, n)]), d = bf_lo(sR[toff(m, n)]);
+      sR[toff(m, n)] = bf16_of(d * gv);
+      sG[toff(m, n)] = bf16_of(d * acc[0][j][r] * gv * (1.f - gv));
     }
-    const u32x4 q = pack8u(dyp);
-    *(u32x4 *)(sD + toff(row, c)) = q;
-    *(u32x4 *)(a.dyp + off) = q;
-    *(u32x4 *)(a.dgp + off) = pack8u(dgp);
-  }
   __syncthreads();
-  load_block(sB, a.w_out, CH, tid);  // read as rows: B(t = c_out, n = c_in) = Wo[c_in][c_out]
-  __syncthreads();
-  zero(acc);
-  tile_product<ROW, ROW>(sD, sB, wm, wn, lane, CH / 16, acc);  // dxn
-  __syncthreads();
-  stage_f32(lds, acc, wm, wn, lane, [](float x) { return x; });
+  store_rows<NT8>(sR, a.dyp + p0 * CH, CH, tid);
+  store_rows<NT8>(sG, a.dgp + p0 * CH, CH, tid);
+  zero<1>(acc);
+  tile_product<ROW, ROW, 1>(sR, sB, wm, wn, lane, CH / 16, acc);  // dxn: B(t = c_out, n = c_in) = Wo[c_in][c_out]
+  __syncthreads();  // dyp and dgp read; the operand tiles are free
+  put_block<NT8>(sR, rx, tid);  // x [channel][position]
+  stage_f32<1>(lds, acc, wm, wn, lane, [](float x) { return x; });
   __syncthreads();
   float *part = a.ln_out_part + (long long)tile * 2 * CH;
-  column_sums(lds, s_half, 1, part + CH, tid);  // sum of dxn: the offset gradient's partial
+  column_sums8(lds, s_part, part + CH, tid);  // sum of dxn: the offset gradient's partial
   {
-    const int pr = tid >> 1, c0 = 64 * (tid & 1);
+    // thread -> position tid / 4, channels 32 (tid % 4) .. + 31
+    const int pr = tid >> 2, c0 = 32 * (tid & 3);
     const f32x2 st = *(const f32x2 *)(a.stats_out + 2 * (p0 + pr));
     const float mean = st[0], rstd = st[1];
     float s1 = 0.f, s2 = 0.f;
-    float dx[64], xh[64];
+    float dx[32], xh[32];
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
+    for (int i = 0; i < 32; ++i) {
       const int c = c0 + i;
       const float d = lds[foff(pr, c)];
-      xh[i] = (bf_lo(sX[toff(c, pr)]) - mean) * rstd;
+      xh[i] = (bf_lo(sR[toff(c, pr)]) - mean) * rstd;
       dx[i] = d * a.ln_out_w[c];
       s1 += dx[i];
       s2 = fmaf(dx[i], xh[i], s2);
       lds[foff(pr, c)] = d * xh[i];  // dxn * xhat, in place, for the scale gradient
     }
+    // the four quarters of the position: (q0 + q1) + (q2 + q3) on all four lanes
     s1 += __shfl_xor(s1, 1);
     s2 += __shfl_xor(s2, 1);
+    s1 += __shfl_xor(s1, 2);
+    s2 += __shfl_xor(s2, 2);
     const float m1 = s1 * (1.f / CH), m2 = s2 * (1.f / CH);
 #pragma unroll
-    for (int i = 0; i < 64; ++i) sD[toff(c0 + i, pr)] = bf16_of(rstd * (dx[i] - m1 - xh[i] * m2));
+    for (int i = 0; i < 32; ++i) sR[toff(c0 + i, pr)] = bf16_of(rstd * (dx[i] - m1 - xh[i] * m2));
   }
   __syncthreads();
-  column_sums(lds, s_half, 0, part, tid);  // sum of dxn * xhat
-  store_rows(sD, a.dx + cm, a.NN, tid);
+  column_sums8(lds, s_part, part, tid);  // sum of dxn * xhat
+  store_rows<NT8>(sR, a.dx + cm, a.NN, tid);
 }
 
 // Backward, part 2: the gated projections' gradients from da and db (channel-major),
 //   d(ap) = da sigmoid(ag) m,  d(ag) = da ap m sigmoid(ag) (1 - sigmoid(ag))   (b likewise)
-// with ag, ap, bg, bp recomputed from zn; stored channel-major.
-__global__ __launch_bounds__(NT, 1) void tmb_grad_proj_kernel(TmbArgs a) {
+// with ag, ap, bg, bp recomputed from zn; stored channel-major.  8 waves, each owning
+// 32 x 64 of the products.
+__global__ __launch_bounds__(NT8, 1) void tmb_grad_proj_kernel(TmbArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[TP * CH];  // zn
   __shared__ __attribute__((aligned(16))) uint16_t sB[CH * CH];  // weights, then d(proj)
   __shared__ __attribute__((aligned(16))) uint16_t sT[CH * TP];  // da, then d(gate)
@@ -1012,86 +1072,128 @@ __global__ __launch_bounds__(NT, 1) void tmb_grad_proj_kernel(TmbArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long long p0 = (long long)xcd_remap(blockIdx.x, gridDim.x) * TP;
   const long long cm = cm_tile(a, p0);
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64, hh = lane >> 5, ll = lane & 31;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 64, hh = lane >> 5, ll = lane & 31;
   if (tid < TP) s_m[tid] = a.mask ? (a.mask[p0 + tid] ? 1.f : 0.f) : 1.f;
-  load_block(sA, a.zn + p0 * CH, CH, tid);
-  f32x16 acc_g[2][2], acc_p[2][2];
-#pragma unroll 1
+  // the operands of pair pr (the gate and projection weight blocks and da or db) are
+  // fetched one pair ahead: pair 1's loads are in flight while pair 0 computes
+  u32x4 rz[4], rwg[4], rwp[4], rd[4];
+  fetch_block<NT8>(rz, a.zn + p0 * CH, CH, tid);
+  fetch_block<NT8>(rwg, a.w_in, 5 * CH, tid);
+  fetch_block<NT8>(rwp, a.w_in + CH, 5 * CH, tid);
+  fetch_block<NT8>(rd, a.da + cm, a.NN, tid);
+  put_block<NT8>(sA, rz, tid);
+  f32x16 acc_g[1][2], acc_p[1][2];
+#pragma unroll
   for (int pr = 0; pr < 2; ++pr) {
-    if (pr) __syncthreads();
-    load_block(sB, a.w_in + 2 * pr * CH, 5 * CH, tid);  // the gate block
+    if (pr) __syncthreads();  // the previous pair's results are stored
+    put_block<NT8>(sB, rwg, tid);  // the gate block
     __syncthreads();
-    zero(acc_g);
-    tile_product<ROW, TR>(sA, sB, wm, wn, lane, CH / 16, acc_g);
+    zero<1>(acc_g);
+    tile_product<ROW, TR, 1>(sA, sB, wm, wn, lane, CH / 16, acc_g);
     __syncthreads();
-    load_block(sB, a.w_in + (2 * pr + 1) * CH, 5 * CH, tid);  // the projection block
-    load_cm(sT, (pr ? a.db : a.da) + cm, a.NN, tid);
+    put_block<NT8>(sB, rwp, tid);  // the projection block
+    put_block<NT8>(sT, rd, tid);
     __syncthreads();
-    zero(acc_p);
-    tile_product<ROW, TR>(sA, sB, wm, wn, lane, CH / 16, acc_p);
+    if (pr == 0) {
+      fetch_block<NT8>(rwg, a.w_in + 2 * CH, 5 * CH, tid);
+      fetch_block<NT8>(rwp, a.w_in + 3 * CH, 5 * CH, tid);
+      fetch_block<NT8>(rd, a.db + cm, a.NN, tid);
+    }
+    zero<1>(acc_p);
+    tile_product<ROW, TR, 1>(sA, sB, wm, wn, lane, CH / 16, acc_p);
     __syncthreads();  // sB is free for d(proj)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int m = wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3), n = wn + 32 * j + ll;
-          const float d = bf_lo(sT[toff(n, m)]) * s_m[m];
-          const float sg = sigmoidf_(acc_g[i][j][r]);
-          sT[toff(n, m)] = bf16_of(d * acc_p[i][j][r] * sg * (1.f - sg));
-          sB[toff(n, m)] = bf16_of(d * sg);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int m = wm + 8 * (r >> 2) + 4 * hh + (r & 3), n = wn + 32 * j + ll;
+        const float d = bf_lo(sT[toff(n, m)]) * s_m[m];
+        const float sg = sigmoidf_(acc_g[0][j][r]);
+        sT[toff(n, m)] = bf16_of(d * acc_p[0][j][r] * sg * (1.f - sg));
+        sB[toff(n, m)] = bf16_of(d * sg);
+      }
     __syncthreads();
-    store_rows(sT, (pr ? a.dbg : a.dag) + cm, a.NN, tid);
-    store_rows(sB, (pr ? a.dbp : a.dap) + cm, a.NN, tid);
+    store_rows<NT8>(sT, (pr ? a.dbg : a.dag) + cm, a.NN, tid);
+    store_rows<NT8>(sB, (pr ? a.dbp : a.dap) + cm, a.NN, tid);
   }
 }
 
 // Backward, part 3: dzn = [d(ag) d(ap) d(bg) d(bp) dgp] Win^T (five 128-deep blocks), the
 // LayerNorm_in backward to dz and the tile's column sums of dzn xhat and dzn.
-__global__ __launch_bounds__(NT, 1) void tmb_in_bwd_kernel(TmbArgs a) {
+// 8 waves (two per SIMD), each owning 32 x 64 of dzn.  A block's operands (the gradient
+// tile and the weight block, 64 KB) travel as 16-byte pieces in registers: the loads of
+// blocks b + 1 and b + 2 are in flight while block b's products run, and z for the
+// LayerNorm backward while the last one's do.
+__global__ __launch_bounds__(NT8, 1) void tmb_in_bwd_kernel(TmbArgs a) {
   // [sA | sB] operands, then the dzn * xhat fp32 tile; the dzn fp32 tile
   __shared__ __attribute__((aligned(16))) float lds0[TP * CH];
   __shared__ __attribute__((aligned(16))) float lds1[TP * CH];
-  __shared__ float s_half[2][CH];
+  __shared__ float s_part[4][CH];
   uint16_t *sA = (uint16_t *)lds0, *sB = sA + TP * CH;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const long long p0 = (long long)tile * TP;
   const long long cm = cm_tile(a, p0);
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  f32x16 dzn[2][2];
-  zero(dzn);
-#pragma unroll 1
-  for (int blk = 0; blk < 5; ++blk) {
-    if (blk) __syncthreads();
-    load_block(sB, a.w_in + blk * CH, 5 * CH, tid);  // read as rows: B(t = out, n = c_in)
-    if (blk < 4) {
-      const uint16_t *src = blk == 0 ? a.dag : blk == 1 ? a.dap : blk == 2 ? a.dbg : a.dbp;
-      load_cm(sA, src + cm, a.NN, tid);  // [channel][position]
-      __syncthreads();
-      tile_product<TR, ROW>(sA, sB, wm, wn, lane, CH / 16, dzn);
-    } else {
-      load_block(sA, a.dgp + p0 * CH, CH, tid);  // [position][channel]
-      __syncthreads();
-      tile_product<ROW, ROW>(sA, sB, wm, wn, lane, CH / 16, dzn);
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 64;
+  // block blk: A = d(ag), d(ap), d(bg), d(bp) ([channel][position], read transposed) or
+  // dgp ([position][channel]); B(t = out, n = c_in) = Win[c_in][128 blk + t] (rows)
+  auto fetch = [&](int blk, u32x4 (&r)[8]) {
+    const uint16_t *src = blk == 0 ? a.dag + cm : blk == 1 ? a.dap + cm : blk == 2 ? a.dbg + cm
+                        : blk == 3 ? a.dbp + cm : a.dgp + p0 * CH;
+    const long long ld = blk < 4 ? a.NN : CH;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pc = tid + NT8 * i, row = pc >> 4, c = (pc & 15) * 8;
+      r[i] = *(const u32x4 *)(src + (long long)row * ld + c);
+      r[4 + i] = *(const u32x4 *)(a.w_in + (long long)row * 5 * CH + blk * CH + c);
     }
+  };
+  auto put = [&](const u32x4 (&r)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pc = tid + NT8 * i, row = pc >> 4, c = (pc & 15) * 8;
+      *(u32x4 *)(sA + toff(row, c)) = r[i];
+      *(u32x4 *)(sB + toff(row, c)) = r[4 + i];
+    }
+  };
+  // per position in the LayerNorm backward: thread -> position tid / 4, channels
+  // 32 (tid % 4) .. + 31
+  const int pr = tid >> 2, c0 = 32 * (tid & 3);
+  u32x4 r0[8], r1[8], zr[4];
+  f32x16 dzn[1][2];
+  zero<1>(dzn);
+  fetch(0, r0);
+  fetch(1, r1);
+#pragma unroll
+  for (int blk = 0; blk < 5; ++blk) {
+    if (blk) __syncthreads();  // the previous block's operands are consumed
+    if (blk & 1) put(r1);
+    else put(r0);
+    __syncthreads();
+    if (blk + 2 < 5) {
+      if (blk & 1) fetch(blk + 2, r1);
+      else fetch(blk + 2, r0);
+    }
+    if (blk == 3) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zr[i] = *(const u32x4 *)(a.z + (p0 + pr) * CH + c0 + 8 * i);
+    }
+    if (blk < 4) tile_product<TR, ROW, 1>(sA, sB, wm, wn, lane, CH / 16, dzn);
+    else tile_product<ROW, ROW, 1>(sA, sB, wm, wn, lane, CH / 16, dzn);
   }
   float *t_dzn = lds1, *t_dx = lds0;
-  stage_f32(t_dzn, dzn, wm, wn, lane, [](float x) { return x; });
+  stage_f32<1>(t_dzn, dzn, wm, wn, lane, [](float x) { return x; });
   __syncthreads();  // dzn staged, the operand tiles consumed
   float *part = a.ln_in_part + (long long)tile * 2 * CH;
   {
-    const int pr = tid >> 1, c0 = 64 * (tid & 1);
     const f32x2 st = *(const f32x2 *)(a.stats_in + 2 * (p0 + pr));
     const float mean = st[0], rstd = st[1];
     float s1 = 0.f, s2 = 0.f;
-    float dx[64], xh[64];
+    float dx[32], xh[32];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       float zv[8], d[8], dxh[8];
-      unpack8(*(const u32x4 *)(a.z + (p0 + pr) * CH + c0 + 8 * i), zv);
+      unpack8(zr[i], zv);
       read8_f32(t_dzn, pr, c0 + 8 * i, d);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -1105,11 +1207,15 @@ __global__ __launch_bounds__(NT, 1) void tmb_in_bwd_kernel(TmbArgs a) {
       *(f32x4 *)(t_dx + foff(pr, c0 + 8 * i)) = (f32x4){dxh[0], dxh[1], dxh[2], dxh[3]};
       *(f32x4 *)(t_dx + foff(pr, c0 + 8 * i + 4)) = (f32x4){dxh[4], dxh[5], dxh[6], dxh[7]};
     }
+    // the four quarters of the position: (q0 + q1) + (q2 + q3), the same value on all
+    // four lanes
     s1 += __shfl_xor(s1, 1);
     s2 += __shfl_xor(s2, 1);
+    s1 += __shfl_xor(s1, 2);
+    s2 += __shfl_xor(s2, 2);
     const float m1 = s1 * (1.f / CH), m2 = s2 * (1.f / CH);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       float o[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = rstd * (dx[8 * i + e] - m1 - xh[8 * i + e] * m2);
@@ -1117,51 +1223,63 @@ __global__ __launch_bounds__(NT, 1) void tmb_in_bwd_kernel(TmbArgs a) {
     }
   }
   __syncthreads();
-  column_sums(t_dx, s_half, 0, part, tid);
-  column_sums(t_dzn, s_half, 1, part + CH, tid);
+  column_sums8(t_dx, s_part, part, tid);
+  column_sums8(t_dzn, s_part, part + CH, tid);
 }
 
-// Weight gradients of the block: workgroup = (output block, slice of tiles),
-//   blocks 0..3: zn^T d(ag), d(ap), d(bg), d(bp)   (CMB: the gradients channel-major)
-//   block 4:     zn^T dgp
-//   block 5:     xn^T dyp                           (d Wo)
-// launched once with CMB for blocks 0..3 and once without for blocks 4 and 5.
-template <bool CMB>
-__global__ __launch_bounds__(NT, 2) void tmb_wgrad_kernel(TmbArgs a) {
+// Weight gradients of the block: workgroup = (slice of tiles, output block), 8 waves
+// each owning 32 x 64 of the 128 x 128 block; out[m][n] = sum over the slice's positions
+// p of A[p][m] B[p][n] with
+//   blocks 0..3: A = zn, B = d(ag), d(ap), d(bg), d(bp)   (B channel-major)
+//   block 4:     A = zn, B = dgp
+//   block 5:     A = xn, B = dyp                           (d Wo)
+// A tile's operands are fetched into registers a tile ahead.  The six blocks of a slice
+// are neighbouring workgroups on one XCD, so each zn tile comes from HBM about once.
+__global__ __launch_bounds__(NT8, 4) void tmb_wgrad_kernel(TmbArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[TP * CH];
   __shared__ __attribute__((aligned(16))) uint16_t sB[TP * CH];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int nb = CMB ? 4 : 2;
-  const int blk = t % nb + (CMB ? 0 : 4), slice = t / nb;
+  const int blk = t % 6, slice = t / 6;
   const int t0 = (int)((long long)slice * a.tiles / a.slices), t1 = (int)((long long)(slice + 1) * a.tiles / a.slices);
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 64;
   const uint16_t *asrc = blk < 5 ? a.zn : a.xn;
   const uint16_t *bsrc = blk == 0 ? a.dag : blk == 1 ? a.dap : blk == 2 ? a.dbg : blk == 3 ? a.dbp
                        : blk == 4 ? a.dgp : a.dyp;
-  f32x16 acc[2][2];
-  zero(acc);
+  f32x16 acc[1][2];
+  zero<1>(acc);
+  // one copy of the loop per B layout: [channel n][position t] (CMB) or [position t][channel n]
+  auto run = [&](auto cmb_tag) {
+    constexpr bool CMB = decltype(cmb_tag)::value;
+    u32x4 ra[4], rb[4];
+    auto fetch = [&](int tile) {
+      const long long p0 = (long long)tile * TP;
+      fetch_block<NT8>(ra, asrc + p0 * CH, CH, tid);
+      if (CMB) fetch_block<NT8>(rb, bsrc + cm_tile(a, p0), a.NN, tid);
+      else fetch_block<NT8>(rb, bsrc + p0 * CH, CH, tid);
+    };
+    fetch(t0);
 #pragma unroll 1
-  for (int tile = t0; tile < t1; ++tile) {
-    const long long p0 = (long long)tile * TP;
-    if (tile > t0) __syncthreads();
-    load_block(sA, asrc + p0 * CH, CH, tid);
-    if (CMB) load_cm(sB, bsrc + cm_tile(a, p0), a.NN, tid);  // [channel n][position t]
-    else load_block(sB, bsrc + p0 * CH, CH, tid);            // [position t][channel n]
-    __syncthreads();
-    tile_product<TR, CMB ? ROW : TR>(sA, sB, wm, wn, lane, TP / 16, acc);
-  }
+    for (int tile = t0; tile < t1; ++tile) {
+      if (tile > t0) __syncthreads();  // the previous tile's operands are consumed
+      put_block<NT8>(sA, ra, tid);
+      put_block<NT8>(sB, rb, tid);
+      __syncthreads();
+      fetch(min(tile + 1, t1 - 1));  // in flight during the products (the last tile again at the end)
+      tile_product<TR, CMB ? ROW : TR, 1>(sA, sB, wm, wn, lane, TP / 16, acc);
+    }
+  };
+  if (blk < 4) run(std::true_type{});
+  else run(std::false_type{});
   float *dst = a.w_part + ((long long)blk * a.slices + slice) * CH * CH;
   const int hh = lane >> 5, ll = lane & 31;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = wm + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3), n = wn + 32 * j + ll;
-        dst[m * CH + n] = acc[i][j][r];
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int m = wm + 8 * (r >> 2) + 4 * hh + (r & 3), n = wn + 32 * j + ll;
+      dst[m * CH + n] = acc[0][j][r];
+    }
 }
 
 struct TmbReduceArgs {
@@ -1176,25 +1294,10 @@ __global__ __launch_bounds__(256) void tmb_reduce_w_kernel(TmbReduceArgs a) {
   const int blk = e / (CH * CH), mn = e - blk * CH * CH, m = mn >> 7, n = mn & 127;
   const float *src = a.w_part + (long long)blk * a.slices * CH * CH + mn;
   float s = 0.f;
+#pragma unroll 8
   for (int sl = 0; sl < a.slices; ++sl) s += src[(long long)sl * CH * CH];
   if (blk < 5) a.dw_in[m * 5 * CH + blk * CH + n] = s;
   else a.dw_out[m * CH + n] = s;
-}
-
-// 512 outputs: the input LayerNorm's scale and offset gradients, then the output one's
-__global__ __launch_bounds__(64) void tmb_reduce_ln_kernel(TmbReduceArgs a) {
-  const int e = blockIdx.x, which = e >> 8, k = e & 255;
-  const float *part = which ? a.ln_out_part : a.ln_in_part;
-  const int i = threadIdx.x;
-  const int t0 = (int)((long long)i * a.tiles / 64), t1 = (int)((long long)(i + 1) * a.tiles / 64);
-  float s = 0.f;
-  for (int t = t0; t < t1; ++t) s += part[(long long)t * 2 * CH + k];
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) s += __shfl_xor(s, d);
-  if (i == 0) {
-    float *dst = which ? (k < CH ? a.d_ln_out_w : a.d_ln_out_b) : (k < CH ? a.d_ln_in_w : a.d_ln_in_b);
-    dst[k & 127] = s;
-  }
 }
 
 // ------------------------------------------------------------------------------------
@@ -1257,7 +1360,10 @@ ModArgs base_args(const tri_attn_module_problem *p) {
   return a;
 }
 
-int wgrad_slices(int tiles) { return tiles < 64 ? tiles : 64; }
+// Slices of the weight gradients: 6 x 85 = 510 workgroups, one round at two 8-wave
+// workgroups per CU on a 256-CU device (a fixed number, so results do not depend on the
+// device).
+int wgrad_slices(int tiles) { return tiles < 85 ? tiles : 85; }
 
 struct BwdLayout {
   size_t off_do, off_dgp, off_dq, off_dk, off_dv, off_db, off_core, off_w, off_ln, total;
@@ -1447,18 +1553,16 @@ tri_attn_status tri_mul_module_bwd(const tri_mul_module_problem *problem, const 
   a.w_part = (float *)(ws + l.off_w);
   a.ln_in_part = (float *)(ws + l.off_lni);
   a.ln_out_part = (float *)(ws + l.off_lno);
-  hipLaunchKernelGGL(tmb_out_bwd_kernel, dim3((unsigned)a.tiles), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL(tmb_out_bwd_kernel, dim3((unsigned)a.tiles), dim3(NT8), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
   const tri_mul_problem mp = tmb_contraction(problem);
   st = tri_mul_bwd(&mp, saved->a, saved->b, a.dx, ws + l.off_da, ws + l.off_db, stream);
   if (st != TRI_ATTN_SUCCESS) return st;
-  hipLaunchKernelGGL(tmb_grad_proj_kernel, dim3((unsigned)a.tiles), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL(tmb_grad_proj_kernel, dim3((unsigned)a.tiles), dim3(NT8), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
-  hipLaunchKernelGGL(tmb_in_bwd_kernel, dim3((unsigned)a.tiles), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL(tmb_in_bwd_kernel, dim3((unsigned)a.tiles), dim3(NT8), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
-  hipLaunchKernelGGL(tmb_wgrad_kernel<true>, dim3((unsigned)(4 * a.slices)), dim3(NT), 0, stream, a);
-  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
-  hipLaunchKernelGGL(tmb_wgrad_kernel<false>, dim3((unsigned)(2 * a.slices)), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL(tmb_wgrad_kernel, dim3((unsigned)(6 * a.slices)), dim3(NT8), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
   TmbReduceArgs r;
   r.w_part = a.w_part;
@@ -1474,7 +1578,11 @@ tri_attn_status tri_mul_module_bwd(const tri_mul_module_problem *problem, const 
   r.tiles = a.tiles;
   hipLaunchKernelGGL(tmb_reduce_w_kernel, dim3((6 * CH * CH + 255) / 256), dim3(256), 0, stream, r);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
-  hipLaunchKernelGGL(tmb_reduce_ln_kernel, dim3(4 * CH), dim3(64), 0, stream, r);
+  hipLaunchKernelGGL(ln_reduce1_kernel, dim3(kLnGroups, 2), dim3(256), 0, stream, r.ln_in_part, r.ln_out_part,
+                     a.w_part, a.tiles, kLnGroups);
+  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  hipLaunchKernelGGL(ln_reduce2_kernel, dim3(8), dim3(256), 0, stream, (const float *)a.w_part, kLnGroups,
+                     r.d_ln_in_w, r.d_ln_in_b, r.d_ln_out_w, r.d_ln_out_b);
   return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH_FAILED;
 }
 
@@ -1604,7 +1712,7 @@ tri_attn_status tri_attn_module_bwd(const tri_attn_module_problem *problem, cons
   if (st != TRI_ATTN_SUCCESS) return st;
   hipLaunchKernelGGL(mod_in_bwd_kernel, dim3((unsigned)a.tiles), dim3(NT), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
-  hipLaunchKernelGGL(mod_wgrad_kernel, dim3((unsigned)(6 * a.slices)), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL(mod_wgrad_kernel, dim3((unsigned)(6 * a.slices)), dim3(NT8M), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
   ReduceArgs r;
   r.w_part = a.w_part;
@@ -1619,7 +1727,11 @@ tri_attn_status tri_attn_module_bwd(const tri_attn_module_problem *problem, cons
   r.tiles = a.tiles;
   hipLaunchKernelGGL(mod_reduce_w_kernel, dim3((6 * CH * CH + 255) / 256), dim3(256), 0, stream, r);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
-  hipLaunchKernelGGL(mod_reduce_ln_kernel, dim3(2 * CH), dim3(64), 0, stream, r);
+  hipLaunchKernelGGL(ln_reduce1_kernel, dim3(kLnGroups, 1), dim3(256), 0, stream, r.ln_part, r.ln_part, a.w_part,
+                     a.tiles, kLnGroups);
+  if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
+  hipLaunchKernelGGL(ln_reduce2_kernel, dim3(4), dim3(256), 0, stream, (const float *)a.w_part, kLnGroups, r.d_ln_w,
+                     r.d_ln_b, r.d_ln_w, r.d_ln_b);
   return hipGetLastError() == hipSuccess ? TRI_ATTN_SUCCESS : TRI_ATTN_ERROR_LAUNCH_FAILED;
 }
 
