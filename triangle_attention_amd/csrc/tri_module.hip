@@ -226,6 +226,22 @@ __device__ __forceinline__ int xcd_remap(int L, int G) {
   return L;
 }
 
+constexpr int NT8 = 512;  // threads of the 8-wave kernels (two waves per SIMD)
+
+// Column sums over the tile's 128 positions of an fp32 foff tile by 512 threads (thread
+// -> channel tid % 128, quarter tid / 128 of the positions in order, then the quarters
+// in order): channel c's sum to dst[c].  Ends with the workgroup synchronised.
+__device__ __forceinline__ void column_sums8(const float *t32, float (*s_part)[CH], float *dst, int tid) {
+  const int c = tid & 127, q = tid >> 7;
+  float sum = 0.f;
+#pragma unroll 16
+  for (int r = 32 * q; r < 32 * q + 32; ++r) sum += t32[foff(r, c)];
+  s_part[q][c] = sum;
+  __syncthreads();
+  if (q == 0) dst[c] = ((s_part[0][c] + s_part[1][c]) + s_part[2][c]) + s_part[3][c];
+  __syncthreads();
+}
+
 struct ModArgs {
   // forward
   const uint16_t *z;
@@ -469,78 +485,96 @@ __global__ __launch_bounds__(NT, 2) void mod_out_bwd_kernel(ModArgs a) {
 //   dxhat = dzn * w,  dz = rstd (dxhat - mean(dxhat) - xhat mean(dxhat xhat)),
 // and the tile's sums over its positions of dzn * xhat and of dzn (partials of the
 // LayerNorm scale and offset gradients), each in position order.
-__global__ __launch_bounds__(NT, 1) void mod_in_bwd_kernel(ModArgs a) {
+// 8 waves (two per SIMD), each owning 32 x 64 of dzn.  A block's operands (the gradient
+// tile and the weight block, 64 KB) travel as 16-byte pieces in registers: the loads of
+// blocks b + 1 and b + 2 are in flight while block b's products run, and z for the
+// LayerNorm backward while the last ones do.
+__global__ __launch_bounds__(NT8, 1) void mod_in_bwd_kernel(ModArgs a) {
   // [0, 64 KB): the two operand tiles, then the fp32 tile of dzn * xhat;
   // [64, 128 KB): the fp32 tile of dzn
   __shared__ __attribute__((aligned(16))) float lds[2 * TP * CH];
+  __shared__ float s_part[4][CH];
   uint16_t *sA = (uint16_t *)lds, *sB = sA + TP * CH;
   float *s32 = lds + TP * CH, *sx = lds;
-  __shared__ float s_half[2][CH];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const long long p0 = (long long)tile * TP;
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  f32x16 acc[2][2];
-  zero(acc);
-  // block blk < 4 as 16-byte pieces: A = dq, dk, dv, dgp at the tile's positions, B(t,
-  // n = c_in) = Wqkvg[c_in][128 blk + t] (rows); the next block's are loaded while the
-  // current block's products run
-  u32x4 ra[8], rb[8];
-  auto fetch = [&](int blk) {
+  const int wm = (wave >> 1) * 32, wn = (wave & 1) * 64;
+  // block blk < 4: A = dq, dk, dv, dgp at the tile's positions, B(t, n = c_in) =
+  // Wqkvg[c_in][128 blk + t] (rows)
+  auto fetch = [&](int blk, u32x4 (&r)[8]) {
     const uint16_t *src = (blk == 0 ? a.dq : blk == 1 ? a.dk : blk == 2 ? a.dv : a.dgp) + p0 * CH;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
-      ra[i] = *(const u32x4 *)(src + (long long)row * CH + c);
-      rb[i] = *(const u32x4 *)(a.w_qkvg + (long long)row * 4 * CH + blk * CH + c);
+    for (int i = 0; i < 4; ++i) {
+      const int pc = tid + NT8 * i, row = pc >> 4, c = (pc & 15) * 8;
+      r[i] = *(const u32x4 *)(src + (long long)row * CH + c);
+      r[4 + i] = *(const u32x4 *)(a.w_qkvg + (long long)row * 4 * CH + blk * CH + c);
     }
   };
-  fetch(0);
-#pragma unroll 1
-  for (int blk = 0; blk < 5; ++blk) {
-    if (blk) __syncthreads();  // the previous block's operands are consumed
-    if (blk < 4) {
+  auto put = [&](const u32x4 (&r)[8]) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
-        *(u32x4 *)(sA + toff(row, c)) = ra[i];
-        *(u32x4 *)(sB + toff(row, c)) = rb[i];
-      }
-      if (blk + 1 < 4) fetch(blk + 1);
-    } else {
-      // A(position, t = head) = dbias at that position, rounded to bf16;
-      // B(t = head, n = c_in) = Wb[c_in][head]: rows; zeros beyond the H heads
-      const u32x4 z4 = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
-        *(u32x4 *)(sA + toff(row, c)) = z4;
-        *(u32x4 *)(sB + toff(row, c)) = z4;
-      }
-      __syncthreads();
-      const BiasTile bt(a, p0);
-      for (int e = tid; e < TP * a.H; e += NT) {
-        const int row = e / a.H, h = e - row * a.H;
-        sA[toff(row, h)] = (uint16_t)(pack_bf16(a.dbias[bt.at(row, h)], 0.f) & 0xffffu);
-        sB[toff(row, h)] = a.w_bias[e];  // row = input channel: Wb[c_in][h] is element c_in H + h
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int pc = tid + NT8 * i, row = pc >> 4, c = (pc & 15) * 8;
+      *(u32x4 *)(sA + toff(row, c)) = r[i];
+      *(u32x4 *)(sB + toff(row, c)) = r[4 + i];
     }
+  };
+  // per position in the LayerNorm backward: thread -> position tid / 4, channels
+  // 32 (tid % 4) .. + 31
+  const int pr = tid >> 2, c0 = 32 * (tid & 3);
+  u32x4 r0[8], r1[8], zr[4];
+  f32x16 acc[1][2];
+  zero<1>(acc);
+  fetch(0, r0);
+  fetch(1, r1);
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+    if (blk) __syncthreads();  // the previous block's operands are consumed
+    if (blk & 1) put(r1);
+    else put(r0);
     __syncthreads();
-    tile_product<ROW, ROW>(sA, sB, wm, wn, lane, blk < 4 ? CH / 16 : (a.H + 15) / 16, acc);
+    if (blk + 2 < 4) {
+      if (blk & 1) fetch(blk + 2, r1);
+      else fetch(blk + 2, r0);
+    }
+    if (blk == 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zr[i] = *(const u32x4 *)(a.z + (p0 + pr) * CH + c0 + 8 * i);
+    }
+    tile_product<ROW, ROW, 1>(sA, sB, wm, wn, lane, CH / 16, acc);
   }
-  stage_f32(s32, acc, wm, wn, lane, [](float x) { return x; });
-  __syncthreads();  // dzn staged; the operand tiles are free
-  // per position: thread -> position tid / 2, channels 64 (tid % 2) .. + 63
+  // block 4: A(position, t = head) = dbias at that position, rounded to bf16;
+  // B(t = head, n = c_in) = Wb[c_in][head]: rows; zeros beyond the H heads.  One 16-deep
+  // slice: only columns 0..15 of the two tiles are read.
+  __syncthreads();
+  if (tid < 256) {
+    const u32x4 z4 = {0u, 0u, 0u, 0u};
+    const int row = tid >> 1, c = (tid & 1) * 8;
+    *(u32x4 *)(sA + toff(row, c)) = z4;
+    *(u32x4 *)(sB + toff(row, c)) = z4;
+  }
+  __syncthreads();
   {
-    const int pr = tid >> 1, c0 = 64 * (tid & 1);
+    const BiasTile bt(a, p0);
+    for (int e = tid; e < TP * a.H; e += NT8) {
+      const int row = e / a.H, h = e - row * a.H;
+      sA[toff(row, h)] = (uint16_t)(pack_bf16(a.dbias[bt.at(row, h)], 0.f) & 0xffffu);
+      sB[toff(row, h)] = a.w_bias[e];  // row = input channel: Wb[c_in][h] is element c_in H + h
+    }
+  }
+  __syncthreads();
+  tile_product<ROW, ROW, 1>(sA, sB, wm, wn, lane, 1, acc);
+  stage_f32<1>(s32, acc, wm, wn, lane, [](float x) { return x; });
+  __syncthreads();  // dzn staged; the operand tiles are free
+  {
     const f32x2 st = *(const f32x2 *)(a.stats + 2 * (p0 + pr));
     const float mean = st[0], rstd = st[1];
     float s1 = 0.f, s2 = 0.f;
-    float dx[64], xh[64];
+    float dx[32], xh[32];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       float zv[8], d[8], dxh[8];
-      unpack8(*(const u32x4 *)(a.z + (p0 + pr) * CH + c0 + 8 * i), zv);
+      unpack8(zr[i], zv);
       read8_f32(s32, pr, c0 + 8 * i, d);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -554,13 +588,14 @@ __global__ __launch_bounds__(NT, 1) void mod_in_bwd_kernel(ModArgs a) {
       *(f32x4 *)(sx + foff(pr, c0 + 8 * i)) = (f32x4){dxh[0], dxh[1], dxh[2], dxh[3]};
       *(f32x4 *)(sx + foff(pr, c0 + 8 * i + 4)) = (f32x4){dxh[4], dxh[5], dxh[6], dxh[7]};
     }
-    // the two halves of the position: (this half) + (other half) in the same order on
-    // both lanes
+    // the four quarters of the position: (q0 + q1) + (q2 + q3) on all four lanes
     s1 += __shfl_xor(s1, 1);
     s2 += __shfl_xor(s2, 1);
+    s1 += __shfl_xor(s1, 2);
+    s2 += __shfl_xor(s2, 2);
     const float m1 = s1 * (1.f / CH), m2 = s2 * (1.f / CH);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       float o[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] = rstd * (dx[8 * i + e] - m1 - xh[8 * i + e] * m2);
@@ -568,27 +603,9 @@ __global__ __launch_bounds__(NT, 1) void mod_in_bwd_kernel(ModArgs a) {
     }
   }
   __syncthreads();
-  // per channel: thread -> channel tid % 128, positions 64 (tid / 128) .. + 63 in order,
-  // then the lower half plus the upper half
-  {
-    const int c = tid & 127, hp = tid >> 7;
-    float sw = 0.f, sb = 0.f;
-#pragma unroll 16
-    for (int r = 64 * hp; r < 64 * hp + 64; ++r) {
-      sw += sx[foff(r, c)];
-      sb += s32[foff(r, c)];
-    }
-    if (hp) {
-      s_half[0][c] = sw;
-      s_half[1][c] = sb;
-    }
-    __syncthreads();
-    if (!hp) {
-      float *dst = a.ln_part + (long long)tile * 2 * CH;
-      dst[c] = sw + s_half[0][c];
-      dst[CH + c] = sb + s_half[1][c];
-    }
-  }
+  float *part = a.ln_part + (long long)tile * 2 * CH;
+  column_sums8(sx, s_part, part, tid);        // sum of dzn * xhat
+  column_sums8(s32, s_part, part + CH, tid);  // sum of dzn
 }
 
 // Weight gradients: workgroup = (slice of tiles, output block), 8 waves each owning
@@ -600,8 +617,7 @@ __global__ __launch_bounds__(NT, 1) void mod_in_bwd_kernel(ModArgs a) {
 // Both operands are read transposed from position-major tiles, fetched into registers a
 // tile ahead.  The six blocks of a slice are neighbouring workgroups on one XCD.  The
 // fp32 partial of the slice goes to w_part[block][slice].
-constexpr int NT8M = 512;
-__global__ __launch_bounds__(NT8M, 4) void mod_wgrad_kernel(ModArgs a) {
+__global__ __launch_bounds__(NT8, 4) void mod_wgrad_kernel(ModArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sA[TP * CH];
   __shared__ __attribute__((aligned(16))) uint16_t sB[TP * CH];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -616,16 +632,16 @@ __global__ __launch_bounds__(NT8M, 4) void mod_wgrad_kernel(ModArgs a) {
     const u32x4 z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int pc = tid + NT8M * i, row = pc >> 4, c = (pc & 15) * 8;
+      const int pc = tid + NT8 * i, row = pc >> 4, c = (pc & 15) * 8;
       *(u32x4 *)(sB + toff(row, c)) = z4;
     }
   }
   u32x4 ra[4], ro[4], rb[4];
   auto fetch = [&](int tile) {
     const long long p0 = (long long)tile * TP;
-    fetch_block<NT8M>(ra, asrc + p0 * CH, CH, tid);
-    fetch_block<NT8M>(rb, bsrc + p0 * CH, CH, tid);
-    if (blk == 5) fetch_block<NT8M>(ro, a.o + p0 * CH, CH, tid);
+    fetch_block<NT8>(ra, asrc + p0 * CH, CH, tid);
+    fetch_block<NT8>(rb, bsrc + p0 * CH, CH, tid);
+    if (blk == 5) fetch_block<NT8>(ro, a.o + p0 * CH, CH, tid);
   };
   f32x16 acc[1][2];
   zero<1>(acc);
@@ -636,7 +652,7 @@ __global__ __launch_bounds__(NT8M, 4) void mod_wgrad_kernel(ModArgs a) {
     if (tile > t0) __syncthreads();  // the previous tile's operands are consumed
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int pc = tid + NT8M * i, row = pc >> 4, c = (pc & 15) * 8;
+      const int pc = tid + NT8 * i, row = pc >> 4, c = (pc & 15) * 8;
       u32x4 w = ra[i];
       if (blk == 5) {
         float gv[8], ov[8];
@@ -652,7 +668,7 @@ __global__ __launch_bounds__(NT8M, 4) void mod_wgrad_kernel(ModArgs a) {
     if (blk == 4) {
       // the H head columns of the tile (the others were zeroed before the loop)
       const BiasTile bt(a, p0);
-      for (int e = tid; e < TP * a.H; e += NT8M) {
+      for (int e = tid; e < TP * a.H; e += NT8) {
         const int row = e / a.H, h = e - row * a.H;
         sB[toff(row, h)] = (uint16_t)(pack_bf16(a.dbias[bt.at(row, h)], 0.f) & 0xffffu);
       }
@@ -955,22 +971,6 @@ __global__ __launch_bounds__(NT, 2) void tmb_out_kernel(TmbArgs a) {
     for (int e = 0; e < 8; ++e) yp[e] *= gv[e];
     *(u32x4 *)(a.y + off) = pack8u(yp);
   }
-}
-
-constexpr int NT8 = 512;  // threads of the 8-wave kernels (two waves per SIMD)
-
-// Column sums over the tile's 128 positions of an fp32 foff tile by 512 threads (thread
-// -> channel tid % 128, quarter tid / 128 of the positions in order, then the quarters
-// in order): channel c's sum to dst[c].  Ends with the workgroup synchronised.
-__device__ __forceinline__ void column_sums8(const float *t32, float (*s_part)[CH], float *dst, int tid) {
-  const int c = tid & 127, q = tid >> 7;
-  float sum = 0.f;
-#pragma unroll 16
-  for (int r = 32 * q; r < 32 * q + 32; ++r) sum += t32[foff(r, c)];
-  s_part[q][c] = sum;
-  __syncthreads();
-  if (q == 0) dst[c] = ((s_part[0][c] + s_part[1][c]) + s_part[2][c]) + s_part[3][c];
-  __syncthreads();
 }
 
 // Backward, part 1: the output gate and projection and LayerNorm_out's backward:
@@ -1304,6 +1304,7 @@ __global__ __launch_bounds__(256) void tmb_reduce_w_kernel(TmbReduceArgs a) {
 // Host side
 // ------------------------------------------------------------------------------------
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 bool aligned16(const void *p) { return p && ((uintptr_t)p & 15u) == 0; }
 
 // Byte ranges of the tensors of a call: every output must be disjoint from every input
@@ -1710,9 +1711,9 @@ tri_attn_status tri_attn_module_bwd(const tri_attn_module_problem *problem, cons
                     a.d_o, ws + l.off_dq, ws + l.off_dk, ws + l.off_dv, ws + l.off_db, ws + l.off_core, l.core_bytes,
                     stream);
   if (st != TRI_ATTN_SUCCESS) return st;
-  hipLaunchKernelGGL(mod_in_bwd_kernel, dim3((unsigned)a.tiles), dim3(NT), 0, stream, a);
+  hipLaunchKernelGGL(mod_in_bwd_kernel, dim3((unsigned)a.tiles), dim3(NT8), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
-  hipLaunchKernelGGL(mod_wgrad_kernel, dim3((unsigned)(6 * a.slices)), dim3(NT8M), 0, stream, a);
+  hipLaunchKernelGGL(mod_wgrad_kernel, dim3((unsigned)(6 * a.slices)), dim3(NT8), 0, stream, a);
   if (hipGetLastError() != hipSuccess) return TRI_ATTN_ERROR_LAUNCH_FAILED;
   ReduceArgs r;
   r.w_part = a.w_part;
