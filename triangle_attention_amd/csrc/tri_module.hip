@@ -119,6 +119,24 @@ __device__ __forceinline__ void tile_product(const uint16_t *sA, const uint16_t 
   }
 }
 
+// tile_product for one 32 x 64 block per wave with its 16-deep slices unrolled two at
+// a time, which bounds how far ahead their LDS reads are hoisted (fewer registers)
+template <int AL, int BL>
+__device__ __forceinline__ void tile_product_u2(const uint16_t *sA, const uint16_t *sB, int wm, int wn, int lane,
+                                                int slices, f32x16 (&acc)[1][2]) {
+#pragma unroll 2
+  for (int s = 0; s < slices; ++s) {
+    const int kk = 16 * s;
+    const bf16x8 a = AL == ROW ? row_operand(sA, wm, kk, lane) : tr_operand(sA, kk, wm, lane);
+    bf16x8 b[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      b[j] = BL == ROW ? row_operand(sB, wn + 32 * j, kk, lane) : tr_operand(sB, kk, wn + 32 * j, lane);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[0][j] = mfma(a, b[j], acc[0][j]);
+  }
+}
+
 template <int MI = 2>
 __device__ __forceinline__ void zero(f32x16 (&acc)[MI][2]) {
 #pragma unroll
@@ -485,17 +503,16 @@ __global__ __launch_bounds__(NT, 2) void mod_out_bwd_kernel(ModArgs a) {
 //   dxhat = dzn * w,  dz = rstd (dxhat - mean(dxhat) - xhat mean(dxhat xhat)),
 // and the tile's sums over its positions of dzn * xhat and of dzn (partials of the
 // LayerNorm scale and offset gradients), each in position order.
-// 8 waves (two per SIMD), each owning 32 x 64 of dzn.  A block's operands (the gradient
-// tile and the weight block, 64 KB) travel as 16-byte pieces in registers: the loads of
-// blocks b + 1 and b + 2 are in flight while block b's products run, and z for the
-// LayerNorm backward while the last ones do.
-__global__ __launch_bounds__(NT8, 1) void mod_in_bwd_kernel(ModArgs a) {
-  // [0, 64 KB): the two operand tiles, then the fp32 tile of dzn * xhat;
-  // [64, 128 KB): the fp32 tile of dzn
-  __shared__ __attribute__((aligned(16))) float lds[2 * TP * CH];
-  __shared__ float s_part[4][CH];
+// 8 waves (each owning 32 x 64 of dzn), two workgroups per CU: the operand tiles (64 KB)
+// are the only large LDS buffer, and once the products are done they hold the fp32 dzn
+// tile.  A block's operands are fetched into registers while the previous block's
+// products run, z for the LayerNorm backward during the bias block.  The column sums
+// recompute xhat from z (read by channel) and the tile's statistics.
+__global__ __launch_bounds__(NT8, 4) void mod_in_bwd_kernel(ModArgs a) {
+  __shared__ __attribute__((aligned(16))) float lds[TP * CH];  // [sA | sB], then the fp32 dzn tile
+  __shared__ f32x2 s_st[TP];
+  __shared__ float s_part[2][4][CH];
   uint16_t *sA = (uint16_t *)lds, *sB = sA + TP * CH;
-  float *s32 = lds + TP * CH, *sx = lds;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const long long p0 = (long long)tile * TP;
@@ -522,30 +539,23 @@ __global__ __launch_bounds__(NT8, 1) void mod_in_bwd_kernel(ModArgs a) {
   // per position in the LayerNorm backward: thread -> position tid / 4, channels
   // 32 (tid % 4) .. + 31
   const int pr = tid >> 2, c0 = 32 * (tid & 3);
-  u32x4 r0[8], r1[8], zr[4];
+  u32x4 rb[8], zr[4];
   f32x16 acc[1][2];
   zero<1>(acc);
-  fetch(0, r0);
-  fetch(1, r1);
+  fetch(0, rb);
 #pragma unroll
   for (int blk = 0; blk < 4; ++blk) {
     if (blk) __syncthreads();  // the previous block's operands are consumed
-    if (blk & 1) put(r1);
-    else put(r0);
+    put(rb);
     __syncthreads();
-    if (blk + 2 < 4) {
-      if (blk & 1) fetch(blk + 2, r1);
-      else fetch(blk + 2, r0);
-    }
-    if (blk == 2) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) zr[i] = *(const u32x4 *)(a.z + (p0 + pr) * CH + c0 + 8 * i);
-    }
-    tile_product<ROW, ROW, 1>(sA, sB, wm, wn, lane, CH / 16, acc);
+    if (blk < 3) fetch(blk + 1, rb);
+    tile_product_u2<ROW, ROW>(sA, sB, wm, wn, lane, CH / 16, acc);
   }
   // block 4: A(position, t = head) = dbias at that position, rounded to bf16;
   // B(t = head, n = c_in) = Wb[c_in][head]: rows; zeros beyond the H heads.  One 16-deep
   // slice: only columns 0..15 of the two tiles are read.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) zr[i] = *(const u32x4 *)(a.z + (p0 + pr) * CH + c0 + 8 * i);
   __syncthreads();
   if (tid < 256) {
     const u32x4 z4 = {0u, 0u, 0u, 0u};
@@ -553,6 +563,7 @@ __global__ __launch_bounds__(NT8, 1) void mod_in_bwd_kernel(ModArgs a) {
     *(u32x4 *)(sA + toff(row, c)) = z4;
     *(u32x4 *)(sB + toff(row, c)) = z4;
   }
+  if (tid < TP) s_st[tid] = *(const f32x2 *)(a.stats + 2 * (p0 + tid));
   __syncthreads();
   {
     const BiasTile bt(a, p0);
@@ -563,30 +574,28 @@ __global__ __launch_bounds__(NT8, 1) void mod_in_bwd_kernel(ModArgs a) {
     }
   }
   __syncthreads();
-  tile_product<ROW, ROW, 1>(sA, sB, wm, wn, lane, 1, acc);
-  stage_f32<1>(s32, acc, wm, wn, lane, [](float x) { return x; });
-  __syncthreads();  // dzn staged; the operand tiles are free
+  tile_product_u2<ROW, ROW>(sA, sB, wm, wn, lane, 1, acc);
+  __syncthreads();  // the operand tiles are consumed
+  stage_f32<1>(lds, acc, wm, wn, lane, [](float x) { return x; });
+  __syncthreads();
   {
-    const f32x2 st = *(const f32x2 *)(a.stats + 2 * (p0 + pr));
+    const f32x2 st = s_st[pr];
     const float mean = st[0], rstd = st[1];
     float s1 = 0.f, s2 = 0.f;
     float dx[32], xh[32];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float zv[8], d[8], dxh[8];
+      float zv[8], d[8];
       unpack8(zr[i], zv);
-      read8_f32(s32, pr, c0 + 8 * i, d);
+      read8_f32(lds, pr, c0 + 8 * i, d);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int c = 8 * i + e;
         xh[c] = (zv[e] - mean) * rstd;
-        dxh[e] = d[e] * xh[c];
         dx[c] = d[e] * a.ln_w[c0 + c];
         s1 += dx[c];
         s2 = fmaf(dx[c], xh[c], s2);
       }
-      *(f32x4 *)(sx + foff(pr, c0 + 8 * i)) = (f32x4){dxh[0], dxh[1], dxh[2], dxh[3]};
-      *(f32x4 *)(sx + foff(pr, c0 + 8 * i + 4)) = (f32x4){dxh[4], dxh[5], dxh[6], dxh[7]};
     }
     // the four quarters of the position: (q0 + q1) + (q2 + q3) on all four lanes
     s1 += __shfl_xor(s1, 1);
@@ -602,10 +611,28 @@ __global__ __launch_bounds__(NT8, 1) void mod_in_bwd_kernel(ModArgs a) {
       *(u32x4 *)(a.dz + (p0 + pr) * CH + c0 + 8 * i) = pack8u(o);
     }
   }
-  __syncthreads();
-  float *part = a.ln_part + (long long)tile * 2 * CH;
-  column_sums8(sx, s_part, part, tid);        // sum of dzn * xhat
-  column_sums8(s32, s_part, part + CH, tid);  // sum of dzn
+  {
+    // column sums: thread -> channel tid % 128, quarter tid / 128 of the positions in
+    // order, then the quarters in order; xhat recomputed as in the LayerNorm backward
+    const int c = tid & 127, q = tid >> 7;
+    float sw = 0.f, sb = 0.f;
+#pragma unroll 8
+    for (int r = 32 * q; r < 32 * q + 32; ++r) {
+      const float d = lds[foff(r, c)];
+      const f32x2 st = s_st[r];
+      const float xh = (bf_lo(a.z[(p0 + r) * CH + c]) - st[0]) * st[1];
+      sw += d * xh;
+      sb += d;
+    }
+    s_part[0][q][c] = sw;
+    s_part[1][q][c] = sb;
+    __syncthreads();
+    if (q == 0) {
+      float *part = a.ln_part + (long long)tile * 2 * CH;
+      part[c] = ((s_part[0][0][c] + s_part[0][1][c]) + s_part[0][2][c]) + s_part[0][3][c];
+      part[CH + c] = ((s_part[1][0][c] + s_part[1][1][c]) + s_part[1][2][c]) + s_part[1][3][c];
+    }
+  }
 }
 
 // Weight gradients: workgroup = (slice of tiles, output block), 8 waves each owning
@@ -1120,16 +1147,16 @@ __global__ __launch_bounds__(NT8, 1) void tmb_grad_proj_kernel(TmbArgs a) {
 
 // Backward, part 3: dzn = [d(ag) d(ap) d(bg) d(bp) dgp] Win^T (five 128-deep blocks), the
 // LayerNorm_in backward to dz and the tile's column sums of dzn xhat and dzn.
-// 8 waves (two per SIMD), each owning 32 x 64 of dzn.  A block's operands (the gradient
-// tile and the weight block, 64 KB) travel as 16-byte pieces in registers: the loads of
-// blocks b + 1 and b + 2 are in flight while block b's products run, and z for the
-// LayerNorm backward while the last one's do.
-__global__ __launch_bounds__(NT8, 1) void tmb_in_bwd_kernel(TmbArgs a) {
-  // [sA | sB] operands, then the dzn * xhat fp32 tile; the dzn fp32 tile
-  __shared__ __attribute__((aligned(16))) float lds0[TP * CH];
-  __shared__ __attribute__((aligned(16))) float lds1[TP * CH];
-  __shared__ float s_part[4][CH];
-  uint16_t *sA = (uint16_t *)lds0, *sB = sA + TP * CH;
+// 8 waves (each owning 32 x 64 of dzn), two workgroups per CU: the operand tiles (64 KB)
+// are the only large LDS buffer, and once the products are done they hold the fp32 dzn
+// tile.  A block's operands are fetched into registers while the previous block's
+// products run, z for the LayerNorm backward during the last one's.  The column sums
+// recompute xhat from z (read by channel) and the tile's statistics.
+__global__ __launch_bounds__(NT8, 4) void tmb_in_bwd_kernel(TmbArgs a) {
+  __shared__ __attribute__((aligned(16))) float lds[TP * CH];  // [sA | sB], then the fp32 dzn tile
+  __shared__ f32x2 s_st[TP];
+  __shared__ float s_part[2][4][CH];
+  uint16_t *sA = (uint16_t *)lds, *sB = sA + TP * CH;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const long long p0 = (long long)tile * TP;
@@ -1159,56 +1186,48 @@ __global__ __launch_bounds__(NT8, 1) void tmb_in_bwd_kernel(TmbArgs a) {
   // per position in the LayerNorm backward: thread -> position tid / 4, channels
   // 32 (tid % 4) .. + 31
   const int pr = tid >> 2, c0 = 32 * (tid & 3);
-  u32x4 r0[8], r1[8], zr[4];
+  u32x4 rb[8], zr[4];
   f32x16 dzn[1][2];
   zero<1>(dzn);
-  fetch(0, r0);
-  fetch(1, r1);
+  fetch(0, rb);
 #pragma unroll
   for (int blk = 0; blk < 5; ++blk) {
     if (blk) __syncthreads();  // the previous block's operands are consumed
-    if (blk & 1) put(r1);
-    else put(r0);
+    put(rb);
     __syncthreads();
-    if (blk + 2 < 5) {
-      if (blk & 1) fetch(blk + 2, r1);
-      else fetch(blk + 2, r0);
-    }
-    if (blk == 3) {
+    if (blk < 4) {
+      fetch(blk + 1, rb);
+    } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) zr[i] = *(const u32x4 *)(a.z + (p0 + pr) * CH + c0 + 8 * i);
     }
-    if (blk < 4) tile_product<TR, ROW, 1>(sA, sB, wm, wn, lane, CH / 16, dzn);
-    else tile_product<ROW, ROW, 1>(sA, sB, wm, wn, lane, CH / 16, dzn);
+    if (blk < 4) tile_product_u2<TR, ROW>(sA, sB, wm, wn, lane, CH / 16, dzn);
+    else tile_product_u2<ROW, ROW>(sA, sB, wm, wn, lane, CH / 16, dzn);
   }
-  float *t_dzn = lds1, *t_dx = lds0;
-  stage_f32<1>(t_dzn, dzn, wm, wn, lane, [](float x) { return x; });
-  __syncthreads();  // dzn staged, the operand tiles consumed
-  float *part = a.ln_in_part + (long long)tile * 2 * CH;
+  if (tid < TP) s_st[tid] = *(const f32x2 *)(a.stats_in + 2 * (p0 + tid));
+  __syncthreads();  // the operand tiles are consumed
+  stage_f32<1>(lds, dzn, wm, wn, lane, [](float x) { return x; });
+  __syncthreads();
   {
-    const f32x2 st = *(const f32x2 *)(a.stats_in + 2 * (p0 + pr));
+    const f32x2 st = s_st[pr];
     const float mean = st[0], rstd = st[1];
     float s1 = 0.f, s2 = 0.f;
     float dx[32], xh[32];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float zv[8], d[8], dxh[8];
+      float zv[8], d[8];
       unpack8(zr[i], zv);
-      read8_f32(t_dzn, pr, c0 + 8 * i, d);
+      read8_f32(lds, pr, c0 + 8 * i, d);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int c = 8 * i + e;
         xh[c] = (zv[e] - mean) * rstd;
-        dxh[e] = d[e] * xh[c];
         dx[c] = d[e] * a.ln_in_w[c0 + c];
         s1 += dx[c];
         s2 = fmaf(dx[c], xh[c], s2);
       }
-      *(f32x4 *)(t_dx + foff(pr, c0 + 8 * i)) = (f32x4){dxh[0], dxh[1], dxh[2], dxh[3]};
-      *(f32x4 *)(t_dx + foff(pr, c0 + 8 * i + 4)) = (f32x4){dxh[4], dxh[5], dxh[6], dxh[7]};
     }
-    // the four quarters of the position: (q0 + q1) + (q2 + q3), the same value on all
-    // four lanes
+    // the four quarters of the position: (q0 + q1) + (q2 + q3) on all four lanes
     s1 += __shfl_xor(s1, 1);
     s2 += __shfl_xor(s2, 1);
     s1 += __shfl_xor(s1, 2);
@@ -1222,9 +1241,28 @@ __global__ __launch_bounds__(NT8, 1) void tmb_in_bwd_kernel(TmbArgs a) {
       *(u32x4 *)(a.dz + (p0 + pr) * CH + c0 + 8 * i) = pack8u(o);
     }
   }
-  __syncthreads();
-  column_sums8(t_dx, s_part, part, tid);
-  column_sums8(t_dzn, s_part, part + CH, tid);
+  {
+    // column sums: thread -> channel tid % 128, quarter tid / 128 of the positions in
+    // order, then the quarters in order; xhat recomputed as in the LayerNorm backward
+    const int c = tid & 127, q = tid >> 7;
+    float sw = 0.f, sb = 0.f;
+#pragma unroll 8
+    for (int r = 32 * q; r < 32 * q + 32; ++r) {
+      const float d = lds[foff(r, c)];
+      const f32x2 st = s_st[r];
+      const float xh = (bf_lo(a.z[(p0 + r) * CH + c]) - st[0]) * st[1];
+      sw += d * xh;
+      sb += d;
+    }
+    s_part[0][q][c] = sw;
+    s_part[1][q][c] = sb;
+    __syncthreads();
+    if (q == 0) {
+      float *part = a.ln_in_part + (long long)tile * 2 * CH;
+      part[c] = ((s_part[0][0][c] + s_part[0][1][c]) + s_part[0][2][c]) + s_part[0][3][c];
+      part[CH + c] = ((s_part[1][0][c] + s_part[1][1][c]) + s_part[1][2][c]) + s_part[1][3][c];
+    }
+  }
 }
 
 // Weight gradients of the block: workgroup = (slice of tiles, output block), 8 waves
