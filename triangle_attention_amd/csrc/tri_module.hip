@@ -340,6 +340,7 @@ __global__ __launch_bounds__(NT, 2) void mod_proj_kernel(ModArgs a) {
       *(u32x4 *)(sB + toff(row, c)) = wr[i];
     }
   };
+  fetch_w(0);  // in flight during the LayerNorm
   // LayerNorm: thread -> position tid / 2, channels 64 (tid % 2) .. + 63
   {
     const int pr = tid >> 1, c0 = 64 * (tid & 1);
@@ -376,7 +377,6 @@ __global__ __launch_bounds__(NT, 2) void mod_proj_kernel(ModArgs a) {
     }
     if ((tid & 1) == 0) *(f32x2 *)(a.stats + 2 * (p0 + pr)) = (f32x2){mean, rstd};
   }
-  fetch_w(0);
   stage_w();
   __syncthreads();
 
@@ -438,14 +438,18 @@ __global__ __launch_bounds__(NT, 2) void mod_gate_out_kernel(ModArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sB[CH * CH];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long long p0 = (long long)xcd_remap(blockIdx.x, gridDim.x) * TP;
-  load_block(sB, a.w_out, CH, tid);
+  // every load issued before the first wait
+  u32x4 rw[8], rg[8], ro[8];
+  fetch_block<NT>(rw, a.w_out, CH, tid);
+  fetch_block<NT>(rg, a.g + p0 * CH, CH, tid);
+  fetch_block<NT>(ro, a.o + p0 * CH, CH, tid);
+  put_block<NT>(sB, rw, tid);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int pc = tid + NT * i, row = pc >> 4, c = (pc & 15) * 8;
-    const long long off = (p0 + row) * CH + c;
     float gv[8], ov[8];
-    unpack8(*(const u32x4 *)(a.g + off), gv);
-    unpack8(*(const u32x4 *)(a.o + off), ov);
+    unpack8(rg[i], gv);
+    unpack8(ro[i], ov);
 #pragma unroll
     for (int e = 0; e < 8; ++e) gv[e] *= ov[e];
     *(u32x4 *)(sA + toff(row, c)) = pack8u(gv);
@@ -470,8 +474,14 @@ __global__ __launch_bounds__(NT, 2) void mod_out_bwd_kernel(ModArgs a) {
   float *s32 = lds;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long long p0 = (long long)xcd_remap(blockIdx.x, gridDim.x) * TP;
-  load_block(sA, a.dy + p0 * CH, CH, tid);
-  load_block(sB, a.w_out, CH, tid);  // Wo [c_in][c_out]: B(t = c_out, n = c_in) as rows
+  // every load issued at the start: g and o wait in registers for the element-wise step
+  u32x4 rd[8], rw[8], rg[8], ro[8];
+  fetch_block<NT>(rd, a.dy + p0 * CH, CH, tid);
+  fetch_block<NT>(rw, a.w_out, CH, tid);  // Wo [c_in][c_out]: B(t = c_out, n = c_in) as rows
+  fetch_block<NT>(rg, a.g + p0 * CH, CH, tid);
+  fetch_block<NT>(ro, a.o + p0 * CH, CH, tid);
+  put_block<NT>(sA, rd, tid);
+  put_block<NT>(sB, rw, tid);
   __syncthreads();
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   f32x16 acc[2][2];
@@ -486,8 +496,8 @@ __global__ __launch_bounds__(NT, 2) void mod_out_bwd_kernel(ModArgs a) {
     const long long off = (p0 + row) * CH + c;
     float d[8], gv[8], ov[8], dov[8], dgv[8];
     read8_f32(s32, row, c, d);
-    unpack8(*(const u32x4 *)(a.g + off), gv);
-    unpack8(*(const u32x4 *)(a.o + off), ov);
+    unpack8(rg[i], gv);
+    unpack8(ro[i], ov);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       dov[e] = d[e] * gv[e];
@@ -898,8 +908,8 @@ __global__ __launch_bounds__(NT, 1) void tmb_proj_kernel(TmbArgs a) {
     }
   };
   if (tid < TP) s_m[tid] = a.mask ? (a.mask[p0 + tid] ? 1.f : 0.f) : 1.f;
+  fetch_w(0);  // in flight during the LayerNorm
   layer_norm_tile(a.z + p0 * CH, a.ln_in_w, a.ln_in_b, a.eps, sA, a.zn + p0 * CH, a.stats_in + 2 * p0, tid);
-  fetch_w(0);
   stage_w();
   fetch_w(1);
   __syncthreads();
@@ -946,7 +956,12 @@ __global__ __launch_bounds__(NT, 2) void tmb_out_kernel(TmbArgs a) {
   uint16_t *sA = (uint16_t *)lds, *sB = sA + TP * CH;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long long p0 = (long long)xcd_remap(blockIdx.x, gridDim.x) * TP;
-  load_cm(sB, a.x + cm_tile(a, p0), a.NN, tid);  // [channel][position]
+  // every load issued at the start: Wo and g wait in registers
+  u32x4 rx[8], rw[8], rg[8];
+  fetch_block<NT>(rx, a.x + cm_tile(a, p0), a.NN, tid);  // [channel][position]
+  fetch_block<NT>(rw, a.w_out, CH, tid);
+  fetch_block<NT>(rg, a.g + p0 * CH, CH, tid);
+  put_block<NT>(sB, rx, tid);
   __syncthreads();
   {
     const int pr = tid >> 1, c0 = 64 * (tid & 1);
@@ -978,7 +993,7 @@ __global__ __launch_bounds__(NT, 2) void tmb_out_kernel(TmbArgs a) {
     if ((tid & 1) == 0) *(f32x2 *)(a.stats_out + 2 * (p0 + pr)) = (f32x2){mean, rstd};
   }
   __syncthreads();
-  load_block(sB, a.w_out, CH, tid);
+  put_block<NT>(sB, rw, tid);
   __syncthreads();
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
   f32x16 acc[2][2];
@@ -993,7 +1008,7 @@ __global__ __launch_bounds__(NT, 2) void tmb_out_kernel(TmbArgs a) {
     const long long off = (p0 + row) * CH + c;
     float yp[8], gv[8];
     read8_f32(lds, row, c, yp);
-    unpack8(*(const u32x4 *)(a.g + off), gv);
+    unpack8(rg[i], gv);
 #pragma unroll
     for (int e = 0; e < 8; ++e) yp[e] *= gv[e];
     *(u32x4 *)(a.y + off) = pack8u(yp);
