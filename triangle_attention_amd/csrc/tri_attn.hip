@@ -381,9 +381,11 @@ __global__ __launch_bounds__(FwdShape<DIN>::WAVES * 64) void fwd_kernel(FwdArgs 
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, fmaf((float)bw[i >> 2][i & 3], kLog2e, acc[i] * c1));
       return fmaxf(mt, __shfl_xor(mt, 32));
     };
-    // one tile of the output pass against the reference maxima m[s] (m[s] = -inf:
-    // take this tile's maximum); T holds tile kt on entry and tile kt + 1 on return
-    auto tile = [&](int kt, FwdTile<NL> &T, float *m, f32x16 (*oacc)[NC], float *lsum) {
+    // one tile of the output pass against the reference maxima m[s]; T holds tile kt on
+    // entry and tile kt + 1 on return.  CHECK: a query may still have m[s] = -inf (then
+    // this tile's maximum is taken); without it every present query has its maximum.
+    auto tile = [&](auto check_tag, int kt, FwdTile<NL> &T, float *m, f32x16 (*oacc)[NC], float *lsum) {
+      constexpr bool CHECK = decltype(check_tag)::value;
       const unsigned valid = MASKED ? (unsigned)__ballot(T.m != 0u) : 0xffffffffu;
       if (valid != 0u) {
         stage_k(T);
@@ -404,17 +406,22 @@ __global__ __launch_bounds__(FwdShape<DIN>::WAVES * 64) void fwd_kernel(FwdArgs 
         const f32x16 acc = qk(s, valid);
         f16x4 bw[4];
         bias_of(s, kt, bw);
-        if (__builtin_expect(__ballot(m[s] == -INFINITY) != 0ull, 0)) {  // the first attended tile
-          const float mt = tile_max(acc, bw);
-          if (m[s] == -INFINITY) m[s] = mt;
+        float negm = -m[s];
+        if constexpr (CHECK) {
+          if (__builtin_expect(__ballot(m[s] == -INFINITY) != 0ull, 0)) {  // the first attended tile
+            const float mt = tile_max(acc, bw);
+            if (m[s] == -INFINITY) m[s] = mt;
+          }
+          negm = m[s] == -INFINITY ? 0.f : -m[s];  // no finite score yet: every p is 0
         }
-        const float negm = m[s] == -INFINITY ? 0.f : -m[s];  // no finite score yet: every p is 0
-        float p[16], ts = 0.f;
+        float p[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 16; ++i)
           p[i] = __builtin_amdgcn_exp2f(fmaf((float)bw[i >> 2][i & 3], kLog2e, fmaf(acc[i], c1, negm)));
-          ts += p[i];
-        }
+        // the tile's partial sum (in index order), then into the row's
+        float ts = p[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) ts += p[i];
         lsum[s] += ts;
         const bf16x8 pB0 = pack8(p), pB1 = pack8(p + 8);
 #pragma unroll
@@ -434,7 +441,15 @@ __global__ __launch_bounds__(FwdShape<DIN>::WAVES * 64) void fwd_kernel(FwdArgs 
       }
       FwdTile<NL> T;
       fetch(0, T);
-      for (int kt = 0; kt < nkt; ++kt) tile(kt, T, m, oacc, lsum);
+      // tiles with the reference-maximum check until every present query has one (the
+      // first attended tile, normally), then the rest without it
+      int kt = 0;
+      for (; kt < nkt; ++kt) {
+        const bool unset = m[0] == -INFINITY || (NQ == 2 && two && m[NQ - 1] == -INFINITY);
+        if (__ballot(unset) == 0ull) break;
+        tile(std::true_type{}, kt, T, m, oacc, lsum);
+      }
+      for (; kt < nkt; ++kt) tile(std::false_type{}, kt, T, m, oacc, lsum);
 #pragma unroll
       for (int s = 0; s < NQ; ++s) lsum[s] += __shfl_xor(lsum[s], 32);
     };
@@ -492,10 +507,15 @@ __global__ __launch_bounds__(FwdShape<DIN>::WAVES * 64) void fwd_kernel(FwdArgs 
     float *r32t = (float *)kbuf;  // [32 queries][TD channels] fp32: residual (kbuf and vbuf)
     constexpr int LR = TD / 4;  // lanes per query row of the fp32 residual (16 bytes each)
     constexpr int LO = TD / 8;  // lanes per query row of o
+    // a query's row offset within the half: row * sQ < 64 * 2^22 (sQ = N H D at most in
+    // the ending orientation), one 24-bit multiply
+    const unsigned sq = (unsigned)a.f.sQ;
 #pragma unroll
     for (int s = 0; s < NQ; ++s) {
       if (s == 1 && !two) break;
+      const long long qbase = base + (long long)(j0 + 32 * s) * a.f.sQ;  // the half's first query
       float inv = lsum[s] > 0.f ? 1.f / lsum[s] : 0.f;
+      unsigned opk[NC][4][2];  // the packed o words, kept for the store after the residual's
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -507,6 +527,8 @@ __global__ __launch_bounds__(FwdShape<DIN>::WAVES * 64) void fwd_kernel(FwdArgs 
 #pragma unroll
           for (int i = 0; i < 4; ++i) ov[i] = oacc[s][c][4 * g + i] * inv;
           const unsigned p0 = pack_bf16(ov[0], ov[1]), p1 = pack_bf16(ov[2], ov[3]);
+          opk[c][g][0] = p0;
+          opk[c][g][1] = p1;
           // channels 32c + 8g + 4hh .. + 3 of query jl; the residual O - float(o) is
           // exact in fp32 (and rounded once more, to bf16, for a bf16 residual)
           const f32x4 rv = {ov[0] - bf_lo(p0), ov[1] - bf_hi(p0), ov[2] - bf_lo(p1), ov[3] - bf_hi(p1)};
@@ -519,34 +541,28 @@ __global__ __launch_bounds__(FwdShape<DIN>::WAVES * 64) void fwd_kernel(FwdArgs 
         }
       if (RES32) {
         // the residual rows (LR lanes per query's 4 TD bytes), then o into the freed
-        // tile, converted again rather than held.  The lane index passes through an
-        // empty asm: otherwise the compiler hoists these stores' address arithmetic out
-        // of the row loop and the tile loop spills.
+        // tile.  The lane index passes through an empty asm: otherwise the compiler
+        // hoists these stores' address arithmetic out of the row loop and the tile loop
+        // spills.
         if (a.res) {
           int ln = lane;
           __asm__ volatile("" : "+v"(ln));
 #pragma unroll
           for (int k = 0; k < LR / 2; ++k) {
             const int row = (64 / LR) * k + ln / LR, c16 = ln % LR;
-            const long long off = base + (long long)(j0 + 32 * s + row) * a.f.sQ + 4 * c16;
+            const long long off = qbase + (long long)(__umul24((unsigned)row, sq) + 4u * c16);
             if (DIN != 16 || c16 < 4) *(f32x4 *)((float *)a.res + off) = *(const f32x4 *)(r32t + r32_off(row, c16));
           }
         }
-        __asm__ volatile("" : "+v"(inv));
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-#pragma clang fp contract(off)
-            const f32x16 &ac = oacc[s][c];
-            *(u32x2 *)(ot + o_off(jl, 4 * c + g) + 4 * hh) =
-                (u32x2){pack_bf16(ac[4 * g] * inv, ac[4 * g + 1] * inv), pack_bf16(ac[4 * g + 2] * inv, ac[4 * g + 3] * inv)};
-          }
+          for (int g = 0; g < 4; ++g) *(u32x2 *)(ot + o_off(jl, 4 * c + g) + 4 * hh) = (u32x2){opk[c][g][0], opk[c][g][1]};
       }
 #pragma unroll
       for (int k = 0; k < LO / 2; ++k) {
         const int row = lane / LO + (64 / LO) * k, chunk = lane % LO;
-        const long long off = base + (long long)(j0 + 32 * s + row) * a.f.sQ + 8 * chunk;
+        const long long off = qbase + (long long)(__umul24((unsigned)row, sq) + 8u * chunk);
         if (DIN != 16 || chunk < 2) {
           *(u32x4 *)(a.o + off) = *(const u32x4 *)(ot + o_off(row, chunk));
           if (!RES32 && a.res) *(u32x4 *)((uint16_t *)a.res + off) = *(const u32x4 *)(rt + o_off(row, chunk));
