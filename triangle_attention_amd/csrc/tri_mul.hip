@@ -57,12 +57,18 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
 }
 
 // Offset (elements) of (row, col) in a [rows][32] bf16 LDS tile whose 16-byte chunks
-// are permuted by bits 1 and 2 of the row: 16-byte row reads of consecutive rows and
-// the transposing reads below spread over the LDS banks.
+// are permuted by row bits 2 and 3 (XOR row bit 1, which keeps the index arithmetic
+// within the register budget of four workgroups per CU).  With 64 four-byte banks,
+// rows r and r + 4 share banks unless their chunks differ, so the 16-byte row reads of
+// 16 consecutive rows (one chunk each) then touch every bank once; the transposing
+// reads (four consecutive rows per 16-lane group) and the 16-byte piece writes (whole
+// rows) are conflict-free under any per-row permutation.
 __device__ __forceinline__ int toff(int row, int col) {
-  const int sw = (row & 2) | ((row >> 2) & 1);
+  const int sw = ((row >> 2) & 3) ^ (row & 2);
   return row * 32 + (((col >> 3) ^ sw) << 3) + (col & 7);
 }
+
+constexpr int SUB = 32 * 32;  // elements of a [32][32] sub-tile
 
 // Row operand of a [rows][32] tile holding (mn, t) with t contiguous: lane gets
 // tile[row0 + lane % 32][kk + 8 hh + e].
@@ -100,8 +106,10 @@ struct GemmArgs {
 // One 128 x 32 operand tile per step, as 16-byte pieces: 512 pieces, two per thread.
 //   t contiguous (TR = false): piece p -> row mn = p / 4, t = 8 (p % 4); stored [mn][t]
 //     in four [32][32] sub-tiles (mn / 32).
-//   mn contiguous (TR = true): piece p -> t = p / 16, mn = 8 (p % 16); stored [t][mn] in
-//     four [32 t][32 mn] sub-tiles (mn / 32).
+//   mn contiguous (TR = true): stored [t][mn] in four [32 t][32 mn] sub-tiles (mn / 32);
+//     each 16 consecutive pieces cover rows t .. t + 3 of one sub-tile (four 64-byte row
+//     segments: piece p -> sub-tile (p / 16) % 4, t = 4 (p / 64) + (p % 16) / 4,
+//     mn = 32 sub + 8 (p % 4)), so that a 16-lane LDS write covers every bank once.
 // Rows past N (a ragged last tile) load zeros.
 template <bool TR>
 struct TileIO {
@@ -111,8 +119,8 @@ struct TileIO {
       const int p = tid + 256 * i;
       int r, c;
       if (TR) {
-        r = t0 + (p >> 4);
-        c = mn0 + 8 * (p & 15);
+        r = t0 + 4 * (p >> 6) + ((p & 15) >> 2);
+        c = mn0 + 32 * ((p >> 4) & 3) + 8 * (p & 3);
       } else {
         r = mn0 + (p >> 2);
         c = t0 + 8 * (p & 3);
@@ -129,22 +137,21 @@ struct TileIO {
       const int p = tid + 256 * i;
       int sub, row, col;
       if (TR) {
-        const int mn = 8 * (p & 15);
-        sub = mn >> 5;
-        row = p >> 4;
-        col = mn & 31;
+        sub = (p >> 4) & 3;
+        row = 4 * (p >> 6) + ((p & 15) >> 2);
+        col = 8 * (p & 3);
       } else {
         const int mn = p >> 2;
         sub = mn >> 5;
         row = mn & 31;
         col = 8 * (p & 3);
       }
-      *(u32x4 *)(lds + sub * 32 * 32 + toff(row, col)) = w[i];
+      *(u32x4 *)(lds + sub * SUB + toff(row, col)) = w[i];
     }
   }
   // operand for the 32 rows / columns mn32 .. mn32 + 31 of the tile, t = kk .. kk + 15
   __device__ static bf16x8 operand(const uint16_t *lds, int mn32, int kk, int lane) {
-    const uint16_t *sub = lds + (mn32 >> 5) * 32 * 32;
+    const uint16_t *sub = lds + (mn32 >> 5) * SUB;
     return TR ? tr_operand(sub, kk, lane) : row_operand(sub, 0, kk, lane);
   }
 };
