@@ -20,12 +20,15 @@ axes swapped (z and the mask transposed, y transposed back).
 
 Everything here is fp64: the products are numpy matrix products, the core is the
 attention oracle of this package (its C code), and the backward is the chain rule of
-the lines above written out by hand.
+the lines above written out by hand.  `Module.rows` evaluates y and dz at the positions
+of selected pair rows only (the same lines, for sizes where the whole problem is too
+slow for a test).
 """
 from __future__ import annotations
 
 import numpy as np
 
+from . import Problem as _CoreProblem
 from . import forward_backward as _core_fwd_bwd
 from . import forward as _core_fwd
 
@@ -160,3 +163,38 @@ class Module:
         dz = layer_norm_backward(dzn, xhat, rstd, self.ln_w)
         return {"dz": self._out(dz), "d_ln_w": d_ln_w, "d_ln_b": d_ln_b, "dw_qkvg": dw_qkvg,
                 "dw_bias": dw_bias, "dw_out": dw_out}
+
+    def rows(self, rows, dy):
+        """y and dz at the positions of selected pair rows, in the starting-node frame.
+
+        rows: [(b, j), ...]; every position (b, j, k) of those rows is returned (for the
+        ending block, row j of the transposed pair tensor, i.e. column j of the caller's
+        tensors).  The same lines as forward() and backward(), evaluated at those
+        positions only: the projections of every position (the pair bias and dO need
+        them), the core oracle on the selected attention rows, and the pair-bias
+        gradient entries dbias[b, h, j, :] that reach those positions (sums over every
+        attention row).  Returns {"y": [R, N, C], "dz": [R, N, C]}.
+        """
+        dy = _f64(dy)
+        if self.ending:
+            dy = dy.swapaxes(1, 2)
+        B, N, C, H = self.B, self.N, self.C, self.H
+        zn, mean, rstd, xhat, q, k, v, gpre, bias = self._project()
+        g = sigmoid(gpre)
+        dgo = dy @ self.w_out.T                  # [B, N, N, C], every position
+        do = self._heads(dgo * g)                # dO of every attention row
+        core = _CoreProblem(q, k, v, bias, self.mask, do=do)
+        r = core.rows(rows, grads=True)
+        R = len(rows)
+        o = r["o"].reshape(R, N, C)
+        bi = [b for b, _ in rows]
+        ji = [j for _, j in rows]
+        g_r, dgo_r, dy_r = g[bi, ji], dgo[bi, ji], dy[bi, ji]          # [R, N, C]
+        y = (g_r * o) @ self.w_out
+        dgpre = dgo_r * o * g_r * (1.0 - g_r)
+        dproj = np.concatenate([r["dq"].reshape(R, N, C), r["dk"].reshape(R, N, C),
+                                r["dv"].reshape(R, N, C), dgpre], axis=-1)
+        db = core.dbias([(b, h, j) for b, j in rows for h in range(H)]).reshape(R, H, N)
+        dzn = dproj @ self.w_qkvg.T + db.transpose(0, 2, 1) @ self.w_bias.T
+        dz = layer_norm_backward(dzn, xhat[bi, ji], rstd[bi, ji], self.ln_w)
+        return {"y": y, "dz": dz}

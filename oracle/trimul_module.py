@@ -17,7 +17,9 @@ hidden width equal to C) with a pair mask m [B, N, N] in {0, 1}:
 
 with Wag | Wap | Wbg | Wbp | Wg side by side as w_in [C, 5 C] and Wo as w_out [C, C].
 Everything is fp64 NumPy (the contraction is an einsum over the third node); the
-backward is the chain rule of these lines written out by hand.
+backward is the chain rule of these lines written out by hand.  `TriMulModule.rows`
+evaluates y and dz at the positions of selected pair rows only (outgoing edges), for
+sizes where the whole problem is too slow for a test.
 """
 from __future__ import annotations
 
@@ -104,3 +106,48 @@ class TriMulModule:
         dz = layer_norm_backward(dzn, f["xhat"], f["rstd"], self.ln_in_w)
         return {"dz": dz, "d_ln_in_w": d_ln_in_w, "d_ln_in_b": d_ln_in_b, "dw_in": dw_in,
                 "d_ln_out_w": d_ln_out_w, "d_ln_out_b": d_ln_out_b, "dw_out": dw_out}
+
+    def rows(self, rows, dy):
+        """y and dz at the positions (b, p, k) of selected pair rows [(b, p), ...], outgoing
+        edges.  The same lines as forward() and backward(), evaluated where they reach
+        those positions: a, b and g at every position; x, and from it the output side's
+        gradient dx, along row p (x[p, j] for every j: y at the row, and da[p, k] = sum_j
+        dx[p, j] b[j, k]) and along column p (x[i, p] for every i: db[p, k] = sum_i dx[i, p]
+        a[i, k]).  Returns {"y": [R, N, C], "dz": [R, N, C]}."""
+        assert not self.incoming, "row sampling needs outgoing edges (da of a row needs all of dx otherwise)"
+        dy = _f64(dy)
+        C = self.C
+        zn, mean, rstd, xhat = layer_norm(self.z, self.ln_in_w, self.ln_in_b, self.eps)
+        p = zn @ self.w_in
+        ag, ap, bg, bp, gp = (p[..., i * C:(i + 1) * C] for i in range(5))
+        m = self.m[..., None]
+        sa, sb = sigmoid(ag), sigmoid(bg)
+        a = sa * ap * m
+        b = sb * bp * m
+        g = sigmoid(gp)
+
+        def out_side(x, gg, dd):
+            """y and dx at positions with contraction output x, gate g, upstream dy."""
+            xn, _, xrstd, xxhat = layer_norm(x, self.ln_out_w, self.ln_out_b, self.eps)
+            yp = xn @ self.w_out
+            dxn = (dd * gg) @ self.w_out.T
+            return gg * yp, layer_norm_backward(dxn, xxhat, xrstd, self.ln_out_w), dd * yp * gg * (1.0 - gg)
+
+        ys, dzs = [], []
+        for bb, pr in rows:
+            ab, bbb = a[bb], b[bb]
+            x_row = np.einsum("kc,jkc->jc", ab[pr], bbb)        # x[p, j]
+            x_col = np.einsum("ikc,kc->ic", ab, bbb[pr])        # x[i, p]
+            y_row, dx_row, dgp_row = out_side(x_row, g[bb, pr], dy[bb, pr])
+            _, dx_col, _ = out_side(x_col, g[bb, :, pr], dy[bb, :, pr])
+            da = np.einsum("jc,jkc->kc", dx_row, bbb)           # da[p, k]
+            db = np.einsum("ic,ikc->kc", dx_col, ab)            # db[p, k]
+            mr = m[bb, pr]
+            dap = da * sa[bb, pr] * mr
+            dag = da * ap[bb, pr] * mr * sa[bb, pr] * (1.0 - sa[bb, pr])
+            dbp = db * sb[bb, pr] * mr
+            dbg = db * bp[bb, pr] * mr * sb[bb, pr] * (1.0 - sb[bb, pr])
+            dzn = np.concatenate([dag, dap, dbg, dbp, dgp_row], axis=-1) @ self.w_in.T
+            dzs.append(layer_norm_backward(dzn, xhat[bb, pr], rstd[bb, pr], self.ln_in_w))
+            ys.append(y_row)
+        return {"y": np.stack(ys), "dz": np.stack(dzs)}

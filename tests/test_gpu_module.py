@@ -57,11 +57,11 @@ def run(ta, inp, H, ending, fill=0xFF):
 
 
 def tile_errors(x, ref, floor):
-    """Per (position, 32 channels) tile rel-RMSE of [B, N, N, C] arrays; a tile whose norm
-    is below `floor` times the RMS tile norm is compared against that floor instead."""
-    B, N, _, C = ref.shape
-    x = x.reshape(B * N * N, C // 32, 32)
-    r = ref.reshape(B * N * N, C // 32, 32)
+    """Per (position, 32 channels) tile rel-RMSE of [..., C] position arrays; a tile whose
+    norm is below `floor` times the RMS tile norm is compared against that floor instead."""
+    C = ref.shape[-1]
+    x = x.reshape(-1, C // 32, 32)
+    r = ref.reshape(-1, C // 32, 32)
     num = np.sqrt(((x - r) ** 2).sum(-1))
     den = np.maximum(np.sqrt((r ** 2).sum(-1)), floor * np.sqrt((r ** 2).sum(-1).mean()))
     return num / den
@@ -127,6 +127,23 @@ def test_module_tiny64(ta, ending):
 def test_module_shapes(ta, B, N, H, D, mask, ending):
     inp = si.make_module(B, N, H, D, 3100 + N + H, mask)
     compare(ta, inp, H, ending, f"B{B}N{N}H{H}D{D}{mask}-end{int(ending)}")
+
+
+def test_module_crop768_sampled(ta):
+    """The benchmarked size (module_crop768: B=1, N=768, H=4, D=32, starting node): y and
+    dz at the positions of one pair row in each of the core backward's five row chunks
+    and the last row, against the oracle evaluated at those rows (oracle Module.rows)."""
+    inp = si.make_module_workload("module_crop768")
+    y, saved, dz, grads = run(ta, inp, 4, False)
+    rows = [(0, 0), (0, 154), (0, 383), (0, 500), (0, 616), (0, 767)]
+    say(f"[module] crop768 sampled rows {[j for _, j in rows]}")
+    m = om.Module(inp["z"], inp["mask"], inp["ln_w"], inp["ln_b"], inp["w_qkvg"], inp["w_bias"], inp["w_out"], 4)
+    ref = m.rows(rows, inp["dy"])
+    idx = torch.tensor([j for _, j in rows])
+    got_y = to_np(y[0].index_select(0, idx.to(y.device)))[None]      # [1, R, N, C]
+    got_dz = to_np(dz[0].index_select(0, idx.to(dz.device)))[None]
+    check("y", got_y, ref["y"][None], FWD_REL, "crop768-sampled", tiles=True)
+    check("dz", got_dz, ref["dz"][None], GRAD_REL, "crop768-sampled", tiles=True)
 
 
 def test_module_bitwise_reruns(ta):

@@ -53,7 +53,7 @@ def run(ta, inp, incoming):
 
 
 def tile_errors(x, ref, floor=0.1):
-    B, N, _, C = ref.shape
+    C = ref.shape[-1]
     x, r = x.reshape(-1, C // 32, 32), ref.reshape(-1, C // 32, 32)
     num = np.sqrt(((x - r) ** 2).sum(-1))
     den = np.maximum(np.sqrt((r ** 2).sum(-1)), floor * np.sqrt((r ** 2).sum(-1).mean()))
@@ -99,6 +99,21 @@ def test_trimul_block_tiny64(ta, incoming):
                                                 (1, 256, "pad32", False)])
 def test_trimul_block_shapes(ta, B, N, mask, incoming):
     compare(ta, si.make_trimul_module(B, N, 128, 4100 + N, mask), incoming, f"B{B}N{N}{mask}-in{int(incoming)}")
+
+
+def test_trimul_block_crop768_sampled(ta):
+    """The benchmarked size (trimul_block_crop768: B=1, N=768, C=128, outgoing edges): y
+    and dz at the positions of six pair rows spread over the tiles, against the oracle
+    evaluated at those rows (oracle TriMulModule.rows)."""
+    inp = si.make_trimul_module_workload("trimul_block_crop768")
+    y, saved, dz, grads = run(ta, inp, False)
+    rows = [(0, 0), (0, 127), (0, 128), (0, 383), (0, 640), (0, 767)]
+    say(f"[trimul-block] crop768 sampled rows {[p for _, p in rows]}")
+    m = otm.TriMulModule(inp["z"], inp["mask"], *(inp[n] for n in PARAMS))
+    ref = m.rows(rows, inp["dy"])
+    idx = torch.tensor([p for _, p in rows])
+    check("y", to_np(y[0].index_select(0, idx.to(y.device))), ref["y"], FWD_REL, "crop768-sampled", tiles=True)
+    check("dz", to_np(dz[0].index_select(0, idx.to(dz.device))), ref["dz"], GRAD_REL, "crop768-sampled", tiles=True)
 
 
 def test_trimul_block_bitwise_reruns(ta):

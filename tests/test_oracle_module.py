@@ -187,3 +187,21 @@ def test_planted_mistakes_are_caught(monkeypatch, name):
     grads = m.backward(inp["dy"])
     bad = bad or any(rel(grads[n], g_ref[s]) > 1e-6 for n, s in GRAD_NAMES.items())
     assert bad, name
+
+
+@pytest.mark.parametrize("ending,mask", [(False, "none"), (False, "random"), (True, "pad32"), (True, "random")])
+def test_sampled_rows_match_the_whole_block(ending, mask):
+    """Module.rows (y and dz at selected pair rows) against the whole-problem oracle."""
+    inp = small(B=2, N=12, H=2, D=4, seed=9, mask=mask)
+    m = om.Module(inp["z"], inp["mask"], inp["ln_w"], inp["ln_b"], inp["w_qkvg"], inp["w_bias"], inp["w_out"],
+                  2, ending=ending)
+    f, b = m.forward(), m.backward(inp["dy"])
+    rows = [(0, 0), (1, 5), (0, 11), (1, 7)]
+    r = m.rows(rows, inp["dy"])
+    for i, (bb, j) in enumerate(rows):
+        # row j of the attended frame: positions (b, j, :) of the caller's tensors, or
+        # (b, :, j) for the ending block
+        ref_y = f["y"][bb, :, j] if ending else f["y"][bb, j]
+        ref_dz = b["dz"][bb, :, j] if ending else b["dz"][bb, j]
+        np.testing.assert_allclose(r["y"][i], ref_y, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(r["dz"][i], ref_dz, rtol=1e-9, atol=1e-11)

@@ -170,3 +170,17 @@ def test_planted_mistakes_are_caught(monkeypatch, name):
     bad = bad or any(rel(grads[n], g_ref[s]) > 1e-6 for n, s in GRADS.items())
     assert bad, name
 
+
+
+@pytest.mark.parametrize("mask", ["none", "random"])
+def test_sampled_rows_match_the_whole_block(mask):
+    """TriMulModule.rows (y and dz at selected pair rows, outgoing edges) against the
+    whole-problem oracle."""
+    inp = small(B=2, N=9, C=8, seed=11, mask=mask)
+    o = oracle_of(inp, False)
+    f, bwd = o.forward(), o.backward(inp["dy"])
+    rows = [(0, 0), (1, 4), (0, 8), (1, 2)]
+    r = o.rows(rows, inp["dy"])
+    for i, (bb, p) in enumerate(rows):
+        np.testing.assert_allclose(r["y"][i], f["y"][bb, p], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(r["dz"][i], bwd["dz"][bb, p], rtol=1e-9, atol=1e-11)
