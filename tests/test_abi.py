@@ -202,6 +202,19 @@ def test_workspace_grows_with_problem(lib):
     assert sizes[0] < sizes[1] < sizes[2]
 
 
+def test_workspace_is_about_half_a_bf16_score_gradient(lib):
+    """The backward never holds the score gradient dS (B N^3 H bf16 values, 3.62 GB at
+    crop768): its workspace, dominated by one bf16 dQ partial per 64-key block (N / 64
+    partials of B N^2 H D values), is D / 64 of it plus the per-query statistics and the
+    dbias partials, about 0.52 at N = 768, H = 4, D = 32."""
+    B, N, H, D = 1, 768, 4, 32
+    ws = lib.tri_attn_bwd_workspace_bytes(ctypes.byref(ta.make_problem(B, N, H, D)))
+    ds_bytes = B * N ** 3 * H * 2
+    partials = (N // 64) * B * N * N * H * D * 2
+    assert partials <= ws
+    assert 0.5 < ws / ds_bytes < 0.55, ws / ds_bytes
+
+
 def test_bwd_timed_validates_before_any_hip_call(lib):
     """tri_attn_bwd_timed needs its event array, and otherwise validates exactly as
     tri_attn_bwd (five NULL events: nothing is recorded)."""
