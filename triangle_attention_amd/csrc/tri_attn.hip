@@ -186,7 +186,7 @@ struct Frame {
 // costs one multiply-add, one mixed-precision multiply-add (fp16 bias operand) and
 // the exponential; p is summed in fp32 and packed to bf16 for O^T += V^T P^T.
 // m is never raised during the pass: a probability beyond the fp32 range shows up
-// at the end of the row as a non-finite sum or output, and only then is the row
+// at the end of the row as a non-finite (or huge) sum or output, and only then is the row
 // recomputed against its true maximum (a maximum pass, then the pass again).  A key
 // tile's registers are staged to LDS as soon as they arrive and the next tile's
 // K, V and mask byte are fetched into them while the tile is computed; the key mask
@@ -384,8 +384,11 @@ __global__ __launch_bounds__(FwdShape<DIN>::WAVES * 64) void fwd_kernel(FwdArgs 
     // one tile of the output pass against the reference maxima m[s]; T holds tile kt on
     // entry and tile kt + 1 on return.  CHECK: a query may still have m[s] = -inf (then
     // this tile's maximum is taken); without it every present query has its maximum.
-    auto tile = [&](auto check_tag, int kt, FwdTile<NL> &T, float *m, f32x16 (*oacc)[NC], float *lsum) {
-      constexpr bool CHECK = decltype(check_tag)::value;
+    // FIRST: the row's first tile, which starts the output accumulators (the products
+    // take a zero addend instead of a zeroed register tile).
+    auto tile = [&](auto check_tag, auto first_tag, int kt, FwdTile<NL> &T, float *m, f32x16 (*oacc)[NC],
+                    float *lsum) {
+      constexpr bool CHECK = decltype(check_tag)::value, FIRST = decltype(first_tag)::value;
       const unsigned valid = MASKED ? (unsigned)__ballot(T.m != 0u) : 0xffffffffu;
       if (valid != 0u) {
         stage_k(T);
@@ -393,7 +396,15 @@ __global__ __launch_bounds__(FwdShape<DIN>::WAVES * 64) void fwd_kernel(FwdArgs 
         for (int i = 0; i < NL; ++i) *(u32x4 *)(vbuf + tile_off_w<TD>(vkey + RPL * i, vpart * 8)) = T.v[i];
       }
       fetch(kt + 1, T);
-      if (valid == 0u) return;
+      if (valid == 0u) {
+        if constexpr (FIRST) {
+#pragma unroll
+          for (int s = 0; s < NQ; ++s)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) oacc[s][c] = (f32x16){};
+        }
+        return;
+      }
       bf16x8 vA[NC][2];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
@@ -406,18 +417,28 @@ __global__ __launch_bounds__(FwdShape<DIN>::WAVES * 64) void fwd_kernel(FwdArgs 
         const f32x16 acc = qk(s, valid);
         f16x4 bw[4];
         bias_of(s, kt, bw);
-        float negm = -m[s];
+        float p[16];
         if constexpr (CHECK) {
-          if (__builtin_expect(__ballot(m[s] == -INFINITY) != 0ull, 0)) {  // the first attended tile
-            const float mt = tile_max(acc, bw);
+          // t is formed once; the queries still without a maximum take this tile's
+          float t[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) t[i] = fmaf((float)bw[i >> 2][i & 3], kLog2e, acc[i] * c1);
+          if (__ballot(m[s] == -INFINITY) != 0ull) {
+            float mt = t[0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) mt = fmaxf(mt, t[i]);
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
             if (m[s] == -INFINITY) m[s] = mt;
           }
-          negm = m[s] == -INFINITY ? 0.f : -m[s];  // no finite score yet: every p is 0
-        }
-        float p[16];
+          const float mm = m[s] == -INFINITY ? 0.f : m[s];  // no finite score yet: every p is 0
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          p[i] = __builtin_amdgcn_exp2f(fmaf((float)bw[i >> 2][i & 3], kLog2e, fmaf(acc[i], c1, negm)));
+          for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(t[i] - mm);
+        } else {
+          const float negm = -m[s];
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            p[i] = __builtin_amdgcn_exp2f(fmaf((float)bw[i >> 2][i & 3], kLog2e, fmaf(acc[i], c1, negm)));
+        }
         // the tile's partial sum (in index order), then into the row's
         float ts = p[0];
 #pragma unroll
@@ -426,30 +447,29 @@ __global__ __launch_bounds__(FwdShape<DIN>::WAVES * 64) void fwd_kernel(FwdArgs 
         const bf16x8 pB0 = pack8(p), pB1 = pack8(p + 8);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          oacc[s][c] = mfma(vA[c][0], pB0, oacc[s][c]);
+          oacc[s][c] = mfma(vA[c][0], pB0, FIRST ? (f32x16){} : oacc[s][c]);
           oacc[s][c] = mfma(vA[c][1], pB1, oacc[s][c]);
         }
       }
     };
     // the row's pass; lsum[s] = the sum of p over all keys (both lane halves)
+    // (oacc[1] is left unset when the second query half is absent)
     auto pass = [&](float *m, f32x16 (*oacc)[NC], float *lsum) {
 #pragma unroll
-      for (int s = 0; s < NQ; ++s) {
-        lsum[s] = 0.f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) oacc[s][c] = (f32x16){};
-      }
+      for (int s = 0; s < NQ; ++s) lsum[s] = 0.f;
       FwdTile<NL> T;
       fetch(0, T);
       // tiles with the reference-maximum check until every present query has one (the
-      // first attended tile, normally), then the rest without it
-      int kt = 0;
+      // first attended tile, normally), then the rest without it; N >= 32, so there is
+      // a first tile
+      tile(std::true_type{}, std::true_type{}, 0, T, m, oacc, lsum);
+      int kt = 1;
       for (; kt < nkt; ++kt) {
         const bool unset = m[0] == -INFINITY || (NQ == 2 && two && m[NQ - 1] == -INFINITY);
         if (__ballot(unset) == 0ull) break;
-        tile(std::true_type{}, kt, T, m, oacc, lsum);
+        tile(std::true_type{}, std::false_type{}, kt, T, m, oacc, lsum);
       }
-      for (; kt < nkt; ++kt) tile(std::false_type{}, kt, T, m, oacc, lsum);
+      for (; kt < nkt; ++kt) tile(std::false_type{}, std::false_type{}, kt, T, m, oacc, lsum);
 #pragma unroll
       for (int s = 0; s < NQ; ++s) lsum[s] += __shfl_xor(lsum[s], 32);
     };
@@ -460,10 +480,15 @@ __global__ __launch_bounds__(FwdShape<DIN>::WAVES * 64) void fwd_kernel(FwdArgs 
 #pragma unroll
     for (int s = 0; s < NQ; ++s) m[s] = -INFINITY;
     pass(m, oacc, lsum);
+    // a row is redone against its true maxima when a sum or an accumulator left the
+    // fp32 range, and also when a sum reached 2^64 (far above the key count, which
+    // bounds the sums of the exact pass): the epilogue's hardware reciprocal of a
+    // sum is then well inside the normal range
     bool bad = false;
 #pragma unroll
     for (int s = 0; s < NQ; ++s) {
-      bad = bad || !isfinite(lsum[s]);
+      if (s == 1 && !two) break;
+      bad = bad || !(lsum[s] < 0x1p64f);
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
@@ -510,11 +535,26 @@ __global__ __launch_bounds__(FwdShape<DIN>::WAVES * 64) void fwd_kernel(FwdArgs 
     // a query's row offset within the half: row * sQ < 64 * 2^22 (sQ = N H D at most in
     // the ending orientation), one 24-bit multiply
     const unsigned sq = (unsigned)a.f.sQ;
+    // every lane-dependent address of the epilogue derives from el.  In the masked
+    // kernels the lane index passes through an empty asm first: otherwise the compiler
+    // hoists that address arithmetic out of the row loop, and their tile loop, which
+    // also holds the mask state, runs out of registers and spills.  The unmasked
+    // kernels have the registers to keep those addresses across rows.
+    unsigned el = lane;
+    if constexpr (MASKED) __asm__ volatile("" : "+v"(el));
+    el &= 63u;
+    const int ejl = el & 31, ehh = el >> 5;
+    // the lane's LDS offsets in the accumulator layout: a 16-byte chunk index enters
+    // both offset maps only through an XOR with row bits, on bits of its own, so the
+    // offset of chunk x is the offset of chunk 0 with x's bits XORed in
+    const int ob = o_off(ejl, 0) + 4 * ehh;  // o: chunk 4c + g at ob ^ ((4c + g) << 3)
+    const int rb = r32_off(ejl, ehh);        // fp32 residual: chunk 8c + 2g + hh at rb ^ ((8c + 2g) << 2)
 #pragma unroll
     for (int s = 0; s < NQ; ++s) {
       if (s == 1 && !two) break;
       const long long qbase = base + (long long)(j0 + 32 * s) * a.f.sQ;  // the half's first query
-      float inv = lsum[s] > 0.f ? 1.f / lsum[s] : 0.f;
+      // 1 / l by the hardware reciprocal (1 ulp; l is 0, or from about 1 to 2^64)
+      const float inv = lsum[s] > 0.f ? __builtin_amdgcn_rcpf(lsum[s]) : 0.f;
       unsigned opk[NC][4][2];  // the packed o words, kept for the store after the residual's
 #pragma unroll
       for (int c = 0; c < NC; ++c)
@@ -529,49 +569,58 @@ __global__ __launch_bounds__(FwdShape<DIN>::WAVES * 64) void fwd_kernel(FwdArgs 
           const unsigned p0 = pack_bf16(ov[0], ov[1]), p1 = pack_bf16(ov[2], ov[3]);
           opk[c][g][0] = p0;
           opk[c][g][1] = p1;
-          // channels 32c + 8g + 4hh .. + 3 of query jl; the residual O - float(o) is
+          // channels 32c + 8g + 4hh .. + 3 of the lane's query; the residual O - float(o) is
           // exact in fp32 (and rounded once more, to bf16, for a bf16 residual)
           const f32x4 rv = {ov[0] - bf_lo(p0), ov[1] - bf_hi(p0), ov[2] - bf_lo(p1), ov[3] - bf_hi(p1)};
           if (RES32) {
-            *(f32x4 *)(r32t + r32_off(jl, 8 * c + 2 * g + hh)) = rv;
+            *(f32x4 *)(r32t + (rb ^ ((8 * c + 2 * g) << 2))) = rv;
           } else {
-            *(u32x2 *)(ot + o_off(jl, 4 * c + g) + 4 * hh) = (u32x2){p0, p1};
-            *(u32x2 *)(rt + o_off(jl, 4 * c + g) + 4 * hh) = (u32x2){pack_bf16(rv[0], rv[1]), pack_bf16(rv[2], rv[3])};
+            *(u32x2 *)(ot + (ob ^ ((4 * c + g) << 3))) = (u32x2){p0, p1};
+            *(u32x2 *)(rt + (ob ^ ((4 * c + g) << 3))) = (u32x2){pack_bf16(rv[0], rv[1]), pack_bf16(rv[2], rv[3])};
           }
         }
       if (RES32) {
         // the residual rows (LR lanes per query's 4 TD bytes), then o into the freed
-        // tile.  The lane index passes through an empty asm: otherwise the compiler
-        // hoists these stores' address arithmetic out of the row loop and the tile loop
-        // spills.
+        // tile
         if (a.res) {
-          int ln = lane;
-          __asm__ volatile("" : "+v"(ln));
+          const unsigned ln = el;
+          // the lane's query row within each group of 64 / LR rows and its 16-byte
+          // chunk; its byte offset from the group's first query (< 2^31) is the same
+          // for every group, whose own offset is uniform
+          const int rw = ln / LR, c16 = ln % LR;
+          const unsigned lofs = 4u * (__umul24((unsigned)rw, sq) + 4u * c16);
+          char *const rbase = (char *)((float *)a.res + qbase);
+          // the swizzle of row group k repeats with period PH in k, and the groups are
+          // 256 words apart: the lane's LDS word offset in group k is lb[k % PH] + 256 k
+          constexpr int G = 64 / LR, PH = TD == 32 ? 2 : 4;
+          int lb[PH];
+#pragma unroll
+          for (int ph = 0; ph < PH; ++ph) lb[ph] = r32_off(G * ph + rw, c16) - 256 * ph;
 #pragma unroll
           for (int k = 0; k < LR / 2; ++k) {
-            const int row = (64 / LR) * k + ln / LR, c16 = ln % LR;
-            const long long off = qbase + (long long)(__umul24((unsigned)row, sq) + 4u * c16);
-            if (DIN != 16 || c16 < 4) *(f32x4 *)((float *)a.res + off) = *(const f32x4 *)(r32t + r32_off(row, c16));
+            char *const gbase = rbase + 4ll * G * k * (long long)sq;
+            if (DIN != 16 || c16 < 4) *(f32x4 *)(gbase + lofs) = *(const f32x4 *)(r32t + lb[k % PH] + 256 * k);
           }
         }
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) *(u32x2 *)(ot + o_off(jl, 4 * c + g) + 4 * hh) = (u32x2){opk[c][g][0], opk[c][g][1]};
+          for (int g = 0; g < 4; ++g) *(u32x2 *)(ot + (ob ^ ((4 * c + g) << 3))) = (u32x2){opk[c][g][0], opk[c][g][1]};
       }
 #pragma unroll
       for (int k = 0; k < LO / 2; ++k) {
-        const int row = lane / LO + (64 / LO) * k, chunk = lane % LO;
+        const int row = el / LO + (64 / LO) * k, chunk = el % LO;
         const long long off = qbase + (long long)(__umul24((unsigned)row, sq) + 8u * chunk);
         if (DIN != 16 || chunk < 2) {
           *(u32x4 *)(a.o + off) = *(const u32x4 *)(ot + o_off(row, chunk));
           if (!RES32 && a.res) *(u32x4 *)((uint16_t *)a.res + off) = *(const u32x4 *)(rt + o_off(row, chunk));
         }
       }
-      if (hh == 0) {
-        // lse = ln(sum exp(logit)) = ln 2 * (m + log2(sum p))
-        const float L = lsum[s] > 0.f ? kLn2 * m[s] + logf(lsum[s]) : INFINITY;
-        a.lse[(((long long)b * N + r) * a.H + h) * N + j0 + 32 * s + jl] = L;
+      if (ehh == 0) {
+        // lse = ln(sum exp(logit)) = ln 2 * (m + log2(sum p)), with the hardware
+        // base-2 logarithm (l is 1 or more, up to rounding: it holds the maximum's term)
+        const float L = lsum[s] > 0.f ? kLn2 * (m[s] + __builtin_amdgcn_logf(lsum[s])) : INFINITY;
+        a.lse[(((long long)b * N + r) * a.H + h) * N + j0 + 32 * s + ejl] = L;
       }
     }
     int taken = 0;
