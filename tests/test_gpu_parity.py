@@ -474,13 +474,16 @@ def test_fully_masked_rows_and_keys(ta):
     assert torch.all(out["dk"][0, :, 40:63] == 0) and torch.all(out["dv"][0, :, 40:63] == 0)
 
 
-def test_forward_probability_overflow(ta):
-    """A key tile whose logits exceed the first attended tile's maximum by far more
-    than the fp32 exponent range: the forward's per-row overflow check must catch
-    it and recompute the row against the true maximum."""
+@pytest.mark.parametrize("shift", [30.0, 60.0, 150.0])
+def test_forward_probability_overflow(ta, shift):
+    """A key tile whose logits exceed the first attended tile's maximum: by 30 the
+    row's probability sum stays below 2^64 and the pass stands (its reciprocal taken
+    at about 2^48); by 60 the sum is finite but above 2^64, and by 150 it leaves the
+    fp32 range: in both the forward's per-row check must catch the row and recompute
+    it against the true maximum."""
     inp = custom(1, 96, 2, 17, "none")
-    inp["bias"][:, :, :, 64:] += 150.0   # keys 64..95: logits about 150 above the rest
-    out, ref = check_full(ta, inp, tag="overflow")
+    inp["bias"][:, :, :, 64:] += shift   # keys 64..95: logits about `shift` above the rest
+    out, ref = check_full(ta, inp, tag=f"overflow{shift:g}")
     assert torch.isfinite(out["o"].float()).all() and torch.isfinite(out["lse"]).all()
 
 
