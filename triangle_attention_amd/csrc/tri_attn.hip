@@ -72,6 +72,15 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ u32x4 ld16(const uint16_t *p) { return *(const u32x4 *)p; }
+// Store of an output written in whole 128-byte lines that no kernel of the call reads
+// back soon (o's fp32 residual, lse, dQ and its partials), marked non-temporal: such
+// lines then do not push out of L2 the k, v, q and dO lines that the workgroups of one
+// row chunk share.  Outputs of which a workgroup writes half lines (o, a bf16 residual,
+// dK and dV: 64 bytes of a head, the other half from the other head's workgroup) are
+// stored normally, so that the halves meet in L2 (non-temporal, those stores made the
+// backward main kernel slower).
+template <class T>
+__device__ __forceinline__ void st_nt(T *p, T v) { __builtin_nontemporal_store(v, p); }
 __device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 // round-to-nearest-even pack of two floats (v_cvt_pk_bf16_f32)
@@ -599,7 +608,13 @@ __global__ __launch_bounds__(FwdShape<DIN>::WAVES * 64) void fwd_kernel(FwdArgs 
 #pragma unroll
           for (int k = 0; k < LR / 2; ++k) {
             char *const gbase = rbase + 4ll * G * k * (long long)sq;
-            if (DIN != 16 || c16 < 4) *(f32x4 *)(gbase + lofs) = *(const f32x4 *)(r32t + lb[k % PH] + 256 * k);
+            // whole lines of a head's 4 D bytes except at D = 16 (64 bytes)
+            const f32x4 rv = *(const f32x4 *)(r32t + lb[k % PH] + 256 * k);
+            if constexpr (DIN == 16) {
+              if (c16 < 4) *(f32x4 *)(gbase + lofs) = rv;
+            } else {
+              st_nt((f32x4 *)(gbase + lofs), rv);
+            }
           }
         }
 #pragma unroll
@@ -620,7 +635,7 @@ __global__ __launch_bounds__(FwdShape<DIN>::WAVES * 64) void fwd_kernel(FwdArgs 
         // lse = ln(sum exp(logit)) = ln 2 * (m + log2(sum p)), with the hardware
         // base-2 logarithm (l is 1 or more, up to rounding: it holds the maximum's term)
         const float L = lsum[s] > 0.f ? kLn2 * (m[s] + __builtin_amdgcn_logf(lsum[s])) : INFINITY;
-        a.lse[(((long long)b * N + r) * a.H + h) * N + j0 + 32 * s + ejl] = L;
+        st_nt(a.lse + (((long long)b * N + r) * a.H + h) * N + j0 + 32 * s + ejl, L);
       }
     }
     int taken = 0;
@@ -1080,8 +1095,8 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
             w[g][e] = sw[0];
             w[g + 1][e] = sw[1];
           }
-        *(u32x4 *)qout = (u32x4){w[0][0], w[0][1], w[1][0], w[1][1]};
-        if constexpr (DIN == 32) *(u32x4 *)(qout + 16) = (u32x4){w[2][0], w[2][1], w[3][0], w[3][1]};
+        st_nt((u32x4 *)qout, (u32x4){w[0][0], w[0][1], w[1][0], w[1][1]});
+        if constexpr (DIN == 32) st_nt((u32x4 *)(qout + 16), (u32x4){w[2][0], w[2][1], w[3][0], w[3][1]});
       }
     }
 
@@ -1400,8 +1415,8 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main64_kernel(BwdArgs a
             w[g][e] = sw[0];
             w[g + 1][e] = sw[1];
           }
-        *(u32x4 *)(qout + 32 * c) = (u32x4){w[0][0], w[0][1], w[1][0], w[1][1]};
-        *(u32x4 *)(qout + 32 * c + 16) = (u32x4){w[2][0], w[2][1], w[3][0], w[3][1]};
+        st_nt((u32x4 *)(qout + 32 * c), (u32x4){w[0][0], w[0][1], w[1][0], w[1][1]});
+        st_nt((u32x4 *)(qout + 32 * c + 16), (u32x4){w[2][0], w[2][1], w[3][0], w[3][1]});
       }
     }
 
@@ -1501,8 +1516,8 @@ __global__ __launch_bounds__(256) void reduce_dq_kernel(ReduceArgs a) {
     }
   }
   const long long off = (long long)b * a.f.sB + (long long)r * a.f.sR + (long long)q * a.f.sQ + h * a.D + c;
-  *(u32x4 *)(a.dq + off) = (u32x4){pack_bf16(s[0] * a.alpha, s[1] * a.alpha), pack_bf16(s[2] * a.alpha, s[3] * a.alpha),
-                                   pack_bf16(s[4] * a.alpha, s[5] * a.alpha), pack_bf16(s[6] * a.alpha, s[7] * a.alpha)};
+  st_nt((u32x4 *)(a.dq + off), (u32x4){pack_bf16(s[0] * a.alpha, s[1] * a.alpha), pack_bf16(s[2] * a.alpha, s[3] * a.alpha),
+                                      pack_bf16(s[4] * a.alpha, s[5] * a.alpha), pack_bf16(s[6] * a.alpha, s[7] * a.alpha)});
 }
 
 __global__ __launch_bounds__(256) void reduce_dbias_kernel(ReduceArgs a) {
