@@ -1095,8 +1095,26 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main_kernel(BwdArgs a) 
             w[g][e] = sw[0];
             w[g + 1][e] = sw[1];
           }
-        st_nt((u32x4 *)qout, (u32x4){w[0][0], w[0][1], w[1][0], w[1][1]});
-        if constexpr (DIN == 32) st_nt((u32x4 *)(qout + 16), (u32x4){w[2][0], w[2][1], w[3][0], w[3][1]});
+        u32x4 lo = {w[0][0], w[0][1], w[1][0], w[1][1]}, hi = {w[2][0], w[2][1], w[3][0], w[3][1]};
+        if constexpr (DIN == 32) {
+          // whole 128-byte lines per store: lanes l and l + 16 of each half trade runs, so
+          // that the first store writes queries 0..15 of the tile (all four 16-byte runs
+          // of each) and the second queries 16..31.  After the trade, the lanes of
+          // queries 0..15 hold the first run of their own query and of the query 16
+          // above, the lanes of queries 16..31 the second run of the query 16 below and
+          // of their own.
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const auto sw = __builtin_amdgcn_permlane16_swap(lo[k], hi[k], false, false);
+            lo[k] = sw[0];
+            hi[k] = sw[1];
+          }
+          uint16_t *q16 = qout + (16 * (ll >> 4)) * (1 - DIN);  // query ll % 16, run 2 (ll / 16) + hh
+          st_nt((u32x4 *)q16, lo);
+          st_nt((u32x4 *)(q16 + 16 * DIN), hi);
+        } else {
+          st_nt((u32x4 *)qout, lo);
+        }
       }
     }
 
