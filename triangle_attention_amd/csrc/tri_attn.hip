@@ -1328,6 +1328,7 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main64_kernel(BwdArgs a
     load_kv(rn, nk, nv);
     load_mask(rn, nm);
     const long long base = rowbase(r);
+    uint16_t *dq_row = dq_part + (((long long)b * N + r) * a.H + h) * N * TD;  // this row's partial
 
     f32x16 dK[2], dV[2];  // 32-channel halves
 #pragma unroll
@@ -1412,9 +1413,13 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main64_kernel(BwdArgs a
         *(u32x2 *)(wds + tile_off(ll, 24 + 4 * hh)) = (u32x2){s1[2], s1[3]};
       }
       // dQ^T over the block's 32 keys, per channel half, rounded to bf16 as this key
-      // block's partial (stored as in the 32-channel kernel, see there)
+      // block's partial.  A query's 64-channel partial is one 128-byte line; the lanes
+      // hold it in 16-byte runs (lane l < 32: runs 0 and 2 of each channel half of query
+      // l after the lane halves trade channel groups, lane l + 32: runs 1 and 3), so the
+      // runs go through the wave's q tile (free until the next tile is staged), 16-byte
+      // chunks permuted by query (chunk ^ query % 8) against bank conflicts, and leave as
+      // whole lines: each store writes eight queries' partials.
       const bf16x8 dsB0 = tr_operand_sw(wds, 0, lane), dsB1 = tr_operand_sw(wds, 16, lane);
-      uint16_t *qout = dq_part + ((((long long)b * N + r) * a.H + h) * N + j0 + ll) * TD + 8 * hh;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         f32x16 dqT = mfma(tr_operand_w<TD>(s_k, 0, lane, 32 * c), dsB0, (f32x16){});
@@ -1433,8 +1438,16 @@ __global__ __launch_bounds__(BWD_WAVES * 64, 1) void bwd_main64_kernel(BwdArgs a
             w[g][e] = sw[0];
             w[g + 1][e] = sw[1];
           }
-        st_nt((u32x4 *)(qout + 32 * c), (u32x4){w[0][0], w[0][1], w[1][0], w[1][1]});
-        st_nt((u32x4 *)(qout + 32 * c + 16), (u32x4){w[2][0], w[2][1], w[3][0], w[3][1]});
+        const int rlo = 4 * c + hh, rhi = 4 * c + 2 + hh;
+        *(u32x4 *)(wq + ll * TD + ((rlo ^ (ll & 7)) << 3)) = (u32x4){w[0][0], w[0][1], w[1][0], w[1][1]};
+        *(u32x4 *)(wq + ll * TD + ((rhi ^ (ll & 7)) << 3)) = (u32x4){w[2][0], w[2][1], w[3][0], w[3][1]};
+      }
+#pragma unroll
+      for (int sq = 0; sq < 4; ++sq) {
+        // store sq: queries 8 sq .. 8 sq + 7, lane L writing run L % 8 of query 8 sq + L / 8
+        const int jq = 8 * sq + (lane >> 3), run = lane & 7;
+        const u32x4 v = *(const u32x4 *)(wq + jq * TD + ((run ^ (jq & 7)) << 3));
+        st_nt((u32x4 *)(dq_row + (long long)(j0 + jq) * TD + run * 8), v);
       }
     }
 
