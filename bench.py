@@ -139,9 +139,19 @@ def algorithmic_bytes(B: int, N: int, H: int, D: int, masked: bool, residual_byt
 
 
 def row_chunks(groups: int, N: int, cus: int = 256) -> int:
-    """Row chunks per (batch, head, block) in the library's launch plan: one round of
-    workgroups over the MI355X's 256 compute units (at least one chunk, at most N)."""
-    c = max(1, min(N, cus // groups))
+    """Row chunks per (batch, head, block) in the library's launch plan (one workgroup
+    per CU at a time): one round of workgroups over the MI355X's 256 compute units, or,
+    where one round would leave more than 15 % of them idle, the chunk count that
+    minimises rows per CU plus two rows per round (at least one chunk, at most N)."""
+    one = max(1, min(N, cus // groups))
+    c = one
+    if groups * one * 100 < cus * 85 and groups < cus:
+        best_cost = None
+        for C in range(one, min(N, 16 * one) + 1):
+            rounds = -(-groups * C // cus)
+            cost = rounds * -(-N // C) + 2 * rounds
+            if best_cost is None or cost < best_cost:
+                best_cost, c = cost, C
     per = -(-N // c)
     return -(-N // per)
 

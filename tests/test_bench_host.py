@@ -53,6 +53,9 @@ def test_row_chunks_follow_one_round_of_workgroups():
     assert bench.row_chunks(16, 64) == 16
     assert bench.row_chunks(2, 96) == 96      # never more chunks than rows
     assert bench.row_chunks(40, 640) == 6     # 107 rows per chunk: 6 chunks cover 640
+    # 8 heads at D = 16: 96 groups; one round (2 chunks) would leave 64 of 256 CUs idle,
+    # so three full rounds of 8 chunks of 96 rows
+    assert bench.row_chunks(96, 768) == 8
 
 
 def test_bias_dbias_bytes_at_crop768():

@@ -1594,6 +1594,31 @@ int device_cus() {
   return cus;
 }
 
+// Row chunks per (batch, head, block) group of a launch whose workgroups take a CU
+// each (their LDS and registers fill one): G groups of C chunks run in
+// ceil(G C / cus) rounds of ceil(R / C) rows.  One round (C = cus / G) keeps a chunk's
+// workgroups, which share their rows' q, k, v and dO lines in L2, running together;
+// only where one round would leave more than 15 % of the CUs idle (8 heads at head
+// dimension 16: 192 of 256) are more rounds taken, with C minimising rows per CU plus
+// two rows per round for restaging the block's bias.
+int row_chunks(int groups, int R, int cus) {
+  int one = cus / groups;
+  if (one < 1) one = 1;
+  if (one > R) one = R;
+  if (groups * one * 100 >= cus * 85 || groups >= cus) return one;
+  int best = one;
+  long long best_cost = 1LL << 62;
+  for (int C = one; C <= R && C <= 16 * one; ++C) {
+    const long long rounds = ((long long)groups * C + cus - 1) / cus;
+    const long long cost = rounds * ((R + C - 1) / C) + 2 * rounds;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = C;
+    }
+  }
+  return best;
+}
+
 // forward kernels (bit per variant, per device) whose dynamic LDS limit is raised
 std::atomic<unsigned> g_fwd_lds_set[kMaxDevices];
 // the forward's largest dynamic LDS: the fp16 bias block at the widest row stride
@@ -1692,9 +1717,7 @@ BwdPlan plan_bwd(const tri_attn_problem *p, int cus) {
   row_range(p, i0, i1);
   const int R = i1 - i0;
   const int groups = (int)(p->B * p->H * pl.T);
-  int C = cus / groups;
-  if (C < 1) C = 1;
-  if (C > R) C = R;
+  const int C = row_chunks(groups, R, cus);
   pl.rows_per_chunk = (R + C - 1) / C;
   pl.C = (R + pl.rows_per_chunk - 1) / pl.rows_per_chunk;
   pl.lds_bytes = 0;  // static LDS, sized by the JT instantiation
@@ -1809,9 +1832,7 @@ tri_attn_status tri_attn_fwd(const tri_attn_problem *problem, const void *q, con
   row_range(problem, a.row_begin, a.row_end);
   const int R = a.row_end - a.row_begin;
   const int groups = a.B * a.H * a.n_jblocks;
-  int chunks = device_cus() / groups;
-  if (chunks < 1) chunks = 1;
-  if (chunks > R) chunks = R;
+  const int chunks = row_chunks(groups, R, device_cus());
   a.rows_per_chunk = (R + chunks - 1) / chunks;
   a.n_chunks = (R + a.rows_per_chunk - 1) / a.rows_per_chunk;
   const size_t lds = p.D == 64 ? FwdShape<64>::lds_bytes(a.bstride) : FwdShape<32>::lds_bytes(a.bstride);
